@@ -1,0 +1,198 @@
+"""TEST INFRASTRUCTURE ONLY -- Python face of the CPU oracle (qlora_oracle.c).
+
+A thin ctypes wrapper over the plain C oracle plus numpy marshalling.  It
+holds no arithmetic of its own beyond unit conversions (BF16 bit patterns to
+FP32 values).  See qlora_oracle.c for the statement of each step and its
+source on the pages ("第 04 篇：QLoRA 原理", cited [QP §x]; the compassingai
+"QLoRA" concept page, cited [CP]).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+use this module.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qlora_oracle.c")
+_LIB = os.path.join(_HERE, "libqlora_oracle.so")
+
+BLOCK = 64    # first-level block [QP §3.4]
+GROUP = 256   # second-level block [QP §5.2]
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.orc_codebook.argtypes = [P]
+        lib.orc_nf4_index.argtypes = [ctypes.c_float]
+        lib.orc_nf4_index.restype = ctypes.c_uint8
+        lib.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+        lib.orc_fp8_decode.restype = ctypes.c_float
+        lib.orc_fp8_encode.argtypes = [ctypes.c_float]
+        lib.orc_fp8_encode.restype = ctypes.c_uint8
+        lib.orc_bf16_rne.argtypes = [ctypes.c_float]
+        lib.orc_bf16_rne.restype = ctypes.c_uint16
+        lib.orc_scale_mean.argtypes = [P, I]
+        lib.orc_scale_mean.restype = ctypes.c_float
+        lib.orc_quantize_nf4.argtypes = [P, I, P, P, P, P, P]
+        lib.orc_restored_scale.argtypes = [P, P, ctypes.c_float, I]
+        lib.orc_restored_scale.restype = ctypes.c_float
+        lib.orc_dequant_bf16.argtypes = [P, P, P, ctypes.c_float, I, P]
+        lib.orc_linear_fwd_rows.argtypes = [P, P, P, P, I, I, I, ctypes.c_double, P, I, P]
+        lib.orc_linear_bwd.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, I, P, P, P]
+        lib.orc_map_nf4_index.argtypes = [P, I, P]
+        lib.orc_map_fp8_encode.argtypes = [P, I, P]
+        lib.orc_map_bf16_rne.argtypes = [P, I, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- scalars
+
+def codebook() -> np.ndarray:
+    out = np.zeros(16, np.float32)
+    _load().orc_codebook(_ptr(out))
+    return out
+
+
+def nf4_index(x: np.ndarray) -> np.ndarray:
+    """Nearest-level index of each FP32 value (ties to the lower index)."""
+    x = _c(x, np.float32).ravel()
+    out = np.empty(x.size, np.uint8)
+    _load().orc_map_nf4_index(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def fp8_decode(code: int) -> float:
+    return float(_load().orc_fp8_decode(int(code)))
+
+
+def fp8_encode(y: np.ndarray) -> np.ndarray:
+    y = _c(y, np.float32).ravel()
+    out = np.empty(y.size, np.uint8)
+    _load().orc_map_fp8_encode(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """RNE to BF16; returns the uint16 bit patterns."""
+    x = _c(x, np.float32).ravel()
+    out = np.empty(x.size, np.uint16)
+    _load().orc_map_bf16_rne(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------- quantization
+
+def scale_mean(absmax: np.ndarray) -> float:
+    a = _c(absmax, np.float32)
+    return float(_load().orc_scale_mean(_ptr(a), a.size))
+
+
+def quantize_nf4(W: np.ndarray, return_absmax: bool = False):
+    """NF4 + double quantization of an FP32 matrix (row-major flatten).
+
+    Returns (codes uint8[n/2], scale_codes uint8[n/64], s2 float32[G], mean)."""
+    W = _c(W, np.float32)
+    n = W.size
+    assert n % BLOCK == 0
+    n1 = n // BLOCK
+    G = (n1 + GROUP - 1) // GROUP
+    codes = np.empty(n // 2, np.uint8)
+    scodes = np.empty(n1, np.uint8)
+    s2 = np.empty(G, np.float32)
+    mean = np.zeros(1, np.float32)
+    absmax = np.empty(n1, np.float32)
+    _load().orc_quantize_nf4(_ptr(W), n, _ptr(codes), _ptr(scodes), _ptr(s2),
+                             _ptr(mean), _ptr(absmax))
+    out = (codes, scodes, s2, float(mean[0]))
+    return out + (absmax,) if return_absmax else out
+
+
+def restored_scales(scodes: np.ndarray, s2: np.ndarray, mean: float) -> np.ndarray:
+    lib = _load()
+    sc = _c(scodes, np.uint8)
+    s2 = _c(s2, np.float32)
+    return np.array([lib.orc_restored_scale(_ptr(sc), _ptr(s2), mean, b)
+                     for b in range(sc.size)], np.float32)
+
+
+def dequant_bf16(codes, scodes, s2, mean: float, n: int) -> np.ndarray:
+    """Restored weights as BF16 bit patterns, uint16[n]."""
+    codes = _c(codes, np.uint8)
+    scodes = _c(scodes, np.uint8)
+    s2 = _c(s2, np.float32)
+    out = np.empty(n, np.uint16)
+    _load().orc_dequant_bf16(_ptr(codes), _ptr(scodes), _ptr(s2), float(mean), n, _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------- LoRA linear
+
+def linear_fwd(Wh, X, A, B, s: float, rows=None) -> np.ndarray:
+    """Y[rows] = X[rows] Wh^T + s (X[rows] A^T) B^T in FP64.
+
+    Wh [d_out, d_in], X [M, d_in], A [r, d_in], B [d_out, r]: FP32 arrays of
+    exact values.  rows defaults to every token row."""
+    Wh, X, A, B = (_c(t, np.float32) for t in (Wh, X, A, B))
+    d_out, d_in = Wh.shape
+    r = A.shape[0]
+    M = X.shape[0]
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    Y = np.zeros((rows.size, d_out), np.float64)
+    _load().orc_linear_fwd_rows(_ptr(Wh), _ptr(X), _ptr(A), _ptr(B), d_out, d_in, r,
+                                float(s), _ptr(rows), rows.size, _ptr(Y))
+    return Y
+
+
+def linear_bwd(Wh, X, dY, A, B, s: float, rows=None, want_dx=True, want_da=True,
+               want_db=True):
+    """(dX[rows], dA, dB) in FP64 for upstream gradient dY; no dW exists."""
+    Wh, X, dY, A, B = (_c(t, np.float32) for t in (Wh, X, dY, A, B))
+    d_out, d_in = Wh.shape
+    r = A.shape[0]
+    M = X.shape[0]
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    dX = np.zeros((rows.size, d_in), np.float64) if want_dx else None
+    dA = np.zeros((r, d_in), np.float64) if want_da else None
+    dB = np.zeros((d_out, r), np.float64) if want_db else None
+    nul = ctypes.c_void_p(0)
+    _load().orc_linear_bwd(_ptr(Wh), _ptr(X), _ptr(dY), _ptr(A), _ptr(B), M, d_out, d_in, r,
+                           float(s), _ptr(rows), rows.size,
+                           _ptr(dX) if want_dx else nul, _ptr(dA) if want_da else nul,
+                           _ptr(dB) if want_db else nul)
+    return dX, dA, dB

@@ -1,0 +1,367 @@
+/*
+ * qlora_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU statement of what the QLoRA
+ * frozen-base LoRA linear layer computes: NF4 blockwise quantization with
+ * double quantization of the block scales, double dequantization to BF16,
+ * and the LoRA linear forward and backward.  Only the test suite, the smoke
+ * check and the CPU-baseline leg of the benchmark may load this file's
+ * library.  It shares no code, header, table or constant with the HIP
+ * library; the two meet only at the seeded inputs that the tests hand to
+ * both.
+ *
+ * Sources (the pages): "第 04 篇：QLoRA 原理" (jupiter-lab, QLoRA principles),
+ * cited as [QP §x.y], and "QLoRA" (compassingai concept page, "NF4 量化機制詳解"
+ * and "雙重量化"), cited as [CP, <heading>].
+ *
+ * Every floating-point decision that fixes an integer (an NF4 index, an FP8
+ * code, a BF16 pattern) is taken by exact comparison of distances, not by
+ * bit tricks, so that a reader can check each against its definition.
+ * Matrix products accumulate in FP64 over exactly-represented inputs.
+ *
+ * Readings where the pages are silent (each listed in the design doc):
+ *   - flatten order is row-major over W[d_out, d_in]; blocks of 64 follow it;
+ *   - x = w / absmax is an IEEE FP32 division; a zero block maps to index 7;
+ *   - nearest-level ties go to the lower index;
+ *   - element 2j is the low nibble of byte j;
+ *   - the scale mean is one FP32 value per tensor, summed in FP64 by a fixed
+ *     stride-halving tree (per 256-group, then over the groups);
+ *   - "symmetric 8-bit" second-level quantization is OCP FP8 E4M3FN with the
+ *     group's largest |centred scale| mapped to 448, round-to-nearest-even,
+ *     saturating; an all-zero group stores code 0;
+ *   - restored scale = fp8(code) * s2 + mean (FP32, two roundings, no FMA);
+ *     restored weight = RNE_bf16(codebook[idx] * restored scale) (FP32 product).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_BLOCK 64   /* first-level block size B1   [QP §3.4, §5.1] */
+#define ORC_GROUP 256  /* second-level block size B2  [QP §5.2]; [CP, 雙重量化] */
+
+/* ------------------------------------------------------------------------
+ * NF4 codebook: the 16 values printed in [QP §4.3] (the bitsandbytes table
+ * quoted there), parsed as FP32 by the C library.
+ * ---------------------------------------------------------------------- */
+static const char *const ORC_NF4_TEXT[16] = {
+    "-1.0000000", "-0.6961928", "-0.5250731", "-0.3949175",
+    "-0.2844414", "-0.1847734", "-0.0910500", "0.0000000",
+    "0.0795803",  "0.1609302",  "0.2461123",  "0.3379152",
+    "0.4407098",  "0.5626170",  "0.7229568",  "1.0000000"};
+
+static float ORC_NF4[16];
+
+__attribute__((constructor)) static void orc_parse_codebook(void) {
+  for (int i = 0; i < 16; ++i) ORC_NF4[i] = strtof(ORC_NF4_TEXT[i], NULL);
+}
+
+void orc_codebook(float out[16]) {
+  for (int i = 0; i < 16; ++i) out[i] = ORC_NF4[i];
+}
+
+/* Nearest NF4 level to x (x is a normalized weight in [-1, 1]):
+ * argmin_i |x - c_i|, the first (lowest) index on a tie.  [CP, NF4 量化機制詳解
+ * step 3: map the normalized value to the nearest NF4 level.]  The distances
+ * are FP64 differences of two FP32 values; wherever two distances are close
+ * enough to compete, x and the levels are of similar magnitude and the
+ * differences are exact. */
+uint8_t orc_nf4_index(float x) {
+  const float *c = ORC_NF4;
+  int best = 0;
+  double bestd = fabs((double)x - (double)c[0]);
+  for (int i = 1; i < 16; ++i) {
+    double d = fabs((double)x - (double)c[i]);
+    if (d < bestd) { bestd = d; best = i; }
+  }
+  return (uint8_t)best;
+}
+
+/* ------------------------------------------------------------------------
+ * FP8 E4M3FN (OCP 8-bit floating point, "FN" = finite + NaN, no infinities):
+ * sign bit, 4 exponent bits with bias 7, 3 mantissa bits.  Exponent field 0
+ * holds subnormals m * 2^-9; S.1111.111 is NaN; the largest finite is 448.
+ * ---------------------------------------------------------------------- */
+float orc_fp8_decode(uint8_t code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) mag = ldexp((double)m, -9);
+  else mag = ldexp(1.0 + m / 8.0, e - 7);
+  return (float)(s ? -mag : mag);
+}
+
+/* Encode y as the nearest of the 127 non-negative finite E4M3FN magnitudes
+ * (codes 0x00..0x7E, increasing), ties to the even code, |y| beyond 448
+ * clamped to 448, sign bit = sign bit of y.  Never produces NaN. */
+uint8_t orc_fp8_encode(float y) {
+  double a = fabs((double)y);
+  int best = 0x7E;                 /* |y| >= 448: the largest finite, 448 */
+  double bestd = INFINITY;
+  for (int code = 0; code <= 0x7E && a < 448.0; ++code) {
+    double v = (double)orc_fp8_decode((uint8_t)code);
+    double d = fabs(a - v);
+    if (d < bestd || (d == bestd && (code & 1) == 0 && (best & 1) == 1)) {
+      bestd = d;
+      best = code;
+    }
+  }
+  return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* ------------------------------------------------------------------------
+ * BF16: the upper 16 bits of an FP32 pattern.  Round-to-nearest-even is
+ * written out as: the two BF16 neighbours of x (toward zero and away from
+ * zero), the closer one wins, a tie goes to the even mantissa.
+ * ---------------------------------------------------------------------- */
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+float orc_bf16_to_float(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+static double bf16_pattern_value(uint32_t hi16) {
+  /* magnitude of a non-negative BF16 pattern; the pattern just past the
+   * largest finite value stands for 2^128 when measuring distances. */
+  if ((hi16 & 0x7FFF) == 0x7F80) return ldexp(1.0, 128);
+  return (double)orc_bf16_to_float((uint16_t)hi16);
+}
+
+uint16_t orc_bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040);
+  if (isinf(x)) return (uint16_t)(u >> 16);
+  uint32_t sign = u & 0x80000000u, mag = u & 0x7FFFFFFFu;
+  uint32_t lo = mag >> 16;      /* neighbour toward zero  */
+  uint32_t hi = lo + 1;          /* neighbour away from zero */
+  double ax = (double)u2f(mag);
+  double dlo = ax - bf16_pattern_value(lo);
+  double dhi = bf16_pattern_value(hi) - ax;
+  uint32_t pick;
+  if (dlo < dhi) pick = lo;
+  else if (dhi < dlo) pick = hi;
+  else pick = (lo & 1) ? hi : lo;
+  return (uint16_t)((sign >> 16) | pick);
+}
+
+/* ------------------------------------------------------------------------
+ * Quantization [QP §3.4, §4.3, §5.2, §6.1]; [CP, NF4 量化機制詳解; 雙重量化]
+ *
+ * W is n = d_out*d_in FP32 values flattened row-major; n % 64 == 0.
+ * Outputs: codes[n/2] (two 4-bit indices per byte, element 2j low nibble,
+ * [QP §2.1]), scale_codes[n/64] (FP8 E4M3FN), s2[ceil(n1/256)] (FP32
+ * second-level scales), *mean (FP32 offset subtracted before the second
+ * level).  absmax_out (optional) receives the FP32 first-level absmax.
+ * ---------------------------------------------------------------------- */
+
+/* Stride-halving FP64 tree over v[0..len), len a power of two:
+ * v[j] += v[j + half] for half = len/2, len/4, ..., 1.  Returns v[0]. */
+static double tree_sum(double *v, int64_t len) {
+  for (int64_t half = len / 2; half >= 1; half /= 2)
+    for (int64_t j = 0; j < half; ++j) v[j] = v[j] + v[j + half];
+  return v[0];
+}
+
+float orc_scale_mean(const float *absmax, int64_t n1) {
+  int64_t G = (n1 + ORC_GROUP - 1) / ORC_GROUP;
+  int64_t Gp = 1;
+  while (Gp < G) Gp *= 2;
+  double *part = (double *)calloc((size_t)Gp, sizeof(double));
+  double grp[ORC_GROUP];
+  for (int64_t g = 0; g < G; ++g) {
+    for (int j = 0; j < ORC_GROUP; ++j) {
+      int64_t b = g * ORC_GROUP + j;
+      grp[j] = (b < n1) ? (double)absmax[b] : 0.0;
+    }
+    part[g] = tree_sum(grp, ORC_GROUP);
+  }
+  double S = tree_sum(part, Gp);
+  free(part);
+  return (float)(S / (double)n1);
+}
+
+void orc_quantize_nf4(const float *W, int64_t n, uint8_t *codes,
+                      uint8_t *scale_codes, float *s2, float *mean,
+                      float *absmax_out) {
+  int64_t n1 = n / ORC_BLOCK;
+  int64_t G = (n1 + ORC_GROUP - 1) / ORC_GROUP;
+  float *a = (float *)malloc((size_t)n1 * sizeof(float));
+
+  /* First level: absmax per block of 64, normalize, nearest level, pack. */
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < n1; ++b) {
+    const float *w = W + b * ORC_BLOCK;
+    float m = 0.0f;
+    for (int j = 0; j < ORC_BLOCK; ++j) {
+      float v = fabsf(w[j]);
+      if (v > m) m = v;
+    }
+    a[b] = m;
+    uint8_t idx[ORC_BLOCK];
+    for (int j = 0; j < ORC_BLOCK; ++j) {
+      float x = (m == 0.0f) ? 0.0f : w[j] / m;
+      idx[j] = orc_nf4_index(x);
+    }
+    for (int j = 0; j < ORC_BLOCK / 2; ++j)
+      codes[b * (ORC_BLOCK / 2) + j] =
+          (uint8_t)(idx[2 * j] | (idx[2 * j + 1] << 4));
+  }
+  if (absmax_out) memcpy(absmax_out, a, (size_t)n1 * sizeof(float));
+
+  /* Second level: subtract the mean, then per group of 256 an FP32 scale
+   * s2 = max|centred| / 448 and FP8 codes of centred / s2. */
+  float mu = orc_scale_mean(a, n1);
+  *mean = mu;
+  for (int64_t g = 0; g < G; ++g) {
+    int64_t b0 = g * ORC_GROUP, b1 = b0 + ORC_GROUP;
+    if (b1 > n1) b1 = n1;
+    float mg = 0.0f;
+    for (int64_t b = b0; b < b1; ++b) {
+      float d = fabsf(a[b] - mu);
+      if (d > mg) mg = d;
+    }
+    float sc = mg / 448.0f;
+    s2[g] = sc;
+    for (int64_t b = b0; b < b1; ++b) {
+      float d = a[b] - mu;
+      scale_codes[b] = (sc == 0.0f) ? (uint8_t)0 : orc_fp8_encode(d / sc);
+    }
+  }
+  free(a);
+}
+
+/* Restored first-level scale of block b [QP §5.2 restore order; §6.1]. */
+float orc_restored_scale(const uint8_t *scale_codes, const float *s2,
+                         float mean, int64_t b) {
+  volatile float p = orc_fp8_decode(scale_codes[b]) * s2[b / ORC_GROUP];
+  return p + mean;
+}
+
+/* Double dequantization to BF16 [QP §2.3, §6.1]: restored weight of element
+ * e is RNE_bf16(codebook[idx_e] * restored_scale(block of e)). */
+void orc_dequant_bf16(const uint8_t *codes, const uint8_t *scale_codes,
+                      const float *s2, float mean, int64_t n, uint16_t *out) {
+  float c[16];
+  orc_codebook(c);
+  int64_t n1 = n / ORC_BLOCK;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < n1; ++b) {
+    float ah = orc_restored_scale(scale_codes, s2, mean, b);
+    for (int j = 0; j < ORC_BLOCK; ++j) {
+      int64_t e = b * ORC_BLOCK + j;
+      uint8_t byte = codes[e / 2];
+      int idx = (e % 2 == 0) ? (byte & 15) : (byte >> 4);
+      volatile float prod = c[idx] * ah;
+      out[e] = orc_bf16_rne(prod);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * LoRA linear, forward and backward [QP §1.2, §2.2, §2.4, §6.3, §6.4].
+ * Column-vector statement y = W x + s B A x with s = alpha / r, written for
+ * row-major token matrices: Y = X Wh^T + s (X A^T) B^T.
+ *   Wh [d_out, d_in] restored weights, X [M, d_in], A [r, d_in], B [d_out, r].
+ * Inputs are FP32 arrays holding the exact values (BF16 values in use);
+ * every product and sum is FP64.  No gradient is formed for Wh.
+ * ---------------------------------------------------------------------- */
+
+/* Y rows listed in rows[0..nrows): Y[k, :] for token rows[k]. */
+void orc_linear_fwd_rows(const float *Wh, const float *X, const float *A,
+                         const float *B, int64_t d_out, int64_t d_in,
+                         int64_t r, double s, const int64_t *rows,
+                         int64_t nrows, double *Y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t k = 0; k < nrows; ++k) {
+    const float *x = X + rows[k] * d_in;
+    double *t = (double *)malloc((size_t)(r > 0 ? r : 1) * sizeof(double));
+    for (int64_t i = 0; i < r; ++i) {          /* t = A x        */
+      double acc = 0.0;
+      for (int64_t c = 0; c < d_in; ++c) acc += (double)A[i * d_in + c] * x[c];
+      t[i] = acc;
+    }
+    for (int64_t o = 0; o < d_out; ++o) {      /* y = Wh x + s B t */
+      double base = 0.0;
+      for (int64_t c = 0; c < d_in; ++c) base += (double)Wh[o * d_in + c] * x[c];
+      double lora = 0.0;
+      for (int64_t i = 0; i < r; ++i) lora += (double)B[o * r + i] * t[i];
+      Y[k * d_out + o] = base + s * lora;
+    }
+    free(t);
+  }
+}
+
+/* Backward of the same layer for upstream gradient dY [M, d_out]:
+ *   U  = s dY B          [M, r]   (gradient reaching the LoRA bottleneck)
+ *   T  = X A^T           [M, r]
+ *   dX = dY Wh + U A     (listed rows only)
+ *   dA = U^T X           [r, d_in]
+ *   dB = s dY^T T        [d_out, r]
+ * The frozen base contributes to dX but receives no gradient [QP §2.4]. */
+void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
+                    const float *A, const float *B, int64_t M, int64_t d_out,
+                    int64_t d_in, int64_t r, double s, const int64_t *rows,
+                    int64_t nrows, double *dX, double *dA, double *dB) {
+  double *U = (double *)calloc((size_t)(M * r + 1), sizeof(double));
+  double *T = (double *)calloc((size_t)(M * r + 1), sizeof(double));
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t i = 0; i < r; ++i) {
+      double u = 0.0, t = 0.0;
+      for (int64_t o = 0; o < d_out; ++o) u += (double)dY[m * d_out + o] * B[o * r + i];
+      for (int64_t c = 0; c < d_in; ++c) t += (double)X[m * d_in + c] * A[i * d_in + c];
+      U[m * r + i] = s * u;
+      T[m * r + i] = t;
+    }
+  }
+  if (dX) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t k = 0; k < nrows; ++k) {
+      int64_t m = rows[k];
+      for (int64_t c = 0; c < d_in; ++c) {
+        double acc = 0.0;
+        for (int64_t o = 0; o < d_out; ++o) acc += (double)dY[m * d_out + o] * Wh[o * d_in + c];
+        for (int64_t i = 0; i < r; ++i) acc += U[m * r + i] * A[i * d_in + c];
+        dX[k * d_in + c] = acc;
+      }
+    }
+  }
+  if (dA) {      /* dA[i, c] = sum over m ascending of U[m, i] X[m, c] */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < r; ++i) {
+      double *row = dA + i * d_in;
+      for (int64_t c = 0; c < d_in; ++c) row[c] = 0.0;
+      for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < d_in; ++c) row[c] += U[m * r + i] * X[m * d_in + c];
+    }
+  }
+  if (dB) {      /* dB[o, i] = s * sum over m ascending of dY[m, o] T[m, i] */
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < d_out; ++o) {
+      double *row = dB + o * r;
+      for (int64_t i = 0; i < r; ++i) row[i] = 0.0;
+      for (int64_t m = 0; m < M; ++m)
+        for (int64_t i = 0; i < r; ++i) row[i] += (double)dY[m * d_out + o] * T[m * r + i];
+      for (int64_t i = 0; i < r; ++i) row[i] = s * row[i];
+    }
+  }
+  free(U);
+  free(T);
+}
+
+/* ------------------------------------------------------------------------
+ * Elementwise maps over arrays, used by the exhaustive tests.
+ * ---------------------------------------------------------------------- */
+void orc_map_nf4_index(const float *x, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_nf4_index(x[i]);
+}
+
+void orc_map_fp8_encode(const float *y, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_encode(y[i]);
+}
+
+void orc_map_bf16_rne(const float *x, int64_t n, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_rne(x[i]);
+}
