@@ -1,0 +1,26 @@
+"""libqlora: the QLoRA frozen-base NF4 LoRA linear layer on AMD CDNA4 (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+include/qlora.h; this package is a thin ctypes binding over it (see _lib.py)
+plus the seeded synthetic-input generators (inputs.py).
+"""
+from ._lib import (  # noqa: F401
+    FwdItem,
+    NF4Weight,
+    QLORA_MAX_GROUP,
+    QLORA_OP_BWD,
+    QLORA_OP_FWD,
+    QLORA_OP_QUANTIZE,
+    QloraError,
+    header_functions,
+    lib,
+    qlora_abi_version,
+    qlora_dequant_bf16,
+    qlora_linear_bwd,
+    qlora_linear_fwd,
+    qlora_linear_fwd_many,
+    qlora_nf4_sizes,
+    qlora_quantize_nf4,
+    qlora_status_string,
+    qlora_workspace_bytes,
+)

@@ -1,0 +1,257 @@
+"""ctypes binding of libqlora (include/qlora.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libqlora.so.  PyTorch supplies device memory and the current
+stream.  The library must have been built (``build_lib.build()``); there is
+no fallback of any kind, and calls raise when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlora.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qlora.h")
+
+QLORA_OP_QUANTIZE, QLORA_OP_FWD, QLORA_OP_BWD = 0, 1, 2
+QLORA_MAX_GROUP = 8
+BLOCK, GROUP = 64, 256
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+class _Nf4(ctypes.Structure):
+    _fields_ = [("d_out", _I64), ("d_in", _I64), ("codes", _P), ("scale_codes", _P),
+                ("scale2", _P), ("scale_mean", _P)]
+
+
+class _FwdItem(ctypes.Structure):
+    _fields_ = [("w", _Nf4), ("X", _P), ("A", _P), ("B", _P), ("r", _I64),
+                ("lora_alpha", ctypes.c_float), ("Y", _P), ("T_save", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {qlora_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqlora.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libqlora.so is not built ({LIB_PATH}); run "
+                              "python -m bit_quantized_lora_quantize_amd.build_lib")
+        L = ctypes.CDLL(LIB_PATH)
+        L.qlora_status_string.restype = ctypes.c_char_p
+        L.qlora_status_string.argtypes = [ctypes.c_int]
+        L.qlora_abi_version.restype = ctypes.c_int
+        L.qlora_nf4_sizes.argtypes = [_I64, _I64] + [ctypes.POINTER(ctypes.c_size_t)] * 4
+        L.qlora_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64]
+        L.qlora_quantize_nf4.argtypes = [_P, ctypes.POINTER(_Nf4), _P, ctypes.c_size_t, _P]
+        L.qlora_dequant_bf16.argtypes = [ctypes.POINTER(_Nf4), _P, _P]
+        L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
+                                       ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+        L.qlora_linear_fwd_many.argtypes = [ctypes.c_int, ctypes.POINTER(_FwdItem), _I64, _P]
+        L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
+                                       ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/qlora.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def qlora_status_string(status: int) -> str:
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def qlora_abi_version() -> int:
+    return lib().qlora_abi_version()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QloraError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def qlora_nf4_sizes(d_out: int, d_in: int) -> tuple[int, int, int, int]:
+    out = [ctypes.c_size_t() for _ in range(4)]
+    _check(lib().qlora_nf4_sizes(d_out, d_in, *[ctypes.byref(o) for o in out]), "qlora_nf4_sizes")
+    return tuple(o.value for o in out)
+
+
+def qlora_workspace_bytes(op: int, d_out: int, d_in: int, M: int = 0, r: int = 1) -> int:
+    return int(lib().qlora_workspace_bytes(op, d_out, d_in, M, r))
+
+
+# ------------------------------------------------------------- weight state
+
+@dataclass
+class NF4Weight:
+    """The four device buffers of an NF4 + double-quantized weight."""
+    d_out: int
+    d_in: int
+    codes: torch.Tensor        # uint8 [n/2]
+    scale_codes: torch.Tensor  # uint8 [n/64]
+    scale2: torch.Tensor       # float32 [ceil(n/64/256)]
+    scale_mean: torch.Tensor   # float32 [1]
+
+    @staticmethod
+    def empty(d_out: int, d_in: int, device="cuda") -> "NF4Weight":
+        cb, sb, s2b, _ = qlora_nf4_sizes(d_out, d_in)
+        return NF4Weight(d_out, d_in,
+                         torch.empty(cb, dtype=torch.uint8, device=device),
+                         torch.empty(sb, dtype=torch.uint8, device=device),
+                         torch.empty(s2b // 4, dtype=torch.float32, device=device),
+                         torch.empty(1, dtype=torch.float32, device=device))
+
+    def c_struct(self) -> _Nf4:
+        return _Nf4(self.d_out, self.d_in, self.codes.data_ptr(), self.scale_codes.data_ptr(),
+                    self.scale2.data_ptr(), self.scale_mean.data_ptr())
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.codes, self.scale_codes, self.scale2, self.scale_mean))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+# ---------------------------------------------------------------- entry points
+
+def qlora_quantize_nf4(W: torch.Tensor, out: Optional[NF4Weight] = None,
+                       workspace: Optional[torch.Tensor] = None) -> NF4Weight:
+    d_out, d_in = W.shape
+    _need(W, torch.float32, (d_out, d_in), "W")
+    q = out if out is not None else NF4Weight.empty(d_out, d_in, W.device)
+    need = qlora_workspace_bytes(QLORA_OP_QUANTIZE, d_out, d_in)
+    ws = workspace if workspace is not None else _workspace(need, W.device)
+    qs = q.c_struct()
+    _check(lib().qlora_quantize_nf4(_ptr(W), ctypes.byref(qs), _ptr(ws), ws.numel(),
+                                    _stream(W.device)), "qlora_quantize_nf4")
+    return q
+
+
+def qlora_dequant_bf16(q: NF4Weight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    Wb = out if out is not None else torch.empty((q.d_out, q.d_in), dtype=torch.bfloat16,
+                                                 device=q.device)
+    _need(Wb, torch.bfloat16, (q.d_out, q.d_in), "W_bf16")
+    qs = q.c_struct()
+    _check(lib().qlora_dequant_bf16(ctypes.byref(qs), _ptr(Wb), _stream(q.device)),
+           "qlora_dequant_bf16")
+    return Wb
+
+
+def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                     lora_alpha: float, Y: Optional[torch.Tensor] = None,
+                     T_save: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M = X.shape[0]
+    r = A.shape[0]
+    _need(X, torch.bfloat16, (M, q.d_in), "X")
+    _need(A, torch.bfloat16, (r, q.d_in), "A")
+    _need(B, torch.bfloat16, (q.d_out, r), "B")
+    Y = Y if Y is not None else torch.empty((M, q.d_out), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, (M, q.d_out), "Y")
+    if T_save is not None:
+        _need(T_save, torch.float32, (M, r), "T_save")
+    need = qlora_workspace_bytes(QLORA_OP_FWD, q.d_out, q.d_in, M, r)
+    ws = workspace if workspace is not None else _workspace(need, X.device)
+    qs = q.c_struct()
+    _check(lib().qlora_linear_fwd(ctypes.byref(qs), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                  float(lora_alpha), _ptr(Y), _ptr(T_save), _ptr(ws), ws.numel(),
+                                  _stream(X.device)), "qlora_linear_fwd")
+    return Y
+
+
+@dataclass
+class FwdItem:
+    q: NF4Weight
+    X: torch.Tensor
+    A: torch.Tensor
+    B: torch.Tensor
+    lora_alpha: float
+    Y: torch.Tensor
+    workspace: torch.Tensor
+    T_save: Optional[torch.Tensor] = None
+
+
+def qlora_linear_fwd_many(items: Sequence[FwdItem], M: int) -> None:
+    arr = (_FwdItem * len(items))()
+    for i, it in enumerate(items):
+        r = it.A.shape[0]
+        _need(it.X, torch.bfloat16, (M, it.q.d_in), "X")
+        _need(it.A, torch.bfloat16, (r, it.q.d_in), "A")
+        _need(it.B, torch.bfloat16, (it.q.d_out, r), "B")
+        _need(it.Y, torch.bfloat16, (M, it.q.d_out), "Y")
+        arr[i] = _FwdItem(it.q.c_struct(), it.X.data_ptr(), it.A.data_ptr(), it.B.data_ptr(), r,
+                          float(it.lora_alpha), it.Y.data_ptr(),
+                          it.T_save.data_ptr() if it.T_save is not None else None,
+                          it.workspace.data_ptr(), it.workspace.numel())
+    dev = items[0].X.device
+    _check(lib().qlora_linear_fwd_many(len(items), arr, M, _stream(dev)), "qlora_linear_fwd_many")
+
+
+def qlora_linear_bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, lora_alpha: float, T_saved: Optional[torch.Tensor] = None,
+                     need_dx: bool = True, dX: Optional[torch.Tensor] = None,
+                     dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    M = X.shape[0]
+    r = A.shape[0]
+    dev = X.device
+    _need(X, torch.bfloat16, (M, q.d_in), "X")
+    _need(dY, torch.bfloat16, (M, q.d_out), "dY")
+    _need(A, torch.bfloat16, (r, q.d_in), "A")
+    _need(B, torch.bfloat16, (q.d_out, r), "B")
+    if T_saved is not None:
+        _need(T_saved, torch.float32, (M, r), "T_saved")
+    if need_dx and dX is None:
+        dX = torch.empty((M, q.d_in), dtype=torch.bfloat16, device=dev)
+    dA = dA if dA is not None else torch.empty((r, q.d_in), dtype=torch.float32, device=dev)
+    dB = dB if dB is not None else torch.empty((q.d_out, r), dtype=torch.float32, device=dev)
+    need = qlora_workspace_bytes(QLORA_OP_BWD, q.d_out, q.d_in, M, r)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    qs = q.c_struct()
+    _check(lib().qlora_linear_bwd(ctypes.byref(qs), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r,
+                                  float(lora_alpha), _ptr(T_saved), _ptr(dX if need_dx else None),
+                                  _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)),
+           "qlora_linear_bwd")
+    return (dX if need_dx else None), dA, dB

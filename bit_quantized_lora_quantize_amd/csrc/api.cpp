@@ -1,0 +1,500 @@
+// api.cpp -- host side of libqlora's C ABI: argument checks, workspace
+// planning and kernel launch sequences.  The operations are stated in
+// include/qlora.h with their sources on the pages.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "qlora.h"
+#include "qlora_device.h"
+#include "qlora_kernels.h"
+
+using namespace qlora;
+
+namespace {
+
+constexpr int64_t kMaxRank = 256;
+constexpr int64_t kSmallM = 16;      // M <= 16 streams the weight (GEMV path)
+constexpr int kTargetWgs = 512;      // workgroups aimed for when splitting K
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Sequential carving of a workspace into 256-byte aligned pieces; with a null
+// base it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(int64_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += size_t(std::max<int64_t>(count, 0)) * sizeof(T);
+    return p;
+  }
+};
+
+bool shape_ok(int64_t d_out, int64_t d_in) {
+  return d_out >= 1 && d_in >= kBlock && d_in % kBlock == 0 && d_out <= (int64_t(1) << 31) &&
+         d_in <= (int64_t(1) << 31) && d_out * d_in <= (int64_t(1) << 40);
+}
+
+int check_nf4(const qlora_nf4_t* q) {
+  if (!q) return QLORA_ERR_NULL;
+  if (!shape_ok(q->d_out, q->d_in)) return QLORA_ERR_SHAPE;
+  if (!q->codes || !q->scale_codes || !q->scale2 || !q->scale_mean) return QLORA_ERR_NULL;
+  if (!aligned16(q->codes) || (reinterpret_cast<uintptr_t>(q->scale2) & 3u) ||
+      (reinterpret_cast<uintptr_t>(q->scale_mean) & 3u))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+// --------------------------------------------------------------- plans
+struct QuantPlan {
+  int64_t n, n1, G, Gp;
+  float* absmax;
+  double* part;
+  size_t bytes;
+};
+
+QuantPlan plan_quant(int64_t d_out, int64_t d_in, void* ws) {
+  QuantPlan p{};
+  p.n = d_out * d_in;
+  p.n1 = p.n / kBlock;
+  p.G = cdiv(p.n1, kGroup);
+  p.Gp = 1;
+  while (p.Gp < p.G) p.Gp *= 2;
+  Carver c(ws);
+  p.absmax = c.take<float>(p.n1);
+  p.part = c.take<double>(p.Gp);
+  p.bytes = c.off + 256;
+  return p;
+}
+
+// Rank-down split of K (multiple of 32 per split).
+struct KSplit {
+  int splits;
+  int64_t per;
+};
+KSplit split_k(int64_t K, int splits) {
+  splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, cdiv(K, 32)));
+  int64_t per = round_up(cdiv(K, splits), 32);
+  return {(int)cdiv(K, per), per};
+}
+
+struct GemvSplit {
+  int ksplit, ss_per, tiles;
+};
+GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t total_tiles) {
+  const int64_t tiles = cdiv(d_out, 64);
+  const int64_t nss = cdiv(d_in / kBlock, 4);
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(kTargetWgs, total_tiles), nss));
+  const int64_t per = cdiv(nss, ks);
+  return {(int)cdiv(nss, per), (int)per, (int)tiles};
+}
+
+struct FwdPlan {
+  bool small;
+  KSplit tk;          // rank-down split of X A^T
+  int64_t tiles_m, tiles_n;
+  float* t_part;      // [tk.splits][M][r]
+  float* t_buf;       // [M][r] (large M, when T_save is NULL)
+  uint16_t* xp;       // [M][d_in] permuted X (small M)
+  float* gemv_part;   // [ksplit][16][d_out]
+  uint32_t* counters; // [tiles]
+  GemvSplit gs;
+  size_t bytes;
+};
+
+FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
+  FwdPlan p{};
+  p.small = M <= kSmallM;
+  Carver c(ws);
+  p.tiles_n = cdiv(r, 64);
+  if (p.small) {
+    p.tiles_m = 1;
+    p.tk = split_k(d_in, (int)std::min<int64_t>(8, std::max<int64_t>(1, d_in / 1024)));
+    p.t_part = c.take<float>(p.tk.splits * M * r);
+    p.xp = c.take<uint16_t>(M * d_in);
+    p.gs = gemv_split(d_out, d_in, cdiv(d_out, 64));
+    p.gemv_part = c.take<float>((int64_t)p.gs.ksplit * 16 * d_out);
+    p.counters = c.take<uint32_t>(p.gs.tiles);
+  } else {
+    p.tiles_m = cdiv(M, 16);
+    const int64_t base = p.tiles_m * p.tiles_n;
+    p.tk = split_k(d_in, (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base))));
+    p.t_part = c.take<float>(p.tk.splits * M * r);
+    p.t_buf = c.take<float>(M * r);
+  }
+  p.bytes = c.off + 256;
+  return p;
+}
+
+struct BwdPlan {
+  FwdPlan t;          // recomputation of T (large-M form, always finished)
+  KSplit uk;          // rank-down split of dY B over d_out
+  int64_t ldbt;       // row stride of B^T
+  uint16_t* bt;       // [r][ldbt]
+  float* u_part;      // [uk.splits][M][r]
+  float* u;           // [M][r]
+  int ms_a, ms_b;     // token splits of dA and dB
+  int64_t mper_a, mper_b;
+  float* da_part;     // [ms_a][r][d_in]
+  float* db_part;     // [ms_b][r][d_out]
+  size_t bytes;
+};
+
+int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
+  const int64_t tiles = cdiv(N, 128) * cdiv(r, 64);
+  int64_t ms = std::max<int64_t>(1, std::min<int64_t>(cdiv(M, 32), cdiv(kTargetWgs, tiles)));
+  *per = round_up(cdiv(M, ms), 32);
+  return (int)cdiv(M, *per);
+}
+
+BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
+  BwdPlan p{};
+  Carver c(ws);
+  p.t.small = false;
+  p.t.tiles_m = cdiv(M, 16);
+  p.t.tiles_n = cdiv(r, 64);
+  const int64_t base = p.t.tiles_m * p.t.tiles_n;
+  const int want = (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base)));
+  p.t.tk = split_k(d_in, want);
+  p.t.t_part = c.take<float>(p.t.tk.splits * M * r);
+  p.t.t_buf = c.take<float>(M * r);
+  p.uk = split_k(d_out, want);
+  p.ldbt = round_up(d_out, 64);
+  p.bt = c.take<uint16_t>(r * p.ldbt);
+  p.u_part = c.take<float>(p.uk.splits * M * r);
+  p.u = c.take<float>(M * r);
+  p.ms_a = token_splits(M, d_in, r, &p.mper_a);
+  p.ms_b = token_splits(M, d_out, r, &p.mper_b);
+  p.da_part = c.take<float>((int64_t)p.ms_a * r * d_in);
+  p.db_part = c.take<float>((int64_t)p.ms_b * r * d_out);
+  p.bytes = c.off + 256;
+  return p;
+}
+
+// ------------------------------------------------ nearest-level table
+// Decision thresholds between adjacent NF4 levels: t_i is the smallest FP32
+// value above the exact midpoint, so x >= t_i <=> x > midpoint, and a value
+// exactly on a midpoint keeps the lower index.
+IndexLut make_lut() {
+  const float c[16] = {QLORA_NF4_LEVELS};
+  float t[15];
+  for (int i = 0; i < 15; ++i) {
+    const double mid = ((double)c[i] + (double)c[i + 1]) / 2.0;
+    const float f = (float)mid;
+    t[i] = ((double)f > mid) ? f : std::nextafter(f, INFINITY);
+  }
+  IndexLut lut;
+  for (int b = 0; b < kLutSize; ++b) {
+    const double lo = (b - 64) / 64.0, hi = lo + 1.0 / 64.0;
+    int base = 0;
+    float thr = 2.0f;  // never reached: x <= 1
+    for (int i = 0; i < 15; ++i) {
+      if ((double)t[i] <= lo) ++base;
+      else if ((double)t[i] < hi) thr = t[i];
+    }
+    lut.thr[b] = thr;
+    lut.base[b] = (uint8_t)base;
+  }
+  return lut;
+}
+
+const IndexLut& lut() {
+  static const IndexLut l = make_lut();
+  return l;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+// --------------------------------------------------------- rank-down setup
+void fill_rank_desc(RankDownDesc& d, const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N,
+                    int64_t K, int64_t ldq, const KSplit& ks, float* part, uint16_t* xp,
+                    int wg_begin) {
+  d.P = P;
+  d.Q = Q;
+  d.part = part;
+  d.Xp = xp;
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  d.ldq = ldq;
+  d.k_per_split = ks.per;
+  d.splits = ks.splits;
+  d.wg_begin = wg_begin;
+  d.tiles_m = (int)cdiv(M, 16);
+  d.tiles_n = (int)cdiv(N, 64);
+}
+
+int rank_down_single(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N, int64_t K,
+                     int64_t ldq, const KSplit& ks, float* part, hipStream_t st) {
+  RankDownArgs a{};
+  fill_rank_desc(a.d[0], P, Q, M, N, K, ldq, ks, part, nullptr, 0);
+  a.count = 1;
+  const int wgs = a.d[0].tiles_m * a.d[0].tiles_n * a.d[0].splits;
+  return hip_status(launch_rank_down(a, wgs, st));
+}
+
+struct FwdItemArgs {
+  const qlora_nf4_t* q;
+  const uint16_t* X;
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t r;
+  float alpha;
+  uint16_t* Y;
+  float* T_save;
+  void* ws;
+  size_t ws_bytes;
+};
+
+int check_fwd_item(const FwdItemArgs& f, int64_t M) {
+  int s = check_nf4(f.q);
+  if (s) return s;
+  if (M < 0 || M > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
+  if (f.r < 1 || f.r > kMaxRank) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!f.X || !f.A || !f.B || !f.Y) return QLORA_ERR_NULL;
+  if (!aligned16(f.X) || !aligned16(f.A) || !aligned16(f.Y) || !aligned16(f.T_save) ||
+      !aligned16(f.ws))
+    return QLORA_ERR_ALIGN;
+  if (!f.ws) return QLORA_ERR_NULL;
+  if (f.ws_bytes < plan_fwd(f.q->d_out, f.q->d_in, M, f.r, nullptr).bytes)
+    return QLORA_ERR_WORKSPACE;
+  return QLORA_OK;
+}
+
+// Forward of up to kMaxGroup layers sharing the token count M.
+int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
+  if (count < 1 || count > kMaxGroup) return QLORA_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    int s = check_fwd_item(items[i], M);
+    if (s) return s;
+  }
+  if (M == 0) return QLORA_OK;
+
+  if (M > kSmallM) {
+    for (int i = 0; i < count; ++i) {
+      const FwdItemArgs& f = items[i];
+      const qlora_nf4_t* q = f.q;
+      FwdPlan p = plan_fwd(q->d_out, q->d_in, M, f.r, f.ws);
+      float* T = f.T_save ? f.T_save : p.t_buf;
+      int s = rank_down_single(f.X, f.A, M, f.r, q->d_in, q->d_in, p.tk, p.t_part, st);
+      if (s) return s;
+      s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, f.r, f.alpha / (float)f.r, T, st));
+      if (s) return s;
+      GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, T, f.B, f.Y,
+                 M,        q->d_out,      q->d_in,  f.r};
+      s = hip_status(launch_gemm_fwd(g, st));
+      if (s) return s;
+    }
+    return QLORA_OK;
+  }
+
+  // Small M: one rank-down launch and one weight-streaming launch for the group.
+  FwdPlan plans[kMaxGroup];
+  int64_t total_tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    plans[i] = plan_fwd(items[i].q->d_out, items[i].q->d_in, M, items[i].r, items[i].ws);
+    total_tiles += cdiv(items[i].q->d_out, 64);
+  }
+  RankDownArgs ra{};
+  ra.count = count;
+  int rwgs = 0;
+  GemvArgs ga{};
+  ga.count = count;
+  ga.M = (int)M;
+  int gwgs = 0;
+  for (int i = 0; i < count; ++i) {
+    const FwdItemArgs& f = items[i];
+    const qlora_nf4_t* q = f.q;
+    FwdPlan& p = plans[i];
+    fill_rank_desc(ra.d[i], f.X, f.A, M, f.r, q->d_in, q->d_in, p.tk, p.t_part, p.xp, rwgs);
+    rwgs += ra.d[i].tiles_m * ra.d[i].tiles_n * ra.d[i].splits;
+
+    const GemvSplit gs = gemv_split(q->d_out, q->d_in, total_tiles);
+    GemvDesc& d = ga.d[i];
+    d.codes = q->codes;
+    d.scodes = q->scale_codes;
+    d.scale2 = q->scale2;
+    d.mean = q->scale_mean;
+    d.Xp = p.xp;
+    d.t_part = p.t_part;
+    d.B = f.B;
+    d.Y = f.Y;
+    d.part = p.gemv_part;
+    d.counters = p.counters;
+    d.d_out = q->d_out;
+    d.d_in = q->d_in;
+    d.r = f.r;
+    d.t_scale = f.alpha / (float)f.r;
+    d.t_splits = p.tk.splits;
+    d.ksplit = gs.ksplit;
+    d.ss_per_split = gs.ss_per;
+    d.tiles = gs.tiles;
+    d.wg_begin = gwgs;
+    gwgs += gs.tiles * gs.ksplit;
+  }
+  for (int i = 0; i < count; ++i) {
+    if (ga.d[i].ksplit > 1) {
+      ra.zero[i] = ga.d[i].counters;
+      ra.zero_count[i] = ga.d[i].tiles;
+    }
+  }
+  int s = hip_status(launch_rank_down(ra, rwgs, st));
+  if (s) return s;
+  s = hip_status(launch_gemv(ga, gwgs, st));
+  if (s) return s;
+  for (int i = 0; i < count; ++i) {
+    if (items[i].T_save) {
+      s = hip_status(launch_rank_finish(plans[i].t_part, plans[i].tk.splits, M, items[i].r,
+                                        items[i].alpha / (float)items[i].r, items[i].T_save, st));
+      if (s) return s;
+    }
+  }
+  return QLORA_OK;
+}
+
+}  // namespace
+
+// ===================================================================== ABI
+extern "C" {
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "a size is out of range";
+    case QLORA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int qlora_abi_version(void) { return (1 << 16) | 0; }
+
+int qlora_nf4_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* scale_codes_bytes,
+                    size_t* scale2_bytes, size_t* scale_mean_bytes) {
+  if (!codes_bytes || !scale_codes_bytes || !scale2_bytes || !scale_mean_bytes)
+    return QLORA_ERR_NULL;
+  if (!shape_ok(d_out, d_in)) return QLORA_ERR_SHAPE;
+  const int64_t n = d_out * d_in, n1 = n / kBlock;
+  *codes_bytes = size_t(n / 2);
+  *scale_codes_bytes = size_t(n1);
+  *scale2_bytes = size_t(cdiv(n1, kGroup)) * sizeof(float);
+  *scale_mean_bytes = sizeof(float);
+  return QLORA_OK;
+}
+
+size_t qlora_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t M, int64_t r) {
+  if (!shape_ok(d_out, d_in)) return 0;
+  if (op == QLORA_OP_QUANTIZE) return plan_quant(d_out, d_in, nullptr).bytes;
+  if (M < 0 || r < 1 || r > kMaxRank) return 0;
+  if (op == QLORA_OP_FWD) return plan_fwd(d_out, d_in, M, r, nullptr).bytes;
+  if (op == QLORA_OP_BWD) return plan_bwd(d_out, d_in, M, r, nullptr).bytes;
+  return 0;
+}
+
+int qlora_quantize_nf4(const float* W, const qlora_nf4_t* q, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int s = check_nf4(q);
+  if (s) return s;
+  if (!W || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  QuantPlan p = plan_quant(q->d_out, q->d_in, ws);
+  if (ws_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
+  QuantWorkspace w{p.absmax, p.part};
+  return hip_status(launch_quantize(W, p.n, q->codes, q->scale_codes, q->scale2, q->scale_mean, w,
+                                    lut(), static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dequant_bf16(const qlora_nf4_t* q, uint16_t* W_bf16, void* stream) {
+  int s = check_nf4(q);
+  if (s) return s;
+  if (!W_bf16) return QLORA_ERR_NULL;
+  if (!aligned16(W_bf16)) return QLORA_ERR_ALIGN;
+  return hip_status(launch_dequant(q->codes, q->scale_codes, q->scale2, q->scale_mean,
+                                   q->d_out * q->d_in, W_bf16, static_cast<hipStream_t>(stream)));
+}
+
+int qlora_linear_fwd(const qlora_nf4_t* q, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int64_t r, float lora_alpha, uint16_t* Y, float* T_save,
+                     void* ws, size_t ws_bytes, void* stream) {
+  FwdItemArgs f{q, X, A, B, r, lora_alpha, Y, T_save, ws, ws_bytes};
+  return fwd_group(&f, 1, M, static_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_fwd_many(int count, const qlora_fwd_item* items, int64_t M, void* stream) {
+  if (!items) return QLORA_ERR_NULL;
+  if (count < 1 || count > kMaxGroup) return QLORA_ERR_SHAPE;
+  FwdItemArgs f[kMaxGroup];
+  for (int i = 0; i < count; ++i) {
+    const qlora_fwd_item& it = items[i];
+    f[i] = FwdItemArgs{&it.w, it.X, it.A, it.B, it.r, it.lora_alpha, it.Y, it.T_save,
+                       it.workspace, it.workspace_bytes};
+  }
+  return fwd_group(f, count, M, static_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int64_t r, float lora_alpha,
+                     const float* T_saved, uint16_t* dX, float* dA, float* dB, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int s = check_nf4(q);
+  if (s) return s;
+  if (M < 0 || M > (int64_t(1) << 31) || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
+  if (!dA || !dB || !ws) return QLORA_ERR_NULL;
+  if (M > 0 && (!X || !dY || !A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(T_saved) ||
+      !aligned16(dX) || !aligned16(dA) || !aligned16(dB) || !aligned16(ws))
+    return QLORA_ERR_ALIGN;
+  const int64_t d_out = q->d_out, d_in = q->d_in;
+  BwdPlan p = plan_bwd(d_out, d_in, M, r, ws);
+  if (ws_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    s = hip_status(hipMemsetAsync(dA, 0, size_t(r * d_in) * sizeof(float), st));
+    if (!s) s = hip_status(hipMemsetAsync(dB, 0, size_t(d_out * r) * sizeof(float), st));
+    return s;
+  }
+  const float sc = lora_alpha / (float)r;
+  // T = s X A^T (unless saved by the forward)
+  const float* T = T_saved;
+  if (!T) {
+    s = rank_down_single(X, A, M, r, d_in, d_in, p.t.tk, p.t.t_part, st);
+    if (s) return s;
+    s = hip_status(launch_rank_finish(p.t.t_part, p.t.tk.splits, M, r, sc, p.t.t_buf, st));
+    if (s) return s;
+    T = p.t.t_buf;
+  }
+  // U = s dY B, through B^T so the contraction over d_out is contiguous
+  s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
+  if (s) return s;
+  s = rank_down_single(dY, p.bt, M, r, d_out, p.ldbt, p.uk, p.u_part, st);
+  if (s) return s;
+  s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, p.u, st));
+  if (s) return s;
+  // dX = dY Wh + U A
+  if (dX) {
+    GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, dY, p.u, A, dX,
+               M,        d_out,          d_in,      r};
+    s = hip_status(launch_gemm_bwd(g, st));
+    if (s) return s;
+  }
+  // dA = U^T X ; dB = (T^T dY)^T
+  s = hip_status(launch_gram(p.u, X, M, r, d_in, p.mper_a, p.ms_a, p.da_part, st));
+  if (!s) s = hip_status(launch_gram_finish(p.da_part, p.ms_a, r, d_in, false, dA, st));
+  if (!s) s = hip_status(launch_gram(T, dY, M, r, d_out, p.mper_b, p.ms_b, p.db_part, st));
+  if (!s) s = hip_status(launch_gram_finish(p.db_part, p.ms_b, r, d_out, true, dB, st));
+  return s;
+}
+
+}  // extern "C"

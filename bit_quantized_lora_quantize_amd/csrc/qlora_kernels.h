@@ -1,0 +1,127 @@
+// qlora_kernels.h -- launch interfaces between the host library (api.cpp) and
+// the HIP kernels of libqlora.  Internal; not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+// ----------------------------------------------------------- quantization
+constexpr int kLutSize = 129;     // buckets floor(64 x) + 64 for x in [-1, 1]
+constexpr int64_t kTreeLds = 4096; // top tree levels done in one workgroup
+
+// Nearest-level decision table for x in [-1, 1]: bucket b covers
+// [(b-64)/64, (b-63)/64) and idx = base[b] + (x >= thr[b]).
+struct IndexLut {
+  float thr[kLutSize];
+  uint8_t base[kLutSize];
+};
+
+struct QuantWorkspace {
+  float* absmax;  // [n1]
+  double* part;   // [Gp] group sums, Gp = next power of two >= G
+};
+
+hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale_codes,
+                           float* scale2, float* mean, const QuantWorkspace& ws,
+                           const IndexLut& lut, hipStream_t st);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, const float* scale2,
+                          const float* mean, int64_t n, uint16_t* out, hipStream_t st);
+
+// ------------------------------------------------------------- rank-r work
+constexpr int kMaxGroup = 8;
+
+// part[s][m][n] = sum over k in split s of P[m][k] * Q[n][k]   (FP32)
+// P BF16 [M][K] (row stride K), Q BF16 [N][ldq] (K contiguous).  When Xp is
+// set, the workgroups of column tile 0 also write P permuted within each
+// group of eight (the order of nf4_dequant8_perm).  The launch also clears
+// the zero[] ranges (split-K counters of the following weight-streaming
+// launch).
+struct RankDownDesc {
+  const uint16_t* P;
+  const uint16_t* Q;
+  float* part;
+  uint16_t* Xp;
+  int64_t M, N, K, ldq;
+  int64_t k_per_split;  // multiple of 32
+  int splits;
+  int wg_begin;         // first workgroup of this item in the grid
+  int tiles_m, tiles_n;
+};
+struct RankDownArgs {
+  RankDownDesc d[kMaxGroup];
+  int count;
+  uint32_t* zero[kMaxGroup];   // u32 ranges cleared by the launch (or null)
+  int zero_count[kMaxGroup];
+};
+hipError_t launch_rank_down(const RankDownArgs& a, int total_wgs, hipStream_t st);
+
+// out[m][n] = scale * sum_s part[s][m][n], s ascending.
+hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
+                              float* out, hipStream_t st);
+
+// Transpose of a BF16 matrix in[rows][cols] into out[cols][ldo]:
+// out[c][i] = in[i][c] for i < rows, and 0 for i in [rows, ldo).
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                 int64_t ldo, hipStream_t st);
+
+// part[s][i][c] = sum over tokens m in split s of P[m][i] * Q[m][c], with P
+// FP32 [M][R] entering as a hi + lo BF16 pair and Q BF16 [M][N].
+hipError_t launch_gram(const float* P, const uint16_t* Q, int64_t M, int64_t R, int64_t N,
+                       int64_t m_per_split, int splits, float* part, hipStream_t st);
+// out = sum_s part[s] (s ascending); transposed: out[c][i] else out[i][c].
+hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,
+                              bool transposed, float* out, hipStream_t st);
+
+// ------------------------------------------------- small-M forward (GEMV)
+// Y[m][n] = RNE_bf16( sum_k Xp-order X[m][k] Wh[n][k] + sum_i T[m][i] B[n][i] )
+// for m < M <= 16.  T = t_scale * sum_s t_part[s][m][i] (s ascending).
+// The weight is streamed once; ksplit > 1 splits K across workgroups and the
+// last workgroup of a row tile (counted in counters[tile]) reduces the FP32
+// partials in split order and applies the LoRA term.
+struct GemvDesc {
+  const uint8_t* codes;
+  const uint8_t* scodes;
+  const float* scale2;
+  const float* mean;
+  const uint16_t* Xp;
+  const float* t_part;
+  const uint16_t* B;
+  uint16_t* Y;
+  float* part;
+  uint32_t* counters;
+  int64_t d_out, d_in, r;
+  float t_scale;
+  int t_splits;
+  int ksplit;
+  int ss_per_split;  // 256-wide K super-steps per split
+  int tiles;         // 64-row tiles
+  int wg_begin;
+};
+struct GemvArgs {
+  GemvDesc d[kMaxGroup];
+  int count;
+  int M;
+};
+hipError_t launch_gemv(const GemvArgs& a, int total_wgs, hipStream_t st);
+
+// ------------------------------------------------- large-M fused GEMM
+// Forward: Y = RNE_bf16(X Wh^T + [T_hi T_lo] [B B]^T), dequant tiles in LDS.
+// Backward: dX = RNE_bf16(dY Wh + [U_hi U_lo] [A A]), W tiles written
+// transposed into LDS.
+struct GemmArgs {
+  const uint8_t* codes;
+  const uint8_t* scodes;
+  const float* scale2;
+  const float* mean;
+  const uint16_t* act;    // X [M][d_in] (forward) or dY [M][d_out] (backward)
+  const float* lr;        // T or U, FP32 [M][r]
+  const uint16_t* lw;     // B [d_out][r] (forward) or A [r][d_in] (backward)
+  uint16_t* out;          // Y [M][d_out] or dX [M][d_in]
+  int64_t M, d_out, d_in, r;
+};
+hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st);
+
+}  // namespace qlora

@@ -1,0 +1,208 @@
+/*
+ * qlora.h -- C ABI of libqlora: the frozen-base NF4 LoRA linear layer on an
+ * AMD CDNA4 (gfx950) GPU.
+ *
+ * Sources of the operations (the pages):
+ *   [QP]  "第 04 篇：QLoRA 原理" (jupiter-lab.pages.dev, QLoRA principles)
+ *   [CP]  "QLoRA" concept page (compassingai.com), sections
+ *         "NF4 量化機制詳解" (NF4 steps) and "雙重量化" (double quantization).
+ *
+ * Conventions for every entry point
+ *   - Every array argument is a DEVICE pointer to caller-owned memory.  The
+ *     library allocates nothing, frees nothing and keeps no state between
+ *     calls; it never synchronizes.  Work is enqueued on `stream` (a
+ *     hipStream_t; NULL means the null stream) and the call returns at once.
+ *   - All matrices are dense row-major.  BF16 values are passed as their
+ *     uint16_t bit patterns.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error the call returns a negative qlora_status and enqueues nothing.
+ *     A failing kernel launch returns QLORA_ERR_HIP (work enqueued before it
+ *     on the same call may have run).  Non-finite inputs are a precondition
+ *     violation and are not detected.
+ *   - Pointers marked (16B) must be 16-byte aligned.
+ *   - Calls that share a workspace buffer must be ordered (same stream or
+ *     explicit events); calls on different buffers may overlap freely.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,       /* a required pointer is NULL                  */
+  QLORA_ERR_SHAPE = -2,      /* a size is out of its documented range        */
+  QLORA_ERR_ALIGN = -3,      /* a (16B) pointer is not 16-byte aligned       */
+  QLORA_ERR_WORKSPACE = -4,  /* workspace smaller than qlora_workspace_bytes */
+  QLORA_ERR_HIP = -5         /* the HIP runtime reported an error            */
+} qlora_status;
+
+/* Block sizes fixed by the method: 64 weights share one first-level scale
+ * ([QP §3.4], [CP, NF4 量化機制詳解] step 1), 256 first-level scales share one
+ * second-level FP32 scale ([QP §5.2], [CP, 雙重量化]). */
+#define QLORA_BLOCK 64
+#define QLORA_GROUP 256
+
+/*
+ * NF4 + double-quantized weight W[d_out, d_in] ([QP §2.1, §5.2, §6.1]).
+ * n = d_out*d_in weights, flattened row-major; n1 = n/64 blocks;
+ * G = ceil(n1/256) groups.  Requires d_in % 64 == 0 (no block straddles a
+ * row), d_out >= 1.
+ *   codes        uint8[n/2] (16B)  4-bit level indices, two per byte; element
+ *                                  2j in the low nibble of byte j [QP §2.1].
+ *   scale_codes  uint8[n1]         OCP FP8 E4M3FN codes of the centred block
+ *                                  scales, (absmax_b - mean) / scale2[b/256].
+ *   scale2       float[G]          second-level scales: the group's largest
+ *                                  |absmax - mean| divided by 448.
+ *   scale_mean   float[1]          mean of all n1 block absmax values.
+ * The restored weight of element e in block b is
+ *   RNE_bf16(codebook[idx_e] * (fp8(scale_codes[b]) * scale2[b/256] + mean))
+ * with every FP32 operation rounded separately (no fused multiply-add), and
+ * codebook = the 16 NF4 levels printed in [QP §4.3].
+ */
+typedef struct {
+  int64_t d_out;
+  int64_t d_in;
+  uint8_t *codes;
+  uint8_t *scale_codes;
+  float *scale2;
+  float *scale_mean;
+} qlora_nf4_t;
+
+/* Byte sizes of the four buffers of an NF4 weight (host only, no GPU use).
+ * Returns QLORA_ERR_SHAPE for d_out < 1, d_in < 64 or d_in % 64 != 0, and
+ * QLORA_ERR_NULL when an output pointer is NULL. */
+int qlora_nf4_sizes(int64_t d_out, int64_t d_in, size_t *codes_bytes,
+                    size_t *scale_codes_bytes, size_t *scale2_bytes,
+                    size_t *scale_mean_bytes);
+
+/* Operations for qlora_workspace_bytes. */
+#define QLORA_OP_QUANTIZE 0
+#define QLORA_OP_FWD 1
+#define QLORA_OP_BWD 2
+
+/* Device workspace (bytes) that one call of `op` needs for these sizes
+ * (M and r are ignored for QLORA_OP_QUANTIZE).  Host only.  Returns 0 for
+ * sizes the call would reject. */
+size_t qlora_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t M,
+                             int64_t r);
+
+/*
+ * Quantize W (FP32 [d_out, d_in], (16B)) into `q` ([QP §3.4, §4.3, §5.2];
+ * [CP, NF4 量化機制詳解; 雙重量化]):
+ *   1. absmax a_b of each 64-element block;
+ *   2. x = w / a_b (IEEE FP32 division); a zero block gives x = 0;
+ *   3. index of the nearest NF4 level, ties to the lower index;
+ *   4. two indices per byte;
+ *   5. mean of the a_b (FP64 sum in a fixed stride-halving tree: pairs
+ *      (j, j+128), (j, j+64), ... within each group of 256, then the same
+ *      tree over the group sums padded with zeros to a power of two; the
+ *      FP64 quotient by n1 is rounded to FP32);
+ *   6. per group: scale2 = max |a_b - mean| / 448 and FP8 E4M3FN codes of
+ *      (a_b - mean) / scale2, round to nearest even, saturating at 448;
+ *      a group whose scale2 is 0 stores code 0.
+ * Deterministic: repeated calls give identical bytes.
+ * q->codes (16B), q->scale_codes, q->scale2, q->scale_mean are outputs.
+ * workspace (16B) >= qlora_workspace_bytes(QLORA_OP_QUANTIZE, ...).
+ */
+int qlora_quantize_nf4(const float *W, const qlora_nf4_t *q, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * Double dequantization ([QP §2.3, §6.1]): W_bf16[d_out, d_in] (16B) gets the
+ * restored weights of `q` as BF16 bit patterns, bit-exact with the formula
+ * under qlora_nf4_t.  Needs no workspace.
+ */
+int qlora_dequant_bf16(const qlora_nf4_t *q, uint16_t *W_bf16, void *stream);
+
+/*
+ * Forward of the LoRA linear layer on the frozen NF4 base
+ * ([QP §1.2, §2.2, §2.3, §6.3]; column-vector form y = W x + (alpha/r) B A x,
+ * written here for token rows):
+ *     Y = X Wh^T + s (X A^T) B^T,      s = lora_alpha / r (FP32),
+ * where Wh is the restored BF16 weight.  Products take BF16 inputs and
+ * accumulate in FP32; Y is rounded once to BF16.  The rank-r intermediate
+ * T = s X A^T is formed in FP32 and enters the second product as the sum of
+ * two BF16 terms (hi + lo), so it carries about 16 significant bits.
+ *   X       BF16 [M, d_in]  (16B)        M >= 0 tokens (M = 0: no work)
+ *   A       BF16 [r, d_in]  (16B)        1 <= r <= 256
+ *   B       BF16 [d_out, r]              any alignment
+ *   Y       BF16 [M, d_out] (16B)        output
+ *   T_save  FP32 [M, r]     (16B) or NULL: receives T for the backward.
+ * workspace (16B) >= qlora_workspace_bytes(QLORA_OP_FWD, d_out, d_in, M, r).
+ * M <= 16 runs a weight-streaming kernel (HBM-bound); larger M runs the
+ * fused dequant-GEMM on the matrix cores.  No full BF16 copy of W is made.
+ */
+int qlora_linear_fwd(const qlora_nf4_t *q, const uint16_t *X, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int64_t r,
+                     float lora_alpha, uint16_t *Y, float *T_save,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of the same layer for the upstream gradient dY ([QP §2.4, §6.4,
+ * §6.5]; [CP, 推論與訓練的精度關係]): gradients reach X, A and B; the frozen
+ * base takes part in dX but gets no gradient of its own.
+ *     U  = s dY B                 (FP32, [M, r])
+ *     dX = dY Wh + U A            (BF16 out, FP32 accumulation)
+ *     dA = U^T X                  (FP32 [r, d_in])
+ *     dB = s dY^T (X A^T) = dY^T T (FP32 [d_out, r])
+ * U and T enter the products as hi + lo BF16 pairs as in the forward.
+ *   X, A, B, r, lora_alpha as in qlora_linear_fwd; dY BF16 [M, d_out] (16B).
+ *   T_saved FP32 [M, r] (16B) from qlora_linear_fwd, or NULL to recompute.
+ *   dX      BF16 [M, d_in] (16B) or NULL to skip the input gradient.
+ *   dA      FP32 [r, d_in] (16B), dB FP32 [d_out, r] (16B): overwritten
+ *           (M = 0 writes zeros).
+ * workspace (16B) >= qlora_workspace_bytes(QLORA_OP_BWD, d_out, d_in, M, r).
+ * dA and dB are reduced over tokens in a fixed order: results are
+ * deterministic.
+ */
+int qlora_linear_bwd(const qlora_nf4_t *q, const uint16_t *X,
+                     const uint16_t *dY, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int64_t r, float lora_alpha,
+                     const float *T_saved, uint16_t *dX, float *dA, float *dB,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward of up to QLORA_MAX_GROUP layers that share the token count M, in
+ * one pass: the same operation as qlora_linear_fwd for every item (each with
+ * its own weight, LoRA factors, outputs and workspace sized by
+ * qlora_workspace_bytes(QLORA_OP_FWD, ...)).  For M <= 16 all items run in
+ * one rank-r launch and one weight-streaming launch, so the projections of a
+ * decoder layer stream their packed weights back to back; for larger M the
+ * items run one after another.  Items must not share outputs or workspace.
+ * Returns the first failing item's status (nothing enqueued on argument
+ * errors).
+ */
+#define QLORA_MAX_GROUP 8
+typedef struct {
+  qlora_nf4_t w;
+  const uint16_t *X;
+  const uint16_t *A;
+  const uint16_t *B;
+  int64_t r;
+  float lora_alpha;
+  uint16_t *Y;
+  float *T_save;
+  void *workspace;
+  size_t workspace_bytes;
+} qlora_fwd_item;
+
+int qlora_linear_fwd_many(int count, const qlora_fwd_item *items, int64_t M,
+                          void *stream);
+
+/* Static English text for a qlora_status value. */
+const char *qlora_status_string(int status);
+
+/* ABI version: (major << 16) | minor. */
+int qlora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every entry point include/qlora.h
+declares, and rejects bad arguments on the host before touching a GPU.
+
+No call here reaches a kernel: every call either is host-only or fails
+argument validation (fake device addresses are never dereferenced)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import bit_quantized_lora_quantize_amd as q
+from bit_quantized_lora_quantize_amd import _lib
+
+OK, ENULL, ESHAPE, EALIGN, EWS, EHIP = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def L():
+    import os
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return q.lib()
+
+
+def test_exports_every_declared_function(L):
+    declared = q.header_functions()
+    assert {"qlora_quantize_nf4", "qlora_dequant_bf16", "qlora_linear_fwd",
+            "qlora_linear_bwd"} <= set(declared)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(L, f)
+
+
+def test_status_strings_and_version(L):
+    assert q.qlora_abi_version() >> 16 == 1
+    for s in (OK, ENULL, ESHAPE, EALIGN, EWS, EHIP):
+        assert q.qlora_status_string(s) and q.qlora_status_string(s) != "unknown status"
+    assert q.qlora_status_string(12345) == "unknown status"
+
+
+def test_nf4_sizes_closed_form(L):
+    """codes n/2, FP8 scale codes n/64, FP32 second-level scales ceil(n/64/256),
+    one FP32 mean."""
+    for d_out, d_in in ((256, 256), (4096, 4096), (11008, 4096), (4096, 11008), (3, 64),
+                        (8192, 22016)):
+        n = d_out * d_in
+        assert q.qlora_nf4_sizes(d_out, d_in) == (n // 2, n // 64, 4 * (-(-(n // 64) // 256)), 4)
+    with pytest.raises(q.QloraError):
+        q.qlora_nf4_sizes(4, 100)
+    with pytest.raises(q.QloraError):
+        q.qlora_nf4_sizes(0, 64)
+
+
+def test_workspace_sizes(L):
+    ws = q.qlora_workspace_bytes
+    assert ws(0, 256, 256) > 0
+    assert ws(1, 4096, 4096, 16, 64) > 0 and ws(2, 4096, 4096, 4096, 64) > 0
+    assert ws(1, 4096, 4096, 0, 64) > 0           # M = 0 is valid
+    assert ws(1, 4096, 4096, 16, 0) == 0          # r out of range
+    assert ws(1, 4096, 4096, 16, 257) == 0
+    assert ws(1, 4096, 100, 16, 8) == 0           # d_in % 64 != 0
+    assert ws(7, 4096, 4096, 16, 8) == 0          # unknown op
+    # larger problems never need less
+    assert ws(2, 4096, 4096, 4096, 64) >= ws(2, 4096, 4096, 2048, 64)
+
+
+def _nf4(d_out=64, d_in=64, base=0x10000):
+    return _lib._Nf4(d_out, d_in, base, base + 0x1000, base + 0x2000, base + 0x3000)
+
+
+def test_quantize_argument_errors(L):
+    P = ctypes.c_void_p
+    good = _nf4()
+    W, wsp = P(0x20000), P(0x30000)
+    big = 1 << 30
+    assert L.qlora_quantize_nf4(None, ctypes.byref(good), wsp, big, None) == ENULL
+    assert L.qlora_quantize_nf4(W, None, wsp, big, None) == ENULL
+    assert L.qlora_quantize_nf4(W, ctypes.byref(good), None, big, None) == ENULL
+    assert L.qlora_quantize_nf4(P(0x20004), ctypes.byref(good), wsp, big, None) == EALIGN
+    assert L.qlora_quantize_nf4(W, ctypes.byref(good), wsp, 16, None) == EWS
+    bad = _nf4(64, 100)
+    assert L.qlora_quantize_nf4(W, ctypes.byref(bad), wsp, big, None) == ESHAPE
+    bad = _nf4(0, 64)
+    assert L.qlora_quantize_nf4(W, ctypes.byref(bad), wsp, big, None) == ESHAPE
+    mis = _lib._Nf4(64, 64, 0x10008, 0x11000, 0x12000, 0x13000)
+    assert L.qlora_quantize_nf4(W, ctypes.byref(mis), wsp, big, None) == EALIGN
+    nul = _lib._Nf4(64, 64, 0x10000, None, 0x12000, 0x13000)
+    assert L.qlora_quantize_nf4(W, ctypes.byref(nul), wsp, big, None) == ENULL
+    assert L.qlora_dequant_bf16(ctypes.byref(good), None, None) == ENULL
+    assert L.qlora_dequant_bf16(ctypes.byref(good), P(0x40002), None) == EALIGN
+
+
+def test_linear_argument_errors(L):
+    P = ctypes.c_void_p
+    w = _nf4(128, 64)
+    X, A, B, Y, ws = P(0x50000), P(0x60000), P(0x70000), P(0x80000), P(0x90000)
+    big = 1 << 30
+    f = L.qlora_linear_fwd
+    assert f(ctypes.byref(w), X, 4, A, B, 0, 16.0, Y, None, ws, big, None) == ESHAPE
+    assert f(ctypes.byref(w), X, 4, A, B, 300, 16.0, Y, None, ws, big, None) == ESHAPE
+    assert f(ctypes.byref(w), X, -1, A, B, 8, 16.0, Y, None, ws, big, None) == ESHAPE
+    assert f(ctypes.byref(w), None, 4, A, B, 8, 16.0, Y, None, ws, big, None) == ENULL
+    assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, None, None, ws, big, None) == ENULL
+    assert f(ctypes.byref(w), P(0x50002), 4, A, B, 8, 16.0, Y, None, ws, big, None) == EALIGN
+    assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, Y, P(0x1234), ws, big, None) == EALIGN
+    assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, Y, None, ws, 64, None) == EWS
+    assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, Y, None, None, big, None) == ENULL
+    # M = 0 is an empty batch: valid, nothing to do, no GPU work
+    assert f(ctypes.byref(w), None, 0, None, None, 8, 16.0, None, None, None, 0, None) == OK
+    b = L.qlora_linear_bwd
+    dA, dB = P(0xA0000), P(0xB0000)
+    assert b(ctypes.byref(w), X, X, 4, A, B, 8, 16.0, None, None, None, dB, ws, big, None) == ENULL
+    assert b(ctypes.byref(w), X, X, 4, A, B, 8, 16.0, None, None, dA, dB, ws, 64, None) == EWS
+    assert b(ctypes.byref(w), X, P(0x50006), 4, A, B, 8, 16.0, None, None, dA, dB, ws, big,
+             None) == EALIGN
+    assert b(ctypes.byref(w), X, X, 4, A, B, 0, 16.0, None, None, dA, dB, ws, big, None) == ESHAPE
+
+
+def test_grouped_forward_argument_errors(L):
+    items = (_lib._FwdItem * 9)()
+    assert L.qlora_linear_fwd_many(0, items, 4, None) == ESHAPE
+    assert L.qlora_linear_fwd_many(9, items, 4, None) == ESHAPE
+    assert L.qlora_linear_fwd_many(1, None, 4, None) == ENULL
+    # an all-zero item has no valid shape; with a shape but NULL buffers it is
+    # a NULL error; either way nothing is enqueued
+    assert L.qlora_linear_fwd_many(1, items, 4, None) == ESHAPE
+    items[0].w.d_out, items[0].w.d_in, items[0].r = 64, 64, 8
+    assert L.qlora_linear_fwd_many(1, items, 4, None) == ENULL

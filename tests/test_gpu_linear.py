@@ -1,0 +1,161 @@
+"""GPU parity of the NF4 LoRA linear layer, forward and backward, against the
+CPU oracle: Y, dX, dA, dB within 1e-2 normwise-max and 2e-3 relative-
+Frobenius error of the FP64-accumulating oracle; T = s X A^T likewise."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_lora_quantize_amd as q
+from bit_quantized_lora_quantize_amd import inputs
+from parity_util import assert_close, assert_quant_equal, f32, oracle_quant, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+ALPHA = 16.0
+
+
+def _layer(d_out, d_in, M, r, config, layer=0, proj=0, device="cpu"):
+    W = inputs.weight(d_out, d_in, config=config, layer=layer, device=device, proj=proj)
+    A, B = inputs.lora_factors(d_out, d_in, r, config=config, layer=layer, device=device,
+                               proj=proj)
+    X = inputs.activations(M, d_in, config, layer, inputs.T_X, device=device, proj=proj)
+    dY = inputs.activations(M, d_out, config, layer, inputs.T_DY, device=device, proj=proj)
+    return W, A, B, X, dY
+
+
+def _check_layer(orc, W, A, B, X, dY, rows=None, label="", check_bwd=True):
+    d_out, d_in = W.shape
+    M, r = X.shape[0], A.shape[0]
+    s = ALPHA / r
+    say(f"linear parity: {label} d_out={d_out} d_in={d_in} M={M} r={r}")
+    ref_q, _, Wh = oracle_quant(orc, W.cpu())
+    w = q.qlora_quantize_nf4(W.to(DEV).contiguous())
+    Xd, Ad, Bd, dYd = (t.to(DEV).contiguous() for t in (X, A, B, dY))
+    T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    Y = q.qlora_linear_fwd(w, Xd, Ad, Bd, ALPHA, T_save=T)
+    torch.cuda.synchronize()
+    assert_quant_equal(w, ref_q)
+    Xn, An, Bn, dYn = (f32(t) for t in (X, A, B, dY))
+    sel = slice(None) if rows is None else rows
+    Yr = orc.linear_fwd(Wh, Xn, An, Bn, s, rows=rows)
+    assert_close("Y", f32(Y)[sel], Yr)
+    Tr = s * (Xn.astype(np.float64) @ An.astype(np.float64).T)
+    assert_close("T", f32(T), Tr, fro_tol=1e-4, max_tol=1e-4)
+    if not check_bwd:
+        return
+    dXr, dAr, dBr = orc.linear_bwd(Wh, Xn, dYn, An, Bn, s, rows=rows)
+    dX, dA, dB = q.qlora_linear_bwd(w, Xd, dYd, Ad, Bd, ALPHA, T_saved=T)
+    dX2, dA2, dB2 = q.qlora_linear_bwd(w, Xd, dYd, Ad, Bd, ALPHA, T_saved=None)
+    torch.cuda.synchronize()
+    assert_close("dX", f32(dX)[sel], dXr)
+    assert_close("dA", f32(dA), dAr)
+    assert_close("dB", f32(dB), dBr)
+    # recomputing T inside the backward gives the same bytes
+    assert torch.equal(dX.view(torch.int16), dX2.view(torch.int16))
+    assert torch.equal(dA, dA2) and torch.equal(dB, dB2)
+
+
+SMALL = [  # (d_out, d_in, M, r)
+    (256, 256, 16, 8),      # the 256 x 256, 16-token, rank-8 configuration
+    (64, 64, 1, 1),
+    (100, 192, 3, 4),
+    (130, 320, 17, 16),
+    (64, 128, 100, 64),
+    (300, 256, 16, 256),
+    (1, 64, 5, 3),
+    (513, 1088, 33, 24),
+    (200, 4096, 16, 64),
+    (96, 512, 129, 7),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_linear_small(orc, shape):
+    d_out, d_in, M, r = shape
+    cfg = 0 if shape == (256, 256, 16, 8) else 80 + (d_out + d_in + M + r) % 9
+    _check_layer(orc, *_layer(d_out, d_in, M, r, cfg), label=str(shape))
+
+
+def test_linear_empty_batch(orc):
+    d_out, d_in, r = 64, 128, 8
+    W, A, B, _, _ = _layer(d_out, d_in, 1, r, 70)
+    w = q.qlora_quantize_nf4(W.to(DEV))
+    X = torch.empty((0, d_in), dtype=torch.bfloat16, device=DEV)
+    dY = torch.empty((0, d_out), dtype=torch.bfloat16, device=DEV)
+    Y = q.qlora_linear_fwd(w, X, A.to(DEV), B.to(DEV), ALPHA)
+    dA = torch.full((r, d_in), 7.0, device=DEV)
+    dB = torch.full((d_out, r), 7.0, device=DEV)
+    dX, dA, dB = q.qlora_linear_bwd(w, X, dY, A.to(DEV), B.to(DEV), ALPHA, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, d_out) and dX.shape == (0, d_in)
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+
+
+def test_special_cases(orc):
+    """W = 0: Y is the LoRA branch alone.  B = 0: dA = 0 exactly.  A = 0: dB = 0."""
+    d_out, d_in, M, r = 96, 256, 12, 8
+    W, A, B, X, dY = _layer(d_out, d_in, M, r, 71)
+    _check_layer(orc, torch.zeros_like(W), A, B, X, dY, label="W = 0")
+    w = q.qlora_quantize_nf4(W.to(DEV))
+    Xd, dYd = X.to(DEV), dY.to(DEV)
+    _, dA, _ = q.qlora_linear_bwd(w, Xd, dYd, A.to(DEV), torch.zeros_like(B).to(DEV), ALPHA)
+    _, _, dB = q.qlora_linear_bwd(w, Xd, dYd, torch.zeros_like(A).to(DEV), B.to(DEV), ALPHA)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+
+
+def test_deterministic(orc):
+    d_out, d_in, M, r = 320, 1024, 16, 64
+    W, A, B, X, dY = (t.to(DEV) for t in _layer(d_out, d_in, M, r, 72))
+    w = q.qlora_quantize_nf4(W)
+    outs = []
+    for _ in range(2):
+        Y = q.qlora_linear_fwd(w, X, A, B, ALPHA)
+        dX, dA, dB = q.qlora_linear_bwd(w, X, dY, A, B, ALPHA)
+        outs.append((Y.clone(), dX.clone(), dA.clone(), dB.clone()))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+
+
+def test_grouped_forward_matches_oracle(orc):
+    """qlora_linear_fwd_many over projections of different shapes (M = 4)."""
+    M, r = 4, 64
+    shapes = [(256, 512), (1000, 256), (64, 1088)]
+    items, refs = [], []
+    for i, (d_out, d_in) in enumerate(shapes):
+        W, A, B, X, _ = _layer(d_out, d_in, M, r, 73, proj=i)
+        _, _, Wh = oracle_quant(orc, W)
+        refs.append(orc.linear_fwd(Wh, f32(X), f32(A), f32(B), ALPHA / r))
+        w = q.qlora_quantize_nf4(W.to(DEV))
+        ws = torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_FWD, d_out, d_in, M, r),
+                         dtype=torch.uint8, device=DEV)
+        Y = torch.empty((M, d_out), dtype=torch.bfloat16, device=DEV)
+        items.append(q.FwdItem(w, X.to(DEV), A.to(DEV), B.to(DEV), ALPHA, Y, ws))
+    q.qlora_linear_fwd_many(items, M)
+    torch.cuda.synchronize()
+    for it, ref in zip(items, refs):
+        assert_close(f"Y[{it.q.d_out}x{it.q.d_in}]", f32(it.Y), ref)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("proj", [0, 4, 6])
+def test_llama7b_decode_forward(orc, M, proj):
+    """Decode-sized forward (M = 1, 4, 16; r = 64) on the 7B projection
+    shapes, full output compared."""
+    name, d_out, d_in = inputs.LLAMA_7B[proj]
+    W, A, B, X, dY = _layer(d_out, d_in, M, 64, 2, proj=proj, device=DEV)
+    _check_layer(orc, W, A, B, X, dY, label=f"7B {name}", check_bwd=False)
+
+
+@pytest.mark.parametrize("proj", [0, 4, 6])
+def test_llama7b_training_shape(orc, proj):
+    """M = 4096 tokens, r = 64, fwd + bwd on the 7B projection shapes: Y and
+    dX on 24 sampled token rows (first, last, random), dA and dB in full."""
+    name, d_out, d_in = inputs.LLAMA_7B[proj]
+    M = 4096
+    W, A, B, X, dY = _layer(d_out, d_in, M, 64, 3, proj=proj, device=DEV)
+    rng = np.random.default_rng(proj)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 22, replace=False)]))
+    _check_layer(orc, W, A, B, X, dY, rows=rows, label=f"7B {name} train")
