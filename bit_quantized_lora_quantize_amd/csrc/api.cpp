@@ -98,6 +98,14 @@ GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t total_tiles) {
   return {(int)cdiv(nss, per), (int)per, (int)tiles};
 }
 
+// Split of the X A^T reduction over d_in, shared by the forward and the
+// backward's recomputation so a saved and a recomputed T are the same bytes.
+KSplit t_split(int64_t d_in, int64_t M, int64_t r) {
+  if (M <= kSmallM) return split_k(d_in, (int)std::min<int64_t>(8, std::max<int64_t>(1, d_in / 1024)));
+  const int64_t base = cdiv(M, 16) * cdiv(r, 64);
+  return split_k(d_in, (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base))));
+}
+
 struct FwdPlan {
   bool small;
   KSplit tk;          // rank-down split of X A^T
@@ -118,7 +126,7 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.tiles_n = cdiv(r, 64);
   if (p.small) {
     p.tiles_m = 1;
-    p.tk = split_k(d_in, (int)std::min<int64_t>(8, std::max<int64_t>(1, d_in / 1024)));
+    p.tk = t_split(d_in, M, r);
     p.t_part = c.take<float>(p.tk.splits * M * r);
     p.xp = c.take<uint16_t>(M * d_in);
     p.gs = gemv_split(d_out, d_in, cdiv(d_out, 64));
@@ -126,8 +134,7 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
     p.counters = c.take<uint32_t>(p.gs.tiles);
   } else {
     p.tiles_m = cdiv(M, 16);
-    const int64_t base = p.tiles_m * p.tiles_n;
-    p.tk = split_k(d_in, (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base))));
+    p.tk = t_split(d_in, M, r);
     p.t_part = c.take<float>(p.tk.splits * M * r);
     p.t_buf = c.take<float>(M * r);
   }
@@ -152,8 +159,8 @@ struct BwdPlan {
 int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
   const int64_t tiles = cdiv(N, 128) * cdiv(r, 64);
   int64_t ms = std::max<int64_t>(1, std::min<int64_t>(cdiv(M, 32), cdiv(kTargetWgs, tiles)));
-  *per = round_up(cdiv(M, ms), 32);
-  return (int)cdiv(M, *per);
+  *per = std::max<int64_t>(32, round_up(cdiv(M, ms), 32));
+  return (int)std::max<int64_t>(1, cdiv(M, *per));
 }
 
 BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
@@ -162,9 +169,9 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.t.small = false;
   p.t.tiles_m = cdiv(M, 16);
   p.t.tiles_n = cdiv(r, 64);
-  const int64_t base = p.t.tiles_m * p.t.tiles_n;
+  const int64_t base = std::max<int64_t>(1, p.t.tiles_m * p.t.tiles_n);
   const int want = (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base)));
-  p.t.tk = split_k(d_in, want);
+  p.t.tk = t_split(d_in, M, r);
   p.t.t_part = c.take<float>(p.t.tk.splits * M * r);
   p.t.t_buf = c.take<float>(M * r);
   p.uk = split_k(d_out, want);

@@ -61,6 +61,10 @@ def test_workspace_sizes(L):
     assert ws(0, 256, 256) > 0
     assert ws(1, 4096, 4096, 16, 64) > 0 and ws(2, 4096, 4096, 4096, 64) > 0
     assert ws(1, 4096, 4096, 0, 64) > 0           # M = 0 is valid
+    assert ws(2, 64, 128, 0, 8) > 0
+    for M in (0, 1, 15, 16, 17, 31, 32, 33, 4096):
+        for r in (1, 8, 64, 256):
+            assert ws(1, 100, 192, M, r) > 0 and ws(2, 100, 192, M, r) > 0
     assert ws(1, 4096, 4096, 16, 0) == 0          # r out of range
     assert ws(1, 4096, 4096, 16, 257) == 0
     assert ws(1, 4096, 100, 16, 8) == 0           # d_in % 64 != 0
