@@ -1,0 +1,389 @@
+"""Benchmark of the NF4 LoRA linear layer (libqlora) on one MI355X.
+
+Headline (the JSON line's `value`): forward + backward throughput in TFLOP/s
+of one LLaMA-7B-shaped decoder layer's seven projections (q, k, v, o 4096 x
+4096; gate, up 11008 x 4096; down 4096 x 11008) at M = 4096 tokens (batch 4 x
+sequence 1024), LoRA rank 64, alpha 16, NF4 + FP8 double-quantized frozen
+base, BF16 activations.  One step = for every projection: forward (saving
+T = s X A^T) then backward (dX, dA, dB), 14 library calls.  Useful FLOPs per
+projection = 4 M d_in d_out + 6 M r (d_in + d_out).
+
+The same line also carries, each measured in the same run:
+  decode   fused forward at M = 1, 4, 16 over the 7B layer in one grouped call
+           per layer, scored as HBM GB/s over the packed weight bytes (NF4
+           codes + FP8 scale codes + FP32 second-level scales + mean); four
+           distinct quantized copies of the layer rotate so the 256 MB
+           last-level cache holds none of them;
+  quant    quantize and dequantize of the 7B layer, GB/s over the algorithmic
+           bytes (read FP32 W + write packed state; read packed + write BF16);
+  stack65b forward + backward of all 560 LoRA linears of an 80-layer
+           LLaMA-65B-shaped stack (hidden 8192, FFN 22016) at M = 2048, one
+           layer at a time, packed weights resident in HBM;
+  roofline the dominant kernel (fused dequant-GEMM), timed per launch with HIP
+           events placed around it by the library on the launch stream;
+  cpu_baseline  the CPU oracle on a bounded sample of the headline workload.
+All inputs are seeded synthetic tensors (bit_quantized_lora_quantize_amd.inputs).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+import bit_quantized_lora_quantize_amd as q  # noqa: E402
+from bit_quantized_lora_quantize_amd import inputs  # noqa: E402
+
+METRIC = "NF4-LoRA linear: eff. HBM GB/s (M<=16) & TFLOPS fwd+bwd (M=4096)"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+R, ALPHA = 64, 16.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def packed_bytes(d_out, d_in):
+    return sum(q.qlora_nf4_sizes(d_out, d_in))
+
+
+def useful_flops(M, d_out, d_in, r):
+    return 4 * M * d_in * d_out + 6 * M * r * (d_in + d_out)
+
+
+class KernelTimer:
+    """Per-launch events around the library's weight kernel, on the stream
+    the library launches it on (torch's current stream)."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def arm(self, tag):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        q.qlora_time_next_weight_kernel(s, e)
+        self.pairs.append((tag, s, e))
+
+    def durations_ms(self, tag):
+        return [s.elapsed_time(e) for t, s, e in self.pairs if t == tag]
+
+
+# ------------------------------------------------------------------ layers
+
+class Layer:
+    """Quantized weights and LoRA factors of one decoder layer."""
+
+    def __init__(self, shapes, M, config, layer, dev, fwd_workspace=False):
+        self.items = []
+        for p, (name, d_out, d_in) in enumerate(shapes):
+            W = inputs.weight(d_out, d_in, config, layer, device=dev, proj=p)
+            w = q.qlora_quantize_nf4(W)
+            del W
+            A, B = inputs.lora_factors(d_out, d_in, R, config, layer, device=dev, proj=p)
+            it = dict(name=name, w=w, A=A, B=B, d_out=d_out, d_in=d_in)
+            if fwd_workspace:
+                it["wsf"] = torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_FWD, d_out, d_in, M, R),
+                                        dtype=torch.uint8, device=dev)
+            self.items.append(it)
+
+
+class Activations:
+    """Per projection shape: X, dY, outputs, saved T and workspaces, shared by
+    every layer (layers run one after another on one stream)."""
+
+    def __init__(self, shapes, M, config, dev):
+        self.buf = {}
+        for p, (name, d_out, d_in) in enumerate(shapes):
+            key = (d_out, d_in)
+            if key in self.buf:
+                continue
+            self.buf[key] = dict(
+                X=inputs.activations(M, d_in, config, 0, inputs.T_X, device=dev, proj=p),
+                dY=inputs.activations(M, d_out, config, 0, inputs.T_DY, device=dev, proj=p),
+                Y=torch.empty((M, d_out), dtype=torch.bfloat16, device=dev),
+                dX=torch.empty((M, d_in), dtype=torch.bfloat16, device=dev),
+                dA=torch.empty((R, d_in), dtype=torch.float32, device=dev),
+                dB=torch.empty((d_out, R), dtype=torch.float32, device=dev),
+                T=torch.empty((M, R), dtype=torch.float32, device=dev),
+                wsf=torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_FWD, d_out, d_in, M, R),
+                                dtype=torch.uint8, device=dev),
+                wsb=torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_BWD, d_out, d_in, M, R),
+                                dtype=torch.uint8, device=dev))
+
+
+def train_step(layer, acts, timer=None):
+    for it in layer.items:
+        a = acts.buf[(it["d_out"], it["d_in"])]
+        if timer:
+            timer.arm("fwd")
+        q.qlora_linear_fwd(it["w"], a["X"], it["A"], it["B"], ALPHA, Y=a["Y"], T_save=a["T"],
+                           workspace=a["wsf"])
+        if timer:
+            timer.arm("bwd")
+        q.qlora_linear_bwd(it["w"], a["X"], a["dY"], it["A"], it["B"], ALPHA, T_saved=a["T"],
+                           dX=a["dX"], dA=a["dA"], dB=a["dB"], workspace=a["wsb"])
+
+
+def timed(fn, steps, warmup):
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+# -------------------------------------------------------------- workloads
+
+def bench_train7b(dev, steps, warmup):
+    M = 4096
+    log(f"7B layer fwd+bwd: M={M} r={R}; quantizing 7 projections")
+    layer = Layer(inputs.LLAMA_7B, M, 3, 0, dev)
+    acts = Activations(inputs.LLAMA_7B, M, 3, dev)
+    torch.cuda.synchronize()
+    flops = sum(useful_flops(M, d_out, d_in, R) for _, d_out, d_in in inputs.LLAMA_7B)
+    for _ in range(warmup):
+        train_step(layer, acts)
+    torch.cuda.synchronize()
+    timer = KernelTimer()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        train_step(layer, acts, timer)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    # dominant kernel: the fused dequant-GEMM, forward and backward launches
+    gemm_flops_fwd = [2 * M * d_out * (d_in + R) for _, d_out, d_in in inputs.LLAMA_7B]
+    gemm_flops_bwd = [2 * M * d_in * (d_out + R) for _, d_out, d_in in inputs.LLAMA_7B]
+    dur_f = timer.durations_ms("fwd")
+    dur_b = timer.durations_ms("bwd")
+    fl_f = gemm_flops_fwd * steps
+    fl_b = gemm_flops_bwd * steps
+    ach_f = sum(fl_f) / (sum(dur_f) * 1e-3) / 1e12
+    ach_b = sum(fl_b) / (sum(dur_b) * 1e-3) / 1e12
+    ach = (sum(fl_f) + sum(fl_b)) / ((sum(dur_f) + sum(dur_b)) * 1e-3) / 1e12
+    res = dict(elapsed=el, flops_per_step=flops, tflops=flops * steps / el / 1e12,
+               ms_per_step=el / steps * 1e3,
+               gemm=dict(fwd_avg_us=sum(dur_f) / len(dur_f) * 1e3,
+                         bwd_avg_us=sum(dur_b) / len(dur_b) * 1e3,
+                         fwd_tflops=ach_f, bwd_tflops=ach_b, tflops=ach,
+                         flops_per_launch_avg=(sum(fl_f) + sum(fl_b)) / (len(fl_f) + len(fl_b)),
+                         avg_launch_ms=(sum(dur_f) + sum(dur_b)) / (len(dur_f) + len(dur_b))))
+    log(f"7B fwd+bwd: {res['tflops']:.1f} TFLOP/s ({res['ms_per_step']:.3f} ms/step); "
+        f"fused GEMM fwd {ach_f:.1f} bwd {ach_b:.1f} TFLOP/s")
+    del layer, acts
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode7b(dev, steps, warmup, copies=4):
+    out = {}
+    scored = sum(packed_bytes(d_out, d_in) for _, d_out, d_in in inputs.LLAMA_7B)
+    for M in (1, 4, 16):
+        layers = [Layer(inputs.LLAMA_7B, M, 2, c, dev, fwd_workspace=True)
+                  for c in range(copies)]
+        xs = {}
+        for c in range(copies):
+            for p, (name, d_out, d_in) in enumerate(inputs.LLAMA_7B):
+                xs[(c, p)] = (inputs.activations(M, d_in, 2, c, inputs.T_X, device=dev, proj=p),
+                              torch.empty((M, d_out), dtype=torch.bfloat16, device=dev))
+        groups = []
+        for c, L in enumerate(layers):
+            groups.append([q.FwdItem(it["w"], xs[(c, p)][0], it["A"], it["B"], ALPHA,
+                                     xs[(c, p)][1], it["wsf"]) for p, it in enumerate(L.items)])
+        torch.cuda.synchronize()
+        timer = KernelTimer()
+        n = max(steps, 8) * copies
+
+        def step(i, tm=None):
+            g = groups[(0 if i is None else i) % copies]
+            if tm:
+                tm.arm("gemv")
+            q.qlora_linear_fwd_many(g, M)
+
+        for i in range(max(warmup, 2) * copies):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(i, timer)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        durs = timer.durations_ms("gemv")
+        k_avg = sum(durs) / len(durs) * 1e-3
+        out[f"M{M}"] = dict(layer_us=el / n * 1e6, gbps=scored / (el / n) / 1e9,
+                            gemv_us=k_avg * 1e6, gemv_gbps=scored / k_avg / 1e9,
+                            gemv_frac=scored / k_avg / 1e9 / PEAK_HBM_GBS)
+        log(f"decode M={M}: layer {el / n * 1e6:.1f} us = {scored / (el / n) / 1e9:.0f} GB/s; "
+            f"weight kernel {k_avg * 1e6:.1f} us = {scored / k_avg / 1e9:.0f} GB/s")
+        del layers, groups, xs
+        torch.cuda.empty_cache()
+    out["scored_bytes_per_layer"] = scored
+    return out
+
+
+def bench_quant7b(dev, steps, warmup):
+    Ws = [inputs.weight(d_out, d_in, 1, 0, outliers=True, device=dev, proj=p)
+          for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B)]
+    qs = [q.qlora_quantize_nf4(W) for W in Ws]
+    outs = [torch.empty(W.shape, dtype=torch.bfloat16, device=dev) for W in Ws]
+    wss = [torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_QUANTIZE, *W.shape), dtype=torch.uint8,
+                       device=dev) for W in Ws]
+    n = sum(W.numel() for W in Ws)
+    packed = sum(w.nbytes() for w in qs)
+    bq = 4 * n + packed
+    bd = packed + 2 * n
+
+    def qstep(i, tm=None):
+        for W, w, ws in zip(Ws, qs, wss):
+            if tm:
+                tm.arm("q")
+            q.qlora_quantize_nf4(W, out=w, workspace=ws)
+
+    def dstep(i, tm=None):
+        for w, o in zip(qs, outs):
+            if tm:
+                tm.arm("d")
+            q.qlora_dequant_bf16(w, out=o)
+
+    res = {}
+    for name, fn, nbytes in (("quantize", qstep, bq), ("dequant", dstep, bd)):
+        for _ in range(warmup):
+            fn(None)
+        torch.cuda.synchronize()
+        tm = KernelTimer()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i, tm)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / steps
+        res[name] = dict(layer_us=el * 1e6, gbps=nbytes / el / 1e9, bytes=nbytes)
+        log(f"{name} 7B layer: {el * 1e6:.1f} us = {nbytes / el / 1e9:.0f} GB/s")
+    del Ws, qs, outs, wss
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_stack65b(dev, steps, warmup):
+    M = 2048
+    log(f"65B stack: {inputs.LLAMA_65B_LAYERS} layers x 7, M={M}; quantizing")
+    t0 = time.perf_counter()
+    layers = [Layer(inputs.LLAMA_65B, M, 4, l, dev) for l in range(inputs.LLAMA_65B_LAYERS)]
+    acts = Activations(inputs.LLAMA_65B, M, 4, dev)
+    torch.cuda.synchronize()
+    resident = sum(it["w"].nbytes() for L in layers for it in L.items)
+    log(f"65B stack ready in {time.perf_counter() - t0:.1f} s; packed weights "
+        f"{resident / 1e9:.2f} GB resident")
+    flops = inputs.LLAMA_65B_LAYERS * sum(useful_flops(M, d_out, d_in, R)
+                                          for _, d_out, d_in in inputs.LLAMA_65B)
+
+    def step(i):
+        for L in layers:
+            train_step(L, acts)
+
+    el = timed(step, steps, warmup)
+    res = dict(tflops=flops * steps / el / 1e12, s_per_step=el / steps,
+               resident_packed_gb=resident / 1e9, flops_per_step=flops)
+    log(f"65B stack fwd+bwd: {res['tflops']:.1f} TFLOP/s ({res['s_per_step']:.3f} s/step)")
+    del layers, acts
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(tokens=128):
+    """The oracle's fwd + bwd of the 7B layer on `tokens` token rows."""
+    import numpy as np
+    import oracle
+    log(f"cpu baseline: oracle fwd+bwd of the 7B layer on {tokens} tokens")
+    total_t, flops = 0.0, 0
+    for p, (name, d_out, d_in) in enumerate(inputs.LLAMA_7B):
+        W = inputs.weight(d_out, d_in, 3, 0, proj=p).numpy()
+        codes, scodes, s2, mean = oracle.quantize_nf4(W)
+        Wh = oracle.bf16_bits_to_f32(oracle.dequant_bf16(codes, scodes, s2, mean, W.size)
+                                     ).reshape(d_out, d_in)
+        A, B = (t.float().numpy() for t in inputs.lora_factors(d_out, d_in, R, 3, 0, proj=p))
+        X = inputs.activations(tokens, d_in, 3, 0, inputs.T_X, proj=p).float().numpy()
+        dY = inputs.activations(tokens, d_out, 3, 0, inputs.T_DY, proj=p).float().numpy()
+        t0 = time.perf_counter()
+        oracle.linear_fwd(Wh, X, A, B, ALPHA / R)
+        oracle.linear_bwd(Wh, X, dY, A, B, ALPHA / R)
+        total_t += time.perf_counter() - t0
+        flops += useful_flops(tokens, d_out, d_in, R)
+    return dict(value=flops / total_t / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"fwd+bwd (Y, dX, dA, dB) of the 7 LLaMA-7B projections on {tokens} of "
+                       f"the 4096 tokens, r={R}, FP64 accumulation; quantization untimed; "
+                       f"{total_t:.1f} s of CPU time")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip", default="", help="comma list of: decode,quant,stack65b,cpu")
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    skip = set(s for s in args.skip.split(",") if s)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q.lib()
+    log(f"device {torch.cuda.get_device_name(dev)}; steps={args.steps} warmup={args.warmup}")
+
+    train = bench_train7b(dev, args.steps, args.warmup)
+    extra = {}
+    if "decode" not in skip:
+        extra["decode_7b"] = bench_decode7b(dev, args.steps, args.warmup)
+    if "quant" not in skip:
+        extra["quant_7b"] = bench_quant7b(dev, max(3, args.steps // 2), 1)
+    if "stack65b" not in skip:
+        extra["stack_65b"] = bench_stack65b(dev, max(1, min(args.steps, 2)), 1)
+    cpu = None if "cpu" in skip else cpu_baseline(args.cpu_tokens)
+
+    g = train["gemm"]
+    line = {
+        "metric": METRIC,
+        "value": round(train["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(train["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_layer_7proj_fwd_bwd_M4096_r64",
+                   "tokens": 4096, "rank": R, "lora_alpha": ALPHA,
+                   "projections": [f"{n} {o}x{i}" for n, o, i in inputs.LLAMA_7B],
+                   "quant": "NF4 block 64 + FP8 E4M3FN double quant block 256",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(g["tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_gemm (fused dequant-GEMM, fwd and bwd)",
+                     "avg_launch_us": round(g["avg_launch_ms"] * 1e3, 2),
+                     "fwd_avg_us": round(g["fwd_avg_us"], 2), "bwd_avg_us": round(g["bwd_avg_us"], 2),
+                     "fwd_tflops": round(g["fwd_tflops"], 2), "bwd_tflops": round(g["bwd_tflops"], 2)},
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,5 +22,6 @@ from ._lib import (  # noqa: F401
     qlora_nf4_sizes,
     qlora_quantize_nf4,
     qlora_status_string,
+    qlora_time_next_weight_kernel,
     qlora_workspace_bytes,
 )

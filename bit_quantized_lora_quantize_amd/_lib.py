@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_fwd_many.argtypes = [ctypes.c_int, ctypes.POINTER(_FwdItem), _I64, _P]
         L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.qlora_time_next_weight_kernel.argtypes = [_P, _P]
         _lib = L
     return _lib
 
@@ -98,6 +99,14 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def qlora_time_next_weight_kernel(start: Optional["torch.cuda.Event"],
+                                  stop: Optional["torch.cuda.Event"]) -> None:
+    """Bracket the next weight-kernel launch with two recorded events."""
+    sp = ctypes.c_void_p(start.cuda_event) if start is not None else None
+    ep = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
+    _check(lib().qlora_time_next_weight_kernel(sp, ep), "qlora_time_next_weight_kernel")
 
 
 def qlora_nf4_sizes(d_out: int, d_in: int) -> tuple[int, int, int, int]:

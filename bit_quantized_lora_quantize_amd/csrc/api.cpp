@@ -14,6 +14,24 @@
 
 using namespace qlora;
 
+// ------------------------------------------------------------ timing aid
+namespace {
+hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+bool g_ev_armed = false;
+}  // namespace
+
+namespace qlora {
+void weight_kernel_begin(hipStream_t st) {
+  if (g_ev_armed && g_ev_start) (void)hipEventRecord(g_ev_start, st);
+}
+void weight_kernel_end(hipStream_t st) {
+  if (!g_ev_armed) return;
+  if (g_ev_stop) (void)hipEventRecord(g_ev_stop, st);
+  g_ev_armed = false;
+  g_ev_start = g_ev_stop = nullptr;
+}
+}  // namespace qlora
+
 namespace {
 
 constexpr int64_t kMaxRank = 256;
@@ -387,6 +405,13 @@ const char* qlora_status_string(int status) {
 }
 
 int qlora_abi_version(void) { return (1 << 16) | 0; }
+
+int qlora_time_next_weight_kernel(void* start_event, void* stop_event) {
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
+  g_ev_armed = g_ev_start != nullptr || g_ev_stop != nullptr;
+  return QLORA_OK;
+}
 
 int qlora_nf4_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* scale_codes_bytes,
                     size_t* scale2_bytes, size_t* scale_mean_bytes) {

@@ -237,13 +237,17 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
 
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.d_out + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+  weight_kernel_begin(st);
   hipLaunchKernelGGL(k_gemm<false>, grid, dim3(256), 0, st, a);
+  weight_kernel_end(st);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.d_in + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+  weight_kernel_begin(st);
   hipLaunchKernelGGL(k_gemm<true>, grid, dim3(256), 0, st, a);
+  weight_kernel_end(st);
   return hipGetLastError();
 }
 

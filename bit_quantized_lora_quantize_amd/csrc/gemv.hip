@@ -189,7 +189,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int total_wgs, hipStream_t st) {
+  weight_kernel_begin(st);
   hipLaunchKernelGGL(k_gemv, dim3(total_wgs), dim3(256), 0, st, a);
+  weight_kernel_end(st);
   return hipGetLastError();
 }
 

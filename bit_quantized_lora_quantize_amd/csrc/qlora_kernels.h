@@ -7,6 +7,10 @@
 
 namespace qlora {
 
+// Optional event pair around the next weight-kernel launch (timing aid).
+void weight_kernel_begin(hipStream_t st);
+void weight_kernel_end(hipStream_t st);
+
 // ----------------------------------------------------------- quantization
 constexpr int kLutSize = 129;     // buckets floor(64 x) + 64 for x in [-1, 1]
 constexpr int64_t kTreeLds = 4096; // top tree levels done in one workgroup

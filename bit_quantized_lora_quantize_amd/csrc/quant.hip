@@ -189,8 +189,10 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   const int64_t G = (n1 + kGroup - 1) / kGroup;
   int64_t Gp = 1;
   while (Gp < G) Gp *= 2;
+  weight_kernel_begin(st);
   hipLaunchKernelGGL(k_absmax_encode, dim3(grid_for(n1 * 8, 256, 8192)), dim3(256), 0, st, W,
                      n1, codes, ws.absmax, lut);
+  weight_kernel_end(st);
   hipLaunchKernelGGL(k_group_sums, dim3((unsigned)((Gp + 3) / 4)), dim3(256), 0, st, ws.absmax,
                      n1, G, Gp, ws.part);
   int64_t len = Gp;
@@ -209,8 +211,10 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, const float* scale2,
                           const float* mean, int64_t n, uint16_t* out, hipStream_t st) {
   const int64_t n1 = n / kBlock;
+  weight_kernel_begin(st);
   hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(n1, 256, 8192)), dim3(256), 0, st, codes,
                      scale_codes, scale2, mean, n1, out);
+  weight_kernel_end(st);
   return hipGetLastError();
 }
 

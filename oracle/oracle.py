@@ -65,6 +65,7 @@ def _load():
         lib.orc_map_nf4_index.argtypes = [P, I, P]
         lib.orc_map_fp8_encode.argtypes = [P, I, P]
         lib.orc_map_bf16_rne.argtypes = [P, I, P]
+        lib.orc_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -75,6 +76,11 @@ def _ptr(a: np.ndarray):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 # ---------------------------------------------------------------- scalars

@@ -365,3 +365,11 @@ void orc_map_bf16_rne(const float *x, int64_t n, uint16_t *out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_rne(x[i]);
 }
+
+/* Threads the OpenMP loops above use (1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif
