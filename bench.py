@@ -60,20 +60,48 @@ def useful_flops(M, d_out, d_in, r):
 
 
 class KernelTimer:
-    """Per-launch events around the library's weight kernel, on the stream
-    the library launches it on (torch's current stream)."""
+    """Per-launch HIP events around the library's weight kernel.  The library
+    records them on the stream it launches the kernel on (torch's current
+    stream); elapsed times are read after the timed region synchronizes."""
+
+    _hip = None
 
     def __init__(self):
+        import ctypes
+        if KernelTimer._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            KernelTimer._hip = hip
+        self.ct = ctypes
         self.pairs = []
 
+    def _event(self):
+        ev = self.ct.c_void_p()
+        assert KernelTimer._hip.hipEventCreate(self.ct.byref(ev)) == 0
+        return ev
+
     def arm(self, tag):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        q.qlora_time_next_weight_kernel(s, e)
+        s, e = self._event(), self._event()
+        q.lib().qlora_time_next_weight_kernel(s, e)
         self.pairs.append((tag, s, e))
 
     def durations_ms(self, tag):
-        return [s.elapsed_time(e) for t, s, e in self.pairs if t == tag]
+        out = []
+        for t, s, e in self.pairs:
+            if t != tag:
+                continue
+            ms = self.ct.c_float()
+            assert KernelTimer._hip.hipEventElapsedTime(self.ct.byref(ms), s, e) == 0
+            out.append(ms.value)
+        return out
+
+    def __del__(self):
+        for _, s, e in getattr(self, "pairs", []):
+            KernelTimer._hip.hipEventDestroy(s)
+            KernelTimer._hip.hipEventDestroy(e)
 
 
 # ------------------------------------------------------------------ layers
