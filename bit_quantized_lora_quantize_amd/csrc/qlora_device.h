@@ -168,6 +168,16 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] B[16x32].  Lane l holds row
+// (A) / column (B) l%32 and the eight contraction indices of group l/32; the
+// accumulator element v of lane l holds D[8*(v/4) + 4*(l/32) + v%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // FP32 value -> (hi, lo) BF16 pair with hi + lo = v to about 16 bits.
 __device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
   f32x2 p = {v, 0.0f};
