@@ -94,14 +94,21 @@ QuantPlan plan_quant(int64_t d_out, int64_t d_in, void* ws) {
   return p;
 }
 
-// Rank-down split of K (multiple of 32 per split).
+// Split of a rank-down reduction over K.  Small M (one-wavefront tiles):
+// 128 of K per split.  Large M (256-row tiles): splits chosen to fill the
+// chip, 64-multiples of K per split, at most 16.
 struct KSplit {
   int splits;
   int64_t per;
 };
-KSplit split_k(int64_t K, int splits) {
-  splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, cdiv(K, 32)));
-  int64_t per = round_up(cdiv(K, splits), 32);
+KSplit rank_split(int64_t K, int64_t M, int64_t N) {
+  if (M <= kSmallM) {
+    const int64_t per = 128;
+    return {(int)cdiv(K, per), per};
+  }
+  const int64_t tiles = cdiv(M, 256) * cdiv(N, 64);
+  int64_t S = std::max<int64_t>(1, std::min<int64_t>({16, cdiv(256, tiles), cdiv(K, 64)}));
+  const int64_t per = round_up(cdiv(K, S), 64);
   return {(int)cdiv(K, per), per};
 }
 
@@ -116,20 +123,11 @@ GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t total_tiles) {
   return {(int)cdiv(nss, per), (int)per, (int)tiles};
 }
 
-// Split of the X A^T reduction over d_in, shared by the forward and the
-// backward's recomputation so a saved and a recomputed T are the same bytes.
-KSplit t_split(int64_t d_in, int64_t M, int64_t r) {
-  if (M <= kSmallM) return split_k(d_in, (int)std::min<int64_t>(8, std::max<int64_t>(1, d_in / 1024)));
-  const int64_t base = cdiv(M, 16) * cdiv(r, 64);
-  return split_k(d_in, (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base))));
-}
-
 struct FwdPlan {
   bool small;
-  KSplit tk;          // rank-down split of X A^T
-  int64_t tiles_m, tiles_n;
+  KSplit tk;          // rank-down split of X A^T (shared with the backward)
   float* t_part;      // [tk.splits][M][r]
-  float* t_buf;       // [M][r] (large M, when T_save is NULL)
+  float* t_buf;       // [M][r] when T_save is NULL
   uint16_t* xp;       // [M][d_in] permuted X (small M)
   float* gemv_part;   // [ksplit][16][d_out]
   uint32_t* counters; // [tiles]
@@ -141,32 +139,30 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   FwdPlan p{};
   p.small = M <= kSmallM;
   Carver c(ws);
-  p.tiles_n = cdiv(r, 64);
+  p.tk = rank_split(d_in, M, r);
+  p.t_part = c.take<float>(p.tk.splits * M * r);
+  p.t_buf = c.take<float>(M * r);
   if (p.small) {
-    p.tiles_m = 1;
-    p.tk = t_split(d_in, M, r);
-    p.t_part = c.take<float>(p.tk.splits * M * r);
     p.xp = c.take<uint16_t>(M * d_in);
     p.gs = gemv_split(d_out, d_in, cdiv(d_out, 64));
     p.gemv_part = c.take<float>((int64_t)p.gs.ksplit * 16 * d_out);
     p.counters = c.take<uint32_t>(p.gs.tiles);
-  } else {
-    p.tiles_m = cdiv(M, 16);
-    p.tk = t_split(d_in, M, r);
-    p.t_part = c.take<float>(p.tk.splits * M * r);
-    p.t_buf = c.take<float>(M * r);
   }
   p.bytes = c.off + 256;
   return p;
 }
 
 struct BwdPlan {
-  FwdPlan t;          // recomputation of T (large-M form, always finished)
+  KSplit tk;          // recomputation of T (same split as the forward)
+  float* t_part;      // [tk.splits][M][r]
+  float* t_buf;       // [M][r]
   KSplit uk;          // rank-down split of dY B over d_out
   int64_t ldbt;       // row stride of B^T
   uint16_t* bt;       // [r][ldbt]
   float* u_part;      // [uk.splits][M][r]
   float* u;           // [M][r]
+  int64_t ldp;        // token stride of the transposed hi/lo copies
+  uint16_t *ut_hi, *ut_lo, *tt_hi, *tt_lo;  // [r][ldp]
   int ms_a, ms_b;     // token splits of dA and dB
   int64_t mper_a, mper_b;
   float* da_part;     // [ms_a][r][d_in]
@@ -174,29 +170,32 @@ struct BwdPlan {
   size_t bytes;
 };
 
+// Token split of dA / dB: about 256 workgroups, partials at most a quarter of
+// the activation bytes; a multiple of 16 tokens per split.
 int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
-  const int64_t tiles = cdiv(N, 128) * cdiv(r, 64);
-  int64_t ms = std::max<int64_t>(1, std::min<int64_t>(cdiv(M, 32), cdiv(kTargetWgs, tiles)));
-  *per = std::max<int64_t>(32, round_up(cdiv(M, ms), 32));
+  const int64_t tiles = cdiv(N, 512) * cdiv(r, 64);
+  const int64_t cap = std::max<int64_t>(1, M / (4 * std::max<int64_t>(r, 1)));
+  int64_t ms = std::max<int64_t>(1, std::min<int64_t>({cdiv(256, tiles), cap, cdiv(M, 16)}));
+  *per = std::max<int64_t>(16, round_up(cdiv(M, ms), 16));
   return (int)std::max<int64_t>(1, cdiv(M, *per));
 }
 
 BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   BwdPlan p{};
   Carver c(ws);
-  p.t.small = false;
-  p.t.tiles_m = cdiv(M, 16);
-  p.t.tiles_n = cdiv(r, 64);
-  const int64_t base = std::max<int64_t>(1, p.t.tiles_m * p.t.tiles_n);
-  const int want = (int)std::max<int64_t>(1, std::min<int64_t>(8, cdiv(kTargetWgs, base)));
-  p.t.tk = t_split(d_in, M, r);
-  p.t.t_part = c.take<float>(p.t.tk.splits * M * r);
-  p.t.t_buf = c.take<float>(M * r);
-  p.uk = split_k(d_out, want);
+  p.tk = rank_split(d_in, M, r);
+  p.t_part = c.take<float>(p.tk.splits * M * r);
+  p.t_buf = c.take<float>(M * r);
+  p.uk = rank_split(d_out, M, r);
   p.ldbt = round_up(d_out, 64);
   p.bt = c.take<uint16_t>(r * p.ldbt);
   p.u_part = c.take<float>(p.uk.splits * M * r);
   p.u = c.take<float>(M * r);
+  p.ldp = round_up(std::max<int64_t>(M, 1), 16);
+  p.ut_hi = c.take<uint16_t>(r * p.ldp);
+  p.ut_lo = c.take<uint16_t>(r * p.ldp);
+  p.tt_hi = c.take<uint16_t>(r * p.ldp);
+  p.tt_lo = c.take<uint16_t>(r * p.ldp);
   p.ms_a = token_splits(M, d_in, r, &p.mper_a);
   p.ms_b = token_splits(M, d_out, r, &p.mper_b);
   p.da_part = c.take<float>((int64_t)p.ms_a * r * d_in);
@@ -260,6 +259,8 @@ void fill_rank_desc(RankDownDesc& d, const uint16_t* P, const uint16_t* Q, int64
 
 int rank_down_single(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N, int64_t K,
                      int64_t ldq, const KSplit& ks, float* part, hipStream_t st) {
+  if (M > kSmallM)
+    return hip_status(launch_rank_down_big(P, Q, M, N, K, ldq, ks.per, ks.splits, part, st));
   RankDownArgs a{};
   fill_rank_desc(a.d[0], P, Q, M, N, K, ldq, ks, part, nullptr, 0);
   a.count = 1;
@@ -313,7 +314,8 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       float* T = f.T_save ? f.T_save : p.t_buf;
       int s = rank_down_single(f.X, f.A, M, f.r, q->d_in, q->d_in, p.tk, p.t_part, st);
       if (s) return s;
-      s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, f.r, f.alpha / (float)f.r, T, st));
+      s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, f.r, f.alpha / (float)f.r, T,
+                                        nullptr, nullptr, 0, st));
       if (s) return s;
       GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, T, f.B, f.Y,
                  M,        q->d_out,      q->d_in,  f.r};
@@ -323,7 +325,9 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     return QLORA_OK;
   }
 
-  // Small M: one rank-down launch and one weight-streaming launch for the group.
+  // Small M: for the whole group, one rank-down launch (X A^T partials, the
+  // permuted X copy, counters cleared), one finish launch (T) and one
+  // weight-streaming launch.
   FwdPlan plans[kMaxGroup];
   int64_t total_tiles = 0;
   for (int i = 0; i < count; ++i) {
@@ -337,6 +341,8 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
   ga.count = count;
   ga.M = (int)M;
   int gwgs = 0;
+  FinishArgs fa{};
+  fa.count = count;
   for (int i = 0; i < count; ++i) {
     const FwdItemArgs& f = items[i];
     const qlora_nf4_t* q = f.q;
@@ -351,7 +357,10 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     d.scale2 = q->scale2;
     d.mean = q->scale_mean;
     d.Xp = p.xp;
-    d.t_part = p.t_part;
+    float* T = f.T_save ? f.T_save : p.t_buf;
+    fa.d[i] = FinishDesc{p.t_part, T, nullptr, nullptr, M, f.r, M, f.alpha / (float)f.r,
+                         p.tk.splits, 0};
+    d.t_part = T;
     d.B = f.B;
     d.Y = f.Y;
     d.part = p.gemv_part;
@@ -359,8 +368,8 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     d.d_out = q->d_out;
     d.d_in = q->d_in;
     d.r = f.r;
-    d.t_scale = f.alpha / (float)f.r;
-    d.t_splits = p.tk.splits;
+    d.t_scale = 1.0f;
+    d.t_splits = 1;
     d.ksplit = gs.ksplit;
     d.ss_per_split = gs.ss_per;
     d.tiles = gs.tiles;
@@ -374,17 +383,9 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     }
   }
   int s = hip_status(launch_rank_down(ra, rwgs, st));
-  if (s) return s;
-  s = hip_status(launch_gemv(ga, gwgs, st));
-  if (s) return s;
-  for (int i = 0; i < count; ++i) {
-    if (items[i].T_save) {
-      s = hip_status(launch_rank_finish(plans[i].t_part, plans[i].tk.splits, M, items[i].r,
-                                        items[i].alpha / (float)items[i].r, items[i].T_save, st));
-      if (s) return s;
-    }
-  }
-  return QLORA_OK;
+  if (!s) s = hip_status(launch_rank_finish(fa, st));
+  if (!s) s = hip_status(launch_gemv(ga, gwgs, st));
+  return s;
 }
 
 }  // namespace
@@ -498,21 +499,27 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
     return s;
   }
   const float sc = lora_alpha / (float)r;
-  // T = s X A^T (unless saved by the forward)
+  // T = s X A^T (unless saved by the forward), and its transposed hi/lo copy
   const float* T = T_saved;
   if (!T) {
-    s = rank_down_single(X, A, M, r, d_in, d_in, p.t.tk, p.t.t_part, st);
+    s = rank_down_single(X, A, M, r, d_in, d_in, p.tk, p.t_part, st);
     if (s) return s;
-    s = hip_status(launch_rank_finish(p.t.t_part, p.t.tk.splits, M, r, sc, p.t.t_buf, st));
+    s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, r, sc, p.t_buf, p.tt_hi,
+                                      p.tt_lo, p.ldp, st));
     if (s) return s;
-    T = p.t.t_buf;
+    T = p.t_buf;
+  } else {
+    s = hip_status(launch_rank_finish(T_saved, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
+                                      st));
+    if (s) return s;
   }
   // U = s dY B, through B^T so the contraction over d_out is contiguous
   s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
   if (s) return s;
   s = rank_down_single(dY, p.bt, M, r, d_out, p.ldbt, p.uk, p.u_part, st);
   if (s) return s;
-  s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, p.u, st));
+  s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, p.u, p.ut_hi, p.ut_lo,
+                                    p.ldp, st));
   if (s) return s;
   // dX = dY Wh + U A
   if (dX) {
@@ -522,9 +529,12 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
     if (s) return s;
   }
   // dA = U^T X ; dB = (T^T dY)^T
-  s = hip_status(launch_gram(p.u, X, M, r, d_in, p.mper_a, p.ms_a, p.da_part, st));
+  s = hip_status(launch_gram(p.ut_hi, p.ut_lo, p.ldp, X, M, r, d_in, p.mper_a, p.ms_a,
+                             p.da_part, st));
   if (!s) s = hip_status(launch_gram_finish(p.da_part, p.ms_a, r, d_in, false, dA, st));
-  if (!s) s = hip_status(launch_gram(T, dY, M, r, d_out, p.mper_b, p.ms_b, p.db_part, st));
+  if (!s)
+    s = hip_status(launch_gram(p.tt_hi, p.tt_lo, p.ldp, dY, M, r, d_out, p.mper_b, p.ms_b,
+                               p.db_part, st));
   if (!s) s = hip_status(launch_gram_finish(p.db_part, p.ms_b, r, d_out, true, dB, st));
   return s;
 }

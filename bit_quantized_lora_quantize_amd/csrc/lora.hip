@@ -3,22 +3,23 @@
 // [QP] "第 04 篇：QLoRA 原理" §2.2 (LoRA branch), §2.4 (gradients of A, B and
 // the input), §6.3-6.4.  With s = alpha / r and token rows:
 //   T = s X A^T,  U = s dY B,  dA = U^T X,  dB = dY^T T.
-// Thin products run on the matrix cores (v_mfma_f32_16x16x32_bf16) with FP32
-// accumulation.  Reductions over K or over tokens are split across
-// workgroups into FP32 partials that a finish kernel sums in split order, so
-// every result is deterministic.
+// Thin products run on the matrix cores with FP32 accumulation.  Reductions
+// over K or over tokens are split across workgroups into FP32 partials that a
+// finish kernel sums in split order, so every result is deterministic.  These
+// kernels are bound by one pass over X (or dY); the rank-r operands are small
+// and come from L2.
 #include "qlora_device.h"
 #include "qlora_kernels.h"
 
 namespace qlora {
 
-// Eight BF16 values P[k0 .. k0+7] of a row with K columns, zero past K.
-__device__ __forceinline__ u32x4 load8_bf16(const uint16_t* row, int64_t k0, int64_t K,
+// Eight BF16 values row[k0 .. k0+7], zero at and past `lim`.
+__device__ __forceinline__ u32x4 load8_bf16(const uint16_t* row, int64_t k0, int64_t lim,
                                             bool vec) {
-  if (vec && k0 + 8 <= K) return *reinterpret_cast<const u32x4*>(row + k0);
+  if (vec && k0 + 8 <= lim) return *reinterpret_cast<const u32x4*>(row + k0);
   uint32_t h[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = (k0 + e < K) ? row[k0 + e] : 0u;
+  for (int e = 0; e < 8; ++e) h[e] = (k0 + e < lim) ? row[k0 + e] : 0u;
   u32x4 r;
   r.x = h[0] | (h[1] << 16);
   r.y = h[2] | (h[3] << 16);
@@ -28,8 +29,10 @@ __device__ __forceinline__ u32x4 load8_bf16(const uint16_t* row, int64_t k0, int
 }
 
 // ---------------------------------------------------------------------------
-// part[s][m][n] = sum_{k in split s} P[m][k] Q[n][k].  One wavefront per
-// 16 x 64 output tile and K split; a grid covers up to kMaxGroup problems.
+// Small M: part[s][m][n] = sum_{k in split s} P[m][k] Q[n][k].  One wavefront
+// per 16 x 64 output tile and K split; a grid covers up to kMaxGroup
+// problems.  The column-tile-0 wavefronts also write P permuted within each
+// eight (the X operand of the weight-streaming kernel).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_rank_down(RankDownArgs a) {
   for (int z = 0; z < a.count; ++z) {
@@ -84,14 +87,108 @@ __global__ __launch_bounds__(64) void k_rank_down(RankDownArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_rank_finish(const float* __restrict__ part, int splits,
-                                                     int64_t count, float scale,
-                                                     float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= count) return;
-  float acc = part[i];
-  for (int s = 1; s < splits; ++s) acc = __fadd_rn(acc, part[(int64_t)s * count + i]);
-  out[i] = __fmul_rn(scale, acc);
+// ---------------------------------------------------------------------------
+// Large M: the same product with 256 x 64 workgroup tiles.  Wavefront w owns
+// rows 64w .. 64w+63 of the tile: 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.
+// Operands come straight from global memory (P streamed once, Q shared
+// through L1/L2); each iteration covers 64 of K.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rank_down_big(const uint16_t* __restrict__ P,
+                                                       const uint16_t* __restrict__ Q, int64_t M,
+                                                       int64_t N, int64_t K, int64_t ldq,
+                                                       int64_t k_per_split,
+                                                       float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * 256 + 64 * w;
+  const int64_t n0 = (int64_t)blockIdx.y * 64;
+  const int s = blockIdx.z;
+  const int64_t k_begin = (int64_t)s * k_per_split;
+  int64_t k_end = k_begin + k_per_split;
+  if (k_end > K) k_end = K;
+  const bool fast = (K % 8) == 0 && (ldq % 8) == 0 && m0 + 64 <= M && n0 + 64 <= N;
+
+  f32x16 acc[2][2] = {};
+  const uint16_t* pr[2];
+  const uint16_t* qr[2];
+  bool pok[2], qok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t m = m0 + 32 * i + r32, n = n0 + 32 * i + r32;
+    pok[i] = m < M;
+    qok[i] = n < N;
+    pr[i] = P + (pok[i] ? m : 0) * K;
+    qr[i] = Q + (qok[i] ? n : 0) * ldq;
+  }
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += 64) {
+    u32x4 a[4][2], b[4][2];
+    if (fast && k0 + 64 <= k_end) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          a[ks][i] = *reinterpret_cast<const u32x4*>(pr[i] + k0 + 16 * ks + 8 * h);
+          b[ks][i] = *reinterpret_cast<const u32x4*>(qr[i] + k0 + 16 * ks + 8 * h);
+        }
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int64_t kk = k0 + 16 * ks + 8 * h;
+          a[ks][i] = pok[i] ? load8_bf16(pr[i], kk, k_end, (K % 8) == 0) : z;
+          b[ks][i] = qok[i] ? load8_bf16(qr[i], kk, k_end, (ldq % 8) == 0) : z;
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[ks][i], b[ks][j], acc[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + 32 * j + r32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m < M && n < N) part[((int64_t)s * M + m) * N + n] = acc[i][j][v];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Finish: v = scale * sum_s part[s] (s ascending).  Thread per element of the
+// transposed [N][ldt] index space (the FP32 [M][N] output is written from
+// the same thread when requested).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
+  const int wg = blockIdx.x;
+  int di = 0;
+  while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
+  const FinishDesc& d = a.d[di];
+  const int64_t idx = (int64_t)(wg - d.wg_begin) * 256 + threadIdx.x;
+  const int64_t ldt = d.ldt > 0 ? d.ldt : d.M;
+  if (idx >= d.N * ldt) return;
+  const int64_t n = idx / ldt, m = idx % ldt;
+  float v = 0.0f;
+  if (m < d.M) {
+    const int64_t e = m * d.N + n, count = d.M * d.N;
+    float acc = d.part[e];
+    for (int s = 1; s < d.splits; ++s) acc = __fadd_rn(acc, d.part[(int64_t)s * count + e]);
+    v = __fmul_rn(d.scale, acc);
+    if (d.out) d.out[e] = v;
+  }
+  if (d.ht) {
+    float hi, lo;
+    split_bf16(v, hi, lo);
+    d.ht[idx] = (uint16_t)(__float_as_uint(hi) >> 16);
+    d.lt[idx] = (uint16_t)(pack_bf16x2(lo, 0.0f) & 0xFFFFu);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ in,
@@ -104,86 +201,81 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// part[s][i][c] = sum_{m in split s} P[m][i] Q[m][c].  Workgroup tile 64 (i)
-// x 128 (c); per 32-token step both operands are staged in LDS and read
-// transposed (the contraction runs over tokens, the row index of both).
-// P enters as hi + lo BF16 (two MFMAs per tile).
+// part[s][i][c] = sum_{m in split s} P[m][i] Q[m][c].  The contraction runs
+// over tokens, the row index of both operands.  P arrives transposed
+// (hi/lo BF16 [R][ldp]) so its MFMA operand is one 16-byte load; Q is
+// transposed in registers: lane (c32, h) loads 4 columns of 8 token rows
+// (8-byte loads, a wavefront reads 16 rows x 256 B) and one byte permute per
+// output dword builds the 8-token column operands.  MFMA t of a lane then
+// covers columns 4*c32 + t.  Wavefront tile: 64 (i) x 128 (c), 16 tokens per
+// step; 4 wavefronts per workgroup side by side in c.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gram(const float* __restrict__ P,
+__global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi,
+                                              const uint16_t* __restrict__ Pt_lo, int64_t ldp,
                                               const uint16_t* __restrict__ Q, int64_t M,
                                               int64_t R, int64_t N, int64_t m_per_split,
                                               float* __restrict__ part) {
-  __shared__ float Ps[32][64 + 1];
-  __shared__ uint16_t Qs[32][128 + 2];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t c0 = (int64_t)blockIdx.x * 128, i0 = (int64_t)blockIdx.y * 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int64_t cb = (int64_t)blockIdx.x * 512 + 128 * w;
+  const int64_t i0 = (int64_t)blockIdx.y * 64;
   const int s = blockIdx.z;
   const int64_t m_begin = (int64_t)s * m_per_split;
   int64_t m_end = m_begin + m_per_split;
   if (m_end > M) m_end = M;
+  const int64_t col = cb + 4 * c32;
+  const bool cvec = (N % 4) == 0 && col + 4 <= N;
 
-  f32x4 acc[4][2] = {};
-  for (int64_t m0 = m_begin; m0 < m_end; m0 += 32) {
-    {  // stage P[m0..m0+32][i0..i0+64] (FP32) and Q[m0..m0+32][c0..c0+128]
-      const int row = tid >> 3, col = (tid & 7) * 8;
-      const int64_t m = m0 + row;
+  f32x16 acc[4][2] = {};
+  for (int64_t m0 = m_begin; m0 < m_end; m0 += 16) {
+    uint32_t q[8][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t i = i0 + col + e;
-        Ps[row][col + e] = (m < m_end && i < R) ? P[m * R + i] : 0.0f;
-      }
-      const int qc = (tid & 7) * 16;
+    for (int e = 0; e < 8; ++e) {
+      const int64_t m = m0 + 8 * h + e;
+      if (m < m_end && cvec) {
+        const uint2 v = *reinterpret_cast<const uint2*>(Q + m * N + col);
+        q[e][0] = v.x;
+        q[e][1] = v.y;
+      } else {
+        uint32_t x[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t c = c0 + qc + e;
-        Qs[row][qc + e] = (m < m_end && c < N) ? Q[m * N + c] : (uint16_t)0;
-      }
-    }
-    __syncthreads();
-    u32x4 bq[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int c = 32 * w + 16 * ct + r16;
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = Qs[8 * g + e][c];
-      bq[ct].x = h[0] | (h[1] << 16);
-      bq[ct].y = h[2] | (h[3] << 16);
-      bq[ct].z = h[4] | (h[5] << 16);
-      bq[ct].w = h[6] | (h[7] << 16);
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      float hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) split_bf16(Ps[8 * g + e][16 * it + r16], hi[e], lo[e]);
-      u32x4 ah, al;
-      ah.x = pack_bf16x2(hi[0], hi[1]);
-      ah.y = pack_bf16x2(hi[2], hi[3]);
-      ah.z = pack_bf16x2(hi[4], hi[5]);
-      ah.w = pack_bf16x2(hi[6], hi[7]);
-      al.x = pack_bf16x2(lo[0], lo[1]);
-      al.y = pack_bf16x2(lo[2], lo[3]);
-      al.z = pack_bf16x2(lo[4], lo[5]);
-      al.w = pack_bf16x2(lo[6], lo[7]);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        acc[it][ct] = mfma16(ah, bq[ct], acc[it][ct]);
-        acc[it][ct] = mfma16(al, bq[ct], acc[it][ct]);
+        for (int t = 0; t < 4; ++t) x[t] = (m < m_end && col + t < N) ? Q[m * N + col + t] : 0u;
+        q[e][0] = x[0] | (x[1] << 16);
+        q[e][1] = x[2] | (x[3] << 16);
       }
     }
-    __syncthreads();
+    u32x4 ah[2], al[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int64_t i = i0 + 32 * it + c32;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      ah[it] = i < R ? *reinterpret_cast<const u32x4*>(Pt_hi + i * ldp + m0 + 8 * h) : z;
+      al[it] = i < R ? *reinterpret_cast<const u32x4*>(Pt_lo + i * ldp + m0 + 8 * h) : z;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 b;
+      b.x = __builtin_amdgcn_perm(q[1][t >> 1], q[0][t >> 1], sel);
+      b.y = __builtin_amdgcn_perm(q[3][t >> 1], q[2][t >> 1], sel);
+      b.z = __builtin_amdgcn_perm(q[5][t >> 1], q[4][t >> 1], sel);
+      b.w = __builtin_amdgcn_perm(q[7][t >> 1], q[6][t >> 1], sel);
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        acc[t][it] = mfma32(ah[it], b, acc[t][it]);
+        acc[t][it] = mfma32(al[it], b, acc[t][it]);
+      }
+    }
   }
 #pragma unroll
-  for (int it = 0; it < 4; ++it)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int64_t c = c0 + 32 * w + 16 * ct + r16;
+    for (int it = 0; it < 2; ++it) {
+      const int64_t c = col + t;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t i = i0 + 16 * it + 4 * g + v;
-        if (i < R && c < N) part[((int64_t)s * R + i) * N + c] = acc[it][ct][v];
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + 32 * it + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (i < R && c < N) part[((int64_t)s * R + i) * N + c] = acc[t][it][v];
       }
     }
 }
@@ -206,13 +298,35 @@ hipError_t launch_rank_down(const RankDownArgs& a, int total_wgs, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
-                              float* out, hipStream_t st) {
-  const int64_t count = M * N;
-  if (count == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rank_finish, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
-                     part, splits, count, scale, out);
+hipError_t launch_rank_down_big(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N,
+                                int64_t K, int64_t ldq, int64_t k_per_split, int splits,
+                                float* part, hipStream_t st) {
+  dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 63) / 64), (unsigned)splits);
+  hipLaunchKernelGGL(k_rank_down_big, grid, dim3(256), 0, st, P, Q, M, N, K, ldq, k_per_split,
+                     part);
   return hipGetLastError();
+}
+
+hipError_t launch_rank_finish(const FinishArgs& a0, hipStream_t st) {
+  FinishArgs a = a0;
+  int wgs = 0;
+  for (int i = 0; i < a.count; ++i) {
+    a.d[i].wg_begin = wgs;
+    const int64_t ldt = a.d[i].ldt > 0 ? a.d[i].ldt : a.d[i].M;
+    wgs += (int)((a.d[i].N * ldt + 255) / 256);
+  }
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rank_finish, dim3(wgs), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
+                              float* out, uint16_t* ht, uint16_t* lt, int64_t ldt,
+                              hipStream_t st) {
+  FinishArgs a{};
+  a.count = 1;
+  a.d[0] = FinishDesc{part, out, ht, lt, M, N, ht ? ldt : M, scale, splits, 0};
+  return launch_rank_finish(a, st);
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
@@ -223,10 +337,12 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
-hipError_t launch_gram(const float* P, const uint16_t* Q, int64_t M, int64_t R, int64_t N,
-                       int64_t m_per_split, int splits, float* part, hipStream_t st) {
-  dim3 grid((unsigned)((N + 127) / 128), (unsigned)((R + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, st, P, Q, M, R, N, m_per_split, part);
+hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
+                       const uint16_t* Q, int64_t M, int64_t R, int64_t N, int64_t m_per_split,
+                       int splits, float* part, hipStream_t st) {
+  dim3 grid((unsigned)((N + 511) / 512), (unsigned)((R + 63) / 64), (unsigned)splits);
+  hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, st, Pt_hi, Pt_lo, ldp, Q, M, R, N, m_per_split,
+                     part);
   return hipGetLastError();
 }
 

@@ -61,9 +61,36 @@ struct RankDownArgs {
 };
 hipError_t launch_rank_down(const RankDownArgs& a, int total_wgs, hipStream_t st);
 
-// out[m][n] = scale * sum_s part[s][m][n], s ascending.
+// Large-M form of the same product: 256-row workgroup tiles (4 wavefronts of
+// 64 rows) x 64 columns, v_mfma_f32_32x32x16_bf16, K split across
+// workgroups (k_per_split a multiple of 64).
+hipError_t launch_rank_down_big(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N,
+                                int64_t K, int64_t ldq, int64_t k_per_split, int splits,
+                                float* part, hipStream_t st);
+
+// Finish of split partials: v[m][n] = scale * sum_s part[s][m][n] (s
+// ascending).  out (optional) = v, FP32 [M][N]; ht/lt (optional) = the
+// transposed hi/lo BF16 pair of v, [N][ldt] with zeros for m in [M, ldt).
+// Up to kMaxGroup independent problems per launch.
+struct FinishDesc {
+  const float* part;
+  float* out;
+  uint16_t* ht;
+  uint16_t* lt;
+  int64_t M, N, ldt;
+  float scale;
+  int splits;
+  int wg_begin;
+};
+struct FinishArgs {
+  FinishDesc d[kMaxGroup];
+  int count;
+};
+hipError_t launch_rank_finish(const FinishArgs& a, hipStream_t st);
+// Single-problem convenience form.
 hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
-                              float* out, hipStream_t st);
+                              float* out, uint16_t* ht, uint16_t* lt, int64_t ldt,
+                              hipStream_t st);
 
 // Transpose of a BF16 matrix in[rows][cols] into out[cols][ldo]:
 // out[c][i] = in[i][c] for i < rows, and 0 for i in [rows, ldo).
@@ -71,9 +98,12 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
                                  int64_t ldo, hipStream_t st);
 
 // part[s][i][c] = sum over tokens m in split s of P[m][i] * Q[m][c], with P
-// FP32 [M][R] entering as a hi + lo BF16 pair and Q BF16 [M][N].
-hipError_t launch_gram(const float* P, const uint16_t* Q, int64_t M, int64_t R, int64_t N,
-                       int64_t m_per_split, int splits, float* part, hipStream_t st);
+// given transposed as a hi + lo BF16 pair Pt_hi/Pt_lo [R][ldp] (ldp >= M,
+// a multiple of 16, zero-padded) and Q BF16 [M][N].  m_per_split is a
+// multiple of 16.
+hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
+                       const uint16_t* Q, int64_t M, int64_t R, int64_t N, int64_t m_per_split,
+                       int splits, float* part, hipStream_t st);
 // out = sum_s part[s] (s ascending); transposed: out[c][i] else out[i][c].
 hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,
                               bool transposed, float* out, hipStream_t st);
