@@ -36,6 +36,7 @@ namespace {
 
 constexpr int64_t kMaxRank = 256;
 constexpr int64_t kSmallM = 16;      // M <= 16 streams the weight (GEMV path)
+constexpr int64_t kMaxLinearDim = int64_t(1) << 22;  // keeps device offsets 32-bit
 constexpr int kTargetWgs = 512;      // workgroups aimed for when splitting K
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -129,6 +130,8 @@ struct FwdPlan {
   float* t_part;      // [tk.splits][M][r]
   float* t_buf;       // [M][r] when T_save is NULL
   uint16_t* xp;       // [M][d_in] permuted X (small M)
+  uint16_t* t_hl;     // [M][2 rp] BF16 hi | lo of T (large M)
+  int64_t rp;         // r rounded up to 32
   float* gemv_part;   // [ksplit][16][d_out]
   uint32_t* counters; // [tiles]
   GemvSplit gs;
@@ -142,6 +145,8 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.tk = rank_split(d_in, M, r);
   p.t_part = c.take<float>(p.tk.splits * M * r);
   p.t_buf = c.take<float>(M * r);
+  p.rp = round_up(r, 32);
+  if (!p.small) p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
   if (p.small) {
     p.xp = c.take<uint16_t>(M * d_in);
     p.gs = gemv_split(d_out, d_in, cdiv(d_out, 64));
@@ -160,7 +165,8 @@ struct BwdPlan {
   int64_t ldbt;       // row stride of B^T
   uint16_t* bt;       // [r][ldbt]
   float* u_part;      // [uk.splits][M][r]
-  float* u;           // [M][r]
+  int64_t rp;         // r rounded up to 32
+  uint16_t* u_hl;     // [M][2 rp] BF16 hi | lo of U
   int64_t ldp;        // token stride of the transposed hi/lo copies
   uint16_t *ut_hi, *ut_lo, *tt_hi, *tt_lo;  // [r][ldp]
   int ms_a, ms_b;     // token splits of dA and dB
@@ -190,7 +196,8 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.ldbt = round_up(d_out, 64);
   p.bt = c.take<uint16_t>(r * p.ldbt);
   p.u_part = c.take<float>(p.uk.splits * M * r);
-  p.u = c.take<float>(M * r);
+  p.rp = round_up(r, 32);
+  p.u_hl = c.take<uint16_t>(M * 2 * p.rp);
   p.ldp = round_up(std::max<int64_t>(M, 1), 16);
   p.ut_hi = c.take<uint16_t>(r * p.ldp);
   p.ut_lo = c.take<uint16_t>(r * p.ldp);
@@ -284,6 +291,7 @@ struct FwdItemArgs {
 int check_fwd_item(const FwdItemArgs& f, int64_t M) {
   int s = check_nf4(f.q);
   if (s) return s;
+  if (f.q->d_out > kMaxLinearDim || f.q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
   if (M < 0 || M > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
   if (f.r < 1 || f.r > kMaxRank) return QLORA_ERR_SHAPE;
   if (M == 0) return QLORA_OK;
@@ -315,9 +323,9 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       int s = rank_down_single(f.X, f.A, M, f.r, q->d_in, q->d_in, p.tk, p.t_part, st);
       if (s) return s;
       s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, f.r, f.alpha / (float)f.r, T,
-                                        nullptr, nullptr, 0, st));
+                                        nullptr, nullptr, 0, p.t_hl, p.rp, st));
       if (s) return s;
-      GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, T, f.B, f.Y,
+      GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, p.t_hl, f.B, f.Y,
                  M,        q->d_out,      q->d_in,  f.r};
       s = hip_status(launch_gemm_fwd(g, st));
       if (s) return s;
@@ -484,6 +492,7 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   int s = check_nf4(q);
   if (s) return s;
   if (M < 0 || M > (int64_t(1) << 31) || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
+  if (q->d_out > kMaxLinearDim || q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
   if (!dA || !dB || !ws) return QLORA_ERR_NULL;
   if (M > 0 && (!X || !dY || !A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(T_saved) ||
@@ -505,12 +514,12 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
     s = rank_down_single(X, A, M, r, d_in, d_in, p.tk, p.t_part, st);
     if (s) return s;
     s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, r, sc, p.t_buf, p.tt_hi,
-                                      p.tt_lo, p.ldp, st));
+                                      p.tt_lo, p.ldp, nullptr, 0, st));
     if (s) return s;
     T = p.t_buf;
   } else {
     s = hip_status(launch_rank_finish(T_saved, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
-                                      st));
+                                      nullptr, 0, st));
     if (s) return s;
   }
   // U = s dY B, through B^T so the contraction over d_out is contiguous
@@ -518,12 +527,12 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   if (s) return s;
   s = rank_down_single(dY, p.bt, M, r, d_out, p.ldbt, p.uk, p.u_part, st);
   if (s) return s;
-  s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, p.u, p.ut_hi, p.ut_lo,
-                                    p.ldp, st));
+  s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, nullptr, p.ut_hi, p.ut_lo,
+                                    p.ldp, p.u_hl, p.rp, st));
   if (s) return s;
   // dX = dY Wh + U A
   if (dX) {
-    GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, dY, p.u, A, dX,
+    GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, dY, p.u_hl, A, dX,
                M,        d_out,          d_in,      r};
     s = hip_status(launch_gemm_bwd(g, st));
     if (s) return s;

@@ -8,23 +8,35 @@
 // (transposed); the base gets no gradient.
 //
 // Tiling.  256 threads = 4 wavefronts in a 2 x 2 arrangement; output tile
-// 256 x 256; K step 64 = one quantization block per weight row.  Each
-// wavefront owns a 128 x 128 sub-tile: 4 x 4 tiles of v_mfma_f32_32x32x16_bf16
-// with 256 FP32 accumulators per lane.  Both operands are staged in LDS as
-// BF16, double-buffered (2 x 72 KB): while the matrix cores work on step s,
-// the same wavefronts restore step s+1's weights into the other buffer from
-// registers loaded one step earlier, and issue the global loads of step s+2.
-// One barrier per K step.  Each thread restores exactly one 64-weight block
-// per step: one scale, one 16-entry table, eight byte-permute lookups.
+// 256 x 256; K step 32 (half a quantization block).  Each wavefront owns a
+// 128 x 128 sub-tile: 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with 256 FP32
+// accumulators per lane, two K slices of 16 per step.
 //
-// Forward   Y[m][n]  = sum_k X[m][k] Wh[n][k]   (+ LoRA: T_hi/T_lo x B)
-//   LDS  As[m][k] = X permuted within each eight, Bs[n][k] = table lookups in
-//        the same permuted order (nf4_dequant8_perm).
+// Pipeline (three LDS buffers, two register stages).  During step s the
+// matrix cores consume buffer s%3 while the same wavefronts
+//   * read the operand fragments of the next K slice into the second
+//     fragment register set (slice 1 of step s, then slice 0 of step s+1,
+//     whose buffer was completed one barrier earlier),
+//   * restore step s+2 into buffer (s+2)%3 from registers loaded two steps
+//     earlier (activations copied, weights looked up in the block's
+//     16-entry table), and
+//   * issue the global loads of step s+4 into the freed register stage.
+// One barrier per step; no wavefront waits on LDS data written in the same
+// step.  The restore work (about four VALU instructions per MFMA) is spread
+// between the MFMAs of the step.
+//
+// Forward   Y[m][n]  = sum_k X[m][k] Wh[n][k]   (+ LoRA: T_hi/T_lo x B^T)
+//   LDS  As[m][k] = X permuted within each eight; Bs[n][k] = table lookups in
+//        the same permuted order (nf4_dequant8_perm).  Both fragments are
+//        16-byte LDS reads.
 // Backward  dX[m][c] = sum_n dY[m][n] Wh[n][c]  (+ LoRA: U_hi/U_lo x A)
-//   LDS  As[m][k] = dY in natural order, Bs[c][n] = restored weights written
-//        transposed, one 16-bit LDS store per weight.
+//   LDS  As[m][k] = dY; Bs[k][c] = restored weight rows as stored (row n of
+//        W, columns permuted within each eight).  The B fragments (eight
+//        consecutive k of one column per lane) come from two transposing LDS
+//        reads (ds_read_b64_tr_b16); the column permutation is undone when
+//        the result is stored.
 // LoRA term: extra K steps over [hi(0..RP) | lo(0..RP)], RP = r rounded up
-// to 32, with the FP32 rank-r activations split into two BF16 terms.
+// to 32, from the rank-r activations split into two BF16 terms beforehand.
 //
 // Workgroup order: consecutive workgroup ids are spread over the 8 XCDs, so
 // ids are remapped for each XCD to own a contiguous run of output tiles
@@ -34,192 +46,324 @@
 
 namespace qlora {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDA = BK + 8;                 // padded LDS row, BF16 elements
-constexpr int kBufA = BM * LDA, kBufB = BN * LDA;
-constexpr int kLdsBytes = 2 * (kBufA + kBufB) * 2;
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int kNumBuf = 3;
+constexpr int LDA = BK + 8;                  // As[m][k], forward Bs[n][k] row (BF16 elements)
+constexpr int LDT = BN + 16;                 // backward Bs[k][c] row: 136 dwords, = 8 mod 32
+constexpr int kABytes = BM * LDA * 2;
+constexpr int kBFwdBytes = BN * LDA * 2;
+constexpr int kBBwdBytes = BK * LDT * 2;
+template <bool BWD>
+constexpr int buf_bytes() { return kABytes + (BWD ? kBBwdBytes : kBFwdBytes); }
+template <bool BWD>
+constexpr int lds_bytes() { return kNumBuf * buf_bytes<BWD>(); }
 constexpr int kXcds = 8;
 
-struct GemmStage {
-  u32x4 a[8];     // activations: 8 rows x 8 columns of this thread
-  u32x4 c0, c1;   // the thread's 64-weight block
-  uint32_t sc;
-  float s2, mu;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Global data of one K step held in registers between load and restore.
+struct Stage {
+  u32x4 x[4];     // activation rows of the thread: 4 x 8 BF16
+  u32x4 c;        // 32 packed NF4 codes: one weight row segment
+  uint32_t sc;    // FP8 code of the segment's block scale
+  float s2;       // its FP32 second-level scale
 };
 
-// Activation rows of a K step: thread t loads rows t/8 + 32q (q = 0..7),
-// columns 8*(t%8) .. +8 -- eight threads read one 128-byte row segment.
+struct Frags {
+  u32x4 a[4], b[4];
+};
+
+// Per-thread constants of a tile.
+struct Tile {
+  int64_t m0, n0, K, NOUT;
+  int nk;                          // NF4 K steps
+  bool vec;                        // activation rows 16-byte aligned (K % 8 == 0)
+  __amdgpu_buffer_rsrc_t act;      // activations from row m0
+  __amdgpu_buffer_rsrc_t s2;       // whole second-level scale array
+  uint32_t vx;                     // activation byte offset of pass 0
+  uint32_t sx;                     // activation byte stride between passes (64 rows)
+  // forward weights (tile rows n0 ..)
+  __amdgpu_buffer_rsrc_t codes, scodes;
+  uint32_t vc, vs;                 // byte offsets of the thread's row
+  int64_t blk0;                    // block index of the row's first block
+  // backward weights: row segment (k0 + nl, columns c0 + 32 * cg ..)
+  int nl, cg;
+  float mu;
+  // LDS offsets (bytes, relative to a buffer)
+  uint32_t wa, wb;                 // restore stores
+  uint32_t ra, rb;                 // fragment reads
+};
+
+// ------------------------------------------------------------------ loads
 template <bool BWD>
-__device__ __forceinline__ void load_stage(const GemmArgs& p, int64_t m0, int64_t n0, int64_t k0,
-                                           int tid, GemmStage& s) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  const int64_t K = BWD ? p.d_out : p.d_in;
-  const bool vec = (K % 8) == 0;
-  const int cc = (tid & 7) * 8;
-  const int64_t kk = k0 + cc;
-  // Interior tile (uniform over the workgroup): no per-lane bounds checks.
-  const int64_t NW = BWD ? p.d_in : p.d_out;
-  if (vec && m0 + BM <= p.M && k0 + BK <= K && n0 + BN <= NW) {
+__device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int step,
+                                          bool with_scale, Stage& g) {
+  const uint32_t k0 = (uint32_t)step * BK;
+  if (!BWD || t.vec) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      s.a[q] = *reinterpret_cast<const u32x4*>(p.act + (m0 + (tid >> 3) + 32 * q) * K + kk);
-    const int64_t row = BWD ? k0 + (tid & 63) : n0 + tid;
-    const int64_t col = BWD ? n0 + 64 * (tid >> 6) : k0;
-    const u32x4* cp = reinterpret_cast<const u32x4*>(p.codes + row * (p.d_in / 2) + col / 2);
-    s.c0 = cp[0];
-    s.c1 = cp[1];
-    const int64_t b = (row * p.d_in + col) / kBlock;
-    s.sc = p.scodes[b];
-    s.s2 = p.scale2[b >> 8];
-    s.mu = p.mean[0];
-    return;
-  }
+    for (int q = 0; q < 4; ++q) g.x[q] = ld128(t.act, t.vx + q * t.sx, k0 * 2);
+  } else {
+    // unaligned rows (backward, d_out % 8 != 0): element loads, zero past K
+    const int64_t kc = (int64_t)k0 + 8 * ((threadIdx.x & 63) >> 4);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int64_t m = m0 + (tid >> 3) + 32 * q;
-    const uint16_t* src = p.act + m * K + kk;
-    if (m >= p.M || kk >= K) {
-      s.a[q] = z;
-    } else if (vec && kk + 8 <= K) {
-      s.a[q] = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      uint32_t h[8];
+    for (int q = 0; q < 4; ++q) {
+      uint32_t e2[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (kk + e < K) ? src[e] : 0u;
-      s.a[q].x = h[0] | (h[1] << 16); s.a[q].y = h[2] | (h[3] << 16);
-      s.a[q].z = h[4] | (h[5] << 16); s.a[q].w = h[6] | (h[7] << 16);
+      for (int e = 0; e < 8; ++e)
+        e2[e] = (kc + e < t.K) ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                     t.act, t.vx + q * t.sx + (k0 + e) * 2, 0, 0)
+                               : 0u;
+      g.x[q] = u32x4{e2[0] | (e2[1] << 16), e2[2] | (e2[3] << 16), e2[4] | (e2[5] << 16),
+                     e2[6] | (e2[7] << 16)};
     }
   }
-  int64_t row, col;  // weight row n and first column of the thread's block
   if (!BWD) {
-    row = n0 + tid;
-    col = k0;
+    g.c = ld128(t.codes, t.vc, k0 / 2);
+    if (with_scale) {
+      g.sc = __builtin_amdgcn_raw_buffer_load_b8(t.scodes, t.vs, k0 / 64, 0);
+      const int64_t blk = t.blk0 + k0 / 64;
+      g.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t.s2, (uint32_t)(blk >> 8) * 4, 0, 0));
+    }
   } else {
-    row = k0 + (tid & 63);
-    col = n0 + 64 * (tid >> 6);
-  }
-  s.c0 = z;
-  s.c1 = z;
-  s.sc = 0u;
-  s.s2 = 0.0f;
-  s.mu = 0.0f;
-  if (row < p.d_out && col < p.d_in) {
-    const u32x4* cp = reinterpret_cast<const u32x4*>(p.codes + row * (p.d_in / 2) + col / 2);
-    s.c0 = cp[0];
-    s.c1 = cp[1];
-    const int64_t b = (row * p.d_in + col) / kBlock;
-    s.sc = p.scodes[b];
-    s.s2 = p.scale2[b >> 8];
-    s.mu = p.mean[0];
+    // row k0 + nl of W, columns c0 + 32 cg .. +32
+    const int64_t row = (int64_t)k0;
+    const int64_t nb = p.d_in / kBlock;
+    const uint8_t* cbase = p.codes + row * (p.d_in / 2) + t.n0 / 2;
+    const int64_t cbytes = p.d_out * (p.d_in / 2) - (row * (p.d_in / 2) + t.n0 / 2);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cbase, cbytes);
+    g.c = ld128(rc, (uint32_t)(t.nl * (p.d_in / 2) + 16 * t.cg), 0);
+    const uint8_t* sbase = p.scodes + row * nb + t.n0 / kBlock;
+    const int64_t sbytes = p.d_out * nb - (row * nb + t.n0 / kBlock);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sbase, sbytes);
+    g.sc = __builtin_amdgcn_raw_buffer_load_b8(rs, (uint32_t)(t.nl * nb + (t.cg >> 1)), 0, 0);
+    const int64_t blk = (row + t.nl) * nb + t.n0 / kBlock + (t.cg >> 1);
+    g.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t.s2, (uint32_t)(blk >> 8) * 4, 0, 0));
   }
 }
 
+// ---------------------------------------------------------------- restore
+// Activations: pass q of the thread covers row 64 q + 16 w + (lane & 15),
+// columns 8 (lane >> 4) .. +8 of the step.
 template <bool BWD>
-__device__ __forceinline__ void store_stage(const GemmStage& s, int tid, uint16_t* As,
-                                            uint16_t* Bs) {
-  const int cc = (tid & 7) * 8;
+__device__ __forceinline__ void restore_act(const Tile& t, int step, const Stage& g, uint8_t* buf,
+                                            int lane) {
+  u32x4 v[4];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = (tid >> 3) + 32 * q;
-    *reinterpret_cast<u32x4*>(As + row * LDA + cc) = BWD ? s.a[q] : perm8_bf16(s.a[q]);
-  }
-  const Nf4Table t = nf4_table(restored_scale(s.sc, s.s2, s.mu));
-  const uint32_t cw[8] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w, s.c1.x, s.c1.y, s.c1.z, s.c1.w};
-  if (!BWD) {
+  for (int q = 0; q < 4; ++q) v[q] = g.x[q];
+  if (BWD) {
+    // last, partial step: contraction columns at or past K are zero
+    const int64_t kc = (int64_t)step * BK + 8 * (lane >> 4);
+    if ((int64_t)(step + 1) * BK > t.K && kc >= t.K) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4*>(Bs + tid * LDA + 8 * j) = nf4_dequant8_perm(cw[j], t);
-  } else {
-    // Bs[c][n]: column c of the block's row n (the contraction index)
-    const int nr = tid & 63, cb = tid >> 6;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 v = nf4_dequant8(cw[j], t);  // natural order e = 8j .. 8j+7
-      uint16_t* dst = Bs + (cb * 64 + 8 * j) * LDA + nr;
-      dst[0 * LDA] = (uint16_t)(v.x & 0xFFFFu);
-      dst[1 * LDA] = (uint16_t)(v.x >> 16);
-      dst[2 * LDA] = (uint16_t)(v.y & 0xFFFFu);
-      dst[3 * LDA] = (uint16_t)(v.y >> 16);
-      dst[4 * LDA] = (uint16_t)(v.z & 0xFFFFu);
-      dst[5 * LDA] = (uint16_t)(v.z >> 16);
-      dst[6 * LDA] = (uint16_t)(v.w & 0xFFFFu);
-      dst[7 * LDA] = (uint16_t)(v.w >> 16);
+      for (int q = 0; q < 4; ++q) v[q] = u32x4{0u, 0u, 0u, 0u};
     }
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<u32x4*>(buf + t.wa + q * 64 * LDA * 2) = BWD ? v[q] : perm8_bf16(v[q]);
 }
 
-// 64 MFMAs (v_mfma_f32_32x32x16_bf16) of one wavefront on a staged K step:
-// 4 x 4 tiles of 32 x 32, four K slices of 16.  Operand lane l holds row
-// (A) / column (B) l%32 and contraction elements 8*(l/32) .. +8.
-__device__ __forceinline__ void mma_stage(const uint16_t* As, const uint16_t* Bs, int wm, int wn,
-                                          int r32, int h, f32x16 (&acc)[4][4]) {
+template <bool BWD>
+__device__ __forceinline__ void restore_table(const Tile& t, int step, const Stage& g,
+                                              Nf4Table& tab) {
+  float scale = restored_scale(g.sc, g.s2, t.mu);
+  if (BWD && (int64_t)step * BK + t.nl >= t.K) scale = 0.0f;  // rows past d_out
+  tab = nf4_table(scale);
+}
+
+// Eight weights (codes dword j of the segment) looked up and stored.
+__device__ __forceinline__ void restore_dq(const Tile& t, int j, const Stage& g,
+                                           const Nf4Table& tab, uint8_t* buf) {
+  const uint32_t cw = j == 0 ? g.c.x : j == 1 ? g.c.y : j == 2 ? g.c.z : g.c.w;
+  *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) = nf4_dequant8_perm(cw, tab);
+}
+
+template <bool BWD>
+__device__ __forceinline__ void restore_w(const Tile& t, int step, const Stage& g, Nf4Table& tab,
+                                          bool new_table, uint8_t* buf) {
+  if (new_table) restore_table<BWD>(t, step, g, tab);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 af[4], bf[4];
+  for (int j = 0; j < 4; ++j) restore_dq(t, j, g, tab, buf);
+}
+
+// -------------------------------------------------------------- fragments
+template <bool BWD>
+__device__ __forceinline__ void read_frags(const Tile& t, const uint8_t* buf, int ks, Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const u32x4*>(buf + t.ra + (32 * i * LDA + 16 * ks) * 2);
+  if (!BWD) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.b[i] = *reinterpret_cast<const u32x4*>(buf + kABytes + t.rb + (32 * i * LDA + 16 * ks) * 2);
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      af[i] = *reinterpret_cast<const u32x4*>(As + (128 * wm + 32 * i + r32) * LDA + 16 * ks + 8 * h);
-      bf[i] = *reinterpret_cast<const u32x4*>(Bs + (128 * wn + 32 * i + r32) * LDA + 16 * ks + 8 * h);
+      const uint8_t* pb = buf + kABytes + t.rb + (16 * ks * LDT + 32 * i) * 2;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pb));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(pb + 4 * LDT * 2));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      f.b[i] = u32x4{l2.x, l2.y, h2.x, h2.y};
     }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(af[mt], bf[nt], acc[mt][nt]);
   }
 }
 
-// LoRA extension step e0: As[m][j] = hi/lo of lr[m][kappa], Bs[col][j] = the
-// matching LoRA factor entry, for kappa-columns e0 .. e0+63 of [hi | lo].
-template <bool BWD>
-__device__ __forceinline__ void fill_lora_stage(const GemmArgs& p, int64_t m0, int64_t n0,
-                                                int64_t e0, int64_t RP, int tid, uint16_t* As,
-                                                uint16_t* Bs) {
-  for (int idx = tid; idx < BM * BK; idx += 256) {
-    const int row = idx >> 6, j = idx & 63;
-    const int64_t kv = e0 + j;
-    const int64_t kap = kv < RP ? kv : kv - RP;
-    const int64_t m = m0 + row;
-    float v = 0.0f;
-    if (kv < 2 * RP && kap < p.r && m < p.M) {
-      float hi, lo;
-      split_bf16(p.lr[m * p.r + kap], hi, lo);
-      v = kv < RP ? hi : lo;
-    }
-    f32x2 pr = {v, 0.0f};
-    As[row * LDA + j] =
-        (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)) & 0xFFFFu);
+__device__ __forceinline__ void mma_slice(const Frags& f, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(f.a[mt], f.b[nt], acc[mt][nt]);
+}
+
+// Interleave of half a steady-state step: each of its 16 MFMAs is followed
+// by up to V VALU instructions and one LDS access; with VMEM, the global
+// loads sit between the last eight.
+template <int V, bool VMEM>
+__device__ __forceinline__ void half_schedule() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
+    __builtin_amdgcn_sched_group_barrier(0x300, 1, 0);   // DS read / write
+    if (VMEM && i >= 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
   }
-  for (int idx = tid; idx < BN * BK; idx += 256) {
-    const int col = idx >> 6, j = idx & 63;
-    const int64_t kv = e0 + j;
-    const int64_t kap = kv < RP ? kv : kv - RP;
-    const int64_t c = n0 + col;
-    uint16_t v = 0;
-    if (kv < 2 * RP && kap < p.r) {
-      if (!BWD) {
-        if (c < p.d_out) v = p.lw[c * p.r + kap];      // B[n][kappa]
-      } else {
-        if (c < p.d_in) v = p.lw[kap * p.d_in + c];    // A[kappa][c]
-      }
+}
+
+// Steady-state K step s (s + 4 < nk): consume buffer bc (fragments of
+// slice 0 already in f0), restore step s+2 into bw, load step s+4 into g,
+// read slice 0 of step s+1 from bn.  The three buffers are distinct.  The
+// step runs as two halves of 16 MFMAs each with about half the restore
+// work: (slice 1 reads, activation copy, table or first lookups) and
+// (slice 0 reads of the next step, remaining lookups, global loads).
+template <bool BWD, bool EVEN>
+__device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, int s,
+                                            const uint8_t* __restrict__ bc,
+                                            const uint8_t* __restrict__ bn,
+                                            uint8_t* __restrict__ bw, Stage& g, Nf4Table& tab,
+                                            Frags& f0, Frags& f1, f32x16 (&acc)[4][4],
+                                            int lane) {
+  constexpr bool kTable = BWD || EVEN;
+  constexpr int kFirst = kTable ? 1 : 2;   // lookups in the first half
+  read_frags<BWD>(t, bc, 1, f1);
+  mma_slice(f0, acc);
+  restore_act<BWD>(t, s + 2, g, bw, lane);
+  if (kTable) restore_table<BWD>(t, s + 2, g, tab);
+#pragma unroll
+  for (int j = 0; j < kFirst; ++j) restore_dq(t, j, g, tab, bw);
+  half_schedule<5, false>();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = kFirst; j < 4; ++j) restore_dq(t, j, g, tab, bw);
+  load_step<BWD>(p, t, s + 4, kTable, g);
+  read_frags<BWD>(t, bn, 0, f0);
+  mma_slice(f1, acc);
+  half_schedule<5, true>();
+  __syncthreads();
+}
+
+// Generic K step (any s < nk): the same work with the restore, load and
+// next-step read skipped past the end.
+template <bool BWD>
+__device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s, uint8_t* lds,
+                                       Stage& g, Nf4Table& tab, Frags& f0, Frags& f1,
+                                       f32x16 (&acc)[4][4], int lane) {
+  uint8_t* bc = lds + (s % kNumBuf) * buf_bytes<BWD>();
+  uint8_t* bn = lds + ((s + 1) % kNumBuf) * buf_bytes<BWD>();
+  uint8_t* bw = lds + ((s + 2) % kNumBuf) * buf_bytes<BWD>();
+  // even steps open a quantization block (forward); every backward step
+  // holds new rows
+  const bool even = (s & 1) == 0;
+  read_frags<BWD>(t, bc, 1, f1);
+  mma_slice(f0, acc);
+  if (s + 2 < t.nk) {
+    restore_act<BWD>(t, s + 2, g, bw, lane);
+    restore_w<BWD>(t, s + 2, g, tab, BWD || even, bw);
+  }
+  if (s + 4 < t.nk) load_step<BWD>(p, t, s + 4, BWD || even, g);
+  if (s + 1 < t.nk) read_frags<BWD>(t, bn, 0, f0);
+  mma_slice(f1, acc);
+  __syncthreads();
+}
+
+// LoRA extension step e0 (not pipelined): As[m][j] = ext[m][e0 + j];
+// forward Bs[n][j] = B[n][kappa], backward Bs[j][c] = A[kappa][c], with
+// kappa = (e0 + j) mod RP and zero where kappa >= r.
+template <bool BWD>
+__device__ __forceinline__ void fill_ext(const GemmArgs& p, const Tile& t, int64_t e0, int64_t RP,
+                                         uint8_t* buf, int tid, int lane) {
+  const int w = tid >> 6;
+  {
+    const __amdgpu_buffer_rsrc_t re =
+        make_rsrc(p.ext + t.m0 * 2 * RP, (p.M - t.m0) * 2 * RP * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 64 * q + 16 * w + (lane & 15);
+      const u32x4 v = ld128(re, (uint32_t)((row * 2 * RP + e0 + 8 * (lane >> 4)) * 2), 0);
+      *reinterpret_cast<u32x4*>(buf + t.wa + q * 64 * LDA * 2) = v;
     }
-    Bs[col * LDA + j] = v;
+  }
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  if (!BWD) {
+    // row n = tid of the tile, 32 columns
+    uint8_t* dst = buf + kABytes + t.wb;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.lw + t.n0 * p.r, (p.d_out - t.n0) * p.r * 2);
+    const bool vec = (p.r % 8) == 0 && (reinterpret_cast<uintptr_t>(p.lw) & 15u) == 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t kap = (e0 + 8 * j) % RP;
+      u32x4 v = z;
+      if (vec) {
+        if (kap < p.r) v = ld128(rb, (uint32_t)((tid * p.r + kap) * 2), 0);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h[e] = (kap + e < p.r) ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                       rb, (uint32_t)((tid * p.r + kap + e) * 2), 0, 0)
+                                 : 0u;
+        v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                  h[6] | (h[7] << 16)};
+      }
+      // the weight side of the forward pairs with X permuted within each
+      // eight; the extension keeps both operands in natural order
+      *reinterpret_cast<u32x4*>(dst + 16 * j) = v;
+    }
+  } else {
+    // row j = nl of the step, columns 32 cg .. +32 of the tile
+    const int64_t kap = (e0 + t.nl) % RP;
+    uint8_t* dst = buf + kABytes + (t.nl * LDT + 32 * t.cg) * 2;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.lw + t.n0, (p.r * p.d_in - t.n0) * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = z;
+      if (kap < p.r) v = ld128(ra, (uint32_t)((kap * p.d_in + 32 * t.cg + 8 * j) * 2), 0);
+      // columns in the order of the restored weights (undone at the store)
+      *reinterpret_cast<u32x4*>(dst + 16 * j) = perm8_bf16(v);
+    }
   }
 }
 
 template <bool BWD>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* As0 = lds;
-  uint16_t* Bs0 = lds + kBufA;
-  uint16_t* As1 = lds + kBufA + kBufB;
-  uint16_t* Bs1 = lds + 2 * kBufA + kBufB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w & 1, wn = w >> 1;
   const int r32 = lane & 31, h = lane >> 5;
 
-  const int64_t NOUT = BWD ? p.d_in : p.d_out;
-  const int tiles_n = (int)((NOUT + BN - 1) / BN);
+  Tile t;
+  t.NOUT = BWD ? p.d_in : p.d_out;
+  t.K = BWD ? p.d_out : p.d_in;
+  const int tiles_n = (int)((t.NOUT + BN - 1) / BN);
   const int tiles_m = (int)((p.M + BM - 1) / BM);
   const int total = tiles_n * tiles_m;
   // XCD-aware remap: hardware places workgroup id i on XCD i % 8; give each
@@ -230,10 +374,38 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     const int x = id % kXcds, slot = id / kXcds;
     id = (x < extra ? x * (per + 1) : extra * (per + 1) + (x - extra) * per) + slot;
   }
-  const int64_t n0 = (int64_t)(id % tiles_n) * BN;
-  const int64_t m0 = (int64_t)(id / tiles_n) * BM;
-  const int64_t K = BWD ? p.d_out : p.d_in;
-  const int64_t nsteps = (K + BK - 1) / BK;
+  t.n0 = (int64_t)(id % tiles_n) * BN;
+  t.m0 = (int64_t)(id / tiles_n) * BM;
+  t.nk = (int)((t.K + BK - 1) / BK);
+  t.vec = (t.K % 8) == 0;
+  t.mu = p.mean[0];
+
+  t.act = make_rsrc(p.act + t.m0 * t.K, (p.M - t.m0) * t.K * 2);
+  t.vx = (uint32_t)(((16 * w + (lane & 15)) * t.K + 8 * (lane >> 4)) * 2);
+  t.sx = (uint32_t)(64 * t.K * 2);
+  const int64_t nb = p.d_in / kBlock;
+  t.s2 = make_rsrc(p.scale2, ((p.d_out * nb + kGroup - 1) / kGroup) * 4);
+  if (!BWD) {
+    t.codes = make_rsrc(p.codes + t.n0 * (p.d_in / 2), (p.d_out - t.n0) * (p.d_in / 2));
+    t.scodes = make_rsrc(p.scodes + t.n0 * nb, (p.d_out - t.n0) * nb);
+    t.vc = (uint32_t)(tid * (p.d_in / 2));
+    t.vs = (uint32_t)(tid * nb);
+    t.blk0 = (t.n0 + tid) * nb;
+    t.nl = 0;
+    t.cg = 0;
+    t.wb = (uint32_t)(tid * LDA * 2);
+    t.rb = (uint32_t)(((128 * wn + r32) * LDA + 8 * h) * 2);
+  } else {
+    t.nl = tid & 31;
+    t.cg = tid >> 5;
+    t.wb = (uint32_t)((t.nl * LDT + 32 * t.cg) * 2);
+    // transposing read: lane group g = lane / 16 covers columns
+    // 16 (g & 1) .. +16 and contraction rows 8 (g >> 1) .. +4 (first read)
+    const int g = lane >> 4, j = lane & 15;
+    t.rb = (uint32_t)(((8 * (g >> 1) + (j >> 2)) * LDT + 128 * wn + 16 * (g & 1) + 4 * (j & 3)) * 2);
+  }
+  t.wa = (uint32_t)(((16 * w + (lane & 15)) * LDA + 8 * (lane >> 4)) * 2);
+  t.ra = (uint32_t)(((128 * wm + r32) * LDA + 8 * h) * 2);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -241,49 +413,70 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  GemmStage st;
-  load_stage<BWD>(p, m0, n0, 0, tid, st);
-  store_stage<BWD>(st, tid, As0, Bs0);
-  // step 1's data (a step at or past K loads zeros and is never consumed)
-  load_stage<BWD>(p, m0, n0, BK, tid, st);
-  __syncthreads();
-  uint16_t* Ac = As0;
-  uint16_t* Bc = Bs0;
-  uint16_t* An = As1;
-  uint16_t* Bn = Bs1;
-  for (int64_t s = 0; s + 1 < nsteps; ++s) {
-    mma_stage(Ac, Bc, wm, wn, r32, h, acc);
-    store_stage<BWD>(st, tid, An, Bn);
-    load_stage<BWD>(p, m0, n0, (s + 2) * BK, tid, st);
-    __syncthreads();
-    uint16_t* t0 = Ac; Ac = An; An = t0;
-    uint16_t* t1 = Bc; Bc = Bn; Bn = t1;
+  Stage g0, g1;
+  Nf4Table tab;
+  Frags f0, f1;
+  const int nk = t.nk;
+  // prologue: steps 0 and 1 restored, 2 and 3 in flight
+  load_step<BWD>(p, t, 0, true, g0);
+  if (nk > 1) load_step<BWD>(p, t, 1, BWD, g1);
+  restore_act<BWD>(t, 0, g0, lds, lane);
+  restore_w<BWD>(t, 0, g0, tab, true, lds);
+  if (nk > 1) {
+    restore_act<BWD>(t, 1, g1, lds + buf_bytes<BWD>(), lane);
+    restore_w<BWD>(t, 1, g1, tab, BWD, lds + buf_bytes<BWD>());
   }
-  mma_stage(Ac, Bc, wm, wn, r32, h, acc);
+  if (nk > 2) load_step<BWD>(p, t, 2, true, g0);
+  if (nk > 3) load_step<BWD>(p, t, 3, BWD, g1);
   __syncthreads();
+  read_frags<BWD>(t, lds, 0, f0);
+
+  // steady state: pairs (s, s+1) with s even and s + 5 < nk; buffer of
+  // step j is j % 3
+  int s = 0;
+  int bi = 0;  // s % 3
+  for (; s + 5 < nk; s += 2) {
+    uint8_t* b0 = lds + bi * buf_bytes<BWD>();
+    uint8_t* b1 = lds + (bi == 2 ? 0 : bi + 1) * buf_bytes<BWD>();
+    uint8_t* b2 = lds + (bi == 0 ? 2 : bi - 1) * buf_bytes<BWD>();
+    k_step_full<BWD, true>(p, t, s, b0, b1, b2, g0, tab, f0, f1, acc, lane);
+    k_step_full<BWD, false>(p, t, s + 1, b1, b2, b0, g1, tab, f0, f1, acc, lane);
+    bi = (bi == 0) ? 2 : bi - 1;  // (s + 2) % 3
+  }
+  for (; s + 1 < nk; s += 2) {
+    k_step<BWD>(p, t, s, lds, g0, tab, f0, f1, acc, lane);
+    k_step<BWD>(p, t, s + 1, lds, g1, tab, f0, f1, acc, lane);
+  }
+  if (s < nk) k_step<BWD>(p, t, s, lds, g0, tab, f0, f1, acc, lane);
 
   // ---- LoRA term as extra K steps over [hi | lo] ----
   const int64_t RP = (p.r + 31) / 32 * 32;
   for (int64_t e0 = 0; e0 < 2 * RP; e0 += BK) {
-    fill_lora_stage<BWD>(p, m0, n0, e0, RP, tid, As0, Bs0);
+    fill_ext<BWD>(p, t, e0, RP, lds, tid, lane);
     __syncthreads();
-    mma_stage(As0, Bs0, wm, wn, r32, h, acc);
+    read_frags<BWD>(t, lds, 0, f0);
+    read_frags<BWD>(t, lds, 1, f1);
+    mma_slice(f0, acc);
+    mma_slice(f1, acc);
     __syncthreads();
   }
 
   // ---- epilogue: RNE to BF16.  Accumulator element v of lane l holds row
-  // 8*(v/4) + 4*(l/32) + v%4 and column l%32 of its 32 x 32 tile. ----
+  // 8*(v/4) + 4*(l/32) + v%4 and column l%32 of its 32 x 32 tile; in the
+  // backward direction tile column j holds W column 8 (j/8) + sigma(j%8),
+  // sigma = (0 2 4 6 1 3 5 7), the order of nf4_dequant8_perm. ----
+  const int cj = BWD ? ((r32 & ~7) | (2 * (r32 & 3) + ((r32 >> 2) & 1))) : r32;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int64_t n = n0 + 128 * wn + 32 * nt + r32;
+      const int64_t n = t.n0 + 128 * wn + 32 * nt + cj;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 128 * wm + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < p.M && n < NOUT) {
+        const int64_t m = t.m0 + 128 * wm + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m < p.M && n < t.NOUT) {
           f32x2 pr = {acc[mt][nt][v], 0.0f};
-          p.out[m * NOUT + n] = (uint16_t)(
+          p.out[m * t.NOUT + n] = (uint16_t)(
               __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)) & 0xFFFFu);
         }
       }
@@ -294,12 +487,12 @@ template <bool BWD>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   static hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_gemm<BWD>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kLdsBytes);
+      lds_bytes<BWD>());
   if (attr != hipSuccess) return attr;
   const int64_t NOUT = BWD ? a.d_in : a.d_out;
   const int64_t tiles = ((NOUT + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_gemm<BWD>, dim3((unsigned)tiles), dim3(256), kLdsBytes, st, a);
+  hipLaunchKernelGGL(k_gemm<BWD>, dim3((unsigned)tiles), dim3(256), lds_bytes<BWD>(), st, a);
   weight_kernel_end(st);
   return hipGetLastError();
 }

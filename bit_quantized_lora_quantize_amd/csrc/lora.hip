@@ -183,11 +183,24 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
     v = __fmul_rn(d.scale, acc);
     if (d.out) d.out[e] = v;
   }
+  float hi, lo;
+  split_bf16(v, hi, lo);
+  const uint16_t hb = (uint16_t)(__float_as_uint(hi) >> 16);
+  const uint16_t lb = (uint16_t)(pack_bf16x2(lo, 0.0f) & 0xFFFFu);
   if (d.ht) {
-    float hi, lo;
-    split_bf16(v, hi, lo);
-    d.ht[idx] = (uint16_t)(__float_as_uint(hi) >> 16);
-    d.lt[idx] = (uint16_t)(pack_bf16x2(lo, 0.0f) & 0xFFFFu);
+    d.ht[idx] = hb;
+    d.lt[idx] = lb;
+  }
+  if (d.hl && m < d.M) {
+    uint16_t* row = d.hl + m * 2 * d.rp;
+    row[n] = hb;
+    row[d.rp + n] = lb;
+    if (n == d.N - 1) {
+      for (int64_t j = d.N; j < d.rp; ++j) {
+        row[j] = 0;
+        row[d.rp + j] = 0;
+      }
+    }
   }
 }
 
@@ -322,10 +335,10 @@ hipError_t launch_rank_finish(const FinishArgs& a0, hipStream_t st) {
 
 hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
                               float* out, uint16_t* ht, uint16_t* lt, int64_t ldt,
-                              hipStream_t st) {
+                              uint16_t* hl, int64_t rp, hipStream_t st) {
   FinishArgs a{};
   a.count = 1;
-  a.d[0] = FinishDesc{part, out, ht, lt, M, N, ht ? ldt : M, scale, splits, 0};
+  a.d[0] = FinishDesc{part, out, ht, lt, M, N, ht ? ldt : M, scale, splits, 0, hl, rp};
   return launch_rank_finish(a, st);
 }
 

@@ -81,6 +81,8 @@ struct FinishDesc {
   float scale;
   int splits;
   int wg_begin;
+  uint16_t* hl;   // optional row-major split: hl[m][n] = hi, hl[m][rp + n] = lo, zero for n in [N, rp)
+  int64_t rp;
 };
 struct FinishArgs {
   FinishDesc d[kMaxGroup];
@@ -90,7 +92,7 @@ hipError_t launch_rank_finish(const FinishArgs& a, hipStream_t st);
 // Single-problem convenience form.
 hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
                               float* out, uint16_t* ht, uint16_t* lt, int64_t ldt,
-                              hipStream_t st);
+                              uint16_t* hl, int64_t rp, hipStream_t st);
 
 // Transpose of a BF16 matrix in[rows][cols] into out[cols][ldo]:
 // out[c][i] = in[i][c] for i < rows, and 0 for i in [rows, ldo).
@@ -150,7 +152,7 @@ struct GemmArgs {
   const float* scale2;
   const float* mean;
   const uint16_t* act;    // X [M][d_in] (forward) or dY [M][d_out] (backward)
-  const float* lr;        // T or U, FP32 [M][r]
+  const uint16_t* ext;    // T or U split into BF16 terms: [M][2*RP], hi | lo, RP = r rounded up to 32
   const uint16_t* lw;     // B [d_out][r] (forward) or A [r][d_in] (backward)
   uint16_t* out;          // Y [M][d_out] or dX [M][d_in]
   int64_t M, d_out, d_in, r;
