@@ -86,7 +86,6 @@ struct Frags {
 struct Tile {
   int64_t m0, n0, K, NOUT;
   int nk;                          // NF4 K steps
-  bool vec;                        // activation rows 16-byte aligned (K % 8 == 0)
   __amdgpu_buffer_rsrc_t act;      // activations from row m0
   __amdgpu_buffer_rsrc_t s2;       // whole second-level scale array
   uint32_t vx;                     // activation byte offset of pass 0
@@ -104,11 +103,13 @@ struct Tile {
 };
 
 // ------------------------------------------------------------------ loads
-template <bool BWD>
+// VEC: activation rows 16-byte aligned (K % 8 == 0); always so in the
+// forward direction (K = d_in, a multiple of 64).
+template <bool BWD, bool VEC>
 __device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int step,
                                           bool with_scale, Stage& g) {
   const uint32_t k0 = (uint32_t)step * BK;
-  if (!BWD || t.vec) {
+  if (!BWD || VEC) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) g.x[q] = ld128(t.act, t.vx + q * t.sx, k0 * 2);
   } else {
@@ -153,13 +154,14 @@ __device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int 
 // ---------------------------------------------------------------- restore
 // Activations: pass q of the thread covers row 64 q + 16 w + (lane & 15),
 // columns 8 (lane >> 4) .. +8 of the step.
-template <bool BWD>
+// EDGE: the step may be the last, partial one (backward K = d_out).
+template <bool BWD, bool EDGE = true>
 __device__ __forceinline__ void restore_act(const Tile& t, int step, const Stage& g, uint8_t* buf,
                                             int lane) {
   u32x4 v[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) v[q] = g.x[q];
-  if (BWD) {
+  if (BWD && EDGE) {
     // last, partial step: contraction columns at or past K are zero
     const int64_t kc = (int64_t)step * BK + 8 * (lane >> 4);
     if ((int64_t)(step + 1) * BK > t.K && kc >= t.K) {
@@ -226,69 +228,68 @@ __device__ __forceinline__ void mma_slice(const Frags& f, f32x16 (&acc)[4][4]) {
 
 // Interleave of half a steady-state step: each of its 16 MFMAs is followed
 // by up to V VALU instructions and one LDS access; with VMEM, the global
-// loads sit between the last eight.
+// loads sit between the first eight.
 template <int V, bool VMEM>
 __device__ __forceinline__ void half_schedule() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    if (VMEM && i < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
     __builtin_amdgcn_sched_group_barrier(0x300, 1, 0);   // DS read / write
-    if (VMEM && i >= 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
   }
 }
 
-// Steady-state K step s (s + 4 < nk): consume buffer bc (fragments of
-// slice 0 already in f0), restore step s+2 into bw, load step s+4 into g,
-// read slice 0 of step s+1 from bn.  The three buffers are distinct.  The
-// step runs as two halves of 16 MFMAs each with about half the restore
-// work: (slice 1 reads, activation copy, table or first lookups) and
-// (slice 0 reads of the next step, remaining lookups, global loads).
-template <bool BWD, bool EVEN>
+// Steady-state K step s (s + 4 < nk).  Register stages hold the global data
+// of three steps: gl receives step s+4 (issued first, so that the newest
+// loads in flight are always a step old), gr holds step s+2, restored into
+// bw during this step.  Buffer bc is consumed (fragments of slice 0 already
+// in f0) and slice 0 of step s+1 is read from bn.  The three buffers and the
+// stages are distinct.  The step runs as two halves of 16 MFMAs, each with
+// about half the restore work.
+template <bool BWD, bool VEC, bool EVEN>
 __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, int s,
                                             const uint8_t* __restrict__ bc,
                                             const uint8_t* __restrict__ bn,
-                                            uint8_t* __restrict__ bw, Stage& g, Nf4Table& tab,
-                                            Frags& f0, Frags& f1, f32x16 (&acc)[4][4],
-                                            int lane) {
+                                            uint8_t* __restrict__ bw, const Stage& gr,
+                                            Stage& gl, Nf4Table& tab, Frags& f0, Frags& f1,
+                                            f32x16 (&acc)[4][4], int lane) {
+  // even steps open a quantization block (forward); every backward step
+  // holds new rows
   constexpr bool kTable = BWD || EVEN;
   constexpr int kFirst = kTable ? 1 : 2;   // lookups in the first half
+  load_step<BWD, VEC>(p, t, s + 4, kTable, gl);
   read_frags<BWD>(t, bc, 1, f1);
   mma_slice(f0, acc);
-  restore_act<BWD>(t, s + 2, g, bw, lane);
-  if (kTable) restore_table<BWD>(t, s + 2, g, tab);
+  restore_act<BWD, false>(t, s + 2, gr, bw, lane);   // s + 2 < nk - 1: a full step
+  if (kTable) restore_table<BWD>(t, s + 2, gr, tab);
 #pragma unroll
-  for (int j = 0; j < kFirst; ++j) restore_dq(t, j, g, tab, bw);
-  half_schedule<5, false>();
+  for (int j = 0; j < kFirst; ++j) restore_dq(t, j, gr, tab, bw);
+  half_schedule<5, true>();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = kFirst; j < 4; ++j) restore_dq(t, j, g, tab, bw);
-  load_step<BWD>(p, t, s + 4, kTable, g);
+  for (int j = kFirst; j < 4; ++j) restore_dq(t, j, gr, tab, bw);
   read_frags<BWD>(t, bn, 0, f0);
   mma_slice(f1, acc);
-  half_schedule<5, true>();
+  half_schedule<5, false>();
   __syncthreads();
 }
 
-// Generic K step (any s < nk): the same work with the restore, load and
+// Generic K step (any s < nk): the same work with the load, restore and
 // next-step read skipped past the end.
-template <bool BWD>
-__device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s, uint8_t* lds,
-                                       Stage& g, Nf4Table& tab, Frags& f0, Frags& f1,
-                                       f32x16 (&acc)[4][4], int lane) {
-  uint8_t* bc = lds + (s % kNumBuf) * buf_bytes<BWD>();
-  uint8_t* bn = lds + ((s + 1) % kNumBuf) * buf_bytes<BWD>();
-  uint8_t* bw = lds + ((s + 2) % kNumBuf) * buf_bytes<BWD>();
-  // even steps open a quantization block (forward); every backward step
-  // holds new rows
-  const bool even = (s & 1) == 0;
+template <bool BWD, bool VEC, bool EVEN>
+__device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s,
+                                       const uint8_t* bc, const uint8_t* bn, uint8_t* bw,
+                                       const Stage& gr, Stage& gl, Nf4Table& tab, Frags& f0,
+                                       Frags& f1, f32x16 (&acc)[4][4], int lane) {
+  constexpr bool kTable = BWD || EVEN;
+  if (s + 4 < t.nk) load_step<BWD, VEC>(p, t, s + 4, kTable, gl);
   read_frags<BWD>(t, bc, 1, f1);
   mma_slice(f0, acc);
   if (s + 2 < t.nk) {
-    restore_act<BWD>(t, s + 2, g, bw, lane);
-    restore_w<BWD>(t, s + 2, g, tab, BWD || even, bw);
+    restore_act<BWD>(t, s + 2, gr, bw, lane);
+    restore_w<BWD>(t, s + 2, gr, tab, kTable, bw);
   }
-  if (s + 4 < t.nk) load_step<BWD>(p, t, s + 4, BWD || even, g);
   if (s + 1 < t.nk) read_frags<BWD>(t, bn, 0, f0);
   mma_slice(f1, acc);
   __syncthreads();
@@ -352,7 +353,7 @@ __device__ __forceinline__ void fill_ext(const GemmArgs& p, const Tile& t, int64
   }
 }
 
-template <bool BWD>
+template <bool BWD, bool VEC>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -377,7 +378,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   t.n0 = (int64_t)(id % tiles_n) * BN;
   t.m0 = (int64_t)(id / tiles_n) * BM;
   t.nk = (int)((t.K + BK - 1) / BK);
-  t.vec = (t.K % 8) == 0;
   t.mu = p.mean[0];
 
   t.act = make_rsrc(p.act + t.m0 * t.K, (p.M - t.m0) * t.K * 2);
@@ -413,41 +413,48 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  Stage g0, g1;
+  // Global data of step j sits in register stage j % 3; step j is staged in
+  // LDS buffer j % 3.
+  Stage g0, g1, g2;
   Nf4Table tab;
   Frags f0, f1;
   const int nk = t.nk;
-  // prologue: steps 0 and 1 restored, 2 and 3 in flight
-  load_step<BWD>(p, t, 0, true, g0);
-  if (nk > 1) load_step<BWD>(p, t, 1, BWD, g1);
-  restore_act<BWD>(t, 0, g0, lds, lane);
-  restore_w<BWD>(t, 0, g0, tab, true, lds);
-  if (nk > 1) {
-    restore_act<BWD>(t, 1, g1, lds + buf_bytes<BWD>(), lane);
-    restore_w<BWD>(t, 1, g1, tab, BWD, lds + buf_bytes<BWD>());
-  }
-  if (nk > 2) load_step<BWD>(p, t, 2, true, g0);
-  if (nk > 3) load_step<BWD>(p, t, 3, BWD, g1);
+  uint8_t* const b0 = lds;
+  uint8_t* const b1 = lds + buf_bytes<BWD>();
+  uint8_t* const b2 = lds + 2 * buf_bytes<BWD>();
+  // prologue: steps 0 and 1 restored, 2 and 3 in flight.  Unconditional:
+  // steps past K read zeros (buffer loads are bounds-checked) and are never
+  // consumed.
+  load_step<BWD, VEC>(p, t, 0, true, g0);
+  load_step<BWD, VEC>(p, t, 1, BWD, g1);
+  restore_act<BWD>(t, 0, g0, b0, lane);
+  restore_w<BWD>(t, 0, g0, tab, true, b0);
+  restore_act<BWD>(t, 1, g1, b1, lane);
+  restore_w<BWD>(t, 1, g1, tab, BWD, b1);
+  load_step<BWD, VEC>(p, t, 2, true, g2);
+  load_step<BWD, VEC>(p, t, 3, BWD, g0);
   __syncthreads();
-  read_frags<BWD>(t, lds, 0, f0);
+  read_frags<BWD>(t, b0, 0, f0);
 
-  // steady state: pairs (s, s+1) with s even and s + 5 < nk; buffer of
-  // step j is j % 3
+  // steady state: six steps per iteration (s = 0 mod 6), so that stage,
+  // buffer and table parity are fixed for each of them
   int s = 0;
-  int bi = 0;  // s % 3
-  for (; s + 5 < nk; s += 2) {
-    uint8_t* b0 = lds + bi * buf_bytes<BWD>();
-    uint8_t* b1 = lds + (bi == 2 ? 0 : bi + 1) * buf_bytes<BWD>();
-    uint8_t* b2 = lds + (bi == 0 ? 2 : bi - 1) * buf_bytes<BWD>();
-    k_step_full<BWD, true>(p, t, s, b0, b1, b2, g0, tab, f0, f1, acc, lane);
-    k_step_full<BWD, false>(p, t, s + 1, b1, b2, b0, g1, tab, f0, f1, acc, lane);
-    bi = (bi == 0) ? 2 : bi - 1;  // (s + 2) % 3
+  for (; s + 9 < nk; s += 6) {
+    k_step_full<BWD, VEC, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
+    k_step_full<BWD, VEC, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
+    k_step_full<BWD, VEC, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
+    k_step_full<BWD, VEC, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
+    k_step_full<BWD, VEC, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
+    k_step_full<BWD, VEC, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
   }
-  for (; s + 1 < nk; s += 2) {
-    k_step<BWD>(p, t, s, lds, g0, tab, f0, f1, acc, lane);
-    k_step<BWD>(p, t, s + 1, lds, g1, tab, f0, f1, acc, lane);
+  for (; s < nk; s += 6) {
+    k_step<BWD, VEC, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
+    if (s + 1 < nk) k_step<BWD, VEC, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
+    if (s + 2 < nk) k_step<BWD, VEC, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
+    if (s + 3 < nk) k_step<BWD, VEC, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
+    if (s + 4 < nk) k_step<BWD, VEC, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
+    if (s + 5 < nk) k_step<BWD, VEC, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
   }
-  if (s < nk) k_step<BWD>(p, t, s, lds, g0, tab, f0, f1, acc, lane);
 
   // ---- LoRA term as extra K steps over [hi | lo] ----
   const int64_t RP = (p.r + 31) / 32 * 32;
@@ -483,21 +490,26 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     }
 }
 
-template <bool BWD>
+template <bool BWD, bool VEC>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<BWD>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void*>(&k_gemm<BWD, VEC>), hipFuncAttributeMaxDynamicSharedMemorySize,
       lds_bytes<BWD>());
   if (attr != hipSuccess) return attr;
   const int64_t NOUT = BWD ? a.d_in : a.d_out;
   const int64_t tiles = ((NOUT + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_gemm<BWD>, dim3((unsigned)tiles), dim3(256), lds_bytes<BWD>(), st, a);
+  hipLaunchKernelGGL((k_gemm<BWD, VEC>), dim3((unsigned)tiles), dim3(256), lds_bytes<BWD>(), st, a);
   weight_kernel_end(st);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) { return launch_gemm<false>(a, st); }
-hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) { return launch_gemm<true>(a, st); }
+hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) {
+  return launch_gemm<false, true>(a, st);
+}
+hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
+  // dY rows are 16-byte aligned exactly when d_out % 8 == 0
+  return (a.d_out % 8) == 0 ? launch_gemm<true, true>(a, st) : launch_gemm<true, false>(a, st);
+}
 
 }  // namespace qlora
