@@ -295,27 +295,27 @@ __device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s,
   __syncthreads();
 }
 
-// LoRA extension step e0 (not pipelined): As[m][j] = ext[m][e0 + j];
-// forward Bs[n][j] = B[n][kappa], backward Bs[j][c] = A[kappa][c], with
-// kappa = (e0 + j) mod RP and zero where kappa >= r.
+// LoRA extension steps: As[m][j] = ext[m][e0 + j]; forward Bs[n][j] =
+// B[n][kappa], backward Bs[j][c] = A[kappa][c], with kappa = (e0 + j) mod
+// RP and zero where kappa >= r.  Loaded into registers one step ahead of
+// the LDS store.
+struct ExtStage {
+  u32x4 a[4];   // ext rows, same thread mapping as the activation restore
+  u32x4 b[4];   // factor: forward row n = tid, 32 columns; backward row nl, 32 columns
+};
+
 template <bool BWD>
-__device__ __forceinline__ void fill_ext(const GemmArgs& p, const Tile& t, int64_t e0, int64_t RP,
-                                         uint8_t* buf, int tid, int lane) {
+__device__ __forceinline__ void ext_load(const GemmArgs& p, const Tile& t, int64_t e0, int64_t RP,
+                                         int tid, int lane, ExtStage& E) {
   const int w = tid >> 6;
-  {
-    const __amdgpu_buffer_rsrc_t re =
-        make_rsrc(p.ext + t.m0 * 2 * RP, (p.M - t.m0) * 2 * RP * 2);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(p.ext + t.m0 * 2 * RP, (p.M - t.m0) * 2 * RP * 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 64 * q + 16 * w + (lane & 15);
-      const u32x4 v = ld128(re, (uint32_t)((row * 2 * RP + e0 + 8 * (lane >> 4)) * 2), 0);
-      *reinterpret_cast<u32x4*>(buf + t.wa + q * 64 * LDA * 2) = v;
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int row = 64 * q + 16 * w + (lane & 15);
+    E.a[q] = ld128(re, (uint32_t)((row * 2 * RP + e0 + 8 * (lane >> 4)) * 2), 0);
   }
   const u32x4 z = {0u, 0u, 0u, 0u};
   if (!BWD) {
-    // row n = tid of the tile, 32 columns
-    uint8_t* dst = buf + kABytes + t.wb;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.lw + t.n0 * p.r, (p.d_out - t.n0) * p.r * 2);
     const bool vec = (p.r % 8) == 0 && (reinterpret_cast<uintptr_t>(p.lw) & 15u) == 0;
 #pragma unroll
@@ -334,23 +334,30 @@ __device__ __forceinline__ void fill_ext(const GemmArgs& p, const Tile& t, int64
         v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                   h[6] | (h[7] << 16)};
       }
-      // the weight side of the forward pairs with X permuted within each
-      // eight; the extension keeps both operands in natural order
-      *reinterpret_cast<u32x4*>(dst + 16 * j) = v;
+      E.b[j] = v;
     }
   } else {
-    // row j = nl of the step, columns 32 cg .. +32 of the tile
     const int64_t kap = (e0 + t.nl) % RP;
-    uint8_t* dst = buf + kABytes + (t.nl * LDT + 32 * t.cg) * 2;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.lw + t.n0, (p.r * p.d_in - t.n0) * 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 v = z;
       if (kap < p.r) v = ld128(ra, (uint32_t)((kap * p.d_in + 32 * t.cg + 8 * j) * 2), 0);
-      // columns in the order of the restored weights (undone at the store)
-      *reinterpret_cast<u32x4*>(dst + 16 * j) = perm8_bf16(v);
+      E.b[j] = v;
     }
   }
+}
+
+template <bool BWD>
+__device__ __forceinline__ void ext_store(const Tile& t, const ExtStage& E, uint8_t* buf) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(buf + t.wa + q * 64 * LDA * 2) = E.a[q];
+  // forward: both operands in natural order (the permutation within eights
+  // belongs to the NF4 steps only); backward: factor columns in the order
+  // of the restored weights, undone at the store
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) = BWD ? perm8_bf16(E.b[j]) : E.b[j];
 }
 
 template <bool BWD, bool VEC>
@@ -422,11 +429,32 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   uint8_t* const b0 = lds;
   uint8_t* const b1 = lds + buf_bytes<BWD>();
   uint8_t* const b2 = lds + 2 * buf_bytes<BWD>();
-  // prologue: steps 0 and 1 restored, 2 and 3 in flight.  Unconditional:
-  // steps past K read zeros (buffer loads are bounds-checked) and are never
-  // consumed.
+
+  // Steps 0 and 1 of the weights are loaded first; their latency is covered
+  // by the LoRA term, which runs as the first K steps (over [hi | lo] of
+  // the rank-r activations, buffers 0 and 1 alternating, each step's global
+  // data loaded one step ahead).  Loads are unconditional: steps past K read
+  // zeros (buffer loads are bounds-checked) and are never consumed.
   load_step<BWD, VEC>(p, t, 0, true, g0);
   load_step<BWD, VEC>(p, t, 1, BWD, g1);
+  {
+    const int64_t RP = (p.r + 31) / 32 * 32;
+    const int ne = (int)(2 * RP / BK);
+    ExtStage E;
+    ext_load<BWD>(p, t, 0, RP, tid, lane, E);
+    for (int e = 0; e < ne; ++e) {
+      uint8_t* be = (e & 1) ? b1 : b0;
+      ext_store<BWD>(t, E, be);
+      if (e + 1 < ne) ext_load<BWD>(p, t, (int64_t)(e + 1) * BK, RP, tid, lane, E);
+      __syncthreads();
+      read_frags<BWD>(t, be, 0, f0);
+      read_frags<BWD>(t, be, 1, f1);
+      mma_slice(f0, acc);
+      mma_slice(f1, acc);
+    }
+    __syncthreads();
+  }
+  // weights: steps 0 and 1 restored, 2 and 3 in flight
   restore_act<BWD>(t, 0, g0, b0, lane);
   restore_w<BWD>(t, 0, g0, tab, true, b0);
   restore_act<BWD>(t, 1, g1, b1, lane);
@@ -456,38 +484,49 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     if (s + 5 < nk) k_step<BWD, VEC, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
   }
 
-  // ---- LoRA term as extra K steps over [hi | lo] ----
-  const int64_t RP = (p.r + 31) / 32 * 32;
-  for (int64_t e0 = 0; e0 < 2 * RP; e0 += BK) {
-    fill_ext<BWD>(p, t, e0, RP, lds, tid, lane);
-    __syncthreads();
-    read_frags<BWD>(t, lds, 0, f0);
-    read_frags<BWD>(t, lds, 1, f1);
-    mma_slice(f0, acc);
-    mma_slice(f1, acc);
-    __syncthreads();
-  }
-
-  // ---- epilogue: RNE to BF16.  Accumulator element v of lane l holds row
+  // ---- epilogue: RNE to BF16, staged through LDS so that the global stores
+  // are 16-byte row segments.  Accumulator element v of lane l holds row
   // 8*(v/4) + 4*(l/32) + v%4 and column l%32 of its 32 x 32 tile; in the
   // backward direction tile column j holds W column 8 (j/8) + sigma(j%8),
-  // sigma = (0 2 4 6 1 3 5 7), the order of nf4_dequant8_perm. ----
+  // sigma = (0 2 4 6 1 3 5 7), the order of nf4_dequant8_perm.  Each
+  // wavefront stages its 128 x 128 tile in two halves of 64 rows in a region
+  // of its own (the last K step ended with a barrier). ----
   const int cj = BWD ? ((r32 & ~7) | (2 * (r32 & 3) + ((r32 >> 2) & 1))) : r32;
+  constexpr int EPI_LD = 136;  // staged row, BF16 elements
+  uint16_t* ep = reinterpret_cast<uint16_t*>(lds) + w * 64 * EPI_LD;
+  const bool out_vec = (t.NOUT % 8) == 0;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t n = t.n0 + 128 * wn + 32 * nt + cj;
+    for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = t.m0 + 128 * wm + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < p.M && n < t.NOUT) {
-          f32x2 pr = {acc[mt][nt][v], 0.0f};
-          p.out[m * t.NOUT + n] = (uint16_t)(
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = 32 * mt2 + 8 * (v >> 2) + 4 * h + (v & 3);
+          f32x2 pr = {acc[2 * half + mt2][nt][v], 0.0f};
+          ep[row * EPI_LD + 32 * nt + cj] = (uint16_t)(
               __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2)) & 0xFFFFu);
+        }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = i * 64 + lane, row = idx >> 4, ch = idx & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * EPI_LD + 8 * ch);
+      const int64_t m = t.m0 + 128 * wm + 64 * half + row;
+      const int64_t n = t.n0 + 128 * wn + 8 * ch;
+      if (m < p.M) {
+        uint16_t* dst = p.out + m * t.NOUT + n;
+        if (out_vec && n + 8 <= t.NOUT) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < t.NOUT) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
+  }
 }
 
 template <bool BWD, bool VEC>
