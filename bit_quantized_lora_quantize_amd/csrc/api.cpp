@@ -143,7 +143,7 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.small = M <= kSmallM;
   Carver c(ws);
   p.tk = rank_split(d_in, M, r);
-  p.t_part = c.take<float>(p.tk.splits * M * r);
+  if (p.small) p.t_part = c.take<float>(p.tk.splits * M * r);
   p.t_buf = c.take<float>(M * r);
   p.rp = round_up(r, 32);
   if (!p.small) p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
@@ -176,26 +176,28 @@ struct BwdPlan {
   size_t bytes;
 };
 
-// Token split of dA / dB: about 256 workgroups, partials at most a quarter of
-// the activation bytes; a multiple of 16 tokens per split.
+// Token split of dA / dB: about 512 workgroups (64 columns x one split
+// each); a split is a multiple of 512 tokens (four wavefronts of whole
+// pairs of 64-token blocks).
 int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
-  const int64_t tiles = cdiv(N, 512) * cdiv(r, 64);
-  const int64_t cap = std::max<int64_t>(1, M / (4 * std::max<int64_t>(r, 1)));
-  int64_t ms = std::max<int64_t>(1, std::min<int64_t>({cdiv(256, tiles), cap, cdiv(M, 16)}));
-  *per = std::max<int64_t>(16, round_up(cdiv(M, ms), 16));
+  (void)r;
+  const int64_t ctiles = cdiv(N, 64);
+  const int64_t ms = std::max<int64_t>(1, std::min<int64_t>(cdiv(512, ctiles), cdiv(M, 256)));
+  *per = round_up(cdiv(std::max<int64_t>(M, 1), ms), 512);
   return (int)std::max<int64_t>(1, cdiv(M, *per));
 }
 
 BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   BwdPlan p{};
   Carver c(ws);
+  const bool small = M <= kSmallM;
   p.tk = rank_split(d_in, M, r);
-  p.t_part = c.take<float>(p.tk.splits * M * r);
+  if (small) p.t_part = c.take<float>(p.tk.splits * M * r);
   p.t_buf = c.take<float>(M * r);
   p.uk = rank_split(d_out, M, r);
   p.ldbt = round_up(d_out, 64);
   p.bt = c.take<uint16_t>(r * p.ldbt);
-  p.u_part = c.take<float>(p.uk.splits * M * r);
+  if (small) p.u_part = c.take<float>(p.uk.splits * M * r);
   p.rp = round_up(r, 32);
   p.u_hl = c.take<uint16_t>(M * 2 * p.rp);
   p.ldp = round_up(std::max<int64_t>(M, 1), 16);
@@ -320,10 +322,9 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       const qlora_nf4_t* q = f.q;
       FwdPlan p = plan_fwd(q->d_out, q->d_in, M, f.r, f.ws);
       float* T = f.T_save ? f.T_save : p.t_buf;
-      int s = rank_down_single(f.X, f.A, M, f.r, q->d_in, q->d_in, p.tk, p.t_part, st);
-      if (s) return s;
-      s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, f.r, f.alpha / (float)f.r, T,
-                                        nullptr, nullptr, 0, p.t_hl, p.rp, st));
+      RankRowsArgs ra{f.X,    f.A,     M,       f.r,     q->d_in, q->d_in, f.alpha / (float)f.r,
+                      T,      p.t_hl,  p.rp,    nullptr, nullptr, 0};
+      int s = hip_status(launch_rank_rows(ra, st));
       if (s) return s;
       GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, p.t_hl, f.B, f.Y,
                  M,        q->d_out,      q->d_in,  f.r};
@@ -509,12 +510,20 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   }
   const float sc = lora_alpha / (float)r;
   // T = s X A^T (unless saved by the forward), and its transposed hi/lo copy
+  const bool small = M <= kSmallM;
   const float* T = T_saved;
   if (!T) {
-    s = rank_down_single(X, A, M, r, d_in, d_in, p.tk, p.t_part, st);
-    if (s) return s;
-    s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, r, sc, p.t_buf, p.tt_hi,
-                                      p.tt_lo, p.ldp, nullptr, 0, st));
+    // the same kernels and summation order as the forward, so a recomputed T
+    // equals a saved one bit for bit
+    if (small) {
+      s = rank_down_single(X, A, M, r, d_in, d_in, p.tk, p.t_part, st);
+      if (s) return s;
+      s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, r, sc, p.t_buf, p.tt_hi,
+                                        p.tt_lo, p.ldp, nullptr, 0, st));
+    } else {
+      RankRowsArgs ra{X, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
+      s = hip_status(launch_rank_rows(ra, st));
+    }
     if (s) return s;
     T = p.t_buf;
   } else {
@@ -525,10 +534,15 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   // U = s dY B, through B^T so the contraction over d_out is contiguous
   s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
   if (s) return s;
-  s = rank_down_single(dY, p.bt, M, r, d_out, p.ldbt, p.uk, p.u_part, st);
-  if (s) return s;
-  s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, nullptr, p.ut_hi, p.ut_lo,
-                                    p.ldp, p.u_hl, p.rp, st));
+  if (small) {
+    s = rank_down_single(dY, p.bt, M, r, d_out, p.ldbt, p.uk, p.u_part, st);
+    if (s) return s;
+    s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, nullptr, p.ut_hi,
+                                      p.ut_lo, p.ldp, p.u_hl, p.rp, st));
+  } else {
+    RankRowsArgs ra{dY, p.bt, M, r, d_out, p.ldbt, sc, nullptr, p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
+    s = hip_status(launch_rank_rows(ra, st));
+  }
   if (s) return s;
   // dX = dY Wh + U A
   if (dX) {

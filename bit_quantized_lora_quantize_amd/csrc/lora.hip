@@ -162,6 +162,198 @@ __global__ __launch_bounds__(256) void k_rank_down_big(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Large M, one pass: v[m][n] = scale * sum_k P[m][k] Q[n][k], n < N <= 256.
+// A workgroup owns 16 token rows and the whole K: its W wavefronts take
+// consecutive K ranges (v_mfma_f32_16x16x32_bf16, 16 x 16*NB accumulators
+// each) and the partial sums are added in wavefront order through LDS, so
+// the result is deterministic and no partials reach HBM.  P is read once;
+// Q (r x K, small) is shared through L2.  Loads go through buffer
+// descriptors: rows of P past M and rows of Q past N read as zero.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rank_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Row groups of 16 tokens per workgroup (RG) and wavefronts (W): every
+// wavefront of a workgroup reads all of Q over its K range, so Q's L2
+// traffic is (M / 16 RG) times its size; RG trades that against the number
+// of workgroups.  Each wavefront keeps kRankDepth pairs of K slices (RG + NB
+// 16-byte loads per slice) in flight.
+#ifndef QLORA_RANK_RG4
+#define QLORA_RANK_RG4 1
+#endif
+template <int NB>
+constexpr int rank_rows_rg() { return NB == 4 ? QLORA_RANK_RG4 : 1; }
+template <int NB>
+constexpr int rank_rows_waves() { return NB <= 2 ? 16 : (NB == 4 ? 8 : (NB == 8 ? 4 : 2)); }
+template <int NB, int RG>
+constexpr int rank_depth() { return (RG + NB) * 2 * 4 * 3 + RG * NB * 4 <= 200 ? 3 : 2; }
+
+// Two K slices (32 each, from k0) of the RG P rows and the NB Q rows of a
+// lane.  The descriptors are passed by value so that they stay in scalar
+// registers.
+template <int NB, int RG>
+__device__ __forceinline__ void rank_load_pair(__amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
+                                               const uint32_t (&vp)[RG], const uint32_t (&vq)[NB],
+                                               int64_t k0, u32x4 (&x)[2][RG], u32x4 (&q)[2][NB]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t so = (uint32_t)((k0 + 32 * j) * 2);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      x[j][rg] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, vp[rg], so, 0));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      q[j][nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq[nb], so, 0));
+  }
+}
+
+template <int NB, int RG>
+__device__ __forceinline__ void rank_mma_pair(const u32x4 (&x)[2][RG], const u32x4 (&q)[2][NB],
+                                              f32x4 (&acc)[RG][NB]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[rg][nb] = mfma16(x[j][rg], q[j][nb], acc[rg][nb]);
+}
+
+template <int NB>
+__global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRowsArgs a) {
+  constexpr int W = rank_rows_waves<NB>();
+  constexpr int RG = rank_rows_rg<NB>();
+  constexpr int ROWS = 16 * RG;
+  constexpr int NC = 16 * NB;                       // columns covered
+  __shared__ float red[ROWS][NC];                   // wavefront partials, added in order
+  // wavefront index read as a scalar, so that K offsets stay in scalar registers
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t K = a.K;
+  const int64_t chunk = ((K + W - 1) / W + 31) / 32 * 32;
+  const int64_t k_begin = (int64_t)w * chunk;
+  const int64_t k_end = k_begin + chunk < K ? k_begin + chunk : K;
+
+  const __amdgpu_buffer_rsrc_t rp = rank_rsrc(a.P + m0 * K, (a.M - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(a.Q, a.N * a.ldq * 2);
+  uint32_t vp[RG], vq[NB];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) vp[rg] = (uint32_t)(((16 * rg + r16) * K + 8 * g) * 2);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) vq[nb] = (uint32_t)(((16 * nb + r16) * a.ldq + 8 * g) * 2);
+  const bool vec = (K % 8) == 0 && (a.ldq % 8) == 0;
+
+  f32x4 acc[RG][NB];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rg][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Full slices in pairs through a ring of D pair buffers: the loads of
+  // pair i + D - 1 are issued before the MFMAs of pair i.  The prologue and
+  // the steady loop load unconditionally (pairs past the range read zeros or
+  // unused in-bounds data), which keeps the compiler's wait counts exact;
+  // the last pairs run in a guarded tail.
+  constexpr int D = rank_depth<NB, RG>();
+  const int64_t k_full = k_begin + (vec ? (k_end - k_begin) / 64 * 64 : 0);
+  const int np = (int)((k_full - k_begin) / 64);
+  {
+    u32x4 x[D][2][RG], q[D][2][NB];
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i)
+      rank_load_pair<NB, RG>(rp, rq, vp, vq, k_begin + 64 * i, x[i], q[i]);
+    int i = 0;
+    for (; i + 2 * D - 1 <= np; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        rank_load_pair<NB, RG>(rp, rq, vp, vq, k_begin + 64 * (i + j + D - 1), x[(j + D - 1) % D],
+                               q[(j + D - 1) % D]);
+        rank_mma_pair<NB, RG>(x[j], q[j], acc);
+      }
+    }
+    for (; i < np; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (i + j < np) {
+          if (i + j + D - 1 < np)
+            rank_load_pair<NB, RG>(rp, rq, vp, vq, k_begin + 64 * (i + j + D - 1),
+                                   x[(j + D - 1) % D], q[(j + D - 1) % D]);
+          rank_mma_pair<NB, RG>(x[j], q[j], acc);
+        }
+      }
+    }
+  }
+  for (int64_t k0 = k_full; k0 < k_end; k0 += 32) {
+    // K tail or unaligned rows: element loads, zero at and past k_end
+    const int64_t kk = k0 + 8 * g;
+    uint32_t h[8];
+    u32x4 x[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = kk + e < k_end ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                    rp, (uint32_t)(((16 * rg + r16) * K + kk + e) * 2), 0, 0)
+                              : 0u;
+      x[rg] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                    h[6] | (h[7] << 16)};
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = kk + e < k_end ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                    rq, (uint32_t)(((16 * nb + r16) * a.ldq + kk + e) * 2), 0, 0)
+                              : 0u;
+      const u32x4 q = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                       h[6] | (h[7] << 16)};
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) acc[rg][nb] = mfma16(x[rg], q, acc[rg][nb]);
+    }
+  }
+  // wavefront partials added in wavefront order; accumulator lane l holds
+  // rows 4 (l/16) + v, column l%16 of its 16 x 16 block
+  for (int ww = 0; ww < W; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float* e = &red[16 * rg + 4 * g + v][16 * nb + r16];
+            *e = ww == 0 ? acc[rg][nb][v] : __fadd_rn(*e, acc[rg][nb][v]);
+          }
+    }
+    __syncthreads();
+  }
+
+  const int64_t rows = a.ht ? a.ldt : a.M;   // transposed copies are padded with zeros
+  for (int idx = threadIdx.x; idx < ROWS * NC; idx += W * 64) {
+    const int row = idx / NC, n = idx % NC;
+    const int64_t m = m0 + row;
+    if (m >= rows) continue;
+    const float v = __fmul_rn(a.scale, red[row][n]);   // zero for m >= M and n >= N
+    float hi, lo;
+    split_bf16(v, hi, lo);
+    const uint16_t hb = (uint16_t)(__float_as_uint(hi) >> 16);
+    const uint16_t lb = (uint16_t)(pack_bf16x2(lo, 0.0f) & 0xFFFFu);
+    if (m < a.M) {
+      if (a.out && n < a.N) a.out[m * a.N + n] = v;
+      if (a.hl && n < a.rp) {
+        a.hl[m * 2 * a.rp + n] = hb;
+        a.hl[m * 2 * a.rp + a.rp + n] = lb;
+      }
+    }
+    if (a.ht && n < a.N) {
+      a.ht[(int64_t)n * a.ldt + m] = hb;
+      a.lt[(int64_t)n * a.ldt + m] = lb;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Finish: v = scale * sum_s part[s] (s ascending).  Thread per element of the
 // transposed [N][ldt] index space (the FP32 [M][N] output is written from
 // the same thread when requested).
@@ -214,83 +406,168 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// part[s][i][c] = sum_{m in split s} P[m][i] Q[m][c].  The contraction runs
-// over tokens, the row index of both operands.  P arrives transposed
-// (hi/lo BF16 [R][ldp]) so its MFMA operand is one 16-byte load; Q is
-// transposed in registers: lane (c32, h) loads 4 columns of 8 token rows
-// (8-byte loads, a wavefront reads 16 rows x 256 B) and one byte permute per
-// output dword builds the 8-token column operands.  MFMA t of a lane then
-// covers columns 4*c32 + t.  Wavefront tile: 64 (i) x 128 (c), 16 tokens per
-// step; 4 wavefronts per workgroup side by side in c.
+// part[s][i][c] = sum_{m in split s} P[m][i] Q[m][c], i < R <= 256.  The
+// contraction runs over tokens, the row index of both operands.  P arrives
+// transposed and split (hi / lo BF16 [R][ldp], zero past M), so its MFMA
+// operand (eight consecutive tokens of one row i) is a 16-byte load from L2.
+// Q (X or dY) is streamed from HBM: each wavefront copies blocks of 64 token
+// rows x 64 columns into an LDS region of its own and reads the column
+// operands (eight consecutive tokens of one column) with transposing LDS
+// reads (ds_read_b64_tr_b16); the next block's global loads are issued
+// before the current block's MFMAs.  A workgroup covers all R rows x 64
+// columns x one token split; its four wavefronts take consecutive quarters
+// of the split and their partial tiles are added in wavefront order in LDS.
 // ---------------------------------------------------------------------------
+namespace {
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+constexpr int kGramRows = 64;                      // token rows per wavefront block
+constexpr int kGramLd = 80;                        // LDS row: 64 columns + pad (40 dwords, = 8 mod 32)
+constexpr int kGramWaveBytes = kGramRows * kGramLd * 2;
+}  // namespace
+
+// Q block (rows m .. m+63 of the wavefront, columns c0 .. c0+63): lane l
+// loads row 8 i + l/8, columns 8 (l%8) .. +8, i = 0..7.
+template <bool VEC>
+__device__ __forceinline__ void gram_load(__amdgpu_buffer_rsrc_t rq, int64_t m, int64_t c0,
+                                          int64_t N, int lane, u32x4 (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = m + 8 * i + (lane >> 3), col = c0 + 8 * (lane & 7);
+    if (VEC) {
+      x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rq, (uint32_t)((row * N + col) * 2), 0, 0));
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = col + e < N ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                 rq, (uint32_t)((row * N + col + e) * 2), 0, 0)
+                           : 0u;
+      x[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16)};
+    }
+  }
+}
+
+// One 64-token block of a wavefront: stage Q block x (tokens m ..) in LDS,
+// load the block's rank operands and the Q block two ahead into x, then 4
+// token slices x RB x 2 x (hi, lo) MFMAs.
+template <int RB, bool VEC>
+__device__ __forceinline__ void gram_block(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rh,
+                                           __amdgpu_buffer_rsrc_t rl, int64_t ldp, int64_t c0,
+                                           int64_t N, int64_t m, int lane, uint8_t* wl,
+                                           uint32_t wr, uint32_t rd, u32x4 (&x)[8],
+                                           f32x16 (&acc)[RB][2]) {
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + wr + i * 8 * kGramLd * 2) = x[i];
+  u32x4 ph[4][RB], pl[4][RB];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int ib = 0; ib < RB; ++ib) {
+      const uint32_t po = (uint32_t)(((32 * ib + r32) * ldp + m + 16 * t + 8 * h) * 2);
+      ph[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, po, 0, 0));
+      pl[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, po, 0, 0));
+    }
+  gram_load<VEC>(rq, m + 2 * kGramRows, c0, N, lane, x);
+  __builtin_amdgcn_sched_barrier(0);   // every load of the block ahead of its MFMAs
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    u32x4 b[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const uint8_t* pb = wl + rd + (16 * t * kGramLd + 32 * cb) * 2;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(pb));
+      const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(pb + 4 * kGramLd * 2));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi4);
+      b[cb] = u32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+#pragma unroll
+    for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        acc[ib][cb] = mfma32(ph[t][ib], b[cb], acc[ib][cb]);
+        acc[ib][cb] = mfma32(pl[t][ib], b[cb], acc[ib][cb]);
+      }
+  }
+}
+
+template <int RB, bool VEC>
 __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi,
                                               const uint16_t* __restrict__ Pt_lo, int64_t ldp,
                                               const uint16_t* __restrict__ Q, int64_t M,
                                               int64_t R, int64_t N, int64_t m_per_split,
                                               float* __restrict__ part) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c32 = lane & 31, h = lane >> 5;
-  const int64_t cb = (int64_t)blockIdx.x * 512 + 128 * w;
-  const int64_t i0 = (int64_t)blockIdx.y * 64;
-  const int s = blockIdx.z;
-  const int64_t m_begin = (int64_t)s * m_per_split;
-  int64_t m_end = m_begin + m_per_split;
-  if (m_end > M) m_end = M;
-  const int64_t col = cb + 4 * c32;
-  const bool cvec = (N % 4) == 0 && col + 4 <= N;
+  extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int g = lane >> 4, j = lane & 15;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int s = blockIdx.y;
+  // m_per_split is a multiple of 512: each quarter is whole pairs of
+  // 64-token blocks.  Tokens at or past M read as zero in Q, so their
+  // (finite) products add nothing and every block runs all four slices.
+  const int64_t quarter = m_per_split / 4;
+  const int64_t m_begin = (int64_t)s * m_per_split + (int64_t)w * quarter;
+  int64_t m_end = m_begin + quarter;
+  const int64_t m_lim = (M + 127) / 128 * 128;
+  if (m_end > m_lim) m_end = m_lim;
+  uint8_t* wl = glds + w * kGramWaveBytes;
 
-  f32x16 acc[4][2] = {};
-  for (int64_t m0 = m_begin; m0 < m_end; m0 += 16) {
-    uint32_t q[8][2];
+  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(Q, M * N * 2);       // rows past M read zero
+  const __amdgpu_buffer_rsrc_t rh = rank_rsrc(Pt_hi, R * ldp * 2);  // rows past R read zero
+  const __amdgpu_buffer_rsrc_t rl = rank_rsrc(Pt_lo, R * ldp * 2);
+
+  f32x16 acc[RB][2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t m = m0 + 8 * h + e;
-      if (m < m_end && cvec) {
-        const uint2 v = *reinterpret_cast<const uint2*>(Q + m * N + col);
-        q[e][0] = v.x;
-        q[e][1] = v.y;
-      } else {
-        uint32_t x[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] = (m < m_end && col + t < N) ? Q[m * N + col + t] : 0u;
-        q[e][0] = x[0] | (x[1] << 16);
-        q[e][1] = x[2] | (x[3] << 16);
-      }
-    }
-    u32x4 ah[2], al[2];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int64_t i = i0 + 32 * it + c32;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      ah[it] = i < R ? *reinterpret_cast<const u32x4*>(Pt_hi + i * ldp + m0 + 8 * h) : z;
-      al[it] = i < R ? *reinterpret_cast<const u32x4*>(Pt_lo + i * ldp + m0 + 8 * h) : z;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 b;
-      b.x = __builtin_amdgcn_perm(q[1][t >> 1], q[0][t >> 1], sel);
-      b.y = __builtin_amdgcn_perm(q[3][t >> 1], q[2][t >> 1], sel);
-      b.z = __builtin_amdgcn_perm(q[5][t >> 1], q[4][t >> 1], sel);
-      b.w = __builtin_amdgcn_perm(q[7][t >> 1], q[6][t >> 1], sel);
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        acc[t][it] = mfma32(ah[it], b, acc[t][it]);
-        acc[t][it] = mfma32(al[it], b, acc[t][it]);
-      }
-    }
+  for (int ib = 0; ib < RB; ++ib) acc[ib][0] = acc[ib][1] = f32x16{};
+
+  // LDS block row of element (token k, column c): row k, byte (k * kGramLd + c) * 2.
+  // Transposing read for MFMA column block cb, token slice t16: lane group g
+  // covers columns 16 (g & 1) .. +16 and tokens 8 (g >> 1) .. +4 (+4 second read).
+  const uint32_t wr = (uint32_t)(((8 * 0 + (lane >> 3)) * kGramLd + 8 * (lane & 7)) * 2);
+  const uint32_t rd = (uint32_t)(((8 * (g >> 1) + (j >> 2)) * kGramLd + 16 * (g & 1) + 4 * (j & 3)) * 2);
+
+  // Two Q blocks in flight: block j sits in register set j % 2 until it is
+  // staged, and its registers then receive block j + 2.  Loads past the
+  // range are in bounds or read zero and are never used; issuing them
+  // unconditionally keeps the compiler's wait counts exact.
+  u32x4 xa[8], xb[8];
+  gram_load<VEC>(rq, m_begin, c0, N, lane, xa);
+  __builtin_amdgcn_sched_barrier(0);   // issue order = use order
+  gram_load<VEC>(rq, m_begin + kGramRows, c0, N, lane, xb);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t m = m_begin; m < m_end; m += 2 * kGramRows) {
+    gram_block<RB, VEC>(rq, rh, rl, ldp, c0, N, m, lane, wl, wr, rd, xa, acc);
+    gram_block<RB, VEC>(rq, rh, rl, ldp, c0, N, m + kGramRows, lane, wl, wr, rd, xb, acc);
   }
+
+  // wavefront partials added in order 0, 1, 2, 3 in one FP32 tile
+  // [32 RB][64]; accumulator element v of lane l: row 8 (v/4) + 4 (l/32) + v%4,
+  // column l%32 of its 32 x 32 block
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(glds);
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+      for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int64_t c = col + t;
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + 32 * it + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (i < R && c < N) part[((int64_t)s * R + i) * N + c] = acc[t][it][v];
-      }
+          for (int v = 0; v < 16; ++v) {
+            const int row = 32 * ib + 8 * (v >> 2) + 4 * h + (v & 3);
+            float* e = red + row * 64 + 32 * cb + r32;
+            *e = ww == 0 ? acc[ib][cb][v] : __fadd_rn(*e, acc[ib][cb][v]);
+          }
     }
+    __syncthreads();
+  }
+  for (int idx = threadIdx.x; idx < 32 * RB * 64; idx += 256) {
+    const int64_t i = idx / 64, c = c0 + idx % 64;
+    if (i < R && c < N) part[((int64_t)s * R + i) * N + c] = red[idx];
+  }
 }
 
 __global__ __launch_bounds__(256) void k_gram_finish(const float* __restrict__ part, int splits,
@@ -317,6 +594,23 @@ hipError_t launch_rank_down_big(const uint16_t* P, const uint16_t* Q, int64_t M,
   dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 63) / 64), (unsigned)splits);
   hipLaunchKernelGGL(k_rank_down_big, grid, dim3(256), 0, st, P, Q, M, N, K, ldq, k_per_split,
                      part);
+  return hipGetLastError();
+}
+
+template <int NB>
+static void launch_rank_rows_t(const RankRowsArgs& a, hipStream_t st) {
+  const int64_t rows = a.ht ? a.ldt : a.M;
+  constexpr int R = 16 * rank_rows_rg<NB>();
+  const unsigned grid = (unsigned)((rows + R - 1) / R);
+  if (grid == 0) return;
+  hipLaunchKernelGGL(k_rank_rows<NB>, dim3(grid), dim3(64 * rank_rows_waves<NB>()), 0, st, a);
+}
+
+hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st) {
+  if (a.N <= 32) launch_rank_rows_t<2>(a, st);
+  else if (a.N <= 64) launch_rank_rows_t<4>(a, st);
+  else if (a.N <= 128) launch_rank_rows_t<8>(a, st);
+  else launch_rank_rows_t<16>(a, st);
   return hipGetLastError();
 }
 
@@ -350,13 +644,34 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
+template <int RB, bool VEC>
+static hipError_t launch_gram_t(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
+                                const uint16_t* Q, int64_t M, int64_t R, int64_t N,
+                                int64_t m_per_split, int splits, float* part, hipStream_t st) {
+  constexpr int lds = 4 * kGramWaveBytes > 32 * RB * 64 * 4 ? 4 * kGramWaveBytes : 32 * RB * 64 * 4;
+  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gram<RB, VEC>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  dim3 grid((unsigned)((N + 63) / 64), (unsigned)splits);
+  hipLaunchKernelGGL((k_gram<RB, VEC>), grid, dim3(256), lds, st, Pt_hi, Pt_lo, ldp, Q, M, R, N,
+                     m_per_split, part);
+  return hipGetLastError();
+}
+
 hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
                        const uint16_t* Q, int64_t M, int64_t R, int64_t N, int64_t m_per_split,
                        int splits, float* part, hipStream_t st) {
-  dim3 grid((unsigned)((N + 511) / 512), (unsigned)((R + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, st, Pt_hi, Pt_lo, ldp, Q, M, R, N, m_per_split,
-                     part);
-  return hipGetLastError();
+  const bool vec = (N % 8) == 0;
+#define QLORA_GRAM(RB)                                                                       \
+  return vec ? launch_gram_t<RB, true>(Pt_hi, Pt_lo, ldp, Q, M, R, N, m_per_split, splits,   \
+                                       part, st)                                             \
+             : launch_gram_t<RB, false>(Pt_hi, Pt_lo, ldp, Q, M, R, N, m_per_split, splits,  \
+                                        part, st)
+  if (R <= 32) { QLORA_GRAM(1); }
+  if (R <= 64) { QLORA_GRAM(2); }
+  if (R <= 128) { QLORA_GRAM(4); }
+  QLORA_GRAM(8);
+#undef QLORA_GRAM
 }
 
 hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,

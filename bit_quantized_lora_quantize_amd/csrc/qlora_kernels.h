@@ -68,6 +68,26 @@ hipError_t launch_rank_down_big(const uint16_t* P, const uint16_t* Q, int64_t M,
                                 int64_t K, int64_t ldq, int64_t k_per_split, int splits,
                                 float* part, hipStream_t st);
 
+// Large-M rank-r product in one pass, no partials:
+//   v[m][n] = scale * sum_k P[m][k] Q[n][k],  P [M][K], Q [N][ldq], N <= 256.
+// Outputs, each optional (NULL skips): out FP32 [M][N]; hl BF16 [M][2 rp],
+// hi | lo split of v with zeros for n in [N, rp) (rp a multiple of 32,
+// rp >= N); ht / lt BF16 [N][ldt] transposed hi / lo with zeros for m in
+// [M, ldt) (ldt a multiple of 16, >= M).
+struct RankRowsArgs {
+  const uint16_t* P;
+  const uint16_t* Q;
+  int64_t M, N, K, ldq;
+  float scale;
+  float* out;
+  uint16_t* hl;
+  int64_t rp;
+  uint16_t* ht;
+  uint16_t* lt;
+  int64_t ldt;
+};
+hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st);
+
 // Finish of split partials: v[m][n] = scale * sum_s part[s][m][n] (s
 // ascending).  out (optional) = v, FP32 [M][N]; ht/lt (optional) = the
 // transposed hi/lo BF16 pair of v, [N][ldt] with zeros for m in [M, ldt).
@@ -101,8 +121,8 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
 
 // part[s][i][c] = sum over tokens m in split s of P[m][i] * Q[m][c], with P
 // given transposed as a hi + lo BF16 pair Pt_hi/Pt_lo [R][ldp] (ldp >= M,
-// a multiple of 16, zero-padded) and Q BF16 [M][N].  m_per_split is a
-// multiple of 16.
+// a multiple of 16, zero-padded) and Q BF16 [M][N] (16-byte aligned), R <=
+// 256.  m_per_split is a multiple of 512.
 hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
                        const uint16_t* Q, int64_t M, int64_t R, int64_t N, int64_t m_per_split,
                        int splits, float* part, hipStream_t st);

@@ -66,6 +66,9 @@ SMALL = [  # (d_out, d_in, M, r)
     (513, 1088, 33, 24),
     (200, 4096, 16, 64),
     (96, 512, 129, 7),
+    (72, 192, 70, 100),     # large-M rank path, r in (64, 128]
+    (136, 256, 48, 256),    # large-M rank path at the maximum rank
+    (264, 320, 300, 40),    # two row tiles of the weight kernel, ragged in M and N
 ]
 
 
