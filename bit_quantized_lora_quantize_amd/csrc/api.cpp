@@ -95,24 +95,6 @@ QuantPlan plan_quant(int64_t d_out, int64_t d_in, void* ws) {
   return p;
 }
 
-// Split of a rank-down reduction over K.  Small M (one-wavefront tiles):
-// 128 of K per split.  Large M (256-row tiles): splits chosen to fill the
-// chip, 64-multiples of K per split, at most 16.
-struct KSplit {
-  int splits;
-  int64_t per;
-};
-KSplit rank_split(int64_t K, int64_t M, int64_t N) {
-  if (M <= kSmallM) {
-    const int64_t per = 128;
-    return {(int)cdiv(K, per), per};
-  }
-  const int64_t tiles = cdiv(M, 256) * cdiv(N, 64);
-  int64_t S = std::max<int64_t>(1, std::min<int64_t>({16, cdiv(256, tiles), cdiv(K, 64)}));
-  const int64_t per = round_up(cdiv(K, S), 64);
-  return {(int)cdiv(K, per), per};
-}
-
 struct GemvSplit {
   int ksplit, ss_per, tiles;
 };
@@ -126,9 +108,8 @@ GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t total_tiles) {
 
 struct FwdPlan {
   bool small;
-  KSplit tk;          // rank-down split of X A^T (shared with the backward)
-  float* t_part;      // [tk.splits][M][r]
   float* t_buf;       // [M][r] when T_save is NULL
+  float* t_part;      // [kRankSmallSplits][M][r] (small M)
   uint16_t* xp;       // [M][d_in] permuted X (small M)
   uint16_t* t_hl;     // [M][2 rp] BF16 hi | lo of T (large M)
   int64_t rp;         // r rounded up to 32
@@ -142,11 +123,10 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   FwdPlan p{};
   p.small = M <= kSmallM;
   Carver c(ws);
-  p.tk = rank_split(d_in, M, r);
-  if (p.small) p.t_part = c.take<float>(p.tk.splits * M * r);
   p.t_buf = c.take<float>(M * r);
   p.rp = round_up(r, 32);
   if (!p.small) p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
+  if (p.small) p.t_part = c.take<float>(kRankSmallSplits * M * r);
   if (p.small) {
     p.xp = c.take<uint16_t>(M * d_in);
     p.gs = gemv_split(d_out, d_in, cdiv(d_out, 64));
@@ -158,13 +138,10 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
 }
 
 struct BwdPlan {
-  KSplit tk;          // recomputation of T (same split as the forward)
-  float* t_part;      // [tk.splits][M][r]
   float* t_buf;       // [M][r]
-  KSplit uk;          // rank-down split of dY B over d_out
+  float* r_part;      // [kRankSmallSplits][M][r] (small M)
   int64_t ldbt;       // row stride of B^T
   uint16_t* bt;       // [r][ldbt]
-  float* u_part;      // [uk.splits][M][r]
   int64_t rp;         // r rounded up to 32
   uint16_t* u_hl;     // [M][2 rp] BF16 hi | lo of U
   int64_t ldp;        // token stride of the transposed hi/lo copies
@@ -190,16 +167,12 @@ int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
 BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   BwdPlan p{};
   Carver c(ws);
-  const bool small = M <= kSmallM;
-  p.tk = rank_split(d_in, M, r);
-  if (small) p.t_part = c.take<float>(p.tk.splits * M * r);
   p.t_buf = c.take<float>(M * r);
-  p.uk = rank_split(d_out, M, r);
   p.ldbt = round_up(d_out, 64);
   p.bt = c.take<uint16_t>(r * p.ldbt);
-  if (small) p.u_part = c.take<float>(p.uk.splits * M * r);
   p.rp = round_up(r, 32);
   p.u_hl = c.take<uint16_t>(M * 2 * p.rp);
+  if (M <= kSmallM) p.r_part = c.take<float>(kRankSmallSplits * M * r);
   p.ldp = round_up(std::max<int64_t>(M, 1), 16);
   p.ut_hi = c.take<uint16_t>(r * p.ldp);
   p.ut_lo = c.take<uint16_t>(r * p.ldp);
@@ -247,34 +220,22 @@ const IndexLut& lut() {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
 
-// --------------------------------------------------------- rank-down setup
-void fill_rank_desc(RankDownDesc& d, const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N,
-                    int64_t K, int64_t ldq, const KSplit& ks, float* part, uint16_t* xp,
-                    int wg_begin) {
-  d.P = P;
-  d.Q = Q;
-  d.part = part;
-  d.Xp = xp;
-  d.M = M;
-  d.N = N;
-  d.K = K;
-  d.ldq = ldq;
-  d.k_per_split = ks.per;
-  d.splits = ks.splits;
-  d.wg_begin = wg_begin;
-  d.tiles_m = (int)cdiv(M, 16);
-  d.tiles_n = (int)cdiv(N, 64);
-}
-
-int rank_down_single(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N, int64_t K,
-                     int64_t ldq, const KSplit& ks, float* part, hipStream_t st) {
-  if (M > kSmallM)
-    return hip_status(launch_rank_down_big(P, Q, M, N, K, ldq, ks.per, ks.splits, part, st));
-  RankDownArgs a{};
-  fill_rank_desc(a.d[0], P, Q, M, N, K, ldq, ks, part, nullptr, 0);
+// ------------------------------------------------------------- rank-r products
+// v = scale * P Q^T (P [M][K], Q [N][ldq]) with the outputs of RankRowsArgs;
+// small M and large M use different kernels, each deterministic, and the
+// forward and the backward call the same one for the same M.
+// Small M goes through kRankSmallSplits partials (part, FP32 [splits][M][N])
+// and the finish kernel, the order the weight-streaming epilogue also uses.
+int rank_product(const RankRowsArgs& ra, float* part, hipStream_t st) {
+  if (ra.M > kSmallM) return hip_status(launch_rank_rows(ra, st));
+  RankSmallArgs a{};
   a.count = 1;
-  const int wgs = a.d[0].tiles_m * a.d[0].tiles_n * a.d[0].splits;
-  return hip_status(launch_rank_down(a, wgs, st));
+  a.M = ra.M;
+  a.d[0] = RankSmallDesc{ra.P, ra.Q, ra.K, ra.ldq, ra.N, part, nullptr, nullptr, 0, 0};
+  int s = hip_status(launch_rank_small(a, st));
+  if (s) return s;
+  return hip_status(launch_rank_finish(part, kRankSmallSplits, ra.M, ra.N, ra.scale, ra.out,
+                                       ra.ht, ra.lt, ra.ldt, ra.hl, ra.rp, st));
 }
 
 struct FwdItemArgs {
@@ -324,7 +285,7 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       float* T = f.T_save ? f.T_save : p.t_buf;
       RankRowsArgs ra{f.X,    f.A,     M,       f.r,     q->d_in, q->d_in, f.alpha / (float)f.r,
                       T,      p.t_hl,  p.rp,    nullptr, nullptr, 0};
-      int s = hip_status(launch_rank_rows(ra, st));
+      int s = rank_product(ra, nullptr, st);
       if (s) return s;
       GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, p.t_hl, f.B, f.Y,
                  M,        q->d_out,      q->d_in,  f.r};
@@ -343,21 +304,17 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     plans[i] = plan_fwd(items[i].q->d_out, items[i].q->d_in, M, items[i].r, items[i].ws);
     total_tiles += cdiv(items[i].q->d_out, 64);
   }
-  RankDownArgs ra{};
+  RankSmallArgs ra{};
   ra.count = count;
-  int rwgs = 0;
+  ra.M = M;
   GemvArgs ga{};
   ga.count = count;
   ga.M = (int)M;
   int gwgs = 0;
-  FinishArgs fa{};
-  fa.count = count;
   for (int i = 0; i < count; ++i) {
     const FwdItemArgs& f = items[i];
     const qlora_nf4_t* q = f.q;
     FwdPlan& p = plans[i];
-    fill_rank_desc(ra.d[i], f.X, f.A, M, f.r, q->d_in, q->d_in, p.tk, p.t_part, p.xp, rwgs);
-    rwgs += ra.d[i].tiles_m * ra.d[i].tiles_n * ra.d[i].splits;
 
     const GemvSplit gs = gemv_split(q->d_out, q->d_in, total_tiles);
     GemvDesc& d = ga.d[i];
@@ -366,10 +323,9 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     d.scale2 = q->scale2;
     d.mean = q->scale_mean;
     d.Xp = p.xp;
-    float* T = f.T_save ? f.T_save : p.t_buf;
-    fa.d[i] = FinishDesc{p.t_part, T, nullptr, nullptr, M, f.r, M, f.alpha / (float)f.r,
-                         p.tk.splits, 0};
-    d.t_part = T;
+    ra.d[i] = RankSmallDesc{f.X, f.A, q->d_in, q->d_in, f.r, p.t_part, p.xp, nullptr, 0, 0};
+    d.t_part = p.t_part;
+    d.t_out = f.T_save;
     d.B = f.B;
     d.Y = f.Y;
     d.part = p.gemv_part;
@@ -377,8 +333,8 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     d.d_out = q->d_out;
     d.d_in = q->d_in;
     d.r = f.r;
-    d.t_scale = 1.0f;
-    d.t_splits = 1;
+    d.t_scale = f.alpha / (float)f.r;
+    d.t_splits = kRankSmallSplits;
     d.ksplit = gs.ksplit;
     d.ss_per_split = gs.ss_per;
     d.tiles = gs.tiles;
@@ -387,12 +343,11 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
   }
   for (int i = 0; i < count; ++i) {
     if (ga.d[i].ksplit > 1) {
-      ra.zero[i] = ga.d[i].counters;
-      ra.zero_count[i] = ga.d[i].tiles;
+      ra.d[i].zero = ga.d[i].counters;
+      ra.d[i].zero_count = ga.d[i].tiles;
     }
   }
-  int s = hip_status(launch_rank_down(ra, rwgs, st));
-  if (!s) s = hip_status(launch_rank_finish(fa, st));
+  int s = hip_status(launch_rank_small(ra, st));
   if (!s) s = hip_status(launch_gemv(ga, gwgs, st));
   return s;
 }
@@ -510,20 +465,12 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   }
   const float sc = lora_alpha / (float)r;
   // T = s X A^T (unless saved by the forward), and its transposed hi/lo copy
-  const bool small = M <= kSmallM;
   const float* T = T_saved;
   if (!T) {
     // the same kernels and summation order as the forward, so a recomputed T
     // equals a saved one bit for bit
-    if (small) {
-      s = rank_down_single(X, A, M, r, d_in, d_in, p.tk, p.t_part, st);
-      if (s) return s;
-      s = hip_status(launch_rank_finish(p.t_part, p.tk.splits, M, r, sc, p.t_buf, p.tt_hi,
-                                        p.tt_lo, p.ldp, nullptr, 0, st));
-    } else {
-      RankRowsArgs ra{X, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
-      s = hip_status(launch_rank_rows(ra, st));
-    }
+    RankRowsArgs ra{X, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
+    s = rank_product(ra, p.r_part, st);
     if (s) return s;
     T = p.t_buf;
   } else {
@@ -534,14 +481,9 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   // U = s dY B, through B^T so the contraction over d_out is contiguous
   s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
   if (s) return s;
-  if (small) {
-    s = rank_down_single(dY, p.bt, M, r, d_out, p.ldbt, p.uk, p.u_part, st);
-    if (s) return s;
-    s = hip_status(launch_rank_finish(p.u_part, p.uk.splits, M, r, sc, nullptr, p.ut_hi,
-                                      p.ut_lo, p.ldp, p.u_hl, p.rp, st));
-  } else {
+  {
     RankRowsArgs ra{dY, p.bt, M, r, d_out, p.ldbt, sc, nullptr, p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
-    s = hip_status(launch_rank_rows(ra, st));
+    s = rank_product(ra, p.r_part, st);
   }
   if (s) return s;
   // dX = dY Wh + U A

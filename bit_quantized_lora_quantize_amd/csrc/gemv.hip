@@ -19,49 +19,63 @@
 
 namespace qlora {
 
+// Global data of one 256-wide super-step for one lane, held in registers
+// between its loads and its MFMAs.
 struct StepData {
   u32x4 c0, c1;   // 32 bytes of codes: the lane's block
   u32x4 x[8];     // X operand for the eight MFMAs
   uint32_t sc;    // FP8 scale code
-  float s2;       // second-level scale
-  float mu;       // scale mean, or 0 for a row past d_out / block past d_in
+  float s2;       // second-level scale (0 for a block past d_in)
+  float mu;       // scale mean (0 for a block past d_in)
 };
 
-__device__ __forceinline__ void load_step(const GemvDesc& d, int64_t ss, int64_t n, int g,
-                                          int m, int M, int64_t nblk, float mean, StepData& s) {
-  const int64_t kb = ss * 4 + g;
-  const bool kb_ok = kb < nblk;
-  const bool w_ok = kb_ok && n < d.d_out;
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  s.c0 = z;
-  s.c1 = z;
-  s.sc = 0u;
-  s.s2 = 0.0f;
-  s.mu = 0.0f;
-  if (w_ok) {
-    const u32x4* cp = reinterpret_cast<const u32x4*>(d.codes + n * (d.d_in / 2) + kb * 32);
-    s.c0 = __builtin_nontemporal_load(cp);
-    s.c1 = __builtin_nontemporal_load(cp + 1);
-    const int64_t b = n * nblk + kb;
-    s.sc = d.scodes[b];
-    s.s2 = d.scale2[b >> 8];
-    s.mu = mean;
-  }
-  const bool x_ok = kb_ok && m < M;
-  const u32x4* xp = reinterpret_cast<const u32x4*>(d.Xp + (int64_t)m * d.d_in + kb * 64);
+// Buffer descriptor of a workgroup-uniform range, in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), 0,
+                                           __builtin_amdgcn_readfirstlane(n), 0x00020000);
+}
+
+struct GemvLane {
+  __amdgpu_buffer_rsrc_t codes, scodes, s2, x;
+  uint32_t vc, vs, vx;   // lane byte offsets (step 0)
+  int64_t blk0;          // first-level block index of the lane's row, step 0
+  int64_t nblk;
+  int g;
+};
+
+// Super-step ss (lane block kb = 4 ss + g).  Rows past d_out and X rows past
+// M read as zero (descriptor bounds); a block past d_in gets s2 = 0, so its
+// restored scale, table and products are zero whatever codes it reads.
+__device__ __forceinline__ void load_step(const GemvLane& L, int64_t ss, float mean, StepData& s) {
+  const uint32_t so_c = (uint32_t)(ss * 128), so_x = (uint32_t)(ss * 512);
+  s.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.codes, L.vc, so_c, 0));
+  s.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.codes, L.vc + 16, so_c, 0));
+  s.sc = __builtin_amdgcn_raw_buffer_load_b8(L.scodes, L.vs, (uint32_t)(ss * 4), 0);
+  const int64_t kb = ss * 4 + L.g;
+  const uint32_t grp = (uint32_t)((L.blk0 + ss * 4) >> 8);
+  const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(L.s2, grp * 4, 0, 0));
+  s.s2 = kb < L.nblk ? s2 : 0.0f;
+  s.mu = kb < L.nblk ? mean : 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s.x[j] = x_ok ? xp[j] : z;
+  for (int j = 0; j < 8; ++j)
+    s.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.x, L.vx + 16 * j, so_x, 0));
 }
 
 __device__ __forceinline__ f32x4 compute_step(const StepData& s, f32x4 acc) {
-  // A row past d_out or a block past d_in has code 0, s2 = 0 and mean 0: its
-  // restored scale and table are zero and it adds nothing.
+  // a masked block has s2 = 0 and mean 0: restored scale, table and
+  // products are zero
   const Nf4Table t = nf4_table(restored_scale(s.sc, s.s2, s.mu));
   const uint32_t cw[8] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w, s.c1.x, s.c1.y, s.c1.z, s.c1.w};
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc = mfma16(s.x[j], nf4_dequant8_perm(cw[j], t), acc);
   return acc;
 }
+
+constexpr int kGemvDepth = 3;   // super-steps in flight per lane
 
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int wg = blockIdx.x;
@@ -72,7 +86,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int split = local % d.ksplit;
   const int tile = local / d.ksplit;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int M = a.M;
   const int64_t n = (int64_t)tile * 64 + 16 * w + r16;  // B-operand row and output column
@@ -83,14 +97,45 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   if (ss1 > nss) ss1 = nss;
   const float mean = d.mean[0];
 
+  GemvLane L;
+  L.codes = gemv_rsrc(d.codes, d.d_out * (d.d_in / 2));
+  L.scodes = gemv_rsrc(d.scodes, d.d_out * nblk);
+  L.s2 = gemv_rsrc(d.scale2, ((d.d_out * nblk + kGroup - 1) / kGroup) * 4);
+  L.x = gemv_rsrc(d.Xp, (int64_t)M * d.d_in * 2);
+  L.vc = (uint32_t)(n * (d.d_in / 2) + 32 * g);
+  L.vs = (uint32_t)(n * nblk + g);
+  L.vx = (uint32_t)((int64_t)r16 * d.d_in * 2 + 128 * g);
+  L.blk0 = n * nblk + g;
+  L.nblk = nblk;
+  L.g = g;
+
+  // Ring of kGemvDepth steps: the loads of step ss + D - 1 are issued before
+  // the MFMAs of step ss.  Prologue and steady loop load unconditionally
+  // (steps past ss1 read in bounds or zero and are never used), which keeps
+  // the compiler's wait counts exact; the last steps run in a guarded tail.
+  constexpr int D = kGemvDepth;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (ss0 < ss1) {
-    StepData cur, nxt;
-    load_step(d, ss0, n, g, r16, M, nblk, mean, cur);
-    for (int64_t ss = ss0; ss < ss1; ++ss) {
-      if (ss + 1 < ss1) load_step(d, ss + 1, n, g, r16, M, nblk, mean, nxt);
-      acc = compute_step(cur, acc);
-      cur = nxt;
+  const int nsteps = (int)(ss1 - ss0);
+  {
+    StepData st[D];
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) load_step(L, ss0 + i, mean, st[i]);
+    int i = 0;
+    for (; i + 2 * D - 1 <= nsteps; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        load_step(L, ss0 + i + j + D - 1, mean, st[(j + D - 1) % D]);
+        acc = compute_step(st[j], acc);
+      }
+    }
+    for (; i < nsteps; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (i + j < nsteps) {
+          if (i + j + D - 1 < nsteps) load_step(L, ss0 + i + j + D - 1, mean, st[(j + D - 1) % D]);
+          acc = compute_step(st[j], acc);
+        }
+      }
     }
   }
 
@@ -152,9 +197,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         for (int e = 0; e < 8; ++e) t[e] = (s == 0) ? v8[e] : __fadd_rn(t[e], v8[e]);
       }
     }
-    float hi[8], lo[8];
+    float hi[8], lo[8], tv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(__fmul_rn(d.t_scale, t[e]), hi[e], lo[e]);
+    for (int e = 0; e < 8; ++e) {
+      tv[e] = __fmul_rn(d.t_scale, t[e]);
+      split_bf16(tv[e], hi[e], lo[e]);
+    }
+    // T itself, once per problem: the first wavefront of tile 0 (of the
+    // split that reached this epilogue)
+    if (d.t_out && tile == 0 && w == 0 && r16 < M) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (kk + e < d.r) d.t_out[(int64_t)r16 * d.r + kk + e] = tv[e];
+    }
     u32x4 ah, al;
     ah.x = pack_bf16x2(hi[0], hi[1]); ah.y = pack_bf16x2(hi[2], hi[3]);
     ah.z = pack_bf16x2(hi[4], hi[5]); ah.w = pack_bf16x2(hi[6], hi[7]);

@@ -13,154 +13,6 @@
 
 namespace qlora {
 
-// Eight BF16 values row[k0 .. k0+7], zero at and past `lim`.
-__device__ __forceinline__ u32x4 load8_bf16(const uint16_t* row, int64_t k0, int64_t lim,
-                                            bool vec) {
-  if (vec && k0 + 8 <= lim) return *reinterpret_cast<const u32x4*>(row + k0);
-  uint32_t h[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = (k0 + e < lim) ? row[k0 + e] : 0u;
-  u32x4 r;
-  r.x = h[0] | (h[1] << 16);
-  r.y = h[2] | (h[3] << 16);
-  r.z = h[4] | (h[5] << 16);
-  r.w = h[6] | (h[7] << 16);
-  return r;
-}
-
-// ---------------------------------------------------------------------------
-// Small M: part[s][m][n] = sum_{k in split s} P[m][k] Q[n][k].  One wavefront
-// per 16 x 64 output tile and K split; a grid covers up to kMaxGroup
-// problems.  The column-tile-0 wavefronts also write P permuted within each
-// eight (the X operand of the weight-streaming kernel).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_rank_down(RankDownArgs a) {
-  for (int z = 0; z < a.count; ++z) {
-    if (!a.zero[z]) continue;
-    for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < a.zero_count[z];
-         i += (int64_t)gridDim.x * 64)
-      a.zero[z][i] = 0u;
-  }
-  const int wg = blockIdx.x;
-  int di = 0;
-  while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
-  const RankDownDesc& d = a.d[di];
-  int local = wg - d.wg_begin;
-  const int s = local % d.splits;
-  local /= d.splits;
-  const int tn = local % d.tiles_n;
-  const int tm = local / d.tiles_n;
-
-  const int lane = threadIdx.x;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t m = (int64_t)tm * 16 + r16;
-  const int64_t k_begin = (int64_t)s * d.k_per_split;
-  int64_t k_end = k_begin + d.k_per_split;
-  if (k_end > d.K) k_end = d.K;
-  const bool pvec = (d.K % 8) == 0;
-  const bool qvec = (d.ldq % 8) == 0;
-
-  f32x4 acc[4] = {};
-  const uint16_t* prow = d.P + m * d.K;
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += 32) {
-    const int64_t kk = k0 + 8 * g;
-    u32x4 av = {0u, 0u, 0u, 0u};
-    if (m < d.M && kk < k_end) av = load8_bf16(prow, kk, k_end, pvec);
-    if (d.Xp && tn == 0 && m < d.M && kk < k_end)
-      *reinterpret_cast<u32x4*>(d.Xp + m * d.K + kk) = perm8_bf16(av);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t n = (int64_t)tn * 64 + 16 * t + r16;
-      u32x4 bv = {0u, 0u, 0u, 0u};
-      if (n < d.N && kk < k_end) bv = load8_bf16(d.Q + n * d.ldq, kk, k_end, qvec);
-      acc[t] = mfma16(av, bv, acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t n = (int64_t)tn * 64 + 16 * t + r16;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t mm = (int64_t)tm * 16 + 4 * g + v;
-      if (mm < d.M && n < d.N) d.part[((int64_t)s * d.M + mm) * d.N + n] = acc[t][v];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Large M: the same product with 256 x 64 workgroup tiles.  Wavefront w owns
-// rows 64w .. 64w+63 of the tile: 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.
-// Operands come straight from global memory (P streamed once, Q shared
-// through L1/L2); each iteration covers 64 of K.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_rank_down_big(const uint16_t* __restrict__ P,
-                                                       const uint16_t* __restrict__ Q, int64_t M,
-                                                       int64_t N, int64_t K, int64_t ldq,
-                                                       int64_t k_per_split,
-                                                       float* __restrict__ part) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r32 = lane & 31, h = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.x * 256 + 64 * w;
-  const int64_t n0 = (int64_t)blockIdx.y * 64;
-  const int s = blockIdx.z;
-  const int64_t k_begin = (int64_t)s * k_per_split;
-  int64_t k_end = k_begin + k_per_split;
-  if (k_end > K) k_end = K;
-  const bool fast = (K % 8) == 0 && (ldq % 8) == 0 && m0 + 64 <= M && n0 + 64 <= N;
-
-  f32x16 acc[2][2] = {};
-  const uint16_t* pr[2];
-  const uint16_t* qr[2];
-  bool pok[2], qok[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t m = m0 + 32 * i + r32, n = n0 + 32 * i + r32;
-    pok[i] = m < M;
-    qok[i] = n < N;
-    pr[i] = P + (pok[i] ? m : 0) * K;
-    qr[i] = Q + (qok[i] ? n : 0) * ldq;
-  }
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += 64) {
-    u32x4 a[4][2], b[4][2];
-    if (fast && k0 + 64 <= k_end) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          a[ks][i] = *reinterpret_cast<const u32x4*>(pr[i] + k0 + 16 * ks + 8 * h);
-          b[ks][i] = *reinterpret_cast<const u32x4*>(qr[i] + k0 + 16 * ks + 8 * h);
-        }
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int64_t kk = k0 + 16 * ks + 8 * h;
-          a[ks][i] = pok[i] ? load8_bf16(pr[i], kk, k_end, (K % 8) == 0) : z;
-          b[ks][i] = qok[i] ? load8_bf16(qr[i], kk, k_end, (ldq % 8) == 0) : z;
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[ks][i], b[ks][j], acc[i][j]);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + 32 * j + r32;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < M && n < N) part[((int64_t)s * M + m) * N + n] = acc[i][j][v];
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Large M, one pass: v[m][n] = scale * sum_k P[m][k] Q[n][k], n < N <= 256.
 // A workgroup owns 16 token rows and the whole K: its W wavefronts take
@@ -170,9 +22,15 @@ __global__ __launch_bounds__(256) void k_rank_down_big(const uint16_t* __restric
 // Q (r x K, small) is shared through L2.  Loads go through buffer
 // descriptors: rows of P past M and rows of Q past N read as zero.
 // ---------------------------------------------------------------------------
+// Buffer descriptor of a workgroup-uniform range, read through scalar
+// registers so that every load using it is a single instruction.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rank_rsrc(const void* base, int64_t bytes) {
   const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), 0,
+                                           __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
 // Row groups of 16 tokens per workgroup (RG) and wavefronts (W): every
@@ -351,6 +209,132 @@ __global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRo
       a.lt[(int64_t)n * a.ldt + m] = lb;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Small M (<= 16 tokens): partial sums part[s][m][n] of P Q^T over quarters
+// of K, for a group of problems.  Workgroup = one 16-column block, problem
+// and quarter; its four wavefronts take consecutive parts of the quarter
+// (v_mfma_f32_16x16x32_bf16, rows past M read as zero; each part's loads
+// issued in groups ahead of the MFMAs) and add their sums in wavefront
+// order in LDS.  The problem's workgroups also write the permuted copy of P
+// and clear the counters of the following weight-streaming launch.
+// ---------------------------------------------------------------------------
+constexpr int kSmallGroup = 4;   // K slices per load group
+
+template <int G>
+__device__ __forceinline__ void small_load(__amdgpu_buffer_rsrc_t rp, __amdgpu_buffer_rsrc_t rq,
+                                           uint32_t vp, uint32_t vq, int64_t k0, u32x4 (&x)[G],
+                                           u32x4 (&q)[G]) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const uint32_t so = (uint32_t)((k0 + 32 * j) * 2);
+    x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, vp, so, 0));
+    q[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq, so, 0));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rank_small(RankSmallArgs a) {
+  constexpr int S = kRankSmallSplits;
+  __shared__ float red[16][16];
+  const int wg = blockIdx.x;
+  int di = 0;
+  while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
+  const RankSmallDesc& d = a.d[di];
+  const int local = wg - d.wg_begin;
+  const int nblk = (int)((d.N + 15) / 16);
+  const int cb = local % nblk, sq = local / nblk;   // column block, K quarter
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t M = a.M, K = d.K;
+
+  if (local == 0 && d.zero)
+    for (int64_t i = threadIdx.x; i < d.zero_count; i += 256) d.zero[i] = 0u;
+  if (d.xp) {
+    // eight BF16 values per item, permuted as the table lookup orders them;
+    // shared by the problem's workgroups
+    const int64_t n8 = M * K / 8;
+    for (int64_t i = (int64_t)local * 256 + threadIdx.x; i < n8; i += (int64_t)nblk * S * 256)
+      reinterpret_cast<u32x4*>(d.xp)[i] = perm8_bf16(reinterpret_cast<const u32x4*>(d.P)[i]);
+  }
+
+  // K part of the wavefront: part 4 sq + w of 16, whole load groups
+  const int64_t chunk = ((K + 4 * S - 1) / (4 * S) + 32 * kSmallGroup - 1) / (32 * kSmallGroup) *
+                        (32 * kSmallGroup);
+  const int64_t part_id = (int64_t)sq * 4 + w;
+  const int64_t k_begin = part_id * chunk < K ? part_id * chunk : K;
+  const int64_t k_end = k_begin + chunk < K ? k_begin + chunk : K;
+  const __amdgpu_buffer_rsrc_t rp = rank_rsrc(d.P, M * K * 2);             // rows past M: zero
+  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(d.Q + (int64_t)16 * cb * d.ldq,
+                                             (d.N - 16 * cb) * d.ldq * 2);  // rows past N: zero
+  const uint32_t vp = (uint32_t)((r16 * K + 8 * g) * 2);
+  const uint32_t vq = (uint32_t)((r16 * d.ldq + 8 * g) * 2);
+  const bool vec = (K % 8) == 0 && (d.ldq % 8) == 0;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // full load groups (two in flight; loads unconditional in the prologue and
+  // the steady loop, so the compiler's wait counts stay exact), then a tail
+  constexpr int G = kSmallGroup;
+  const int64_t k_full = k_begin + (vec ? (k_end - k_begin) / (32 * G) * (32 * G) : 0);
+  const int ng = (int)((k_full - k_begin) / (32 * G));
+  {
+    u32x4 xa[G], qa[G], xb[G], qb[G];
+    small_load<G>(rp, rq, vp, vq, k_begin, xa, qa);
+    int i = 0;
+    for (; i + 2 <= ng; i += 2) {
+      small_load<G>(rp, rq, vp, vq, k_begin + 32 * G * (i + 1), xb, qb);
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc = mfma16(xa[j], qa[j], acc);
+      small_load<G>(rp, rq, vp, vq, k_begin + 32 * G * (i + 2), xa, qa);
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc = mfma16(xb[j], qb[j], acc);
+    }
+    if (i < ng) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc = mfma16(xa[j], qa[j], acc);
+    }
+  }
+  for (int64_t k0 = k_full; k0 < k_end; k0 += 32) {
+    const int64_t kk = k0 + 8 * g;
+    uint32_t hx[8], hq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool in = kk + e < k_end;
+      hx[e] = in ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rp, (uint32_t)((r16 * K + kk + e) * 2), 0, 0) : 0u;
+      hq[e] = in ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, (uint32_t)((r16 * d.ldq + kk + e) * 2), 0, 0) : 0u;
+    }
+    const u32x4 x = {hx[0] | (hx[1] << 16), hx[2] | (hx[3] << 16), hx[4] | (hx[5] << 16), hx[6] | (hx[7] << 16)};
+    const u32x4 q = {hq[0] | (hq[1] << 16), hq[2] | (hq[3] << 16), hq[4] | (hq[5] << 16), hq[6] | (hq[7] << 16)};
+    acc = mfma16(x, q, acc);
+  }
+  // wavefront sums added in order; accumulator lane l holds rows 4 (l/16) + v,
+  // column l%16
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float* e = &red[4 * g + v][r16];
+        *e = ww == 0 ? acc[v] : __fadd_rn(*e, acc[v]);
+      }
+    }
+    __syncthreads();
+  }
+  {
+    const int row = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int64_t n = 16 * cb + c;
+    if (row < M && n < d.N) d.part[((int64_t)sq * M + row) * d.N + n] = red[row][c];
+  }
+}
+
+hipError_t launch_rank_small(const RankSmallArgs& a0, hipStream_t st) {
+  RankSmallArgs a = a0;
+  int wgs = 0;
+  for (int i = 0; i < a.count; ++i) {
+    a.d[i].wg_begin = wgs;
+    wgs += (int)((a.d[i].N + 15) / 16) * kRankSmallSplits;
+  }
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rank_small, dim3(wgs), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -583,20 +567,6 @@ __global__ __launch_bounds__(256) void k_gram_finish(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_rank_down(const RankDownArgs& a, int total_wgs, hipStream_t st) {
-  hipLaunchKernelGGL(k_rank_down, dim3(total_wgs), dim3(64), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_rank_down_big(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N,
-                                int64_t K, int64_t ldq, int64_t k_per_split, int splits,
-                                float* part, hipStream_t st) {
-  dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL(k_rank_down_big, grid, dim3(256), 0, st, P, Q, M, N, K, ldq, k_per_split,
-                     part);
-  return hipGetLastError();
-}
-
 template <int NB>
 static void launch_rank_rows_t(const RankRowsArgs& a, hipStream_t st) {
   const int64_t rows = a.ht ? a.ldt : a.M;

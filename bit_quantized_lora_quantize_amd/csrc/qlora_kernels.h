@@ -36,37 +36,35 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, cons
 // ------------------------------------------------------------- rank-r work
 constexpr int kMaxGroup = 8;
 
-// part[s][m][n] = sum over k in split s of P[m][k] * Q[n][k]   (FP32)
-// P BF16 [M][K] (row stride K), Q BF16 [N][ldq] (K contiguous).  When Xp is
-// set, the workgroups of column tile 0 also write P permuted within each
-// group of eight (the order of nf4_dequant8_perm).  The launch also clears
-// the zero[] ranges (split-K counters of the following weight-streaming
-// launch).
-struct RankDownDesc {
+// Small-M rank-r product (M <= 16), up to kMaxGroup problems per launch, as
+// kRankSmallSplits partial sums over consecutive quarters of K:
+//   part[s][m][n] = sum_{k in quarter s} P[m][k] Q[n][k],
+// P [M][K] BF16, Q [N][ldq] BF16, part FP32 [kRankSmallSplits][M][N].
+// v = scale * (((part[0] + part[1]) + part[2]) + part[3]) is formed by the
+// consumer (weight-streaming epilogue or launch_rank_finish) in that order,
+// so every path gets the same bits.  One 4-wavefront workgroup per
+// 16-column block, problem and quarter; wavefronts take consecutive parts
+// of the quarter and add their sums in wavefront order.  The workgroups of
+// a problem also write xp (P permuted within each group of eight, the order
+// of nf4_dequant8_perm; [M][K], optional) and clear zero[0 .. zero_count)
+// (split-K counters of the following weight-streaming launch).
+constexpr int kRankSmallSplits = 4;
+struct RankSmallDesc {
   const uint16_t* P;
   const uint16_t* Q;
+  int64_t K, ldq, N;
   float* part;
-  uint16_t* Xp;
-  int64_t M, N, K, ldq;
-  int64_t k_per_split;  // multiple of 32
-  int splits;
-  int wg_begin;         // first workgroup of this item in the grid
-  int tiles_m, tiles_n;
+  uint16_t* xp;
+  uint32_t* zero;
+  int64_t zero_count;
+  int wg_begin;     // first workgroup of this problem (set by the launcher)
 };
-struct RankDownArgs {
-  RankDownDesc d[kMaxGroup];
+struct RankSmallArgs {
+  RankSmallDesc d[kMaxGroup];
   int count;
-  uint32_t* zero[kMaxGroup];   // u32 ranges cleared by the launch (or null)
-  int zero_count[kMaxGroup];
+  int64_t M;
 };
-hipError_t launch_rank_down(const RankDownArgs& a, int total_wgs, hipStream_t st);
-
-// Large-M form of the same product: 256-row workgroup tiles (4 wavefronts of
-// 64 rows) x 64 columns, v_mfma_f32_32x32x16_bf16, K split across
-// workgroups (k_per_split a multiple of 64).
-hipError_t launch_rank_down_big(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t N,
-                                int64_t K, int64_t ldq, int64_t k_per_split, int splits,
-                                float* part, hipStream_t st);
+hipError_t launch_rank_small(const RankSmallArgs& a, hipStream_t st);
 
 // Large-M rank-r product in one pass, no partials:
 //   v[m][n] = scale * sum_k P[m][k] Q[n][k],  P [M][K], Q [N][ldq], N <= 256.
@@ -143,6 +141,7 @@ struct GemvDesc {
   const float* mean;
   const uint16_t* Xp;
   const float* t_part;
+  float* t_out;      // optional: T = t_scale * sum_s t_part[s], FP32 [M][r]
   const uint16_t* B;
   uint16_t* Y;
   float* part;
