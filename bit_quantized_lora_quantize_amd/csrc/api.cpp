@@ -37,7 +37,6 @@ namespace {
 constexpr int64_t kMaxRank = 256;
 constexpr int64_t kSmallM = 16;      // M <= 16 streams the weight (GEMV path)
 constexpr int64_t kMaxLinearDim = int64_t(1) << 22;  // keeps device offsets 32-bit
-constexpr int kTargetWgs = 512;      // workgroups aimed for when splitting K
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -98,23 +97,38 @@ QuantPlan plan_quant(int64_t d_out, int64_t d_in, void* ws) {
 struct GemvSplit {
   int ksplit, ss_per, tiles;
 };
-GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t total_tiles) {
-  const int64_t tiles = cdiv(d_out, 64);
+// K split of the weight-streaming launch.  The work of a group is counted in
+// units of one kGemvRows-row tile times one 256-wide super-step; every item
+// gets about the same number of super-steps per workgroup (so that no long
+// K range finishes alone), chosen to give about kGemvTargetWgs workgroups in
+// all, with at most kGemvMaxSplit splits per item (bounding the partials)
+// and few enough super-steps that the staged X fits the kernel's LDS.
+#ifndef QLORA_GEMV_TARGET_WGS
+#define QLORA_GEMV_TARGET_WGS 1024
+#endif
+constexpr int64_t kGemvTargetWgs = QLORA_GEMV_TARGET_WGS;
+constexpr int64_t kGemvMaxSplit = 16;
+int64_t gemv_units(int64_t d_out, int64_t d_in) {
+  return cdiv(d_out, kGemvRows) * cdiv(d_in / kBlock, 4);
+}
+GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t M, int64_t total_units) {
+  const int64_t tiles = cdiv(d_out, kGemvRows);
   const int64_t nss = cdiv(d_in / kBlock, 4);
-  int64_t ks = std::max<int64_t>(1, std::min<int64_t>(cdiv(kTargetWgs, total_tiles), nss));
-  const int64_t per = cdiv(nss, ks);
-  return {(int)cdiv(nss, per), (int)per, (int)tiles};
+  const int64_t ss_max = ((kGemvMaxLds - gemv_lds_bytes(M, 0)) / (M + 1)) / 512;
+  int64_t per = std::max<int64_t>(1, cdiv(total_units, kGemvTargetWgs));
+  per = std::max(per, cdiv(nss, kGemvMaxSplit));
+  per = std::min({per, nss, ss_max});
+  const int64_t ks = cdiv(nss, per);
+  return {(int)ks, (int)cdiv(nss, ks), (int)tiles};
 }
 
 struct FwdPlan {
   bool small;
   float* t_buf;       // [M][r] when T_save is NULL
-  float* t_part;      // [kRankSmallSplits][M][r] (small M)
-  uint16_t* xp;       // [M][d_in] permuted X (small M)
+  float* t_part;      // [4 ksplit][M][r] (small M)
   uint16_t* t_hl;     // [M][2 rp] BF16 hi | lo of T (large M)
   int64_t rp;         // r rounded up to 32
-  float* gemv_part;   // [ksplit][16][d_out]
-  uint32_t* counters; // [tiles]
+  float* gemv_part;   // [ksplit][16][d_out] (small M)
   GemvSplit gs;
   size_t bytes;
 };
@@ -126,12 +140,11 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.t_buf = c.take<float>(M * r);
   p.rp = round_up(r, 32);
   if (!p.small) p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
-  if (p.small) p.t_part = c.take<float>(kRankSmallSplits * M * r);
   if (p.small) {
-    p.xp = c.take<uint16_t>(M * d_in);
-    p.gs = gemv_split(d_out, d_in, cdiv(d_out, 64));
+    // a problem alone gets the most splits it can get in any group
+    p.gs = gemv_split(d_out, d_in, M, gemv_units(d_out, d_in));
+    p.t_part = c.take<float>((int64_t)p.gs.ksplit * M * r);
     p.gemv_part = c.take<float>((int64_t)p.gs.ksplit * 16 * d_out);
-    p.counters = c.take<uint32_t>(p.gs.tiles);
   }
   p.bytes = c.off + 256;
   return p;
@@ -231,7 +244,7 @@ int rank_product(const RankRowsArgs& ra, float* part, hipStream_t st) {
   RankSmallArgs a{};
   a.count = 1;
   a.M = ra.M;
-  a.d[0] = RankSmallDesc{ra.P, ra.Q, ra.K, ra.ldq, ra.N, part, nullptr, nullptr, 0, 0};
+  a.d[0] = RankSmallDesc{ra.P, ra.Q, ra.K, ra.ldq, ra.N, part, nullptr, 0, 0};
   int s = hip_status(launch_rank_small(a, st));
   if (s) return s;
   return hip_status(launch_rank_finish(part, kRankSmallSplits, ra.M, ra.N, ra.scale, ra.out,
@@ -295,61 +308,48 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     return QLORA_OK;
   }
 
-  // Small M: for the whole group, one rank-down launch (X A^T partials, the
-  // permuted X copy, counters cleared), one finish launch (T) and one
-  // weight-streaming launch.
+  // Small M: one weight-streaming launch for the whole group (which also
+  // forms the X A^T partials) and one finish launch.
   FwdPlan plans[kMaxGroup];
-  int64_t total_tiles = 0;
+  int64_t total_units = 0;
   for (int i = 0; i < count; ++i) {
     plans[i] = plan_fwd(items[i].q->d_out, items[i].q->d_in, M, items[i].r, items[i].ws);
-    total_tiles += cdiv(items[i].q->d_out, 64);
+    total_units += gemv_units(items[i].q->d_out, items[i].q->d_in);
   }
-  RankSmallArgs ra{};
-  ra.count = count;
-  ra.M = M;
   GemvArgs ga{};
   ga.count = count;
   ga.M = (int)M;
-  int gwgs = 0;
+  int gwgs = 0, fwgs = 0;
   for (int i = 0; i < count; ++i) {
     const FwdItemArgs& f = items[i];
     const qlora_nf4_t* q = f.q;
-    FwdPlan& p = plans[i];
-
-    const GemvSplit gs = gemv_split(q->d_out, q->d_in, total_tiles);
+    const FwdPlan& p = plans[i];
+    const GemvSplit gs = gemv_split(q->d_out, q->d_in, M, total_units);
     GemvDesc& d = ga.d[i];
     d.codes = q->codes;
     d.scodes = q->scale_codes;
     d.scale2 = q->scale2;
     d.mean = q->scale_mean;
-    d.Xp = p.xp;
-    ra.d[i] = RankSmallDesc{f.X, f.A, q->d_in, q->d_in, f.r, p.t_part, p.xp, nullptr, 0, 0};
+    d.X = f.X;
+    d.A = f.A;
+    d.B = f.B;
     d.t_part = p.t_part;
     d.t_out = f.T_save;
-    d.B = f.B;
     d.Y = f.Y;
     d.part = p.gemv_part;
-    d.counters = p.counters;
     d.d_out = q->d_out;
     d.d_in = q->d_in;
     d.r = f.r;
     d.t_scale = f.alpha / (float)f.r;
-    d.t_splits = kRankSmallSplits;
     d.ksplit = gs.ksplit;
     d.ss_per_split = gs.ss_per;
     d.tiles = gs.tiles;
     d.wg_begin = gwgs;
+    d.fin_begin = fwgs;
     gwgs += gs.tiles * gs.ksplit;
+    fwgs += (int)cdiv(q->d_out, 64);
   }
-  for (int i = 0; i < count; ++i) {
-    if (ga.d[i].ksplit > 1) {
-      ra.d[i].zero = ga.d[i].counters;
-      ra.d[i].zero_count = ga.d[i].tiles;
-    }
-  }
-  int s = hip_status(launch_rank_small(ra, st));
-  if (!s) s = hip_status(launch_gemv(ga, gwgs, st));
-  return s;
+  return hip_status(launch_gemv(ga, gwgs, fwgs, st));
 }
 
 }  // namespace

@@ -5,28 +5,38 @@
 // the quantization state, unpacks, restores the scales, looks up the NF4
 // levels, converts to BF16 and multiplies, without writing a BF16 copy of W.
 //
-// Mapping.  A workgroup of four wavefronts owns 64 output rows (16 per
-// wavefront) and a K range.  K advances in 256-wide super-steps: lane
-// (n = l%16, g = l/16) owns the whole 64-weight block g of row n, so it
-// restores that block's scale once and builds its 16-entry BF16 table once
-// (nf4_table), then feeds eight v_mfma_f32_16x16x32_bf16 with eight weights
-// each.  The MFMA pairs A lane (m, g) with B lane (n, g), so lane group g of
-// the X operand reads the same 64 columns, already permuted within each
-// eight (Xp) to match the table lookup's output order.  M is padded to 16
-// rows with zeros.
+// Mapping.  A workgroup of four wavefronts owns kGemvRows output rows and a
+// K range; wavefront w holds kSets = kGemvRows / 64 sets of 16 rows (rows
+// 16 (kSets w + t) + l%16 of the tile).  K advances in 256-wide super-steps:
+// lane (n = l%16, g = l/16) owns the whole 64-weight block g of its row in
+// each set, so it restores that block's scale once and builds its 16-entry
+// BF16 table once (nf4_table), then feeds eight v_mfma_f32_16x16x32_bf16 with
+// eight weights each.  The MFMA pairs A lane (m, g) with B lane (n, g), so
+// lane group g of the X operand reads the same 64 columns.  The workgroup
+// stages its K slice of X in LDS once, permuted within each eight to match
+// the table lookup's output order, and every wavefront reads its X fragments
+// there once per step for all of its sets.  M is padded to 16 rows with a
+// zero row.  Each workgroup writes the FP32 partial sums of its K split; the
+// workgroups of the first row tiles also form the split's share of the LoRA
+// down-projection X A^T from the staged X.  A second, small kernel adds the
+// splits in order, applies the LoRA term and rounds Y, so that no workgroup
+// waits on another and no device-wide fence (an L2 write-back and
+// invalidate on this chip) is needed.
 #include "qlora_device.h"
 #include "qlora_kernels.h"
 
+#include <algorithm>
+
 namespace qlora {
 
-// Global data of one 256-wide super-step for one lane, held in registers
-// between its loads and its MFMAs.
+constexpr int kSets = kGemvRows / 64;   // 16-row sets per wavefront
+
+// Codes and scales of one 256-wide super-step for one lane, held in
+// registers between their loads and the MFMAs.
 struct StepData {
-  u32x4 c0, c1;   // 32 bytes of codes: the lane's block
-  u32x4 x[8];     // X operand for the eight MFMAs
-  uint32_t sc;    // FP8 scale code
-  float s2;       // second-level scale (0 for a block past d_in)
-  float mu;       // scale mean (0 for a block past d_in)
+  u32x4 c[kSets][2];     // 32 bytes of codes per set: the lane's block
+  uint32_t sc[kSets];    // FP8 scale codes
+  float s2[kSets];       // second-level scales as loaded
 };
 
 // Buffer descriptor of a workgroup-uniform range, in scalar registers.
@@ -40,44 +50,81 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, in
 }
 
 struct GemvLane {
-  __amdgpu_buffer_rsrc_t codes, scodes, s2, x;
-  uint32_t vc, vs, vx;   // lane byte offsets (step 0)
-  int64_t blk0;          // first-level block index of the lane's row, step 0
-  int64_t nblk;
-  int g;
+  __amdgpu_buffer_rsrc_t codes, scodes, s2;   // codes, scodes based at the tile's first row
+  uint32_t vc[kSets], vs[kSets];              // lane byte offsets (step 0)
+  int64_t blk0[kSets];                        // first-level block of the lane, step 0
 };
 
-// Super-step ss (lane block kb = 4 ss + g).  Rows past d_out and X rows past
-// M read as zero (descriptor bounds); a block past d_in gets s2 = 0, so its
-// restored scale, table and products are zero whatever codes it reads.
-__device__ __forceinline__ void load_step(const GemvLane& L, int64_t ss, float mean, StepData& s) {
-  const uint32_t so_c = (uint32_t)(ss * 128), so_x = (uint32_t)(ss * 512);
-  s.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.codes, L.vc, so_c, 0));
-  s.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.codes, L.vc + 16, so_c, 0));
-  s.sc = __builtin_amdgcn_raw_buffer_load_b8(L.scodes, L.vs, (uint32_t)(ss * 4), 0);
-  const int64_t kb = ss * 4 + L.g;
-  const uint32_t grp = (uint32_t)((L.blk0 + ss * 4) >> 8);
-  const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(L.s2, grp * 4, 0, 0));
-  s.s2 = kb < L.nblk ? s2 : 0.0f;
-  s.mu = kb < L.nblk ? mean : 0.0f;
+// Super-step ss.  Rows past d_out read as zero (descriptor bounds).  Blocks
+// past d_in read whatever lies there; compute_step gives them scale zero.
+__device__ __forceinline__ void load_step(const GemvLane& L, int64_t ss, StepData& s) {
+  const uint32_t so_c = (uint32_t)(ss * 128), so_s = (uint32_t)(ss * 4);
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    s.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.x, L.vx + 16 * j, so_x, 0));
+  for (int t = 0; t < kSets; ++t) {
+    s.c[t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.codes, L.vc[t], so_c, 0));
+    s.c[t][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(L.codes, L.vc[t] + 16, so_c, 0));
+    s.sc[t] = __builtin_amdgcn_raw_buffer_load_b8(L.scodes, L.vs[t], so_s, 0);
+    const uint32_t grp = (uint32_t)((L.blk0[t] + ss * 4) >> 8);
+    s.s2[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(L.s2, grp * 4, 0, 0));
+  }
 }
 
-__device__ __forceinline__ f32x4 compute_step(const StepData& s, f32x4 acc) {
-  // a masked block has s2 = 0 and mean 0: restored scale, table and
-  // products are zero
-  const Nf4Table t = nf4_table(restored_scale(s.sc, s.s2, s.mu));
-  const uint32_t cw[8] = {s.c0.x, s.c0.y, s.c0.z, s.c0.w, s.c1.x, s.c1.y, s.c1.z, s.c1.w};
+// The 8 kSets MFMAs of a step.  X fragment j (columns 64 g + 8 j of the
+// step, permuted within each eight) comes from the lane's staged row; the
+// weights of set t come from its block's table.  A block past d_in (ok
+// false) gets scale 0, so its table and products are zero whatever codes it
+// read.
+__device__ __forceinline__ void compute_step(const StepData& s, bool ok, float mean,
+                                             const uint8_t* xrow, f32x4 (&acc)[kSets]) {
+  if constexpr (kSets == 1) {
+    // one set: X fragments read as they are used, four at a time
+    const Nf4Table tab = nf4_table(restored_scale(s.sc[0], ok ? s.s2[0] : 0.0f, ok ? mean : 0.0f));
+    const uint32_t cw[8] = {s.c[0][0].x, s.c[0][0].y, s.c[0][0].z, s.c[0][0].w,
+                            s.c[0][1].x, s.c[0][1].y, s.c[0][1].z, s.c[0][1].w};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc = mfma16(s.x[j], nf4_dequant8_perm(cw[j], t), acc);
-  return acc;
+    for (int h = 0; h < 2; ++h) {
+      u32x4 xf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const u32x4*>(xrow + 64 * h + 16 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[0] = mfma16(xf[j], nf4_dequant8_perm(cw[4 * h + j], tab), acc[0]);
+    }
+  } else {
+    u32x4 xf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xf[j] = *reinterpret_cast<const u32x4*>(xrow + 16 * j);
+#pragma unroll
+    for (int t = 0; t < kSets; ++t) {
+      const Nf4Table tab = nf4_table(restored_scale(s.sc[t], ok ? s.s2[t] : 0.0f, ok ? mean : 0.0f));
+      const uint32_t cw[8] = {s.c[t][0].x, s.c[t][0].y, s.c[t][0].z, s.c[t][0].w,
+                              s.c[t][1].x, s.c[t][1].y, s.c[t][1].z, s.c[t][1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[t] = mfma16(xf[j], nf4_dequant8_perm(cw[j], tab), acc[t]);
+    }
+  }
 }
 
-constexpr int kGemvDepth = 3;   // super-steps in flight per lane
+// Four 16-byte pieces of row `arow` of A (element offset) at columns
+// col + 8 j; columns past din read as zero.
+__device__ __forceinline__ void load_a_half(__amdgpu_buffer_rsrc_t ra, uint32_t arow, uint32_t col,
+                                            uint32_t din, u32x4 (&av)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t cj = col + 8 * j;
+    const uint32_t off = cj < din ? (arow + cj) * 2 : 0x80000000u;
+    av[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+  }
+}
 
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+#ifndef QLORA_GEMV_DEPTH
+#define QLORA_GEMV_DEPTH 4
+#endif
+constexpr int kGemvDepth = QLORA_GEMV_DEPTH;   // super-steps in flight per lane
+constexpr int kStageBatch = 4;  // 16-byte X chunks per thread per staging round
+
+__global__ __launch_bounds__(256)
+void k_gemv(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   const int wg = blockIdx.x;
   int di = 0;
   while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
@@ -89,7 +136,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int M = a.M;
-  const int64_t n = (int64_t)tile * 64 + 16 * w + r16;  // B-operand row and output column
+  const int64_t row0 = (int64_t)tile * kGemvRows;        // first row of the tile
   const int64_t nblk = d.d_in / kBlock;
   const int64_t nss = (nblk + 3) / 4;
   const int64_t ss0 = (int64_t)split * d.ss_per_split;
@@ -97,118 +144,230 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   if (ss1 > nss) ss1 = nss;
   const float mean = d.mean[0];
 
+  // X rows of the split staged in LDS, permuted within each eight, at a
+  // padded row stride; row M is zero and serves the rows past M, and columns
+  // past d_in are zero (d_in is a multiple of 64, so chunks of eight never
+  // straddle it).  Loads go out kStageBatch at a time; a chunk outside the
+  // data gets an offset past the descriptor and reads zero.  Staged before
+  // the weight loads start, so that every pass into the main loop finds the
+  // same loads in flight.
+  const int64_t kl = (int64_t)d.ss_per_split * 256;
+  const int64_t ld = kl * 2 + 16;                       // staged row, bytes
+  {
+    const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(d.X, (int64_t)M * d.d_in * 2);
+    // 32-bit index math: (M + 1) * per_row is below 2^16 (the LDS limit)
+    const uint32_t per_row = (uint32_t)(kl / 8);        // 16-byte chunks
+    const uint32_t nchunk = (uint32_t)(M + 1) * per_row;
+    const uint32_t col0 = (uint32_t)(ss0 * 256), din = (uint32_t)d.d_in;
+    for (uint32_t base = 0; base < nchunk; base += 256 * kStageBatch) {
+      u32x4 v[kStageBatch];
+      uint32_t dst[kStageBatch];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const uint32_t i = base + 256 * u + threadIdx.x;
+        const uint32_t row = i / per_row, c = i - row * per_row, col = col0 + 8 * c;
+        const bool in = row < (uint32_t)M && col < din;
+        const uint32_t off = in ? (row * din + col) * 2 : 0x80000000u;
+        v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        dst[u] = i < nchunk ? row * (uint32_t)ld + 16 * c : 0xFFFFFFFFu;
+      }
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u)
+        if (dst[u] != 0xFFFFFFFFu) *reinterpret_cast<u32x4*>(xs + dst[u]) = perm8_bf16(v[u]);
+    }
+  }
+  __syncthreads();
+
   GemvLane L;
-  L.codes = gemv_rsrc(d.codes, d.d_out * (d.d_in / 2));
-  L.scodes = gemv_rsrc(d.scodes, d.d_out * nblk);
+  L.codes = gemv_rsrc(d.codes + row0 * (d.d_in / 2), (d.d_out - row0) * (d.d_in / 2));
+  L.scodes = gemv_rsrc(d.scodes + row0 * nblk, (d.d_out - row0) * nblk);
   L.s2 = gemv_rsrc(d.scale2, ((d.d_out * nblk + kGroup - 1) / kGroup) * 4);
-  L.x = gemv_rsrc(d.Xp, (int64_t)M * d.d_in * 2);
-  L.vc = (uint32_t)(n * (d.d_in / 2) + 32 * g);
-  L.vs = (uint32_t)(n * nblk + g);
-  L.vx = (uint32_t)((int64_t)r16 * d.d_in * 2 + 128 * g);
-  L.blk0 = n * nblk + g;
-  L.nblk = nblk;
-  L.g = g;
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) {
+    const int64_t rl = 16 * (kSets * w + t) + r16;           // row within the tile
+    L.vc[t] = (uint32_t)(rl * (d.d_in / 2) + 32 * g);
+    L.vs[t] = (uint32_t)(rl * nblk + g);
+    L.blk0[t] = (row0 + rl) * nblk + g;
+  }
 
   // Ring of kGemvDepth steps: the loads of step ss + D - 1 are issued before
-  // the MFMAs of step ss.  Prologue and steady loop load unconditionally
-  // (steps past ss1 read in bounds or zero and are never used), which keeps
-  // the compiler's wait counts exact; the last steps run in a guarded tail.
+  // the MFMAs of step ss.  The prologue and the steady loop load
+  // unconditionally (steps past ss1 read in bounds or zero and are never
+  // used), which keeps the compiler's wait counts exact; the last steps run
+  // in a guarded tail.
   constexpr int D = kGemvDepth;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int nsteps = (int)(ss1 - ss0);
-  {
-    StepData st[D];
+  StepData st[D];
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i) load_step(L, ss0 + i, mean, st[i]);
+  for (int i = 0; i < D - 1; ++i) {
+    load_step(L, ss0 + i, st[i]);
+    __builtin_amdgcn_sched_barrier(0);   // issue order = use order
+  }
+
+  const uint8_t* xrow = xs + (r16 < M ? r16 : M) * ld + 128 * g;   // step 0 of this lane
+  const int64_t kb0 = ss0 * 4 + g;                                  // lane block, step 0
+
+  f32x4 acc[kSets];
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
     int i = 0;
     for (; i + 2 * D - 1 <= nsteps; i += D) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
-        load_step(L, ss0 + i + j + D - 1, mean, st[(j + D - 1) % D]);
-        acc = compute_step(st[j], acc);
+        load_step(L, ss0 + i + j + D - 1, st[(j + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);   // loads issued ahead of the step's math
+        compute_step(st[j], kb0 + 4 * (i + j) < nblk, mean, xrow + 512 * (i + j), acc);
       }
     }
     for (; i < nsteps; i += D) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         if (i + j < nsteps) {
-          if (i + j + D - 1 < nsteps) load_step(L, ss0 + i + j + D - 1, mean, st[(j + D - 1) % D]);
-          acc = compute_step(st[j], acc);
+          if (i + j + D - 1 < nsteps) load_step(L, ss0 + i + j + D - 1, st[(j + D - 1) % D]);
+          compute_step(st[j], kb0 + 4 * (i + j) < nblk, mean, xrow + 512 * (i + j), acc);
         }
       }
     }
   }
 
-  // ---- split-K: partials, then the last workgroup of this tile reduces ----
-  if (d.ksplit > 1) {
+  // ---- partial sums of the split: part[split][m][n] ----
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) {
+    const int64_t n = row0 + 16 * (kSets * w + t) + r16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * g + v;
-      if (m < M && n < d.d_out) d.part[((int64_t)split * 16 + m) * d.d_out + n] = acc[v];
+      if (m < M && n < d.d_out) d.part[((int64_t)split * 16 + m) * d.d_out + n] = acc[t][v];
     }
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t prev = atomicAdd(&d.counters[tile], 1u);
-      s_last = (prev == (uint32_t)(d.ksplit - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g + v;
-      float tot = 0.0f;
-      if (m < M && n < d.d_out) {
-        tot = __hip_atomic_load(&d.part[(int64_t)m * d.d_out + n], __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-        for (int s = 1; s < d.ksplit; ++s)
-          tot = __fadd_rn(tot, __hip_atomic_load(&d.part[((int64_t)s * 16 + m) * d.d_out + n],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      }
-      acc[v] = tot;
-    }
-    if (threadIdx.x == 0) d.counters[tile] = 0u;
   }
 
-  // ---- LoRA term: acc += [T_hi | T_lo] [B | B]^T, two MFMAs per 32 ranks ----
+  // ---- LoRA down-projection over the split's K slice:
+  // t_part[split][m][i] = sum_k X[m][k] A[i][k] for the 16-rank blocks
+  // b = tile, tile + tiles, ...  Wavefront w takes the steps w, w + 4, ...
+  // (loads of its next step in flight while it multiplies), and the four
+  // wavefront sums are added in order 0..3 through LDS.  A is read as the
+  // MFMA B operand, permuted within each eight like the staged X; columns
+  // past d_in and rows past r read as zero.
+  {
+    const int nrb = (int)((d.r + 15) / 16);
+    const __amdgpu_buffer_rsrc_t ra = gemv_rsrc(d.A, d.r * d.d_in * 2);
+    const uint32_t din = (uint32_t)d.d_in;
+    float* red = reinterpret_cast<float*>(xs + (M + 1) * ld);   // [4][16][16] after the staged X
+    for (int b = tile; b < nrb; b += d.tiles) {
+      const uint32_t arow = (uint32_t)(16 * b + r16) * din;
+      // half steps q = 0, 1, ... of this wavefront: step w + 4 (q / 2),
+      // fragments 4 (q % 2) .. + 3; the next half step's loads are in flight
+      // while the current one multiplies
+      f32x4 ta = {0.f, 0.f, 0.f, 0.f};
+      u32x4 h0[4], h1[4];
+      const int nq = w < nsteps ? 2 * ((nsteps - 1 - w) / 4 + 1) : 0;
+      const uint32_t colw = (uint32_t)((ss0 + w) * 256 + 64 * g);
+      if (nq > 0) load_a_half(ra, arow, colw, din, h0);
+      for (int q = 0; q < nq; q += 2) {
+        const int sl = w + 4 * (q >> 1);
+        load_a_half(ra, arow, colw + 1024 * (q >> 1) + 32, din, h1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ta = mfma16(*reinterpret_cast<const u32x4*>(xrow + 512 * sl + 16 * j), perm8_bf16(h0[j]), ta);
+        if (q + 2 < nq) load_a_half(ra, arow, colw + 1024 * ((q >> 1) + 1), din, h0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ta = mfma16(*reinterpret_cast<const u32x4*>(xrow + 512 * sl + 64 + 16 * j),
+                      perm8_bf16(h1[j]), ta);
+      }
+      // accumulator lane (r16, g): rows m = 4 g + v, rank 16 b + r16
+      __syncthreads();   // red free (a previous block's readers are done)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * g + v) * 16 + r16] = ta[v];
+      __syncthreads();
+      if (w == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * g + v, i = 16 * b + r16;
+          float sum = red[(4 * g + v) * 16 + r16];
+#pragma unroll
+          for (int ww = 1; ww < 4; ++ww) sum = __fadd_rn(sum, red[(ww * 16 + 4 * g + v) * 16 + r16]);
+          if (m < M && i < d.r) d.t_part[((int64_t)split * M + m) * d.r + i] = sum;
+        }
+      }
+    }
+  }
+}
+
+// Finish: one workgroup per 64 output columns of a problem; wavefront w
+// takes columns 16 w .. 16 w + 15, lane (n = l%16, g = l/16) rows 4 g .. 4 g
+// + 3 as in the MFMA accumulator.
+//   T   = t_scale * sum_s t_part[s]          (s ascending; into LDS)
+//   acc = sum_s part[s]                      (s ascending)
+//   acc += [T_hi | T_lo] [B | B]^T           (two MFMAs per 32 ranks)
+//   Y   = RNE_bf16(acc);  t_out = T (optional, by the first workgroup)
+// Partials are loaded kFinBatch splits at a time, so the sums do not wait on
+// one load after another.
+constexpr int kFinBatch = 4;
+
+__global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
+  __shared__ float ts[16 * kMaxRankGemv];
+  const int wg = blockIdx.x;
+  int di = 0;
+  while (di + 1 < a.count && wg >= a.d[di + 1].fin_begin) ++di;
+  const GemvDesc& d = a.d[di];
+  const int ct = wg - d.fin_begin;                 // 64-column tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int M = a.M;
+  const int64_t n = (int64_t)ct * 64 + 16 * w + r16;
+  const int ks = d.ksplit;
+  const int64_t mr = (int64_t)M * d.r;
+
+  // T into LDS, row-major [m][r]
+  for (int64_t e0 = 0; e0 < mr; e0 += 256) {
+    const int64_t e = e0 + threadIdx.x;
+    float t = 0.0f;
+    for (int s0 = 0; s0 < ks; s0 += kFinBatch) {
+      float v[kFinBatch];
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u)
+        v[u] = (e < mr && s0 + u < ks) ? d.t_part[(int64_t)(s0 + u) * mr + e] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u)
+        if (s0 + u < ks) t = (s0 + u == 0) ? v[u] : __fadd_rn(t, v[u]);
+    }
+    if (e < mr) {
+      t = __fmul_rn(d.t_scale, t);
+      ts[e] = t;
+      if (d.t_out && ct == 0) d.t_out[e] = t;
+    }
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bool col_ok = n < d.d_out;
+  for (int s0 = 0; s0 < ks; s0 += kFinBatch) {
+    float v[kFinBatch][4];
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 4 * g + q;
+        v[u][q] = (s0 + u < ks && m < M && col_ok)
+                      ? d.part[((int64_t)(s0 + u) * 16 + m) * d.d_out + n] : 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (s0 + u < ks) acc[q] = (s0 + u == 0) ? v[u][q] : __fadd_rn(acc[q], v[u][q]);
+  }
+  __syncthreads();
+
   const bool bvec = (d.r % 8) == 0 && ((uintptr_t)d.B % 16) == 0;
-  const bool tvec = (d.r % 4) == 0 && ((uintptr_t)d.t_part % 16) == 0;
   for (int64_t k0 = 0; k0 < d.r; k0 += 32) {
     const int64_t kk = k0 + 8 * g;
-    float t[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = 0.0f;
-    if (r16 < M && kk < d.r) {
-      for (int s = 0; s < d.t_splits; ++s) {
-        const float* tp = d.t_part + ((int64_t)s * M + r16) * d.r + kk;
-        float v8[8];
-        if (tvec && kk + 8 <= d.r) {
-          const float4 a0 = reinterpret_cast<const float4*>(tp)[0];
-          const float4 a1 = reinterpret_cast<const float4*>(tp)[1];
-          v8[0] = a0.x; v8[1] = a0.y; v8[2] = a0.z; v8[3] = a0.w;
-          v8[4] = a1.x; v8[5] = a1.y; v8[6] = a1.z; v8[7] = a1.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] = (kk + e < d.r) ? tp[e] : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (s == 0) ? v8[e] : __fadd_rn(t[e], v8[e]);
-      }
-    }
-    float hi[8], lo[8], tv[8];
+    float hi[8], lo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      tv[e] = __fmul_rn(d.t_scale, t[e]);
-      split_bf16(tv[e], hi[e], lo[e]);
-    }
-    // T itself, once per problem: the first wavefront of tile 0 (of the
-    // split that reached this epilogue)
-    if (d.t_out && tile == 0 && w == 0 && r16 < M) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (kk + e < d.r) d.t_out[(int64_t)r16 * d.r + kk + e] = tv[e];
+      const float t = (r16 < M && kk + e < d.r) ? ts[r16 * d.r + kk + e] : 0.0f;
+      split_bf16(t, hi[e], lo[e]);
     }
     u32x4 ah, al;
     ah.x = pack_bf16x2(hi[0], hi[1]); ah.y = pack_bf16x2(hi[2], hi[3]);
@@ -216,7 +375,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     al.x = pack_bf16x2(lo[0], lo[1]); al.y = pack_bf16x2(lo[2], lo[3]);
     al.z = pack_bf16x2(lo[4], lo[5]); al.w = pack_bf16x2(lo[6], lo[7]);
     u32x4 bw = {0u, 0u, 0u, 0u};
-    if (n < d.d_out && kk < d.r) {
+    if (col_ok && kk < d.r) {
       const uint16_t* brow = d.B + n * d.r;
       if (bvec && kk + 8 <= d.r) {
         bw = *reinterpret_cast<const u32x4*>(brow + kk);
@@ -235,7 +394,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int m = 4 * g + v;
-    if (m < M && n < d.d_out) {
+    if (m < M && col_ok) {
       f32x2 p = {acc[v], 0.0f};
       d.Y[(int64_t)m * d.d_out + n] =
           (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2)) & 0xFFFFu);
@@ -243,10 +402,22 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   }
 }
 
-hipError_t launch_gemv(const GemvArgs& a, int total_wgs, hipStream_t st) {
+hipError_t launch_gemv(const GemvArgs& a, int total_wgs, int fin_wgs, hipStream_t st) {
+  // staged X: (M + 1) rows of the largest split, padded
+  int64_t lds = 0;
+  for (int i = 0; i < a.count; ++i)
+    lds = std::max<int64_t>(lds, gemv_lds_bytes(a.M, a.d[i].ss_per_split));
+  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kGemvMaxLds);
+  if (attr != hipSuccess) return attr;
+  if (lds > kGemvMaxLds) return hipErrorInvalidValue;
   weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_gemv, dim3(total_wgs), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_gemv, dim3(total_wgs), dim3(256), (unsigned)lds, st, a);
   weight_kernel_end(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gemv_finish, dim3(fin_wgs), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

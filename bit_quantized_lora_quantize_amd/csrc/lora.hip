@@ -250,13 +250,6 @@ __global__ __launch_bounds__(256) void k_rank_small(RankSmallArgs a) {
 
   if (local == 0 && d.zero)
     for (int64_t i = threadIdx.x; i < d.zero_count; i += 256) d.zero[i] = 0u;
-  if (d.xp) {
-    // eight BF16 values per item, permuted as the table lookup orders them;
-    // shared by the problem's workgroups
-    const int64_t n8 = M * K / 8;
-    for (int64_t i = (int64_t)local * 256 + threadIdx.x; i < n8; i += (int64_t)nblk * S * 256)
-      reinterpret_cast<u32x4*>(d.xp)[i] = perm8_bf16(reinterpret_cast<const u32x4*>(d.P)[i]);
-  }
 
   // K part of the wavefront: part 4 sq + w of 16, whole load groups
   const int64_t chunk = ((K + 4 * S - 1) / (4 * S) + 32 * kSmallGroup - 1) / (32 * kSmallGroup) *

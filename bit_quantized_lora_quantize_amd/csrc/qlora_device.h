@@ -28,15 +28,11 @@ constexpr int kGroup = 256;  // first-level scales per FP32 second-level scale [
 // ---------------------------------------------------------------- FP8 E4M3FN
 // OCP 8-bit float: sign, 4 exponent bits (bias 7), 3 mantissa bits, no
 // infinities; exponent 0 holds subnormals m * 2^-9; largest finite 448.
-// Branch-free: magnitude = (m + 8 [e > 0]) * 2^(max(e, 1) - 10), exact (a
-// small integer scaled by a power of two), covering subnormals and normals
-// alike.
+// gfx950's v_cvt_f32_fp8 decodes this format exactly (every value is a small
+// integer times a power of two); it reads the low byte of `code`.  The
+// encoder below never produces the NaN codes 0x7F / 0xFF.
 __device__ __forceinline__ float fp8e4m3_to_f32(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  const uint32_t mm = m | (e != 0u ? 8u : 0u);
-  const int ex = (int)(e != 0u ? e : 1u) - 10;
-  const float mag = __builtin_amdgcn_ldexpf((float)mm, ex);
-  return __uint_as_float(__float_as_uint(mag) | ((code & 0x80u) << 24));
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
 // Round-to-nearest-even encode with saturation at 448; sign bit = sign of y.

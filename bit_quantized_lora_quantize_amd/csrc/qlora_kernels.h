@@ -44,17 +44,15 @@ constexpr int kMaxGroup = 8;
 // consumer (weight-streaming epilogue or launch_rank_finish) in that order,
 // so every path gets the same bits.  One 4-wavefront workgroup per
 // 16-column block, problem and quarter; wavefronts take consecutive parts
-// of the quarter and add their sums in wavefront order.  The workgroups of
-// a problem also write xp (P permuted within each group of eight, the order
-// of nf4_dequant8_perm; [M][K], optional) and clear zero[0 .. zero_count)
-// (split-K counters of the following weight-streaming launch).
+// of the quarter and add their sums in wavefront order.  The first
+// workgroup of a problem also clears zero[0 .. zero_count) (split-K counters
+// of the following weight-streaming launch).
 constexpr int kRankSmallSplits = 4;
 struct RankSmallDesc {
   const uint16_t* P;
   const uint16_t* Q;
   int64_t K, ldq, N;
   float* part;
-  uint16_t* xp;
   uint32_t* zero;
   int64_t zero_count;
   int wg_begin;     // first workgroup of this problem (set by the launcher)
@@ -129,37 +127,54 @@ hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t 
                               bool transposed, float* out, hipStream_t st);
 
 // ------------------------------------------------- small-M forward (GEMV)
-// Y[m][n] = RNE_bf16( sum_k Xp-order X[m][k] Wh[n][k] + sum_i T[m][i] B[n][i] )
-// for m < M <= 16.  T = t_scale * sum_s t_part[s][m][i] (s ascending).
-// The weight is streamed once; ksplit > 1 splits K across workgroups and the
-// last workgroup of a row tile (counted in counters[tile]) reduces the FP32
-// partials in split order and applies the LoRA term.
+// Y[m][n] = RNE_bf16( sum_k X[m][k] Wh[n][k] + sum_i T[m][i] B[n][i] ),
+// T = t_scale * X A^T, for m < M <= 16.  The weight-streaming kernel: each
+// workgroup owns kGemvRows rows and a K split of ss_per_split 256-wide
+// super-steps, stages its K slice of X in LDS and writes FP32 partials
+// part[split][m][n]; the workgroups of the first row tiles of each split
+// also write t_part[split][m][i] (X A^T over the split).  The finish kernel (one
+// workgroup per 64 columns) adds the splits in ascending order, applies the
+// LoRA term and writes Y (and T to t_out when given).
+#ifndef QLORA_GEMV_ROWS
+#define QLORA_GEMV_ROWS 64
+#endif
+constexpr int kGemvRows = QLORA_GEMV_ROWS;   // a multiple of 64
 struct GemvDesc {
   const uint8_t* codes;
   const uint8_t* scodes;
   const float* scale2;
   const float* mean;
-  const uint16_t* Xp;
-  const float* t_part;
-  float* t_out;      // optional: T = t_scale * sum_s t_part[s], FP32 [M][r]
-  const uint16_t* B;
-  uint16_t* Y;
-  float* part;
-  uint32_t* counters;
+  const uint16_t* X;      // [M][d_in], 16-byte aligned
+  const uint16_t* A;      // [r][d_in], 16-byte aligned
+  const uint16_t* B;      // [d_out][r]
+  float* t_part;          // [ksplit][M][r]
+  float* t_out;           // optional: T FP32 [M][r]
+  uint16_t* Y;            // [M][d_out]
+  float* part;            // [ksplit][16][d_out]
   int64_t d_out, d_in, r;
   float t_scale;
-  int t_splits;
   int ksplit;
-  int ss_per_split;  // 256-wide K super-steps per split
-  int tiles;         // 64-row tiles
-  int wg_begin;
+  int ss_per_split;       // 256-wide K super-steps per split
+  int tiles;              // kGemvRows-row tiles
+  int wg_begin;           // first workgroup of the streaming launch
+  int fin_begin;          // first workgroup of the finish launch
 };
 struct GemvArgs {
   GemvDesc d[kMaxGroup];
   int count;
   int M;
 };
-hipError_t launch_gemv(const GemvArgs& a, int total_wgs, hipStream_t st);
+// LDS of one workgroup (the staged X) and its limit: a quarter of the CU's
+// 160 KB for four resident workgroups
+#ifndef QLORA_GEMV_MAX_LDS
+#define QLORA_GEMV_MAX_LDS 40960
+#endif
+constexpr int64_t kGemvMaxLds = QLORA_GEMV_MAX_LDS;
+inline int64_t gemv_lds_bytes(int64_t M, int64_t ss_per_split) {
+  return (M + 1) * (ss_per_split * 512 + 16) + 4 * 16 * 16 * 4;   // X rows + X A^T reduction
+}
+constexpr int kMaxRankGemv = 256;   // largest r of the weight-streaming forward
+hipError_t launch_gemv(const GemvArgs& a, int total_wgs, int fin_wgs, hipStream_t st);
 
 // ------------------------------------------------- large-M fused GEMM
 // Forward: Y = RNE_bf16(X Wh^T + [T_hi T_lo] [B B]^T), dequant tiles in LDS.
