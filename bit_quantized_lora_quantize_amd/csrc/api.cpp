@@ -114,7 +114,7 @@ int64_t gemv_units(int64_t d_out, int64_t d_in) {
 GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t M, int64_t total_units) {
   const int64_t tiles = cdiv(d_out, kGemvRows);
   const int64_t nss = cdiv(d_in / kBlock, 4);
-  const int64_t ss_max = ((kGemvMaxLds - gemv_lds_bytes(M, 0)) / (M + 1)) / 512;
+  const int64_t ss_max = (kGemvMaxLds / (M + 1) - 16) / 512;
   int64_t per = std::max<int64_t>(1, cdiv(total_units, kGemvTargetWgs));
   per = std::max(per, cdiv(nss, kGemvMaxSplit));
   per = std::min({per, nss, ss_max});
@@ -125,7 +125,6 @@ GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t M, int64_t total_units
 struct FwdPlan {
   bool small;
   float* t_buf;       // [M][r] when T_save is NULL
-  float* t_part;      // [4 ksplit][M][r] (small M)
   uint16_t* t_hl;     // [M][2 rp] BF16 hi | lo of T (large M)
   int64_t rp;         // r rounded up to 32
   float* gemv_part;   // [ksplit][16][d_out] (small M)
@@ -143,7 +142,6 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   if (p.small) {
     // a problem alone gets the most splits it can get in any group
     p.gs = gemv_split(d_out, d_in, M, gemv_units(d_out, d_in));
-    p.t_part = c.take<float>((int64_t)p.gs.ksplit * M * r);
     p.gemv_part = c.take<float>((int64_t)p.gs.ksplit * 16 * d_out);
   }
   p.bytes = c.off + 256;
@@ -264,6 +262,51 @@ struct FwdItemArgs {
   size_t ws_bytes;
 };
 
+// Descriptors of the small-M forward for a group: T into T_save (or the
+// workspace), K splits balanced over the group.  Returns the group's units.
+int64_t small_gemv_args(const FwdItemArgs* items, int count, int64_t M, GemvArgs* ga, int* gwgs,
+                        int* fwgs) {
+  int64_t total_units = 0;
+  for (int i = 0; i < count; ++i)
+    total_units += gemv_units(items[i].q->d_out, items[i].q->d_in);
+  ga->count = count;
+  ga->M = (int)M;
+  int twgs = 0;
+  *gwgs = *fwgs = 0;
+  for (int i = 0; i < count; ++i) {
+    const FwdItemArgs& f = items[i];
+    const qlora_nf4_t* q = f.q;
+    const FwdPlan p = plan_fwd(q->d_out, q->d_in, M, f.r, f.ws);
+    const GemvSplit gs = gemv_split(q->d_out, q->d_in, M, total_units);
+    GemvDesc& d = ga->d[i];
+    d.codes = q->codes;
+    d.scodes = q->scale_codes;
+    d.scale2 = q->scale2;
+    d.mean = q->scale_mean;
+    d.X = f.X;
+    d.A = f.A;
+    d.B = f.B;
+    d.t_buf = f.T_save ? f.T_save : p.t_buf;
+    d.Y = f.Y;
+    d.part = p.gemv_part;
+    d.d_out = q->d_out;
+    d.d_in = q->d_in;
+    d.r = f.r;
+    d.t_scale = f.alpha / (float)f.r;
+    d.ksplit = gs.ksplit;
+    d.ss_per_split = gs.ss_per;
+    d.tiles = gs.tiles;
+    d.tb_begin = twgs;
+    d.wg_begin = *gwgs;
+    d.fin_begin = *fwgs;
+    twgs += (int)cdiv(f.r, 16);
+    *gwgs += gs.tiles * gs.ksplit;
+    *fwgs += (int)cdiv(q->d_out, 64);
+  }
+  ga->t_wgs = twgs;
+  return total_units;
+}
+
 int check_fwd_item(const FwdItemArgs& f, int64_t M) {
   int s = check_nf4(f.q);
   if (s) return s;
@@ -308,47 +351,11 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
     return QLORA_OK;
   }
 
-  // Small M: one weight-streaming launch for the whole group (which also
-  // forms the X A^T partials) and one finish launch.
-  FwdPlan plans[kMaxGroup];
-  int64_t total_units = 0;
-  for (int i = 0; i < count; ++i) {
-    plans[i] = plan_fwd(items[i].q->d_out, items[i].q->d_in, M, items[i].r, items[i].ws);
-    total_units += gemv_units(items[i].q->d_out, items[i].q->d_in);
-  }
+  // Small M: one weight-streaming launch for the whole group (whose first
+  // workgroups form T = s X A^T) and one finish launch.
   GemvArgs ga{};
-  ga.count = count;
-  ga.M = (int)M;
   int gwgs = 0, fwgs = 0;
-  for (int i = 0; i < count; ++i) {
-    const FwdItemArgs& f = items[i];
-    const qlora_nf4_t* q = f.q;
-    const FwdPlan& p = plans[i];
-    const GemvSplit gs = gemv_split(q->d_out, q->d_in, M, total_units);
-    GemvDesc& d = ga.d[i];
-    d.codes = q->codes;
-    d.scodes = q->scale_codes;
-    d.scale2 = q->scale2;
-    d.mean = q->scale_mean;
-    d.X = f.X;
-    d.A = f.A;
-    d.B = f.B;
-    d.t_part = p.t_part;
-    d.t_out = f.T_save;
-    d.Y = f.Y;
-    d.part = p.gemv_part;
-    d.d_out = q->d_out;
-    d.d_in = q->d_in;
-    d.r = f.r;
-    d.t_scale = f.alpha / (float)f.r;
-    d.ksplit = gs.ksplit;
-    d.ss_per_split = gs.ss_per;
-    d.tiles = gs.tiles;
-    d.wg_begin = gwgs;
-    d.fin_begin = fwgs;
-    gwgs += gs.tiles * gs.ksplit;
-    fwgs += (int)cdiv(q->d_out, 64);
-  }
+  small_gemv_args(items, count, M, &ga, &gwgs, &fwgs);
   return hip_status(launch_gemv(ga, gwgs, fwgs, st));
 }
 
@@ -465,16 +472,33 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   }
   const float sc = lora_alpha / (float)r;
   // T = s X A^T (unless saved by the forward), and its transposed hi/lo copy
+  // (the same kernels and summation order as the forward, so a recomputed T
+  // equals a saved one bit for bit)
   const float* T = T_saved;
-  if (!T) {
-    // the same kernels and summation order as the forward, so a recomputed T
-    // equals a saved one bit for bit
+  if (!T && M > kSmallM) {
     RankRowsArgs ra{X, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
     s = rank_product(ra, p.r_part, st);
     if (s) return s;
     T = p.t_buf;
   } else {
-    s = hip_status(launch_rank_finish(T_saved, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
+    if (!T) {
+      GemvArgs ga{};
+      ga.count = 1;
+      ga.M = (int)M;
+      ga.t_wgs = (int)cdiv(r, 16);
+      GemvDesc& d = ga.d[0];
+      d.X = X;
+      d.A = A;
+      d.t_buf = p.t_buf;
+      d.d_in = d_in;
+      d.d_out = d_out;
+      d.r = r;
+      d.t_scale = sc;
+      s = hip_status(launch_lora_down(ga, st));
+      if (s) return s;
+      T = p.t_buf;
+    }
+    s = hip_status(launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
                                       nullptr, 0, st));
     if (s) return s;
   }

@@ -16,9 +16,9 @@
 // stages its K slice of X in LDS once, permuted within each eight to match
 // the table lookup's output order, and every wavefront reads its X fragments
 // there once per step for all of its sets.  M is padded to 16 rows with a
-// zero row.  Each workgroup writes the FP32 partial sums of its K split; the
-// workgroups of the first row tiles also form the split's share of the LoRA
-// down-projection X A^T from the staged X.  A second, small kernel adds the
+// zero row.  Each workgroup writes the FP32 partial sums of its K split.
+// The first workgroups of the launch form T = t_scale X A^T instead, one
+// 16-rank block each over the whole of K.  A second, small kernel adds the
 // splits in order, applies the LoRA term and rounds Y, so that no workgroup
 // waits on another and no device-wide fence (an L2 write-back and
 // invalidate on this chip) is needed.
@@ -116,8 +116,90 @@ __device__ __forceinline__ void load_a_half(__amdgpu_buffer_rsrc_t ra, uint32_t 
   }
 }
 
+// ---- LoRA down-projection, one 16-rank block per workgroup:
+// T[m][i] = t_scale * sum_k X[m][k] A[i][k] for i in 16 b .. 16 b + 15.
+// Wavefront w takes the w-th quarter of the 256-wide super-steps; lane
+// (l%16, g = l/16) reads X row l%16 and A row 16 b + l%16 at columns 64 g +
+// 8 j of each super-step (both in natural order, so the MFMA sees the same
+// column set in both operands), with the next half step's loads in flight
+// while the current one multiplies.  The four wavefront sums are added in
+// order 0..3 through LDS.  Rows past M or r and columns past d_in read as
+// zero.  The forward (weight-streaming launch) and the backward's recompute
+// (k_lora_down) run this same code, so both get the same T.
+__device__ __forceinline__ void load_half(__amdgpu_buffer_rsrc_t r, uint32_t row, uint32_t col,
+                                          uint32_t din, u32x4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t cj = col + 8 * j;
+    const uint32_t off = cj < din ? (row + cj) * 2 : 0x80000000u;
+    v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void lora_down_block(const GemvDesc& d, int M, int b, float* red) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t din = (uint32_t)d.d_in;
+  const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(d.X, (int64_t)M * d.d_in * 2);   // rows past M: zero
+  const __amdgpu_buffer_rsrc_t ra = gemv_rsrc(d.A, d.r * d.d_in * 2);          // rows past r: zero
+  const uint32_t xrow = (uint32_t)r16 * din, arow = (uint32_t)(16 * b + r16) * din;
+  const int nss = (int)((d.d_in / kBlock + 3) / 4);
+  const int qn = (nss + 3) / 4;
+  const int q0 = w * qn < nss ? w * qn : nss;
+  const int q1 = q0 + qn < nss ? q0 + qn : nss;
+  const int nh = 2 * (q1 - q0);                       // half steps of this wavefront
+  const uint32_t col0 = (uint32_t)(q0 * 256 + 64 * g);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  u32x4 x0[4], a0[4], x1[4], a1[4];
+  if (nh > 0) {
+    load_half(rx, xrow, col0, din, x0);
+    load_half(ra, arow, col0, din, a0);
+  }
+  for (int h = 0; h < nh; h += 2) {
+    const uint32_t col = col0 + 128 * h;              // super-step q0 + h / 2
+    load_half(rx, xrow, col + 32, din, x1);
+    load_half(ra, arow, col + 32, din, a1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma16(x0[j], a0[j], acc);
+    if (h + 2 < nh) {
+      load_half(rx, xrow, col + 256, din, x0);
+      load_half(ra, arow, col + 256, din, a0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma16(x1[j], a1[j], acc);
+  }
+  // accumulator lane (r16, g): rows m = 4 g + v, rank 16 b + r16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * g + v) * 16 + r16] = acc[v];
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g + v, i = 16 * b + r16;
+      float sum = red[(4 * g + v) * 16 + r16];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) sum = __fadd_rn(sum, red[(ww * 16 + 4 * g + v) * 16 + r16]);
+      if (m < M && i < d.r) d.t_buf[(int64_t)m * d.r + i] = __fmul_rn(d.t_scale, sum);
+    }
+  }
+}
+
+// Workgroup -> (problem, 16-rank block) of the LoRA down-projection part of a
+// launch (the first t_wgs workgroups).
+__device__ __forceinline__ void lora_down_dispatch(const GemvArgs& a, int wg, float* red) {
+  int di = 0;
+  while (di + 1 < a.count && wg >= a.d[di + 1].tb_begin) ++di;
+  lora_down_block(a.d[di], a.M, wg - a.d[di].tb_begin, red);
+}
+
+__global__ __launch_bounds__(256) void k_lora_down(GemvArgs a) {
+  __shared__ float red[4 * 16 * 16];
+  lora_down_dispatch(a, blockIdx.x, red);
+}
+
 #ifndef QLORA_GEMV_DEPTH
-#define QLORA_GEMV_DEPTH 4
+#define QLORA_GEMV_DEPTH 3
 #endif
 constexpr int kGemvDepth = QLORA_GEMV_DEPTH;   // super-steps in flight per lane
 constexpr int kStageBatch = 4;  // 16-byte X chunks per thread per staging round
@@ -125,7 +207,11 @@ constexpr int kStageBatch = 4;  // 16-byte X chunks per thread per staging round
 __global__ __launch_bounds__(256)
 void k_gemv(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
-  const int wg = blockIdx.x;
+  if ((int)blockIdx.x < a.t_wgs) {       // LoRA down-projection blocks first
+    lora_down_dispatch(a, blockIdx.x, reinterpret_cast<float*>(xs));
+    return;
+  }
+  const int wg = blockIdx.x - a.t_wgs;
   int di = 0;
   while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
   const GemvDesc& d = a.d[di];
@@ -242,72 +328,19 @@ void k_gemv(GemvArgs a) {
     }
   }
 
-  // ---- LoRA down-projection over the split's K slice:
-  // t_part[split][m][i] = sum_k X[m][k] A[i][k] for the 16-rank blocks
-  // b = tile, tile + tiles, ...  Wavefront w takes the steps w, w + 4, ...
-  // (loads of its next step in flight while it multiplies), and the four
-  // wavefront sums are added in order 0..3 through LDS.  A is read as the
-  // MFMA B operand, permuted within each eight like the staged X; columns
-  // past d_in and rows past r read as zero.
-  {
-    const int nrb = (int)((d.r + 15) / 16);
-    const __amdgpu_buffer_rsrc_t ra = gemv_rsrc(d.A, d.r * d.d_in * 2);
-    const uint32_t din = (uint32_t)d.d_in;
-    float* red = reinterpret_cast<float*>(xs + (M + 1) * ld);   // [4][16][16] after the staged X
-    for (int b = tile; b < nrb; b += d.tiles) {
-      const uint32_t arow = (uint32_t)(16 * b + r16) * din;
-      // half steps q = 0, 1, ... of this wavefront: step w + 4 (q / 2),
-      // fragments 4 (q % 2) .. + 3; the next half step's loads are in flight
-      // while the current one multiplies
-      f32x4 ta = {0.f, 0.f, 0.f, 0.f};
-      u32x4 h0[4], h1[4];
-      const int nq = w < nsteps ? 2 * ((nsteps - 1 - w) / 4 + 1) : 0;
-      const uint32_t colw = (uint32_t)((ss0 + w) * 256 + 64 * g);
-      if (nq > 0) load_a_half(ra, arow, colw, din, h0);
-      for (int q = 0; q < nq; q += 2) {
-        const int sl = w + 4 * (q >> 1);
-        load_a_half(ra, arow, colw + 1024 * (q >> 1) + 32, din, h1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ta = mfma16(*reinterpret_cast<const u32x4*>(xrow + 512 * sl + 16 * j), perm8_bf16(h0[j]), ta);
-        if (q + 2 < nq) load_a_half(ra, arow, colw + 1024 * ((q >> 1) + 1), din, h0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ta = mfma16(*reinterpret_cast<const u32x4*>(xrow + 512 * sl + 64 + 16 * j),
-                      perm8_bf16(h1[j]), ta);
-      }
-      // accumulator lane (r16, g): rows m = 4 g + v, rank 16 b + r16
-      __syncthreads();   // red free (a previous block's readers are done)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * g + v) * 16 + r16] = ta[v];
-      __syncthreads();
-      if (w == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = 4 * g + v, i = 16 * b + r16;
-          float sum = red[(4 * g + v) * 16 + r16];
-#pragma unroll
-          for (int ww = 1; ww < 4; ++ww) sum = __fadd_rn(sum, red[(ww * 16 + 4 * g + v) * 16 + r16]);
-          if (m < M && i < d.r) d.t_part[((int64_t)split * M + m) * d.r + i] = sum;
-        }
-      }
-    }
-  }
 }
 
 // Finish: one workgroup per 64 output columns of a problem; wavefront w
 // takes columns 16 w .. 16 w + 15, lane (n = l%16, g = l/16) rows 4 g .. 4 g
 // + 3 as in the MFMA accumulator.
-//   T   = t_scale * sum_s t_part[s]          (s ascending; into LDS)
 //   acc = sum_s part[s]                      (s ascending)
 //   acc += [T_hi | T_lo] [B | B]^T           (two MFMAs per 32 ranks)
-//   Y   = RNE_bf16(acc);  t_out = T (optional, by the first workgroup)
-// Partials are loaded kFinBatch splits at a time, so the sums do not wait on
+//   Y   = RNE_bf16(acc)
+// Partials are loaded kFinBatch splits at a time, so the sum does not wait on
 // one load after another.
 constexpr int kFinBatch = 4;
 
 __global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
-  __shared__ float ts[16 * kMaxRankGemv];
   const int wg = blockIdx.x;
   int di = 0;
   while (di + 1 < a.count && wg >= a.d[di + 1].fin_begin) ++di;
@@ -318,27 +351,6 @@ __global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
   const int M = a.M;
   const int64_t n = (int64_t)ct * 64 + 16 * w + r16;
   const int ks = d.ksplit;
-  const int64_t mr = (int64_t)M * d.r;
-
-  // T into LDS, row-major [m][r]
-  for (int64_t e0 = 0; e0 < mr; e0 += 256) {
-    const int64_t e = e0 + threadIdx.x;
-    float t = 0.0f;
-    for (int s0 = 0; s0 < ks; s0 += kFinBatch) {
-      float v[kFinBatch];
-#pragma unroll
-      for (int u = 0; u < kFinBatch; ++u)
-        v[u] = (e < mr && s0 + u < ks) ? d.t_part[(int64_t)(s0 + u) * mr + e] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < kFinBatch; ++u)
-        if (s0 + u < ks) t = (s0 + u == 0) ? v[u] : __fadd_rn(t, v[u]);
-    }
-    if (e < mr) {
-      t = __fmul_rn(d.t_scale, t);
-      ts[e] = t;
-      if (d.t_out && ct == 0) d.t_out[e] = t;
-    }
-  }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const bool col_ok = n < d.d_out;
@@ -358,17 +370,25 @@ __global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
       for (int q = 0; q < 4; ++q)
         if (s0 + u < ks) acc[q] = (s0 + u == 0) ? v[u][q] : __fadd_rn(acc[q], v[u][q]);
   }
-  __syncthreads();
 
   const bool bvec = (d.r % 8) == 0 && ((uintptr_t)d.B % 16) == 0;
+  const bool tvec = (d.r % 4) == 0;
   for (int64_t k0 = 0; k0 < d.r; k0 += 32) {
     const int64_t kk = k0 + 8 * g;
+    float t8[8];
+    const float* tp = d.t_buf + (int64_t)r16 * d.r + kk;
+    if (r16 < M && tvec && kk + 8 <= d.r) {
+      const float4 t0 = reinterpret_cast<const float4*>(tp)[0];
+      const float4 t1 = reinterpret_cast<const float4*>(tp)[1];
+      t8[0] = t0.x; t8[1] = t0.y; t8[2] = t0.z; t8[3] = t0.w;
+      t8[4] = t1.x; t8[5] = t1.y; t8[6] = t1.z; t8[7] = t1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t8[e] = (r16 < M && kk + e < d.r) ? tp[e] : 0.0f;
+    }
     float hi[8], lo[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = (r16 < M && kk + e < d.r) ? ts[r16 * d.r + kk + e] : 0.0f;
-      split_bf16(t, hi[e], lo[e]);
-    }
+    for (int e = 0; e < 8; ++e) split_bf16(t8[e], hi[e], lo[e]);
     u32x4 ah, al;
     ah.x = pack_bf16x2(hi[0], hi[1]); ah.y = pack_bf16x2(hi[2], hi[3]);
     ah.z = pack_bf16x2(hi[4], hi[5]); ah.w = pack_bf16x2(hi[6], hi[7]);
@@ -402,6 +422,11 @@ __global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
   }
 }
 
+hipError_t launch_lora_down(const GemvArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_lora_down, dim3(a.t_wgs), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(const GemvArgs& a, int total_wgs, int fin_wgs, hipStream_t st) {
   // staged X: (M + 1) rows of the largest split, padded
   int64_t lds = 0;
@@ -413,7 +438,7 @@ hipError_t launch_gemv(const GemvArgs& a, int total_wgs, int fin_wgs, hipStream_
   if (attr != hipSuccess) return attr;
   if (lds > kGemvMaxLds) return hipErrorInvalidValue;
   weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_gemv, dim3(total_wgs), dim3(256), (unsigned)lds, st, a);
+  hipLaunchKernelGGL(k_gemv, dim3(a.t_wgs + total_wgs), dim3(256), (unsigned)lds, st, a);
   weight_kernel_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace qlora {
 
 // Optional event pair around the next weight-kernel launch (timing aid).
@@ -128,13 +130,14 @@ hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t 
 
 // ------------------------------------------------- small-M forward (GEMV)
 // Y[m][n] = RNE_bf16( sum_k X[m][k] Wh[n][k] + sum_i T[m][i] B[n][i] ),
-// T = t_scale * X A^T, for m < M <= 16.  The weight-streaming kernel: each
-// workgroup owns kGemvRows rows and a K split of ss_per_split 256-wide
-// super-steps, stages its K slice of X in LDS and writes FP32 partials
-// part[split][m][n]; the workgroups of the first row tiles of each split
-// also write t_part[split][m][i] (X A^T over the split).  The finish kernel (one
-// workgroup per 64 columns) adds the splits in ascending order, applies the
-// LoRA term and writes Y (and T to t_out when given).
+// T = t_scale * X A^T, for m < M <= 16.  The weight-streaming launch: its
+// first t_wgs workgroups each form one 16-rank block of T over the whole of
+// K into t_buf; the others each own kGemvRows rows and a K split of
+// ss_per_split 256-wide super-steps, stage their K slice of X in LDS and
+// write FP32 partials part[split][m][n].  The finish launch (one workgroup
+// per 64 columns) adds the splits in ascending order, applies the LoRA term
+// and writes Y.  launch_lora_down runs the T blocks alone (same code, same
+// bits).
 #ifndef QLORA_GEMV_ROWS
 #define QLORA_GEMV_ROWS 64
 #endif
@@ -147,8 +150,7 @@ struct GemvDesc {
   const uint16_t* X;      // [M][d_in], 16-byte aligned
   const uint16_t* A;      // [r][d_in], 16-byte aligned
   const uint16_t* B;      // [d_out][r]
-  float* t_part;          // [ksplit][M][r]
-  float* t_out;           // optional: T FP32 [M][r]
+  float* t_buf;           // T FP32 [M][r], 16-byte aligned
   uint16_t* Y;            // [M][d_out]
   float* part;            // [ksplit][16][d_out]
   int64_t d_out, d_in, r;
@@ -156,13 +158,15 @@ struct GemvDesc {
   int ksplit;
   int ss_per_split;       // 256-wide K super-steps per split
   int tiles;              // kGemvRows-row tiles
-  int wg_begin;           // first workgroup of the streaming launch
+  int tb_begin;           // first T-block workgroup (blocks cdiv(r, 16))
+  int wg_begin;           // first streaming workgroup, counted after the T blocks
   int fin_begin;          // first workgroup of the finish launch
 };
 struct GemvArgs {
   GemvDesc d[kMaxGroup];
   int count;
   int M;
+  int t_wgs;              // T-block workgroups of all problems
 };
 // LDS of one workgroup (the staged X) and its limit: a quarter of the CU's
 // 160 KB for four resident workgroups
@@ -171,10 +175,10 @@ struct GemvArgs {
 #endif
 constexpr int64_t kGemvMaxLds = QLORA_GEMV_MAX_LDS;
 inline int64_t gemv_lds_bytes(int64_t M, int64_t ss_per_split) {
-  return (M + 1) * (ss_per_split * 512 + 16) + 4 * 16 * 16 * 4;   // X rows + X A^T reduction
+  return std::max<int64_t>((M + 1) * (ss_per_split * 512 + 16), 4 * 16 * 16 * 4);  // X rows | T sums
 }
-constexpr int kMaxRankGemv = 256;   // largest r of the weight-streaming forward
 hipError_t launch_gemv(const GemvArgs& a, int total_wgs, int fin_wgs, hipStream_t st);
+hipError_t launch_lora_down(const GemvArgs& a, hipStream_t st);
 
 // ------------------------------------------------- large-M fused GEMM
 // Forward: Y = RNE_bf16(X Wh^T + [T_hi T_lo] [B B]^T), dequant tiles in LDS.
