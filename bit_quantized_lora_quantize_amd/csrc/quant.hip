@@ -148,27 +148,29 @@ __global__ __launch_bounds__(256) void k_scale_dq(const float* __restrict__ absm
 }
 
 // ---------------------------------------------------------------------------
-// Double dequantization to BF16.  One lane per 64-weight block: restored
-// scale fp8(code) * s2 + mean, 16-entry BF16 table RNE(level_i * scale),
-// then eight byte-permute lookups of eight weights each; 128 B stored.
+// Double dequantization to BF16: restored scale fp8(code) * s2 + mean,
+// 16-entry BF16 table RNE(level_i * scale), byte-permute lookups of eight
+// weights per lane.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scale_codes,
                                                       const float* __restrict__ scale2,
                                                       const float* __restrict__ mean_p,
                                                       int64_t n1, uint16_t* __restrict__ out) {
+  // One code dword (eight weights, 16 output bytes) per thread: eight
+  // consecutive threads share a block (each builds its table), and a
+  // wavefront reads 256 contiguous code bytes and writes 1 KB of contiguous
+  // output, so every store fills whole cache lines.
   const float mean = mean_p[0];
+  const int64_t nunits = n1 * 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n1; b += stride) {
-    const u32x4* cp = reinterpret_cast<const u32x4*>(codes + b * 32);
-    u32x4 c0 = __builtin_nontemporal_load(cp);
-    u32x4 c1 = __builtin_nontemporal_load(cp + 1);
-    const float sc = restored_scale(scale_codes[b], scale2[b >> 8], mean);
-    const Nf4Table t = nf4_table(sc);
-    u32x4* op = reinterpret_cast<u32x4*>(out + b * 64);
-    uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(nf4_dequant8(cw[j], t), op + j);
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += stride) {
+    const int64_t b = u >> 3;
+    const uint32_t c = __builtin_nontemporal_load(cw + u);
+    const Nf4Table t = nf4_table(restored_scale(scale_codes[b], scale2[b >> 8], mean));
+    __builtin_nontemporal_store(nf4_dequant8(c, t), ov + u);
   }
 }
 
@@ -212,7 +214,7 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, cons
                           const float* mean, int64_t n, uint16_t* out, hipStream_t st) {
   const int64_t n1 = n / kBlock;
   weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(n1, 256, 8192)), dim3(256), 0, st, codes,
+  hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(n1 * 8, 256, 8192)), dim3(256), 0, st, codes,
                      scale_codes, scale2, mean, n1, out);
   weight_kernel_end(st);
   return hipGetLastError();
