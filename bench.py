@@ -46,6 +46,24 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 R, ALPHA = 64, 16.0
 
+# HBM bytes per fused-GEMM launch (mean over the 14 launches of one training
+# step), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a
+# 1024 MB device copy (factors 2.0 and 1.0).  Valid only for the kernel
+# sources with this SHA-1 (gemm.hip, qlora_device.h, qlora_kernels.h);
+# reported as null otherwise.
+GEMM_TRAFFIC_BYTES = 268.81e6
+GEMM_TRAFFIC_SHA1 = "8faa01196ddc704d5312d9c537886989720e7f49"
+
+
+def gemm_traffic():
+    import hashlib
+    csrc = os.path.join(_ROOT, "bit_quantized_lora_quantize_amd", "csrc")
+    h = hashlib.sha1()
+    for f in ("gemm.hip", "qlora_device.h", "qlora_kernels.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return GEMM_TRAFFIC_BYTES if h.hexdigest() == GEMM_TRAFFIC_SHA1 else None
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -360,6 +378,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip", default="", help="comma list of: decode,quant,stack65b,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run one device-to-device copy of this many MB (a plain copy "
+                         "kernel of known size, for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -370,6 +391,15 @@ def main():
     torch.cuda.set_device(dev)
     q.lib()
     log(f"device {torch.cuda.get_device_name(dev)}; steps={args.steps} warmup={args.warmup}")
+    if args.copy_mb > 0:
+        n = args.copy_mb * 1000 * 1000 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_mb} MB read + {args.copy_mb} MB written")
+        del src, dst
 
     train = bench_train7b(dev, args.steps, args.warmup)
     extra = {}
@@ -402,7 +432,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(g["tflops"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(g["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic(),
                      "kernel": "k_gemm (fused dequant-GEMM, fwd and bwd)",
                      "avg_launch_us": round(g["avg_launch_ms"] * 1e3, 2),
                      "fwd_avg_us": round(g["fwd_avg_us"], 2), "bwd_avg_us": round(g["bwd_avg_us"], 2),

@@ -174,9 +174,12 @@ int qlora_linear_bwd(const qlora_nf4_t *q, const uint16_t *X,
  * one pass: the same operation as qlora_linear_fwd for every item (each with
  * its own weight, LoRA factors, outputs and workspace sized by
  * qlora_workspace_bytes(QLORA_OP_FWD, ...)).  For M <= 16 all items run in
- * one rank-r launch and one weight-streaming launch, so the projections of a
- * decoder layer stream their packed weights back to back; for larger M the
- * items run one after another.  Items must not share outputs or workspace.
+ * one weight-streaming launch (which also forms every T) and one finish
+ * launch, so the projections of a decoder layer stream their packed weights
+ * back to back; the K split of each weight is chosen over the whole group,
+ * so an item's Y may differ from a single call's by FP32 summation order
+ * (T does not).  For larger M the items run one after another.  Items must
+ * not share outputs or workspace.
  * Returns the first failing item's status (nothing enqueued on argument
  * errors).
  */
