@@ -128,6 +128,7 @@ struct FwdPlan {
   uint16_t* t_hl;     // [M][2 rp] BF16 hi | lo of T (large M)
   int64_t rp;         // r rounded up to 32
   float* gemv_part;   // [ksplit][16][d_out] (small M)
+  float* r_part;      // [rank_k_splits(M, d_in)][M][r] (large M)
   GemvSplit gs;
   size_t bytes;
 };
@@ -138,7 +139,11 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   Carver c(ws);
   p.t_buf = c.take<float>(M * r);
   p.rp = round_up(r, 32);
-  if (!p.small) p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
+  if (!p.small) {
+    int64_t kper;
+    p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
+    p.r_part = c.take<float>((int64_t)rank_k_splits(M, d_in, &kper) * M * r);
+  }
   if (p.small) {
     // a problem alone gets the most splits it can get in any group
     p.gs = gemv_split(d_out, d_in, M, gemv_units(d_out, d_in));
@@ -150,7 +155,8 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
 
 struct BwdPlan {
   float* t_buf;       // [M][r]
-  float* r_part;      // [kRankSmallSplits][M][r] (small M)
+  float* r_part;      // rank-r partials: [kRankSmallSplits][M][r] (small M), else
+                      // [max K splits of T and U][M][r]
   int64_t ldbt;       // row stride of B^T
   uint16_t* bt;       // [r][ldbt]
   int64_t rp;         // r rounded up to 32
@@ -183,7 +189,13 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.bt = c.take<uint16_t>(r * p.ldbt);
   p.rp = round_up(r, 32);
   p.u_hl = c.take<uint16_t>(M * 2 * p.rp);
-  if (M <= kSmallM) p.r_part = c.take<float>(kRankSmallSplits * M * r);
+  if (M <= kSmallM) {
+    p.r_part = c.take<float>(kRankSmallSplits * M * r);
+  } else {
+    int64_t kper;
+    const int64_t ks = std::max(rank_k_splits(M, d_in, &kper), rank_k_splits(M, d_out, &kper));
+    p.r_part = c.take<float>(ks * M * r);
+  }
   p.ldp = round_up(std::max<int64_t>(M, 1), 16);
   p.ut_hi = c.take<uint16_t>(r * p.ldp);
   p.ut_lo = c.take<uint16_t>(r * p.ldp);
@@ -234,11 +246,12 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_
 // ------------------------------------------------------------- rank-r products
 // v = scale * P Q^T (P [M][K], Q [N][ldq]) with the outputs of RankRowsArgs;
 // small M and large M use different kernels, each deterministic, and the
-// forward and the backward call the same one for the same M.
-// Small M goes through kRankSmallSplits partials (part, FP32 [splits][M][N])
-// and the finish kernel, the order the weight-streaming epilogue also uses.
+// forward and the backward call the same one for the same M.  Both go
+// through FP32 partials (part, [splits][M][N]) and the finish kernel, which
+// adds the splits in order: kRankSmallSplits K quarters for small M, the K
+// splits of rank_k_splits for large M.
 int rank_product(const RankRowsArgs& ra, float* part, hipStream_t st) {
-  if (ra.M > kSmallM) return hip_status(launch_rank_rows(ra, st));
+  if (ra.M > kSmallM) return hip_status(launch_rank_split(ra, part, st));
   RankSmallArgs a{};
   a.count = 1;
   a.M = ra.M;
@@ -341,7 +354,7 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       float* T = f.T_save ? f.T_save : p.t_buf;
       RankRowsArgs ra{f.X,    f.A,     M,       f.r,     q->d_in, q->d_in, f.alpha / (float)f.r,
                       T,      p.t_hl,  p.rp,    nullptr, nullptr, 0};
-      int s = rank_product(ra, nullptr, st);
+      int s = rank_product(ra, p.r_part, st);
       if (s) return s;
       GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, p.t_hl, f.B, f.Y,
                  M,        q->d_out,      q->d_in,  f.r};
@@ -498,8 +511,11 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
       if (s) return s;
       T = p.t_buf;
     }
-    s = hip_status(launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
-                                      nullptr, 0, st));
+    s = hip_status(M > kSmallM
+                       ? launch_rank_finish_rows(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo,
+                                                 p.ldp, nullptr, 0, st)
+                       : launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
+                                            nullptr, 0, st));
     if (s) return s;
   }
   // U = s dY B, through B^T so the contraction over d_out is contiguous

@@ -212,6 +212,112 @@ __global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRo
 }
 
 // ---------------------------------------------------------------------------
+// Large M, split over K: part[s][m][n] = sum over k in split s of P[m][k]
+// Q[n][k] (FP32), P [M][K], Q [N][ldq], N <= 16 NB.  Workgroup = 64 rows
+// (16 per wavefront) x one K split.  K advances in chunks of KC columns: the
+// Q chunk is staged in LDS once per workgroup (double-buffered, loaded into
+// registers one chunk ahead) and read by all four wavefronts, so Q's L2
+// traffic is (M / 64) times its size; each wavefront's P rows come straight
+// from memory, one chunk ahead.  Rows past M or N and columns past the
+// split read as zero.  k_rank_finish adds the splits in order.  K and ldq
+// are multiples of 8 and P, Q 16-byte aligned (checked by the launcher).
+template <int NB>
+constexpr int rank_kc() { return NB <= 4 ? 128 : (NB <= 8 ? 64 : 32); }
+
+template <int NB>
+__global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __restrict__ part,
+                                                   int64_t kper, int ks) {
+  constexpr int KC = rank_kc<NB>();
+  constexpr int NR = 16 * NB;                 // Q rows staged (zero past N)
+  constexpr int LQ = KC + 8;                  // LDS row, BF16 elements (16 B pad: conflict-free reads)
+  constexpr int PIECES = NR * KC / 8 / 256;   // 16-byte Q pieces per thread per chunk
+  constexpr int NS = KC / 32;                 // MFMA K slices per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][NR * LQ];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int rb = blockIdx.x / ks, sp = blockIdx.x % ks;
+  const int64_t m0 = (int64_t)rb * 64;
+  const int64_t K = a.K;
+  const int64_t k_begin = (int64_t)sp * kper;
+  const int64_t k_end = k_begin + kper < K ? k_begin + kper : K;
+  const int nchunks = (int)((k_end - k_begin + KC - 1) / KC);
+
+  const __amdgpu_buffer_rsrc_t rp = rank_rsrc(a.P + m0 * K, (a.M - m0) * K * 2);   // rows past M: zero
+  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(a.Q, a.N * a.ldq * 2);               // rows past N: zero
+  const uint32_t prow = (uint32_t)((16 * w + r16) * K);                             // element offset
+  // Q pieces of this thread: row pr[u], 8 columns from pc[u] within the chunk
+  uint32_t qrow[PIECES], qcol[PIECES];
+#pragma unroll
+  for (int u = 0; u < PIECES; ++u) {
+    const int piece = threadIdx.x + 256 * u;
+    qrow[u] = (uint32_t)(piece / (KC / 8));
+    qcol[u] = (uint32_t)(8 * (piece % (KC / 8)));
+  }
+  const uint32_t kend = (uint32_t)k_end;
+
+  auto load_chunk = [&](int c, u32x4 (&qv)[PIECES], u32x4 (&xv)[NS]) {
+    const uint32_t kc0 = (uint32_t)(k_begin + (int64_t)c * KC);
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const uint32_t col = kc0 + qcol[u];
+      const uint32_t off = col < kend ? (qrow[u] * (uint32_t)a.ldq + col) * 2 : 0x80000000u;
+      qv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint32_t col = kc0 + 32 * j + 8 * g;
+      const uint32_t off = col < kend ? (prow + col) * 2 : 0x80000000u;
+      xv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+    }
+  };
+  auto store_q = [&](int buf, const u32x4 (&qv)[PIECES]) {
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u)
+      *reinterpret_cast<u32x4*>(&qs[buf][qrow[u] * LQ + qcol[u]]) = qv[u];
+  };
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, const u32x4 (&xv)[NS]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = mfma16(xv[j], *reinterpret_cast<const u32x4*>(&qs[buf][(16 * nb + r16) * LQ + 32 * j + 8 * g]),
+                         acc[nb]);
+  };
+
+  u32x4 q0[PIECES], x0[NS], q1[PIECES], x1[NS];
+  if (nchunks > 0) {
+    load_chunk(0, q0, x0);
+    store_q(0, q0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    if (c + 1 < nchunks) load_chunk(c + 1, q1, x1);
+    compute(0, x0);
+    if (c + 1 >= nchunks) break;
+    store_q(1, q1);
+    __syncthreads();
+    if (c + 2 < nchunks) load_chunk(c + 2, q0, x0);
+    compute(1, x1);
+    if (c + 2 < nchunks) store_q(0, q0);
+    __syncthreads();
+  }
+
+  // accumulator lane (r16, g): rows 4 g + v of the wavefront's 16, column 16 nb + r16
+  float* out = part + (int64_t)sp * a.M * a.N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = m0 + 16 * w + 4 * g + v;
+      const int64_t n = 16 * nb + r16;
+      if (m < a.M && n < a.N) out[m * a.N + n] = acc[nb][v];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Small M (<= 16 tokens): partial sums part[s][m][n] of P Q^T over quarters
 // of K, for a group of problems.  Workgroup = one 16-column block, problem
 // and quarter; its four wavefronts take consecutive parts of the quarter
@@ -369,6 +475,73 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
         row[j] = 0;
         row[d.rp + j] = 0;
       }
+    }
+  }
+}
+
+// Finish for many rows: one workgroup per 16 rows x 64 columns.  Same
+// arithmetic and outputs as k_rank_finish (v = scale * sum of the splits in
+// ascending order; out, hl with zeros for n in [N, rp), ht / lt with zeros
+// for m in [M, ldt)), laid out for coalescing: partials and the row-major
+// outputs are read and written along n, and the transposed copies go
+// through an LDS tile so that they are written along m.  Each thread keeps
+// four elements' partial loads in flight per split.
+__global__ __launch_bounds__(256) void k_rank_finish_rows(FinishDesc d) {
+  constexpr int EU = 4;
+  __shared__ uint16_t th[64][18], tl[64][18];   // [n][m], padded
+  const int64_t m0 = (int64_t)blockIdx.x * 16, nc = (int64_t)blockIdx.y * 64;
+  const int t = threadIdx.x, col = t & 63, rq = t >> 6;
+  const int64_t count = d.M * d.N;
+  const int64_t ldt = d.ldt > 0 ? d.ldt : d.M;
+  const int64_t n = nc + col;
+  float acc[EU];
+  int64_t e[EU];
+  bool ok[EU];
+#pragma unroll
+  for (int u = 0; u < EU; ++u) {
+    const int64_t m = m0 + rq + 4 * u;
+    ok[u] = m < d.M && n < d.N;
+    e[u] = m * d.N + n;
+    acc[u] = 0.0f;
+  }
+  for (int s0 = 0; s0 < d.splits; s0 += 4) {
+    float v[4][EU];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < EU; ++u)
+        v[j][u] = (ok[u] && s0 + j < d.splits) ? d.part[(int64_t)(s0 + j) * count + e[u]] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < EU; ++u)
+        if (s0 + j < d.splits) acc[u] = (s0 + j == 0) ? v[j][u] : __fadd_rn(acc[u], v[j][u]);
+  }
+#pragma unroll
+  for (int u = 0; u < EU; ++u) {
+    const int r = rq + 4 * u;
+    const int64_t m = m0 + r;
+    const float val = ok[u] ? __fmul_rn(d.scale, acc[u]) : 0.0f;
+    float hi, lo;
+    split_bf16(val, hi, lo);
+    const uint16_t hb = (uint16_t)(__float_as_uint(hi) >> 16);
+    const uint16_t lb = (uint16_t)(pack_bf16x2(lo, 0.0f) & 0xFFFFu);
+    if (ok[u] && d.out) d.out[e[u]] = val;
+    if (d.hl && m < d.M && n < d.rp) {
+      d.hl[m * 2 * d.rp + n] = hb;
+      d.hl[m * 2 * d.rp + d.rp + n] = lb;
+    }
+    th[col][r] = hb;
+    tl[col][r] = lb;
+  }
+  if (!d.ht) return;
+  __syncthreads();
+  for (int idx = t; idx < 64 * 16; idx += 256) {
+    const int cn = idx >> 4, r = idx & 15;
+    const int64_t nn = nc + cn, m = m0 + r;
+    if (nn < d.N && m < ldt) {
+      d.ht[nn * ldt + m] = th[cn][r];
+      d.lt[nn * ldt + m] = tl[cn][r];
     }
   }
 }
@@ -567,6 +740,43 @@ static void launch_rank_rows_t(const RankRowsArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((rows + R - 1) / R);
   if (grid == 0) return;
   hipLaunchKernelGGL(k_rank_rows<NB>, dim3(grid), dim3(64 * rank_rows_waves<NB>()), 0, st, a);
+}
+
+template <int NB>
+static hipError_t launch_rank_part_t(const RankRowsArgs& a, float* part, int64_t kper, int ks,
+                                     hipStream_t st) {
+  const unsigned grid = (unsigned)(((a.M + 63) / 64) * ks);
+  hipLaunchKernelGGL(k_rank_part<NB>, dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st) {
+  // 16-byte row pieces need K and ldq multiples of 8 and aligned bases;
+  // other layouts take the one-pass kernel, which loads elements
+  if (a.K % 8 != 0 || a.ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15) ||
+      (reinterpret_cast<uintptr_t>(a.Q) & 15))
+    return launch_rank_rows(a, st);
+  int64_t kper = 0;
+  const int ks = rank_k_splits(a.M, a.K, &kper);
+  hipError_t e;
+  if (a.N <= 32) e = launch_rank_part_t<2>(a, part, kper, ks, st);
+  else if (a.N <= 64) e = launch_rank_part_t<4>(a, part, kper, ks, st);
+  else if (a.N <= 128) e = launch_rank_part_t<8>(a, part, kper, ks, st);
+  else e = launch_rank_part_t<16>(a, part, kper, ks, st);
+  if (e != hipSuccess) return e;
+  return launch_rank_finish_rows(part, ks, a.M, a.N, a.scale, a.out, a.ht, a.lt, a.ldt, a.hl, a.rp,
+                                 st);
+}
+
+hipError_t launch_rank_finish_rows(const float* part, int splits, int64_t M, int64_t N,
+                                   float scale, float* out, uint16_t* ht, uint16_t* lt,
+                                   int64_t ldt, uint16_t* hl, int64_t rp, hipStream_t st) {
+  const FinishDesc d{part, out, ht, lt, M, N, ht ? ldt : M, scale, splits, 0, hl, rp};
+  const int64_t rows = ht && ldt > M ? ldt : M;
+  const int64_t ncols = hl && rp > N ? rp : N;
+  hipLaunchKernelGGL(k_rank_finish_rows, dim3((unsigned)((rows + 15) / 16), (unsigned)((ncols + 63) / 64)),
+                     dim3(256), 0, st, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st) {

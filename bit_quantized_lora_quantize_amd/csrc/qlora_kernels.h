@@ -85,6 +85,22 @@ struct RankRowsArgs {
   int64_t ldt;
 };
 hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st);
+// The same product (same outputs) through K-split partials part
+// [rank_k_splits(M, K)][M][N] FP32 and k_rank_finish (splits added in order);
+// K or ldq not a multiple of 8, or unaligned P / Q, take launch_rank_rows.
+hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st);
+// K splits of launch_rank_split: about 512 workgroups of 64 rows; each split
+// a multiple of 128 columns.  *kper receives the split length.
+inline int rank_k_splits(int64_t M, int64_t K, int64_t* kper) {
+  const int64_t rb = (M + 63) / 64;
+  const int64_t maxs = (K + 127) / 128;
+  int64_t ks = (512 + rb - 1) / rb;
+  ks = ks < 1 ? 1 : (ks > maxs ? maxs : ks);
+  int64_t per = ((K + ks - 1) / ks + 127) / 128 * 128;
+  if (per < 128) per = 128;
+  *kper = per;
+  return (int)((K + per - 1) / per);
+}
 
 // Finish of split partials: v[m][n] = scale * sum_s part[s][m][n] (s
 // ascending).  out (optional) = v, FP32 [M][N]; ht/lt (optional) = the
@@ -111,6 +127,12 @@ hipError_t launch_rank_finish(const FinishArgs& a, hipStream_t st);
 hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t N, float scale,
                               float* out, uint16_t* ht, uint16_t* lt, int64_t ldt,
                               uint16_t* hl, int64_t rp, hipStream_t st);
+
+// The same finish for many rows (one workgroup per 64 rows, coalesced
+// partial reads and transposed writes through LDS); identical outputs.
+hipError_t launch_rank_finish_rows(const float* part, int splits, int64_t M, int64_t N,
+                                   float scale, float* out, uint16_t* ht, uint16_t* lt,
+                                   int64_t ldt, uint16_t* hl, int64_t rp, hipStream_t st);
 
 // Transpose of a BF16 matrix in[rows][cols] into out[cols][ldo]:
 // out[c][i] = in[i][c] for i < rows, and 0 for i in [rows, ldo).
