@@ -352,8 +352,57 @@ __global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
   const int64_t n = (int64_t)ct * 64 + 16 * w + r16;
   const int ks = d.ksplit;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const bool col_ok = n < d.d_out;
+  const bool bvec = (d.r % 8) == 0 && ((uintptr_t)d.B % 16) == 0;
+  const bool tvec = (d.r % 4) == 0;
+  // T (lane row l%16, ranks kk .. kk+7) and B (column n, same ranks) of one
+  // 32-rank chunk
+  auto load_tb = [&](int64_t k0, float (&t8)[8], u32x4& bw) {
+    const int64_t kk = k0 + 8 * g;
+    const float* tp = d.t_buf + (int64_t)r16 * d.r + kk;
+    if (r16 < M && tvec && kk + 8 <= d.r) {
+      const float4 t0 = reinterpret_cast<const float4*>(tp)[0];
+      const float4 t1 = reinterpret_cast<const float4*>(tp)[1];
+      t8[0] = t0.x; t8[1] = t0.y; t8[2] = t0.z; t8[3] = t0.w;
+      t8[4] = t1.x; t8[5] = t1.y; t8[6] = t1.z; t8[7] = t1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t8[e] = (r16 < M && kk + e < d.r) ? tp[e] : 0.0f;
+    }
+    bw = u32x4{0u, 0u, 0u, 0u};
+    if (col_ok && kk < d.r) {
+      const uint16_t* brow = d.B + n * d.r;
+      if (bvec && kk + 8 <= d.r) {
+        bw = *reinterpret_cast<const u32x4*>(brow + kk);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (kk + e < d.r) ? brow[kk + e] : 0u;
+        bw.x = h[0] | (h[1] << 16); bw.y = h[2] | (h[3] << 16);
+        bw.z = h[4] | (h[5] << 16); bw.w = h[6] | (h[7] << 16);
+      }
+    }
+  };
+  auto apply_tb = [&](const float (&t8)[8], const u32x4& bw, f32x4& acc) {
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split_bf16(t8[e], hi[e], lo[e]);
+    u32x4 ah, al;
+    ah.x = pack_bf16x2(hi[0], hi[1]); ah.y = pack_bf16x2(hi[2], hi[3]);
+    ah.z = pack_bf16x2(hi[4], hi[5]); ah.w = pack_bf16x2(hi[6], hi[7]);
+    al.x = pack_bf16x2(lo[0], lo[1]); al.y = pack_bf16x2(lo[2], lo[3]);
+    al.z = pack_bf16x2(lo[4], lo[5]); al.w = pack_bf16x2(lo[6], lo[7]);
+    acc = mfma16(ah, bw, acc);
+    acc = mfma16(al, bw, acc);
+  };
+
+  // the first two rank chunks' loads go out with the partial loads
+  float t0[8], t1[8];
+  u32x4 b0, b1;
+  load_tb(0, t0, b0);
+  if (d.r > 32) load_tb(32, t1, b1);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < ks; s0 += kFinBatch) {
     float v[kFinBatch][4];
 #pragma unroll
@@ -371,44 +420,11 @@ __global__ __launch_bounds__(256) void k_gemv_finish(GemvArgs a) {
         if (s0 + u < ks) acc[q] = (s0 + u == 0) ? v[u][q] : __fadd_rn(acc[q], v[u][q]);
   }
 
-  const bool bvec = (d.r % 8) == 0 && ((uintptr_t)d.B % 16) == 0;
-  const bool tvec = (d.r % 4) == 0;
-  for (int64_t k0 = 0; k0 < d.r; k0 += 32) {
-    const int64_t kk = k0 + 8 * g;
-    float t8[8];
-    const float* tp = d.t_buf + (int64_t)r16 * d.r + kk;
-    if (r16 < M && tvec && kk + 8 <= d.r) {
-      const float4 t0 = reinterpret_cast<const float4*>(tp)[0];
-      const float4 t1 = reinterpret_cast<const float4*>(tp)[1];
-      t8[0] = t0.x; t8[1] = t0.y; t8[2] = t0.z; t8[3] = t0.w;
-      t8[4] = t1.x; t8[5] = t1.y; t8[6] = t1.z; t8[7] = t1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) t8[e] = (r16 < M && kk + e < d.r) ? tp[e] : 0.0f;
-    }
-    float hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(t8[e], hi[e], lo[e]);
-    u32x4 ah, al;
-    ah.x = pack_bf16x2(hi[0], hi[1]); ah.y = pack_bf16x2(hi[2], hi[3]);
-    ah.z = pack_bf16x2(hi[4], hi[5]); ah.w = pack_bf16x2(hi[6], hi[7]);
-    al.x = pack_bf16x2(lo[0], lo[1]); al.y = pack_bf16x2(lo[2], lo[3]);
-    al.z = pack_bf16x2(lo[4], lo[5]); al.w = pack_bf16x2(lo[6], lo[7]);
-    u32x4 bw = {0u, 0u, 0u, 0u};
-    if (col_ok && kk < d.r) {
-      const uint16_t* brow = d.B + n * d.r;
-      if (bvec && kk + 8 <= d.r) {
-        bw = *reinterpret_cast<const u32x4*>(brow + kk);
-      } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (kk + e < d.r) ? brow[kk + e] : 0u;
-        bw.x = h[0] | (h[1] << 16); bw.y = h[2] | (h[3] << 16);
-        bw.z = h[4] | (h[5] << 16); bw.w = h[6] | (h[7] << 16);
-      }
-    }
-    acc = mfma16(ah, bw, acc);
-    acc = mfma16(al, bw, acc);
+  apply_tb(t0, b0, acc);
+  if (d.r > 32) apply_tb(t1, b1, acc);
+  for (int64_t k0 = 64; k0 < d.r; k0 += 32) {
+    load_tb(k0, t0, b0);
+    apply_tb(t0, b0, acc);
   }
 
 #pragma unroll
