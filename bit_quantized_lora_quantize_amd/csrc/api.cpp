@@ -36,7 +36,10 @@ namespace {
 
 constexpr int64_t kMaxRank = 256;
 constexpr int64_t kSmallM = 16;      // M <= 16 streams the weight (GEMV path)
-constexpr int64_t kMaxLinearDim = int64_t(1) << 22;  // keeps device offsets 32-bit
+// Layer sizes and token counts per call: every device byte offset the kernels
+// form within one tile, split or transposed copy then stays below 2^31.
+constexpr int64_t kMaxLinearDim = int64_t(1) << 21;
+constexpr int64_t kMaxTokens = int64_t(1) << 21;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -324,7 +327,7 @@ int check_fwd_item(const FwdItemArgs& f, int64_t M) {
   int s = check_nf4(f.q);
   if (s) return s;
   if (f.q->d_out > kMaxLinearDim || f.q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
-  if (M < 0 || M > (int64_t(1) << 31)) return QLORA_ERR_SHAPE;
+  if (M < 0 || M > kMaxTokens) return QLORA_ERR_SHAPE;
   if (f.r < 1 || f.r > kMaxRank) return QLORA_ERR_SHAPE;
   if (M == 0) return QLORA_OK;
   if (!f.X || !f.A || !f.B || !f.Y) return QLORA_ERR_NULL;
@@ -467,7 +470,7 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
                      size_t ws_bytes, void* stream) {
   int s = check_nf4(q);
   if (s) return s;
-  if (M < 0 || M > (int64_t(1) << 31) || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
+  if (M < 0 || M > kMaxTokens || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
   if (q->d_out > kMaxLinearDim || q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
   if (!dA || !dB || !ws) return QLORA_ERR_NULL;
   if (M > 0 && (!X || !dY || !A || !B)) return QLORA_ERR_NULL;

@@ -578,12 +578,15 @@ constexpr int kGramWaveBytes = kGramRows * kGramLd * 2;
 
 // Q block (rows m .. m+63 of the wavefront, columns c0 .. c0+63): lane l
 // loads row 8 i + l/8, columns 8 (l%8) .. +8, i = 0..7.
+// The descriptor is based at the block's first token, so offsets stay below
+// 64 rows of Q whatever M is; tokens past M read as zero.
 template <bool VEC>
-__device__ __forceinline__ void gram_load(__amdgpu_buffer_rsrc_t rq, int64_t m, int64_t c0,
+__device__ __forceinline__ void gram_load(const uint16_t* Q, int64_t M, int64_t m, int64_t c0,
                                           int64_t N, int lane, u32x4 (&x)[8]) {
+  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(Q + (m < M ? m : M) * N, (M - m) * N * 2);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t row = m + 8 * i + (lane >> 3), col = c0 + 8 * (lane & 7);
+    const int64_t row = 8 * i + (lane >> 3), col = c0 + 8 * (lane & 7);
     if (VEC) {
       x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rq, (uint32_t)((row * N + col) * 2), 0, 0));
@@ -604,7 +607,7 @@ __device__ __forceinline__ void gram_load(__amdgpu_buffer_rsrc_t rq, int64_t m, 
 // load the block's rank operands and the Q block two ahead into x, then 4
 // token slices x RB x 2 x (hi, lo) MFMAs.
 template <int RB, bool VEC>
-__device__ __forceinline__ void gram_block(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rh,
+__device__ __forceinline__ void gram_block(const uint16_t* Q, int64_t M, __amdgpu_buffer_rsrc_t rh,
                                            __amdgpu_buffer_rsrc_t rl, int64_t ldp, int64_t c0,
                                            int64_t N, int64_t m, int lane, uint8_t* wl,
                                            uint32_t wr, uint32_t rd, u32x4 (&x)[8],
@@ -621,7 +624,7 @@ __device__ __forceinline__ void gram_block(__amdgpu_buffer_rsrc_t rq, __amdgpu_b
       ph[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, po, 0, 0));
       pl[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, po, 0, 0));
     }
-  gram_load<VEC>(rq, m + 2 * kGramRows, c0, N, lane, x);
+  gram_load<VEC>(Q, M, m + 2 * kGramRows, c0, N, lane, x);
   __builtin_amdgcn_sched_barrier(0);   // every load of the block ahead of its MFMAs
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -666,7 +669,6 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi
   if (m_end > m_lim) m_end = m_lim;
   uint8_t* wl = glds + w * kGramWaveBytes;
 
-  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(Q, M * N * 2);       // rows past M read zero
   const __amdgpu_buffer_rsrc_t rh = rank_rsrc(Pt_hi, R * ldp * 2);  // rows past R read zero
   const __amdgpu_buffer_rsrc_t rl = rank_rsrc(Pt_lo, R * ldp * 2);
 
@@ -685,13 +687,13 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi
   // range are in bounds or read zero and are never used; issuing them
   // unconditionally keeps the compiler's wait counts exact.
   u32x4 xa[8], xb[8];
-  gram_load<VEC>(rq, m_begin, c0, N, lane, xa);
+  gram_load<VEC>(Q, M, m_begin, c0, N, lane, xa);
   __builtin_amdgcn_sched_barrier(0);   // issue order = use order
-  gram_load<VEC>(rq, m_begin + kGramRows, c0, N, lane, xb);
+  gram_load<VEC>(Q, M, m_begin + kGramRows, c0, N, lane, xb);
   __builtin_amdgcn_sched_barrier(0);
   for (int64_t m = m_begin; m < m_end; m += 2 * kGramRows) {
-    gram_block<RB, VEC>(rq, rh, rl, ldp, c0, N, m, lane, wl, wr, rd, xa, acc);
-    gram_block<RB, VEC>(rq, rh, rl, ldp, c0, N, m + kGramRows, lane, wl, wr, rd, xb, acc);
+    gram_block<RB, VEC>(Q, M, rh, rl, ldp, c0, N, m, lane, wl, wr, rd, xa, acc);
+    gram_block<RB, VEC>(Q, M, rh, rl, ldp, c0, N, m + kGramRows, lane, wl, wr, rd, xb, acc);
   }
 
   // wavefront partials added in order 0, 1, 2, 3 in one FP32 tile

@@ -135,8 +135,9 @@ int qlora_dequant_bf16(const qlora_nf4_t *q, uint16_t *W_bf16, void *stream);
  *   Y       BF16 [M, d_out] (16B)        output
  *   T_save  FP32 [M, r]     (16B) or NULL: receives T for the backward.
  * workspace (16B) >= qlora_workspace_bytes(QLORA_OP_FWD, d_out, d_in, M, r).
- * The layer sizes must satisfy d_out <= 2^22 and d_in <= 2^22 (device byte
- * offsets are 32-bit), else QLORA_ERR_SHAPE; the same holds for the backward.
+ * Sizes per call: d_out <= 2^21, d_in <= 2^21 and M <= 2^21 tokens (the
+ * kernels' device byte offsets are 32-bit within a tile or split), else
+ * QLORA_ERR_SHAPE; the same holds for the backward.
  * M <= 16 runs a weight-streaming kernel (HBM-bound); larger M runs the
  * fused dequant-GEMM on the matrix cores.  No full BF16 copy of W is made.
  */

@@ -114,6 +114,10 @@ def test_linear_argument_errors(L):
     assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, Y, P(0x1234), ws, big, None) == EALIGN
     assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, Y, None, ws, 64, None) == EWS
     assert f(ctypes.byref(w), X, 4, A, B, 8, 16.0, Y, None, None, big, None) == ENULL
+    # size limits: at most 2^21 tokens, layer sides at most 2^21
+    assert f(ctypes.byref(w), X, (1 << 21) + 1, A, B, 8, 16.0, Y, None, ws, big, None) == ESHAPE
+    wide = _nf4(64, (1 << 21) + 64)
+    assert f(ctypes.byref(wide), X, 4, A, B, 8, 16.0, Y, None, ws, big, None) == ESHAPE
     # M = 0 is an empty batch: valid, nothing to do, no GPU work
     assert f(ctypes.byref(w), None, 0, None, None, 8, 16.0, None, None, None, 0, None) == OK
     b = L.qlora_linear_bwd
@@ -123,6 +127,8 @@ def test_linear_argument_errors(L):
     assert b(ctypes.byref(w), X, P(0x50006), 4, A, B, 8, 16.0, None, None, dA, dB, ws, big,
              None) == EALIGN
     assert b(ctypes.byref(w), X, X, 4, A, B, 0, 16.0, None, None, dA, dB, ws, big, None) == ESHAPE
+    assert b(ctypes.byref(w), X, X, (1 << 21) + 1, A, B, 8, 16.0, None, None, dA, dB, ws, big,
+             None) == ESHAPE
 
 
 def test_grouped_forward_argument_errors(L):

@@ -7,7 +7,7 @@ import torch
 
 import bit_quantized_lora_quantize_amd as q
 from bit_quantized_lora_quantize_amd import inputs
-from parity_util import assert_close, assert_quant_equal, f32, oracle_quant, say
+from parity_util import assert_close, assert_quant_equal, f32, oracle_quant, rel_errors, say
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -162,3 +162,45 @@ def test_llama7b_training_shape(orc, proj):
     rng = np.random.default_rng(proj)
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 22, replace=False)]))
     _check_layer(orc, W, A, B, X, dY, rows=rows, label=f"7B {name} train")
+
+
+def test_linear_tokens_beyond_2gib(orc):
+    """Activations larger than 2 GiB, so that byte offsets over a whole
+    tensor would not fit 32 bits: M = 5 x 65536 tokens of width 4096 (2.7 GB
+    each for X and dY).  X and dY are five stacked copies of a 65536-token
+    block.  Every row of Y, T and dX is computed by per-row arithmetic that
+    does not depend on where the row sits, so each copy must reproduce the
+    block's rows bit for bit; dA and dB sum over tokens, so they must equal
+    five times the block's own within FP32 rounding.  The block itself is
+    checked against the oracle on sampled rows."""
+    d_out = d_in = 4096
+    M0, copies, r = 65536, 5, 64
+    W, A, B, X0, dY0 = _layer(d_out, d_in, M0, r, 90, device=DEV)
+    w = q.qlora_quantize_nf4(W)
+    X = X0.repeat(copies, 1).contiguous()
+    dY = dY0.repeat(copies, 1).contiguous()
+    T0 = torch.empty((M0, r), dtype=torch.float32, device=DEV)
+    Y0 = q.qlora_linear_fwd(w, X0, A, B, ALPHA, T_save=T0)
+    dX0, dA0, dB0 = q.qlora_linear_bwd(w, X0, dY0, A, B, ALPHA, T_saved=T0)
+    T = torch.empty((copies * M0, r), dtype=torch.float32, device=DEV)
+    Y = q.qlora_linear_fwd(w, X, A, B, ALPHA, T_save=T)
+    dX, dA, dB = q.qlora_linear_bwd(w, X, dY, A, B, ALPHA, T_saved=T)
+    torch.cuda.synchronize()
+    say(f"large-M: M={copies * M0} d={d_in} X {X.numel() * 2 / 2**30:.2f} GiB")
+    for c in range(copies):
+        rows = slice(c * M0, (c + 1) * M0)
+        assert torch.equal(Y[rows].view(torch.int16), Y0.view(torch.int16)), f"Y copy {c}"
+        assert torch.equal(T[rows], T0), f"T copy {c}"
+        assert torch.equal(dX[rows].view(torch.int16), dX0.view(torch.int16)), f"dX copy {c}"
+    for name, got, ref in (("dA", dA, dA0), ("dB", dB, dB0)):
+        fro, mx = rel_errors(f32(got), copies * f32(ref).astype(np.float64))
+        say(f"  {name} vs {copies} x block: fro {fro:.2e} max {mx:.2e}")
+        assert fro <= 1e-5 and mx <= 1e-5, (name, fro, mx)
+    # the block against the oracle on sampled token rows
+    _, _, Wh = oracle_quant(orc, W.cpu())
+    rows = np.arange(0, M0, 4093)
+    s = ALPHA / r
+    Xn, An, Bn, dYn = (f32(t) for t in (X0, A, B, dY0))
+    assert_close("Y rows", f32(Y0)[rows], orc.linear_fwd(Wh, Xn, An, Bn, s, rows=rows))
+    dXr, _, _ = orc.linear_bwd(Wh, Xn, dYn, An, Bn, s, rows=rows, want_da=False, want_db=False)
+    assert_close("dX rows", f32(dX0)[rows], dXr)
