@@ -16,6 +16,8 @@ The same line also carries, each measured in the same run:
            last-level cache holds none of them;
   quant    quantize and dequantize of the 7B layer, GB/s over the algorithmic
            bytes (read FP32 W + write packed state; read packed + write BF16);
+  merge    LoRA merge into the restored base plus requantization of the 7B
+           layer (r = 64), GB/s over packed-read + FP32 write/read + packed write;
   stack65b forward + backward of all 560 LoRA linears of an 80-layer
            LLaMA-65B-shaped stack (hidden 8192, FFN 22016) at M = 2048, one
            layer at a time, packed weights resident in HBM;
@@ -319,6 +321,39 @@ def bench_quant7b(dev, steps, warmup):
     return res
 
 
+def bench_merge7b(dev, steps, warmup):
+    """LoRA merge (FP32 Wh + s B A, FP64 evaluation) and requantization of the
+    7B layer's seven projections, r = 64.  Bytes: packed state read (0.516
+    B/weight) + FP32 merged weight written and read back by the quantizer (8
+    B/weight) + the new packed state written (0.516 B/weight)."""
+    items = []
+    for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B):
+        W = inputs.weight(d_out, d_in, 5, 0, device=dev, proj=p)
+        w = q.qlora_quantize_nf4(W)
+        del W
+        A, B = inputs.lora_factors(d_out, d_in, R, 5, 0, device=dev, proj=p)
+        Wm = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
+        wo = q.NF4Weight.empty(d_out, d_in, dev)
+        ws = torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_QUANTIZE, d_out, d_in),
+                         dtype=torch.uint8, device=dev)
+        items.append((w, A, B, Wm, wo, ws))
+    n = sum(d_out * d_in for _, d_out, d_in in inputs.LLAMA_7B)
+    packed = sum(it[0].nbytes() for it in items)
+    nbytes = 2 * packed + 8 * n
+
+    def step(i):
+        for w, A, B, Wm, wo, ws in items:
+            q.qlora_merge_nf4(w, A, B, ALPHA, W_merged=Wm, out=wo, workspace=ws)
+
+    el = timed(step, steps, warmup) / steps
+    res = dict(layer_us=el * 1e6, gbps=nbytes / el / 1e9, bytes=nbytes,
+               fp64_gflops=2 * R * n / el / 1e9)
+    log(f"merge + requantize 7B layer: {el * 1e6:.1f} us = {nbytes / el / 1e9:.0f} GB/s")
+    del items
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_stack65b(dev, steps, warmup):
     M = 2048
     log(f"65B stack: {inputs.LLAMA_65B_LAYERS} layers x 7, M={M}; quantizing")
@@ -376,7 +411,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--skip", default="", help="comma list of: decode,quant,stack65b,cpu")
+    ap.add_argument("--skip", default="", help="comma list of: decode,quant,merge,stack65b,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MB (a plain copy "
@@ -407,6 +442,8 @@ def main():
         extra["decode_7b"] = bench_decode7b(dev, args.steps, args.warmup)
     if "quant" not in skip:
         extra["quant_7b"] = bench_quant7b(dev, max(3, args.steps // 2), 1)
+    if "merge" not in skip:
+        extra["merge_7b"] = bench_merge7b(dev, max(3, args.steps // 2), 1)
     if "stack65b" not in skip:
         extra["stack_65b"] = bench_stack65b(dev, max(1, min(args.steps, 2)), 1)
     cpu = None if "cpu" in skip else cpu_baseline(args.cpu_tokens)

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     qlora_linear_bwd,
     qlora_linear_fwd,
     qlora_linear_fwd_many,
+    qlora_merge_nf4,
     qlora_nf4_sizes,
     qlora_quantize_nf4,
     qlora_status_string,

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.qlora_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64]
         L.qlora_quantize_nf4.argtypes = [_P, ctypes.POINTER(_Nf4), _P, ctypes.c_size_t, _P]
         L.qlora_dequant_bf16.argtypes = [ctypes.POINTER(_Nf4), _P, _P]
+        L.qlora_merge_nf4.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, ctypes.c_float, _P,
+                                      ctypes.POINTER(_Nf4), _P, ctypes.c_size_t, _P]
         L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
         L.qlora_linear_fwd_many.argtypes = [ctypes.c_int, ctypes.POINTER(_FwdItem), _I64, _P]
@@ -186,6 +188,33 @@ def qlora_dequant_bf16(q: NF4Weight, out: Optional[torch.Tensor] = None) -> torc
     _check(lib().qlora_dequant_bf16(ctypes.byref(qs), _ptr(Wb), _stream(q.device)),
            "qlora_dequant_bf16")
     return Wb
+
+
+def qlora_merge_nf4(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, lora_alpha: float,
+                    W_merged: Optional[torch.Tensor] = None, requantize: bool = True,
+                    out: Optional[NF4Weight] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Merged FP32 weight Wh + (lora_alpha / r) B A and, with requantize,
+    its NF4 state.  Returns (W_merged, NF4Weight or None)."""
+    r = A.shape[0]
+    _need(A, torch.bfloat16, (r, q.d_in), "A")
+    _need(B, torch.bfloat16, (q.d_out, r), "B")
+    Wm = W_merged if W_merged is not None else torch.empty((q.d_out, q.d_in), dtype=torch.float32,
+                                                           device=q.device)
+    _need(Wm, torch.float32, (q.d_out, q.d_in), "W_merged")
+    qs = q.c_struct()
+    qo, qos, ws = None, None, None
+    if requantize:
+        qo = out if out is not None else NF4Weight.empty(q.d_out, q.d_in, q.device)
+        qos = qo.c_struct()
+        need = qlora_workspace_bytes(QLORA_OP_QUANTIZE, q.d_out, q.d_in)
+        ws = workspace if workspace is not None else _workspace(need, q.device)
+    _check(lib().qlora_merge_nf4(ctypes.byref(qs), _ptr(A), _ptr(B), r, float(lora_alpha),
+                                 _ptr(Wm), ctypes.byref(qos) if qos is not None else None,
+                                 _ptr(ws) if ws is not None else None,
+                                 ws.numel() if ws is not None else 0, _stream(q.device)),
+           "qlora_merge_nf4")
+    return Wm, qo
 
 
 def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -445,6 +445,35 @@ int qlora_dequant_bf16(const qlora_nf4_t* q, uint16_t* W_bf16, void* stream) {
                                    q->d_out * q->d_in, W_bf16, static_cast<hipStream_t>(stream)));
 }
 
+int qlora_merge_nf4(const qlora_nf4_t* q, const uint16_t* A, const uint16_t* B, int64_t r,
+                    float lora_alpha, float* W_merged, const qlora_nf4_t* q_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int s = check_nf4(q);
+  if (s) return s;
+  if (q->d_out > kMaxLinearDim || q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
+  if (r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
+  if (!A || !B || !W_merged) return QLORA_ERR_NULL;
+  if (!aligned16(A) || !aligned16(W_merged)) return QLORA_ERR_ALIGN;
+  QuantPlan p{};
+  if (q_out) {
+    s = check_nf4(q_out);
+    if (s) return s;
+    if (q_out->d_out != q->d_out || q_out->d_in != q->d_in) return QLORA_ERR_SHAPE;
+    if (!ws) return QLORA_ERR_NULL;
+    if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+    p = plan_quant(q->d_out, q->d_in, ws);
+    if (ws_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const MergeArgs m{q->codes, q->scale_codes, q->scale2, q->scale_mean, A, B, W_merged,
+                    q->d_out, q->d_in, r, lora_alpha / (float)r};
+  s = hip_status(launch_merge(m, st));
+  if (s || !q_out) return s;
+  QuantWorkspace w{p.absmax, p.part};
+  return hip_status(launch_quantize(W_merged, p.n, q_out->codes, q_out->scale_codes,
+                                    q_out->scale2, q_out->scale_mean, w, lut(), st));
+}
+
 int qlora_linear_fwd(const qlora_nf4_t* q, const uint16_t* X, int64_t M, const uint16_t* A,
                      const uint16_t* B, int64_t r, float lora_alpha, uint16_t* Y, float* T_save,
                      void* ws, size_t ws_bytes, void* stream) {

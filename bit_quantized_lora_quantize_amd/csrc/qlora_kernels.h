@@ -150,6 +150,22 @@ hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp
 hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,
                               bool transposed, float* out, hipStream_t st);
 
+// ------------------------------------------------- LoRA merge
+// out[n][k] = RN_fp32(Wh[n][k] + scale * sum_i B[n][i] A[i][k]) (FP64
+// evaluation), Wh the restored BF16 weight of the quantized state.
+struct MergeArgs {
+  const uint8_t* codes;
+  const uint8_t* scodes;
+  const float* scale2;
+  const float* mean;
+  const uint16_t* A;      // [r][d_in]
+  const uint16_t* B;      // [d_out][r]
+  float* out;             // [d_out][d_in]
+  int64_t d_out, d_in, r;
+  float scale;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+
 // ------------------------------------------------- small-M forward (GEMV)
 // Y[m][n] = RNE_bf16( sum_k X[m][k] Wh[n][k] + sum_i T[m][i] B[n][i] ),
 // T = t_scale * X A^T, for m < M <= 16.  The weight-streaming launch: its

@@ -121,6 +121,29 @@ int qlora_quantize_nf4(const float *W, const qlora_nf4_t *q, void *workspace,
 int qlora_dequant_bf16(const qlora_nf4_t *q, uint16_t *W_bf16, void *stream);
 
 /*
+ * LoRA merge into the base ([QP §12.3]; restored weight as in
+ * qlora_dequant_bf16): the merged weight
+ *     Wm[n][k] = RN_fp32( Wh[n][k] + s * sum_i B[n][i] A[i][k] ),
+ * s = lora_alpha / r (FP32), with the right-hand side evaluated in FP64
+ * (rank index ascending, every product and sum rounded on its own) and
+ * rounded once to FP32.  When q_out is not NULL the merged weight is then
+ * quantized into q_out exactly as qlora_quantize_nf4 would (the second
+ * rounding that the merge into a 4-bit base implies).
+ *   q        quantized base (input)
+ *   A        BF16 [r, d_in]  (16B)    1 <= r <= 256
+ *   B        BF16 [d_out, r]          any alignment
+ *   W_merged FP32 [d_out, d_in] (16B) output
+ *   q_out    NULL, or a quantized state of the same shape (output; may not
+ *            alias q or W_merged)
+ * workspace (16B) >= qlora_workspace_bytes(QLORA_OP_QUANTIZE, d_out, d_in,
+ * 0, 0) when q_out is given (unused otherwise).  Deterministic.
+ */
+int qlora_merge_nf4(const qlora_nf4_t *q, const uint16_t *A, const uint16_t *B,
+                    int64_t r, float lora_alpha, float *W_merged,
+                    const qlora_nf4_t *q_out, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
  * Forward of the LoRA linear layer on the frozen NF4 base
  * ([QP §1.2, §2.2, §2.3, §6.3]; column-vector form y = W x + (alpha/r) B A x,
  * written here for token rows):

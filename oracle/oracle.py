@@ -62,6 +62,7 @@ def _load():
         lib.orc_dequant_bf16.argtypes = [P, P, P, ctypes.c_float, I, P]
         lib.orc_linear_fwd_rows.argtypes = [P, P, P, P, I, I, I, ctypes.c_double, P, I, P]
         lib.orc_linear_bwd.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, I, P, P, P]
+        lib.orc_merge.argtypes = [P, P, P, I, I, I, ctypes.c_float, P]
         lib.orc_map_nf4_index.argtypes = [P, I, P]
         lib.orc_map_fp8_encode.argtypes = [P, I, P]
         lib.orc_map_bf16_rne.argtypes = [P, I, P]
@@ -168,6 +169,17 @@ def dequant_bf16(codes, scodes, s2, mean: float, n: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------- LoRA linear
+
+def merge(Wh, A, B, s: float) -> np.ndarray:
+    """Merged FP32 weight Wh + s B A (FP64 evaluation, one FP32 rounding);
+    s is the FP32 value alpha / r.  [QP §12.3]"""
+    Wh, A, B = (_c(t, np.float32) for t in (Wh, A, B))
+    d_out, d_in = Wh.shape
+    r = A.shape[0]
+    Wm = np.empty((d_out, d_in), np.float32)
+    _load().orc_merge(_ptr(Wh), _ptr(A), _ptr(B), d_out, d_in, r, float(np.float32(s)), _ptr(Wm))
+    return Wm
+
 
 def linear_fwd(Wh, X, A, B, s: float, rows=None) -> np.ndarray:
     """Y[rows] = X[rows] Wh^T + s (X[rows] A^T) B^T in FP64.

@@ -351,6 +351,26 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
 /* ------------------------------------------------------------------------
  * Elementwise maps over arrays, used by the exhaustive tests.
  * ---------------------------------------------------------------------- */
+/* ------------------------------------------------------------------------
+ * LoRA merge [QP §12.3]: the adapter is added to the base weight,
+ *   Wm = Wh + s B A,          Wh [d_out, d_in] restored weights,
+ * and merging into a 4-bit base quantizes the sum again (a second
+ * rounding).  Reading: each merged element is Wh + s * (sum over the rank
+ * index, ascending, of B[n][i] * A[i][k]) evaluated in FP64 and rounded
+ * once to FP32; the requantization is orc_quantize_nf4 of that FP32 matrix.
+ * ---------------------------------------------------------------------- */
+void orc_merge(const float *Wh, const float *A, const float *B, int64_t d_out,
+               int64_t d_in, int64_t r, float s, float *Wm) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < d_out; ++n) {
+    for (int64_t k = 0; k < d_in; ++k) {
+      double dot = 0.0;
+      for (int64_t i = 0; i < r; ++i) dot += (double)B[n * r + i] * (double)A[i * d_in + k];
+      Wm[n * d_in + k] = (float)((double)Wh[n * d_in + k] + (double)s * dot);
+    }
+  }
+}
+
 void orc_map_nf4_index(const float *x, int64_t n, uint8_t *out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = orc_nf4_index(x[i]);

@@ -141,3 +141,20 @@ def test_grouped_forward_argument_errors(L):
     assert L.qlora_linear_fwd_many(1, items, 4, None) == ESHAPE
     items[0].w.d_out, items[0].w.d_in, items[0].r = 64, 64, 8
     assert L.qlora_linear_fwd_many(1, items, 4, None) == ENULL
+
+
+def test_merge_argument_errors(L):
+    P = ctypes.c_void_p
+    w, wo = _nf4(128, 64), _nf4(128, 64, base=0x40000)
+    other = _nf4(64, 64, base=0x40000)
+    A, B, Wm, ws = P(0x60000), P(0x70000), P(0x80000), P(0x90000)
+    big = 1 << 30
+    f = L.qlora_merge_nf4
+    assert f(ctypes.byref(w), A, B, 0, 16.0, Wm, None, None, 0, None) == ESHAPE
+    assert f(ctypes.byref(w), A, B, 257, 16.0, Wm, None, None, 0, None) == ESHAPE
+    assert f(ctypes.byref(w), None, B, 8, 16.0, Wm, None, None, 0, None) == ENULL
+    assert f(ctypes.byref(w), A, B, 8, 16.0, None, None, None, 0, None) == ENULL
+    assert f(ctypes.byref(w), P(0x60002), B, 8, 16.0, Wm, None, None, 0, None) == EALIGN
+    assert f(ctypes.byref(w), A, B, 8, 16.0, Wm, ctypes.byref(other), ws, big, None) == ESHAPE
+    assert f(ctypes.byref(w), A, B, 8, 16.0, Wm, ctypes.byref(wo), None, big, None) == ENULL
+    assert f(ctypes.byref(w), A, B, 8, 16.0, Wm, ctypes.byref(wo), ws, 16, None) == EWS

@@ -413,3 +413,52 @@ def test_rows_subset_matches_full(orc):
                                   orc.linear_fwd(Wh, X, A, B, 0.5)[rows])
     np.testing.assert_array_equal(orc.linear_bwd(Wh, X, dY, A, B, 0.5, rows=rows)[0],
                                   orc.linear_bwd(Wh, X, dY, A, B, 0.5)[0][rows])
+
+
+# ------------------------------------------------------------------ LoRA merge
+
+def test_merge_planted_powers_of_two(orc):
+    """[QP §12.3] merge with a known answer: a planted base (codebook values
+    times 2^-4, restored exactly), a rank-1 adapter with B = 2^-5 and
+    A = +-2^-6 and s = 2, so every merged value Wh + s B A = Wh +- 2^-10 is
+    representable and the FP32 rounding is exact."""
+    W, idx = _planted_exact_matrix(orc, 4, 128, -4, seed=31)
+    codes, scodes, s2, mean = orc.quantize_nf4(W)
+    Wh = orc.bf16_bits_to_f32(orc.dequant_bf16(codes, scodes, s2, mean, W.size)).reshape(4, 128)
+    sign = np.where(np.arange(128) % 3 == 0, -1.0, 1.0)
+    A = (sign * 2.0 ** -6).astype(np.float32).reshape(1, 128)
+    B = np.full((4, 1), 2.0 ** -5, np.float32)
+    Wm = orc.merge(Wh, A, B, 2.0)
+    expect = Wh.astype(np.float64) + sign[None, :] * 2.0 ** -10
+    np.testing.assert_array_equal(Wm, expect.astype(np.float32))
+    assert np.all(expect.astype(np.float32) == expect)
+
+
+def test_merge_zero_adapter_requantizes_to_same_codes(orc):
+    """A zero adapter leaves the restored weight unchanged (bit for bit), and
+    quantizing it again reproduces every NF4 index: each block's largest
+    element restores to +-bf16(scale) and becomes +-1 after the new absmax
+    division, and every other element moves by at most a BF16 rounding,
+    far less than half the smallest gap between levels."""
+    rng = np.random.default_rng(5)
+    W = rng.normal(0, 0.02, (16, 256)).astype(np.float32)
+    codes, scodes, s2, mean = orc.quantize_nf4(W)
+    Wh = orc.bf16_bits_to_f32(orc.dequant_bf16(codes, scodes, s2, mean, W.size)).reshape(16, 256)
+    A = rng.normal(0, 0.1, (4, 256)).astype(np.float32)
+    Wm = orc.merge(Wh, A, np.zeros((16, 4), np.float32), 4.0)
+    np.testing.assert_array_equal(Wm, Wh)
+    codes2, *_ = orc.quantize_nf4(Wm)
+    np.testing.assert_array_equal(codes2, codes)
+
+
+def test_merge_applied_equals_lora_forward(orc):
+    """The merged weight applied to tokens equals the unmerged LoRA forward
+    up to the one FP32 rounding of each merged element."""
+    Wh, X, A, B, _ = _small_layer(11, d_out=24, d_in=128, M=6, r=4)
+    s = np.float32(16.0) / np.float32(4)
+    Wm = orc.merge(Wh, A, B, float(s))
+    got = X.astype(np.float64) @ Wm.astype(np.float64).T
+    ref = orc.linear_fwd(Wh, X, A, B, float(s))
+    # |rounding| <= 2^-24 |Wm| per element
+    bound = np.abs(X).astype(np.float64) @ (np.abs(Wm).astype(np.float64).T * 2.0 ** -24)
+    assert np.all(np.abs(got - ref) <= bound + 1e-300)
