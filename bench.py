@@ -18,6 +18,11 @@ The same line also carries, each measured in the same run:
            bytes (read FP32 W + write packed state; read packed + write BF16);
   merge    LoRA merge into the restored base plus requantization of the 7B
            layer (r = 64), GB/s over packed-read + FP32 write/read + packed write;
+  adamw    one clipped AdamW step (global-norm sum of squares, then the
+           update with a BF16 copy) over the r = 64 adapters of one 7B layer
+           (14 tensors, 5.0 M parameters) and of all 32 layers (448 tensors,
+           160 M), GB/s over 34 bytes per parameter (gradient read twice,
+           parameter and both moments read and written, BF16 copy written);
   stack65b forward + backward of all 560 LoRA linears of an 80-layer
            LLaMA-65B-shaped stack (hidden 8192, FFN 22016) at M = 2048, one
            layer at a time, packed weights resident in HBM;
@@ -354,6 +359,43 @@ def bench_merge7b(dev, steps, warmup):
     return res
 
 
+def bench_adamw7b(dev, steps, warmup):
+    """Clipped AdamW steps over the 7B adapters (r = 64): one layer's 14
+    tensors, then the 448 tensors of 32 layers.  Per step: zero the FP64
+    accumulator, sum of squares, update.  34 bytes per parameter."""
+    res = {}
+    for name, layers in (("layer", 1), ("model32", 32)):
+        params = []
+        for layer in range(layers):
+            for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B):
+                for n in (R * d_in, d_out * R):
+                    g, m, v = inputs.optimizer_state(n, 6, layer=(7 * layer + p) % 16,
+                                                     device=dev)
+                    params.append(q.AdamwParam(
+                        torch.empty(n, device=dev).normal_(0, 0.02), g, m, v,
+                        torch.empty(n, dtype=torch.bfloat16, device=dev)))
+        ps = q.AdamwParamSet(params)
+        ps.sumsq_workspace()
+        acc = torch.zeros(1, dtype=torch.float64, device=dev)
+        n_total = sum(t.param.numel() for t in params)
+
+        def step(i):
+            acc.zero_()
+            q.qlora_grad_sumsq(ps, acc)
+            q.qlora_adamw_step(ps, lr=2e-4, weight_decay=0.01, step=(i or 0) + 1,
+                               grad_sumsq=acc, max_grad_norm=0.3)
+
+        el = timed(step, steps, warmup) / steps
+        nbytes = 34 * n_total
+        res[name] = dict(params=n_total, tensors=len(params), us=el * 1e6,
+                         gbps=nbytes / el / 1e9)
+        log(f"adamw {name}: {len(params)} tensors, {n_total / 1e6:.1f} M params: "
+            f"{el * 1e6:.1f} us = {nbytes / el / 1e9:.0f} GB/s")
+        del params, ps
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_stack65b(dev, steps, warmup):
     M = 2048
     log(f"65B stack: {inputs.LLAMA_65B_LAYERS} layers x 7, M={M}; quantizing")
@@ -411,7 +453,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--skip", default="", help="comma list of: decode,quant,merge,stack65b,cpu")
+    ap.add_argument("--skip", default="", help="comma list of: decode,quant,merge,adamw,stack65b,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MB (a plain copy "
@@ -444,6 +486,8 @@ def main():
         extra["quant_7b"] = bench_quant7b(dev, max(3, args.steps // 2), 1)
     if "merge" not in skip:
         extra["merge_7b"] = bench_merge7b(dev, max(3, args.steps // 2), 1)
+    if "adamw" not in skip:
+        extra["adamw_7b"] = bench_adamw7b(dev, args.steps, args.warmup)
     if "stack65b" not in skip:
         extra["stack_65b"] = bench_stack65b(dev, max(1, min(args.steps, 2)), 1)
     cpu = None if "cpu" in skip else cpu_baseline(args.cpu_tokens)

@@ -5,6 +5,8 @@ include/qlora.h; this package is a thin ctypes binding over it (see _lib.py)
 plus the seeded synthetic-input generators (inputs.py).
 """
 from ._lib import (  # noqa: F401
+    AdamwParam,
+    AdamwParamSet,
     FwdItem,
     NF4Weight,
     QLORA_MAX_GROUP,
@@ -15,7 +17,10 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     qlora_abi_version,
+    qlora_adamw_step,
     qlora_dequant_bf16,
+    qlora_grad_sumsq,
+    qlora_sumsq_workspace_bytes,
     qlora_linear_bwd,
     qlora_linear_fwd,
     qlora_linear_fwd_many,

@@ -38,6 +38,11 @@ class _FwdItem(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class _AdamwParam(ctypes.Structure):
+    _fields_ = [("param", _P), ("param_bf16", _P), ("grad", _P), ("m", _P), ("v", _P),
+                ("n", _I64)]
+
+
 class QloraError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {qlora_status_string(status)} (status {status})")
@@ -63,6 +68,13 @@ def lib() -> ctypes.CDLL:
         L.qlora_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64, _I64]
         L.qlora_quantize_nf4.argtypes = [_P, ctypes.POINTER(_Nf4), _P, ctypes.c_size_t, _P]
         L.qlora_dequant_bf16.argtypes = [ctypes.POINTER(_Nf4), _P, _P]
+        L.qlora_sumsq_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_sumsq_workspace_bytes.argtypes = [ctypes.c_int, ctypes.POINTER(_AdamwParam)]
+        L.qlora_grad_sumsq.argtypes = [ctypes.c_int, ctypes.POINTER(_AdamwParam), _P, _P,
+                                       ctypes.c_size_t, _P]
+        L.qlora_adamw_step.argtypes = [ctypes.c_int, ctypes.POINTER(_AdamwParam), ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_float, _I64, _P, ctypes.c_float, _P]
         L.qlora_merge_nf4.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, ctypes.c_float, _P,
                                       ctypes.POINTER(_Nf4), _P, ctypes.c_size_t, _P]
         L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
@@ -215,6 +227,92 @@ def qlora_merge_nf4(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, lora_alpha: 
                                  ws.numel() if ws is not None else 0, _stream(q.device)),
            "qlora_merge_nf4")
     return Wm, qo
+
+
+@dataclass
+class AdamwParam:
+    """One trainable tensor of the optimizer step: FP32 master values,
+    gradient and the two moments (all the same shape), and an optional BF16
+    compute copy refreshed after the step."""
+    param: torch.Tensor
+    grad: torch.Tensor
+    m: torch.Tensor
+    v: torch.Tensor
+    param_bf16: Optional[torch.Tensor] = None
+
+
+def _adamw_array(params: Sequence[AdamwParam]):
+    arr = (_AdamwParam * max(1, len(params)))()
+    for i, t in enumerate(params):
+        n = t.param.numel()
+        for name, x in (("grad", t.grad), ("m", t.m), ("v", t.v)):
+            _need(x, torch.float32, tuple(t.param.shape), name)
+        _need(t.param, torch.float32, tuple(t.param.shape), "param")
+        if t.param_bf16 is not None:
+            _need(t.param_bf16, torch.bfloat16, tuple(t.param.shape), "param_bf16")
+        arr[i] = _AdamwParam(t.param.data_ptr(),
+                             t.param_bf16.data_ptr() if t.param_bf16 is not None else None,
+                             t.grad.data_ptr(), t.m.data_ptr(), t.v.data_ptr(), n)
+    return arr
+
+
+class AdamwParamSet:
+    """A list of AdamwParam checked once, with its C descriptor array (and the
+    sum-of-squares workspace) built once, for repeated steps over the same
+    tensors.  The tensors must keep their storage while the set is in use."""
+
+    def __init__(self, params: Sequence[AdamwParam]):
+        self.params = list(params)
+        self.count = len(self.params)
+        self.arr = _adamw_array(self.params)
+        self.device = self.params[0].param.device if self.params else None
+        self._ws = None
+
+    def sumsq_workspace(self) -> torch.Tensor:
+        if self._ws is None:
+            need = int(lib().qlora_sumsq_workspace_bytes(self.count, self.arr))
+            self._ws = _workspace(need, self.device)
+        return self._ws
+
+
+def _as_set(params) -> AdamwParamSet:
+    return params if isinstance(params, AdamwParamSet) else AdamwParamSet(params)
+
+
+def qlora_sumsq_workspace_bytes(params) -> int:
+    ps = _as_set(params)
+    return int(lib().qlora_sumsq_workspace_bytes(ps.count, ps.arr))
+
+
+def qlora_grad_sumsq(params, acc: torch.Tensor,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """acc (FP64 [1], device) += the fixed-order sum of squared gradients of
+    `params` (a list of AdamwParam or an AdamwParamSet)."""
+    ps = _as_set(params)
+    if ps.count == 0:
+        return acc
+    _need(acc, torch.float64, (1,), "acc")
+    ws = workspace if workspace is not None else ps.sumsq_workspace()
+    _check(lib().qlora_grad_sumsq(ps.count, ps.arr, _ptr(acc), _ptr(ws), ws.numel(),
+                                  _stream(acc.device)), "qlora_grad_sumsq")
+    return acc
+
+
+def qlora_adamw_step(params, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.0, step: int = 1,
+                     grad_sumsq: Optional[torch.Tensor] = None,
+                     max_grad_norm: float = 0.0) -> None:
+    """One AdamW step over `params` (a list of AdamwParam or an
+    AdamwParamSet), clipped by the global norm when grad_sumsq is given."""
+    ps = _as_set(params)
+    if ps.count == 0:
+        return
+    if grad_sumsq is not None:
+        _need(grad_sumsq, torch.float64, (1,), "grad_sumsq")
+    _check(lib().qlora_adamw_step(ps.count, ps.arr, float(lr), float(beta1), float(beta2),
+                                  float(eps), float(weight_decay), int(step), _ptr(grad_sumsq),
+                                  float(max_grad_norm), _stream(ps.device)),
+           "qlora_adamw_step")
 
 
 def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "qlora.h"
 #include "qlora_device.h"
@@ -443,6 +444,77 @@ int qlora_dequant_bf16(const qlora_nf4_t* q, uint16_t* W_bf16, void* stream) {
   if (!aligned16(W_bf16)) return QLORA_ERR_ALIGN;
   return hip_status(launch_dequant(q->codes, q->scale_codes, q->scale2, q->scale_mean,
                                    q->d_out * q->d_in, W_bf16, static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_sumsq_workspace_bytes(int count, const qlora_adamw_param* params) {
+  if (count < 0 || (count > 0 && !params)) return 0;
+  int64_t len = 0;
+  for (int i = 0; i < count; ++i) {
+    if (params[i].n < 0 || params[i].n > kOptMaxElems) return 0;
+    len += sumsq_part_len(params[i].n);
+  }
+  Carver c(nullptr);
+  c.take<double>(std::max<int64_t>(len, 1));
+  c.take<double>(std::max(count, 1));
+  return c.off + 256;
+}
+
+int qlora_grad_sumsq(int count, const qlora_adamw_param* params, double* acc, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (count < 0) return QLORA_ERR_SHAPE;
+  if (count == 0) return QLORA_OK;
+  if (!params || !acc || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  int64_t len = 0;
+  for (int i = 0; i < count; ++i) {
+    if (params[i].n < 0 || params[i].n > kOptMaxElems) return QLORA_ERR_SHAPE;
+    if (params[i].n > 0 && !params[i].grad) return QLORA_ERR_NULL;
+    len += sumsq_part_len(params[i].n);
+  }
+  if (ws_bytes < qlora_sumsq_workspace_bytes(count, params)) return QLORA_ERR_WORKSPACE;
+  Carver c(ws);
+  double* part = c.take<double>(std::max<int64_t>(len, 1));
+  double* sums = c.take<double>(count);
+  std::vector<const float*> g(count);
+  std::vector<int64_t> n(count);
+  for (int i = 0; i < count; ++i) {
+    g[i] = params[i].grad;
+    n[i] = params[i].n;
+  }
+  return hip_status(launch_sumsq(g.data(), n.data(), count, acc, part, sums,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int qlora_adamw_step(int count, const qlora_adamw_param* params, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, int64_t step,
+                     const double* grad_sumsq, float max_grad_norm, void* stream) {
+  if (count < 0 || step < 1) return QLORA_ERR_SHAPE;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f)) return QLORA_ERR_SHAPE;
+  if (count == 0) return QLORA_OK;
+  if (!params) return QLORA_ERR_NULL;
+  std::vector<AdamwDesc> d;
+  d.reserve(count);
+  for (int i = 0; i < count; ++i) {
+    const qlora_adamw_param& t = params[i];
+    if (t.n < 0 || t.n > kOptMaxElems) return QLORA_ERR_SHAPE;
+    if (t.n == 0) continue;
+    if (!t.param || !t.grad || !t.m || !t.v) return QLORA_ERR_NULL;
+    d.push_back(AdamwDesc{t.param, t.param_bf16, t.grad, t.m, t.v, t.n});
+  }
+  if (d.empty()) return QLORA_OK;
+  AdamwScalars h{};
+  h.lr = lr;
+  h.lrwd = lr * weight_decay;
+  h.b1 = beta1;
+  h.ob1 = 1.0f - beta1;
+  h.b2 = beta2;
+  h.ob2 = 1.0f - beta2;
+  h.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+  h.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+  h.eps = eps;
+  h.max_norm = max_grad_norm;
+  return hip_status(launch_adamw(d.data(), (int)d.size(), h, grad_sumsq,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int qlora_merge_nf4(const qlora_nf4_t* q, const uint16_t* A, const uint16_t* B, int64_t r,

@@ -150,6 +150,37 @@ hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp
 hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,
                               bool transposed, float* out, hipStream_t st);
 
+// ------------------------------------------------- optimizer step
+// Tensors are handled in batches of up to kOptBatch per launch (descriptors
+// passed by value), so a step over many small adapter tensors costs a few
+// launches rather than a few per tensor.
+constexpr int kOptBatch = 32;
+constexpr int64_t kOptMaxElems = int64_t(1) << 32;  // per tensor
+constexpr int kAdamwChunk = 1024;                   // elements per workgroup
+
+// acc[0] += sum over tensors t (in order) of the FP64 sum of grads[t][i]^2
+// (groups of 256 by the stride-halving tree, then the tree over the group
+// sums padded to a power of two).  part: FP64, sum over t of that power of
+// two (sumsq_part_len); sums: FP64 [count].  grads and n are host arrays.
+int64_t sumsq_part_len(int64_t n);
+hipError_t launch_sumsq(const float* const* grads, const int64_t* n, int count, double* acc,
+                        double* part, double* sums, hipStream_t st);
+struct AdamwDesc {
+  float* param;       // FP32 master [n]
+  uint16_t* p16;      // optional BF16 copy [n]
+  const float* grad;  // [n]
+  float* m;           // first moment [n]
+  float* v;           // second moment [n]
+  int64_t n;
+};
+struct AdamwScalars {
+  float lr, lrwd, b1, ob1, b2, ob2, bc1, bc2, eps, max_norm;
+};
+// One AdamW step over `count` tensors (host array of descriptors, n > 0);
+// sumsq (device, may be NULL: no clipping) gives the clip coefficient.
+hipError_t launch_adamw(const AdamwDesc* d, int count, const AdamwScalars& h,
+                        const double* sumsq, hipStream_t st);
+
 // ------------------------------------------------- LoRA merge
 // out[n][k] = RN_fp32(Wh[n][k] + scale * sum_i B[n][i] A[i][k]) (FP64
 // evaluation), Wh the restored BF16 weight of the quantized state.

@@ -8,7 +8,10 @@ Recipe (std = standard deviation):
   W  FP32 ~ N(0, 0.02), optionally with round(0.001 n) outliers at +-10 std
      (+-0.2, random sign) at positions drawn without replacement;
   A  ~ N(0, 1/r), B ~ N(0, 0.01), both rounded to BF16;
-  X, dY ~ N(0, 1) rounded to BF16.
+  X, dY ~ N(0, 1) rounded to BF16;
+  optimizer state: FP32 gradient ~ N(0, 1e-3), first moment ~ N(0, 1e-4),
+  second moment = (a draw of N(0, 1e-3))^2 (non-negative, as after earlier
+  steps).
 Seeds: seed(config, layer, tensor) = 1000 config + 16 layer + tensor.  A
 torch.Generator on the target device draws the values, so CPU and GPU draws
 of one seed differ; every comparison moves one draw between devices.
@@ -17,7 +20,7 @@ from __future__ import annotations
 
 import torch
 
-T_W, T_A, T_B, T_X, T_DY, T_OUT_POS, T_OUT_SIGN = range(7)
+T_W, T_A, T_B, T_X, T_DY, T_OUT_POS, T_OUT_SIGN, T_G, T_M, T_V = range(10)
 
 # Decoder-layer projections as (name, d_out, d_in) = nn.Linear weight shapes.
 LLAMA_7B = [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096),
@@ -79,3 +82,11 @@ def activations(M: int, d: int, config: int, layer: int = 0, tensor: int = T_X, 
     """X or dY ~ N(0, 1) in BF16."""
     return normal((M, d), 1.0, seed(config, layer, tensor) + 100000 * proj, device,
                   torch.bfloat16)
+
+
+def optimizer_state(n: int, config: int, layer: int = 0, step: int = 0, device="cpu"):
+    """(grad, m, v) FP32 [n]; `step` varies the gradient draw only."""
+    g = normal((n,), 1e-3, seed(config, layer, T_G) + 100000 * step, device)
+    m = normal((n,), 1e-4, seed(config, layer, T_M), device)
+    v = normal((n,), 1e-3, seed(config, layer, T_V), device) ** 2
+    return g, m, v

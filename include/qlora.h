@@ -225,6 +225,62 @@ int qlora_linear_fwd_many(int count, const qlora_fwd_item *items, int64_t M,
                           void *stream);
 
 /*
+ * Optimizer step on the LoRA factors ([QP §7.3]: AdamW with one first and
+ * one second moment per trainable parameter, 32-bit; [QP §10.2]: optional
+ * clipping by the global gradient norm).  Only A and B train.
+ *
+ * Tensors are processed in batches of up to 32 per kernel launch, so a step
+ * over many small adapter tensors costs a few launches.  One tensor of the
+ * step (all arrays device memory, any 4-byte alignment; 16-byte aligned
+ * arrays, 8-byte for the BF16 copy, take wider accesses, same results):
+ */
+typedef struct {
+  float *param;          /* FP32 master values [n], updated in place        */
+  uint16_t *param_bf16;  /* BF16 copy [n] written after the step (RNE), or  */
+                         /* NULL                                            */
+  const float *grad;     /* FP32 gradient [n]                               */
+  float *m;              /* first moment [n], updated in place              */
+  float *v;              /* second moment [n], updated in place             */
+  int64_t n;             /* element count, 0 <= n <= 2^32                   */
+} qlora_adamw_param;
+
+/*
+ * acc[0] += sum over the listed tensors (in list order, FP64) of the sum of
+ * their squared gradients, each taken in groups of 256 by the stride-halving
+ * tree (pairs (j, j+128), (j, j+64), ..., (j, j+1)) and then by the same tree
+ * over the group sums padded with zeros to a power of two.  acc is one FP64
+ * device value the caller zeroes before the first call of a step; several
+ * calls accumulate in call order.  workspace (16B-aligned device memory)
+ * >= qlora_sumsq_workspace_bytes(count, params) for the same list (about
+ * 8 bytes per 128 elements plus 8 per tensor; 0 for an invalid list).
+ * QLORA_ERR_SHAPE for count < 0 or n outside [0, 2^32]; QLORA_ERR_NULL for
+ * a missing acc, workspace or gradient (n > 0); QLORA_ERR_ALIGN,
+ * QLORA_ERR_WORKSPACE.
+ */
+int qlora_grad_sumsq(int count, const qlora_adamw_param *params, double *acc,
+                     void *workspace, size_t workspace_bytes, void *stream);
+size_t qlora_sumsq_workspace_bytes(int count, const qlora_adamw_param *params);
+
+/*
+ * AdamW with decoupled weight decay, step number `step` >= 1 (bias
+ * corrections bc_i = 1 - beta_i^step, evaluated in FP64 on the host and
+ * rounded to FP32).  With grad_sumsq (device FP64 from qlora_grad_sumsq) the
+ * gradients are first scaled by c = min(1, max_grad_norm / (norm + 1e-6)),
+ * norm = FP32(sqrt(sumsq)); with NULL, c = 1.  Per element, FP32, each
+ * operation rounded on its own in this order:
+ *   g = g * c;   p = p - (lr * wd) * p;
+ *   m = b1 * m + (1 - b1) * g;   v = b2 * v + (1 - b2) * (g * g);
+ *   p = p - lr * ((m / bc1) / (sqrt(v / bc2) + eps));   p_bf16 = RNE_bf16(p).
+ * The square root is correctly rounded.  Tensors with n = 0 are skipped.
+ * QLORA_ERR_SHAPE for step < 1, count < 0, n outside [0, 2^32] or beta
+ * outside [0, 1); QLORA_ERR_NULL for a missing array (n > 0).
+ */
+int qlora_adamw_step(int count, const qlora_adamw_param *params, float lr,
+                     float beta1, float beta2, float eps, float weight_decay,
+                     int64_t step, const double *grad_sumsq,
+                     float max_grad_norm, void *stream);
+
+/*
  * Timing aid for profilers and benchmarks.  The next launch of this
  * library's weight kernel -- the one kernel of a call that reads the packed
  * weights: the first quantization pass, the dequantization, the

@@ -63,6 +63,12 @@ def _load():
         lib.orc_linear_fwd_rows.argtypes = [P, P, P, P, I, I, I, ctypes.c_double, P, I, P]
         lib.orc_linear_bwd.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, I, P, P, P]
         lib.orc_merge.argtypes = [P, P, P, I, I, I, ctypes.c_float, P]
+        lib.orc_sumsq.argtypes = [P, I]
+        lib.orc_sumsq.restype = ctypes.c_double
+        lib.orc_clip_coef.argtypes = [ctypes.c_double, ctypes.c_float]
+        lib.orc_clip_coef.restype = ctypes.c_float
+        F = ctypes.c_float
+        lib.orc_adamw.argtypes = [P, P, P, P, P, I, F, F, F, F, F, I, F]
         lib.orc_map_nf4_index.argtypes = [P, I, P]
         lib.orc_map_fp8_encode.argtypes = [P, I, P]
         lib.orc_map_bf16_rne.argtypes = [P, I, P]
@@ -179,6 +185,29 @@ def merge(Wh, A, B, s: float) -> np.ndarray:
     Wm = np.empty((d_out, d_in), np.float32)
     _load().orc_merge(_ptr(Wh), _ptr(A), _ptr(B), d_out, d_in, r, float(np.float32(s)), _ptr(Wm))
     return Wm
+
+
+def sumsq(g: np.ndarray) -> float:
+    """Sum of squares in the fixed order (groups of 256, then the tree over
+    the group sums).  [QP §10.2]"""
+    g = _c(g, np.float32).ravel()
+    return float(_load().orc_sumsq(_ptr(g), g.size))
+
+
+def clip_coef(S: float, max_norm: float) -> float:
+    return float(_load().orc_clip_coef(float(S), float(max_norm)))
+
+
+def adamw(p, g, m, v, lr, beta1, beta2, eps, wd, step, c=1.0, want_bf16=False):
+    """One AdamW step on copies of (p, m, v); returns (p, m, v, p_bf16 bits or
+    None).  [QP §7.3]"""
+    p, m, v = (_c(t, np.float32).copy() for t in (p, m, v))
+    g = _c(g, np.float32)
+    p16 = np.empty(p.shape, np.uint16) if want_bf16 else None
+    _load().orc_adamw(_ptr(p), _ptr(p16) if want_bf16 else ctypes.c_void_p(0), _ptr(g), _ptr(m),
+                      _ptr(v), p.size, float(lr), float(beta1), float(beta2), float(eps),
+                      float(wd), int(step), float(c))
+    return p, m, v, p16
 
 
 def linear_fwd(Wh, X, A, B, s: float, rows=None) -> np.ndarray:

@@ -371,6 +371,68 @@ void orc_merge(const float *Wh, const float *A, const float *B, int64_t d_out,
   }
 }
 
+/* ------------------------------------------------------------------------
+ * Optimizer step on the LoRA factors [QP §7.3] (AdamW, one first and one
+ * second moment per parameter, 32-bit) with optional clipping by the global
+ * gradient norm [QP §10.2].
+ * Readings (the pages strip the formulas):
+ *   - AdamW with decoupled weight decay, bias-corrected moments;
+ *   - the norm's sum of squares is taken per tensor in groups of 256 by the
+ *     stride-halving tree and then by the same tree over the group sums
+ *     (the order of the scale mean above), tensors added in list order;
+ *   - clip coefficient c = min(1, max_norm / (norm + 1e-6)),
+ *     norm = FP32(sqrt(S));
+ *   - FP32 element update, each operation rounded on its own in the order
+ *     written below; bc_i = FP32(1 - beta_i^step) from an FP64 power.
+ * ---------------------------------------------------------------------- */
+double orc_sumsq(const float *g, int64_t n) {
+  int64_t G = (n + ORC_GROUP - 1) / ORC_GROUP;
+  int64_t Gp = 1;
+  while (Gp < G) Gp *= 2;
+  double *part = (double *)calloc((size_t)Gp, sizeof(double));
+  double grp[ORC_GROUP];
+  for (int64_t q = 0; q < G; ++q) {
+    for (int j = 0; j < ORC_GROUP; ++j) {
+      int64_t i = q * ORC_GROUP + j;
+      double x = (i < n) ? (double)g[i] : 0.0;
+      grp[j] = x * x;
+    }
+    part[q] = tree_sum(grp, ORC_GROUP);
+  }
+  double S = tree_sum(part, Gp);
+  free(part);
+  return S;
+}
+
+float orc_clip_coef(double S, float max_norm) {
+  float norm = (float)sqrt(S);
+  float c = max_norm / (norm + 1e-6f);
+  return c < 1.0f ? c : 1.0f;
+}
+
+void orc_adamw(float *p, uint16_t *p16, const float *g, float *m, float *v,
+               int64_t n, float lr, float beta1, float beta2, float eps,
+               float wd, int64_t step, float c) {
+  const float lrwd = lr * wd;
+  const float ob1 = 1.0f - beta1, ob2 = 1.0f - beta2;
+  const float bc1 = (float)(1.0 - pow((double)beta1, (double)step));
+  const float bc2 = (float)(1.0 - pow((double)beta2, (double)step));
+  for (int64_t i = 0; i < n; ++i) {
+    float gi = g[i] * c;
+    float pi = p[i];
+    pi = pi - lrwd * pi;
+    float mi = beta1 * m[i] + ob1 * gi;
+    float vi = beta2 * v[i] + ob2 * (gi * gi);
+    float mh = mi / bc1;
+    float den = sqrtf(vi / bc2) + eps;
+    pi = pi - lr * (mh / den);
+    p[i] = pi;
+    m[i] = mi;
+    v[i] = vi;
+    if (p16) p16[i] = orc_bf16_rne(pi);
+  }
+}
+
 void orc_map_nf4_index(const float *x, int64_t n, uint8_t *out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = orc_nf4_index(x[i]);

@@ -158,3 +158,41 @@ def test_merge_argument_errors(L):
     assert f(ctypes.byref(w), A, B, 8, 16.0, Wm, ctypes.byref(other), ws, big, None) == ESHAPE
     assert f(ctypes.byref(w), A, B, 8, 16.0, Wm, ctypes.byref(wo), None, big, None) == ENULL
     assert f(ctypes.byref(w), A, B, 8, 16.0, Wm, ctypes.byref(wo), ws, 16, None) == EWS
+
+
+def test_optimizer_argument_errors(L):
+    P = ctypes.c_void_p
+    Prm = _lib._AdamwParam
+    good = (Prm * 2)(Prm(0x10000, None, 0x20000, 0x30000, 0x40000, 100),
+                     Prm(0x50000, 0x60000, 0x70000, 0x80000, 0x90000, 0))
+    nograd = (Prm * 1)(Prm(0x10000, None, None, 0x30000, 0x40000, 100))
+    neg = (Prm * 1)(Prm(0x10000, None, 0x20000, 0x30000, 0x40000, -1))
+    f = L.qlora_adamw_step
+    args = (1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert f(0, None, *args, 1, None, 0.0, None) == OK      # nothing to do
+    assert f(-1, good, *args, 1, None, 0.0, None) == ESHAPE
+    assert f(2, good, *args, 0, None, 0.0, None) == ESHAPE  # step counts from 1
+    assert f(2, good, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1, None, 0.0, None) == ESHAPE
+    assert f(2, good, 1e-3, 0.9, -0.1, 1e-8, 0.0, 1, None, 0.0, None) == ESHAPE
+    assert f(2, None, *args, 1, None, 0.0, None) == ENULL
+    assert f(1, nograd, *args, 1, None, 0.0, None) == ENULL
+    assert f(1, neg, *args, 1, None, 0.0, None) == ESHAPE
+    g = L.qlora_grad_sumsq
+    acc, ws = P(0xA0000), P(0xB0000)
+    need = L.qlora_sumsq_workspace_bytes(2, good)
+    assert need >= 16 and L.qlora_sumsq_workspace_bytes(-1, good) == 0
+    assert L.qlora_sumsq_workspace_bytes(1, neg) == 0
+    big = (Prm * 1)(Prm(0x10000, None, 0x20000, 0x30000, 0x40000, 1 << 30))
+    assert L.qlora_sumsq_workspace_bytes(1, big) >= (1 << 30) // 256 * 8
+    huge = (Prm * 1)(Prm(0x10000, None, 0x20000, 0x30000, 0x40000, (1 << 32) + 1))
+    assert L.qlora_sumsq_workspace_bytes(1, huge) == 0
+    assert g(1, huge, acc, ws, 1 << 40, None) == ESHAPE
+    assert f(1, huge, *args, 1, None, 0.0, None) == ESHAPE
+    assert g(0, None, None, None, 0, None) == OK
+    assert g(-1, good, acc, ws, need, None) == ESHAPE
+    assert g(2, good, None, ws, need, None) == ENULL
+    assert g(2, good, acc, None, need, None) == ENULL
+    assert g(2, good, acc, P(0xB0008), need, None) == EALIGN
+    assert g(2, good, acc, ws, need - 1, None) == EWS
+    assert g(1, nograd, acc, ws, need, None) == ENULL
+    assert g(1, neg, acc, ws, need, None) == ESHAPE

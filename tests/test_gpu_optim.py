@@ -1,0 +1,136 @@
+"""GPU parity of the optimizer step on the LoRA factors ([QP §7.3] AdamW
+with 32-bit moments; [QP §10.2] clipping by the global gradient norm):
+sums of squares, parameters, moments and BF16 copies bit-exact against
+the CPU oracle over several steps."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_lora_quantize_amd as q
+from bit_quantized_lora_quantize_amd import inputs
+from parity_util import say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+HP = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)
+
+
+def _params_from_sizes(sizes, cfg, with_bf16):
+    host = []
+    for i, n in enumerate(sizes):
+        p = inputs.normal((n,), 0.05, inputs.seed(cfg, i, inputs.T_A)).numpy()
+        _, m, v = inputs.optimizer_state(n, cfg, layer=i)
+        host.append([p, m.numpy(), v.numpy()])
+    dev = [q.AdamwParam(torch.from_numpy(p).to(DEV), torch.empty(p.size, device=DEV),
+                        torch.from_numpy(m).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.empty(p.size, dtype=torch.bfloat16, device=DEV)
+                        if with_bf16(i) else None)
+           for i, (p, m, v) in enumerate(host)]
+    return host, dev
+
+
+@pytest.mark.parametrize("sizes", [[1], [255, 256, 257], [70000, 0, 3], [262144 + 17]])
+def test_grad_sumsq_bit_exact(orc, sizes):
+    say(f"sumsq parity: sizes={sizes}")
+    grads = [inputs.optimizer_state(n, 150, layer=i)[0] for i, n in enumerate(sizes)]
+    params = [q.AdamwParam(torch.empty(n, device=DEV), g.to(DEV), torch.empty(n, device=DEV),
+                           torch.empty(n, device=DEV)) for n, g in zip(sizes, grads)]
+    acc = torch.full((1,), 0.25, dtype=torch.float64, device=DEV)
+    q.qlora_grad_sumsq(params, acc)
+    q.qlora_grad_sumsq(params[::-1], acc)     # a second call accumulates
+    ref = 0.25
+    for g in grads + grads[::-1]:
+        ref += orc.sumsq(g.numpy())
+    assert acc.item() == ref
+
+
+@pytest.mark.parametrize("clip", [None, "active", "inactive"])
+def test_adamw_steps_bit_exact(orc, clip):
+    sizes = [1000, 4096 * 16 + 5, 37, 0, 64 * 4096]
+    say(f"adamw parity: sizes={sizes} clip={clip}")
+    host, dev = _params_from_sizes(sizes, 151, lambda i: i % 2 == 0)
+    acc = torch.zeros(1, dtype=torch.float64, device=DEV)
+    for step in range(1, 6):
+        grads = [inputs.optimizer_state(n, 151, layer=i, step=step)[0].numpy()
+                 for i, n in enumerate(sizes)]
+        for t, g in zip(dev, grads):
+            t.grad.copy_(torch.from_numpy(g))
+        c, max_norm, gs = 1.0, 0.0, None
+        if clip is not None:
+            S = 0.0
+            for g in grads:
+                S += orc.sumsq(g)
+            norm = float(np.sqrt(S))
+            max_norm = 0.5 * norm if clip == "active" else 4.0 * norm
+            c = orc.clip_coef(S, max_norm)
+            assert (c < 1.0) == (clip == "active")
+            acc.zero_()
+            q.qlora_grad_sumsq(dev, acc)
+            gs = acc
+        q.qlora_adamw_step(dev, step=step, grad_sumsq=gs, max_grad_norm=max_norm, **HP)
+        for h, g in zip(host, grads):
+            p, m, v, p16 = orc.adamw(h[0], g, h[1], h[2], HP["lr"], HP["beta1"], HP["beta2"],
+                                     HP["eps"], HP["weight_decay"], step, c, want_bf16=True)
+            h[:] = [p, m, v, p16]
+        torch.cuda.synchronize()
+        for i, (h, t) in enumerate(zip(host, dev)):
+            for name, ref, got in (("p", h[0], t.param), ("m", h[1], t.m), ("v", h[2], t.v)):
+                assert np.array_equal(_bits(got.cpu().numpy()), _bits(ref)), \
+                    f"step {step} tensor {i}: {name} differs"
+            if t.param_bf16 is not None:
+                got16 = t.param_bf16.cpu().view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(got16, h[3]), f"step {step} tensor {i}: bf16 copy differs"
+
+
+def test_adamw_llama7b_lora_set(orc):
+    """One clipped step over the r = 64 adapters of one 7B decoder layer
+    (seven projections, A and B each: 5.0 M parameters)."""
+    r = 64
+    sizes = []
+    for _, d_out, d_in in inputs.LLAMA_7B:
+        sizes += [r * d_in, d_out * r]
+    say(f"adamw parity: 7B layer LoRA set, {sum(sizes)} parameters")
+    host, dev = _params_from_sizes(sizes, 152, lambda i: True)
+    grads = [inputs.optimizer_state(n, 152, layer=i, step=1)[0].numpy()
+             for i, n in enumerate(sizes)]
+    for t, g in zip(dev, grads):
+        t.grad.copy_(torch.from_numpy(g))
+    acc = torch.zeros(1, dtype=torch.float64, device=DEV)
+    q.qlora_grad_sumsq(dev, acc)
+    S = 0.0
+    for g in grads:
+        S += orc.sumsq(g)
+    torch.cuda.synchronize()
+    assert acc.item() == S
+    max_norm = 0.3 * float(np.sqrt(S))
+    c = orc.clip_coef(S, max_norm)
+    q.qlora_adamw_step(dev, step=7, grad_sumsq=acc, max_grad_norm=max_norm, **HP)
+    torch.cuda.synchronize()
+    for i, (h, g, t) in enumerate(zip(host, grads, dev)):
+        p, m, v, p16 = orc.adamw(h[0], g, h[1], h[2], HP["lr"], HP["beta1"], HP["beta2"],
+                                 HP["eps"], HP["weight_decay"], 7, c, want_bf16=True)
+        assert np.array_equal(_bits(t.param.cpu().numpy()), _bits(p)), f"tensor {i}: p"
+        assert np.array_equal(_bits(t.m.cpu().numpy()), _bits(m)), f"tensor {i}: m"
+        assert np.array_equal(_bits(t.v.cpu().numpy()), _bits(v)), f"tensor {i}: v"
+        got16 = t.param_bf16.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got16, p16), f"tensor {i}: bf16 copy"
+
+
+def test_adamw_zero_grad_decay_only(orc):
+    """Zero gradients with zero moments: the step is the decay alone, and
+    the moments stay zero."""
+    n = 4099
+    p0 = inputs.normal((n,), 0.05, inputs.seed(153, 0, inputs.T_A))
+    t = q.AdamwParam(p0.to(DEV), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                     torch.zeros(n, device=DEV))
+    q.qlora_adamw_step([t], lr=1e-2, weight_decay=0.1, step=3)
+    p, m, v, _ = orc.adamw(p0.numpy(), np.zeros(n, np.float32), np.zeros(n, np.float32),
+                           np.zeros(n, np.float32), 1e-2, 0.9, 0.999, 1e-8, 0.1, 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(t.param.cpu().numpy()), _bits(p))
+    assert not t.m.any().item() and not t.v.any().item()

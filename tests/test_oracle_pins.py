@@ -462,3 +462,87 @@ def test_merge_applied_equals_lora_forward(orc):
     # |rounding| <= 2^-24 |Wm| per element
     bound = np.abs(X).astype(np.float64) @ (np.abs(Wm).astype(np.float64).T * 2.0 ** -24)
     assert np.all(np.abs(got - ref) <= bound + 1e-300)
+
+
+# ---------------------------------------------------------- optimizer step
+
+def test_sumsq_is_the_sum_of_squares(orc):
+    """The fixed-order FP64 sum of squares equals the exactly rounded sum
+    (math.fsum of the exact squares) within n FP64 roundings."""
+    for n in (1, 255, 256, 257, 70000):
+        g = np.random.default_rng(n).normal(0, 1, n).astype(np.float32)
+        S = orc.sumsq(g)
+        ref = math.fsum(float(x) * float(x) for x in g)
+        assert abs(S - ref) <= n * 2.0 ** -52 * ref
+
+
+def test_adamw_first_step_moves_by_lr(orc):
+    """From zero moments the first bias-corrected step is lr * g / (|g| +
+    eps), i.e. each weight moves by lr against its gradient's sign."""
+    rng = np.random.default_rng(2)
+    p0 = rng.normal(0, 1, 512).astype(np.float32)
+    g = rng.normal(0, 1, 512).astype(np.float32)
+    lr, eps = 2e-4, 1e-8
+    p, m, v, _ = orc.adamw(p0, g, np.zeros(512, np.float32), np.zeros(512, np.float32),
+                           lr, 0.9, 0.999, eps, 0.0, 1)
+    step = p0.astype(np.float64) - p
+    expect = lr * np.sign(g)
+    tol = lr * (eps / np.abs(g) + 8 * 2.0 ** -24) + 2 * np.spacing(np.abs(p0))
+    assert np.all(np.abs(step - expect) <= tol)
+
+
+def test_adamw_weight_decay_alone_is_geometric(orc):
+    """Zero gradients leave the moments at zero and the update is the
+    decoupled decay alone: p_t = p_0 (1 - lr wd)^t."""
+    rng = np.random.default_rng(4)
+    p = rng.normal(0, 1, 300).astype(np.float32)
+    m = np.zeros(300, np.float32)
+    v = np.zeros(300, np.float32)
+    z = np.zeros(300, np.float32)
+    lr, wd, T = 1e-2, 0.1, 20
+    q = p.copy()
+    for t in range(1, T + 1):
+        q, m, v, _ = orc.adamw(q, z, m, v, lr, 0.9, 0.999, 1e-8, wd, t)
+    assert np.all(m == 0) and np.all(v == 0)
+    np.testing.assert_allclose(q, p.astype(np.float64) * (1 - lr * wd) ** T, rtol=T * 2.0 ** -22)
+
+
+def test_adamw_matches_torch_adamw(orc):
+    """Special case that reduces to a library routine: the oracle's steps
+    follow torch.optim.AdamW (FP32, decoupled decay) to within FP32
+    rounding-order differences over several steps."""
+    rng = np.random.default_rng(9)
+    p0 = rng.normal(0, 0.1, (64, 96)).astype(np.float32)
+    grads = [rng.normal(0, 1e-2, (64, 96)).astype(np.float32) for _ in range(6)]
+    lr, b1, b2, eps, wd = 2e-4, 0.9, 0.999, 1e-8, 0.01
+    tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    opt = torch.optim.AdamW([tp], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd,
+                            foreach=False)
+    p, m, v = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    for t, g in enumerate(grads, 1):
+        tp.grad = torch.from_numpy(g.copy())
+        opt.step()
+        p, m, v, _ = orc.adamw(p, g, m, v, lr, b1, b2, eps, wd, t)
+    np.testing.assert_allclose(p, tp.detach().numpy(), rtol=0, atol=1e-6)
+
+
+def test_clip_coefficient_matches_torch_and_is_scale_invariant(orc):
+    """The clip coefficient agrees with torch.nn.utils.clip_grad_norm_ for
+    the same gradients, and scaling every gradient by k leaves the clipped
+    gradients unchanged (to FP32 rounding)."""
+    rng = np.random.default_rng(12)
+    gs = [rng.normal(0, 1, n).astype(np.float32) for n in (1000, 4096, 77)]
+    S = sum(orc.sumsq(g) for g in gs)
+    c = orc.clip_coef(S, 0.3)
+    ts = [torch.nn.Parameter(torch.zeros(len(g))) for g in gs]
+    for t, g in zip(ts, gs):
+        t.grad = torch.from_numpy(g.copy())
+    torch.nn.utils.clip_grad_norm_(ts, 0.3)
+    for t, g in zip(ts, gs):
+        np.testing.assert_allclose(t.grad.numpy(), g * c, rtol=2e-6)
+    k = 37.0
+    S2 = sum(orc.sumsq((g * k).astype(np.float32)) for g in gs)
+    c2 = orc.clip_coef(S2, 0.3)
+    for g in gs:
+        np.testing.assert_allclose((g * k).astype(np.float32) * c2, g * c, rtol=1e-6)
+    assert orc.clip_coef(1e-6, 0.3) == 1.0
