@@ -60,8 +60,11 @@ def _load():
         lib.orc_restored_scale.argtypes = [P, P, ctypes.c_float, I]
         lib.orc_restored_scale.restype = ctypes.c_float
         lib.orc_dequant_bf16.argtypes = [P, P, P, ctypes.c_float, I, P]
-        lib.orc_linear_fwd_rows.argtypes = [P, P, P, P, I, I, I, ctypes.c_double, P, I, P]
-        lib.orc_linear_bwd.argtypes = [P, P, P, P, P, I, I, I, I, ctypes.c_double, P, I, P, P, P]
+        D = ctypes.c_double
+        lib.orc_linear_fwd_rows.argtypes = [P, P, P, P, I, I, I, D, P, I, P, D, P]
+        lib.orc_linear_bwd.argtypes = [P, P, P, P, P, I, I, I, I, D, P, I, P, D, P, P, P]
+        lib.orc_philox4x32_10.argtypes = [P, P, P]
+        lib.orc_dropout_keep.argtypes = [I, I, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, P]
         lib.orc_merge.argtypes = [P, P, P, I, I, I, ctypes.c_float, P]
         lib.orc_sumsq.argtypes = [P, I]
         lib.orc_sumsq.restype = ctypes.c_double
@@ -210,25 +213,36 @@ def adamw(p, g, m, v, lr, beta1, beta2, eps, wd, step, c=1.0, want_bf16=False):
     return p, m, v, p16
 
 
-def linear_fwd(Wh, X, A, B, s: float, rows=None) -> np.ndarray:
-    """Y[rows] = X[rows] Wh^T + s (X[rows] A^T) B^T in FP64.
+def _keep_args(keep, M, d_in, p):
+    if keep is None:
+        return ctypes.c_void_p(0), 1.0, None
+    keep = _c(keep, np.uint8)
+    assert keep.shape == (M, d_in)
+    return _ptr(keep), 1.0 - float(np.float32(p)), keep
+
+
+def linear_fwd(Wh, X, A, B, s: float, rows=None, keep=None, p: float = 0.0) -> np.ndarray:
+    """Y[rows] = X[rows] Wh^T + s (D(X)[rows] A^T) B^T in FP64.
 
     Wh [d_out, d_in], X [M, d_in], A [r, d_in], B [d_out, r]: FP32 arrays of
-    exact values.  rows defaults to every token row."""
+    exact values.  rows defaults to every token row.  keep (uint8 [M, d_in])
+    and p give the LoRA dropout D(x) = keep x / (1 - p); None: D(x) = x."""
     Wh, X, A, B = (_c(t, np.float32) for t in (Wh, X, A, B))
     d_out, d_in = Wh.shape
     r = A.shape[0]
     M = X.shape[0]
     rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
     Y = np.zeros((rows.size, d_out), np.float64)
+    kp, q, _hold = _keep_args(keep, M, d_in, p)
     _load().orc_linear_fwd_rows(_ptr(Wh), _ptr(X), _ptr(A), _ptr(B), d_out, d_in, r,
-                                float(s), _ptr(rows), rows.size, _ptr(Y))
+                                float(s), _ptr(rows), rows.size, kp, q, _ptr(Y))
     return Y
 
 
 def linear_bwd(Wh, X, dY, A, B, s: float, rows=None, want_dx=True, want_da=True,
-               want_db=True):
-    """(dX[rows], dA, dB) in FP64 for upstream gradient dY; no dW exists."""
+               want_db=True, keep=None, p: float = 0.0):
+    """(dX[rows], dA, dB) in FP64 for upstream gradient dY; no dW exists.
+    keep / p: the forward's LoRA dropout (see linear_fwd)."""
     Wh, X, dY, A, B = (_c(t, np.float32) for t in (Wh, X, dY, A, B))
     d_out, d_in = Wh.shape
     r = A.shape[0]
@@ -238,8 +252,25 @@ def linear_bwd(Wh, X, dY, A, B, s: float, rows=None, want_dx=True, want_da=True,
     dA = np.zeros((r, d_in), np.float64) if want_da else None
     dB = np.zeros((d_out, r), np.float64) if want_db else None
     nul = ctypes.c_void_p(0)
+    kp, q, _hold = _keep_args(keep, M, d_in, p)
     _load().orc_linear_bwd(_ptr(Wh), _ptr(X), _ptr(dY), _ptr(A), _ptr(B), M, d_out, d_in, r,
-                           float(s), _ptr(rows), rows.size,
+                           float(s), _ptr(rows), rows.size, kp, q,
                            _ptr(dX) if want_dx else nul, _ptr(dA) if want_da else nul,
                            _ptr(dB) if want_db else nul)
     return dX, dA, dB
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 of one 4-word counter under a 2-word key."""
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.zeros(4, np.uint32)
+    _load().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def dropout_keep(M: int, d: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """uint8 [M, d] keep mask of the LoRA dropout (1 = kept).  [QP §6.3]"""
+    keep = np.zeros((M, d), np.uint8)
+    _load().orc_dropout_keep(M, d, float(p), int(seed), int(offset), _ptr(keep))
+    return keep

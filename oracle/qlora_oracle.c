@@ -30,7 +30,9 @@
  *     group's largest |centred scale| mapped to 448, round-to-nearest-even,
  *     saturating; an all-zero group stores code 0;
  *   - restored scale = fp8(code) * s2 + mean (FP32, two roundings, no FMA);
- *     restored weight = RNE_bf16(codebook[idx] * restored scale) (FP32 product).
+ *     restored weight = RNE_bf16(codebook[idx] * restored scale) (FP32 product);
+ *   - LoRA dropout is inverted dropout on the LoRA branch's input, its mask
+ *     drawn from Philox4x32-10 by element position (orc_dropout_keep).
  */
 #include <math.h>
 #include <stdint.h>
@@ -265,18 +267,30 @@ void orc_dequant_bf16(const uint8_t *codes, const uint8_t *scale_codes,
  * every product and sum is FP64.  No gradient is formed for Wh.
  * ---------------------------------------------------------------------- */
 
+/* LoRA dropout in training mode [QP §6.3]: the LoRA branch sees
+ * D(x) = keep * x / (1 - p) instead of x; the base branch sees x.  keep is a
+ * row-major [M, d_in] array of 0/1 (NULL: no dropout, D(x) = x) and
+ * keep_prob = 1 - p.  The value is formed in FP64. */
+static double lora_input(const float *X, const uint8_t *keep, double keep_prob,
+                         int64_t idx) {
+  if (!keep) return (double)X[idx];
+  return keep[idx] ? (double)X[idx] / keep_prob : 0.0;
+}
+
 /* Y rows listed in rows[0..nrows): Y[k, :] for token rows[k]. */
 void orc_linear_fwd_rows(const float *Wh, const float *X, const float *A,
                          const float *B, int64_t d_out, int64_t d_in,
                          int64_t r, double s, const int64_t *rows,
-                         int64_t nrows, double *Y) {
+                         int64_t nrows, const uint8_t *keep, double keep_prob,
+                         double *Y) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t k = 0; k < nrows; ++k) {
     const float *x = X + rows[k] * d_in;
     double *t = (double *)malloc((size_t)(r > 0 ? r : 1) * sizeof(double));
-    for (int64_t i = 0; i < r; ++i) {          /* t = A x        */
+    for (int64_t i = 0; i < r; ++i) {          /* t = A D(x)     */
       double acc = 0.0;
-      for (int64_t c = 0; c < d_in; ++c) acc += (double)A[i * d_in + c] * x[c];
+      for (int64_t c = 0; c < d_in; ++c)
+        acc += (double)A[i * d_in + c] * lora_input(X, keep, keep_prob, rows[k] * d_in + c);
       t[i] = acc;
     }
     for (int64_t o = 0; o < d_out; ++o) {      /* y = Wh x + s B t */
@@ -292,15 +306,17 @@ void orc_linear_fwd_rows(const float *Wh, const float *X, const float *A,
 
 /* Backward of the same layer for upstream gradient dY [M, d_out]:
  *   U  = s dY B          [M, r]   (gradient reaching the LoRA bottleneck)
- *   T  = X A^T           [M, r]
- *   dX = dY Wh + U A     (listed rows only)
- *   dA = U^T X           [r, d_in]
+ *   T  = D(X) A^T        [M, r]
+ *   dX = dY Wh + D'(U A) (listed rows only; D' = keep / (1 - p), the
+ *                         derivative of the dropout map, 1 without dropout)
+ *   dA = U^T D(X)        [r, d_in]
  *   dB = s dY^T T        [d_out, r]
  * The frozen base contributes to dX but receives no gradient [QP §2.4]. */
 void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
                     const float *A, const float *B, int64_t M, int64_t d_out,
                     int64_t d_in, int64_t r, double s, const int64_t *rows,
-                    int64_t nrows, double *dX, double *dA, double *dB) {
+                    int64_t nrows, const uint8_t *keep, double keep_prob,
+                    double *dX, double *dA, double *dB) {
   double *U = (double *)calloc((size_t)(M * r + 1), sizeof(double));
   double *T = (double *)calloc((size_t)(M * r + 1), sizeof(double));
 #pragma omp parallel for schedule(static)
@@ -308,7 +324,8 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
     for (int64_t i = 0; i < r; ++i) {
       double u = 0.0, t = 0.0;
       for (int64_t o = 0; o < d_out; ++o) u += (double)dY[m * d_out + o] * B[o * r + i];
-      for (int64_t c = 0; c < d_in; ++c) t += (double)X[m * d_in + c] * A[i * d_in + c];
+      for (int64_t c = 0; c < d_in; ++c)
+        t += lora_input(X, keep, keep_prob, m * d_in + c) * A[i * d_in + c];
       U[m * r + i] = s * u;
       T[m * r + i] = t;
     }
@@ -318,20 +335,22 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
     for (int64_t k = 0; k < nrows; ++k) {
       int64_t m = rows[k];
       for (int64_t c = 0; c < d_in; ++c) {
-        double acc = 0.0;
-        for (int64_t o = 0; o < d_out; ++o) acc += (double)dY[m * d_out + o] * Wh[o * d_in + c];
-        for (int64_t i = 0; i < r; ++i) acc += U[m * r + i] * A[i * d_in + c];
-        dX[k * d_in + c] = acc;
+        double base = 0.0, lora = 0.0;
+        for (int64_t o = 0; o < d_out; ++o) base += (double)dY[m * d_out + o] * Wh[o * d_in + c];
+        for (int64_t i = 0; i < r; ++i) lora += U[m * r + i] * A[i * d_in + c];
+        if (keep) lora = keep[m * d_in + c] ? lora / keep_prob : 0.0;
+        dX[k * d_in + c] = base + lora;
       }
     }
   }
-  if (dA) {      /* dA[i, c] = sum over m ascending of U[m, i] X[m, c] */
+  if (dA) {      /* dA[i, c] = sum over m ascending of U[m, i] D(X)[m, c] */
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < r; ++i) {
       double *row = dA + i * d_in;
       for (int64_t c = 0; c < d_in; ++c) row[c] = 0.0;
       for (int64_t m = 0; m < M; ++m)
-        for (int64_t c = 0; c < d_in; ++c) row[c] += U[m * r + i] * X[m * d_in + c];
+        for (int64_t c = 0; c < d_in; ++c)
+          row[c] += U[m * r + i] * lora_input(X, keep, keep_prob, m * d_in + c);
     }
   }
   if (dB) {      /* dB[o, i] = s * sum over m ascending of dY[m, o] T[m, i] */
@@ -349,16 +368,61 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
 }
 
 /* ------------------------------------------------------------------------
- * Elementwise maps over arrays, used by the exhaustive tests.
+ * The dropout mask of the LoRA branch [QP §6.3] from a counter-based
+ * generator, so that the backward can regenerate the forward's mask from
+ * (seed, offset) alone: Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O.
+ * Dror, D. E. Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11).
+ *
+ * One round maps counter (c0, c1, c2, c3) under key (k0, k1) to
+ *   (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
+ * with M0 = 0xD2511F53, M1 = 0xCD9E8D57 and hi/lo the halves of the 64-bit
+ * product; the key grows by (0x9E3779B9, 0xBB67AE85) between rounds.
  * ---------------------------------------------------------------------- */
-/* ------------------------------------------------------------------------
- * LoRA merge [QP §12.3]: the adapter is added to the base weight,
- *   Wm = Wh + s B A,          Wh [d_out, d_in] restored weights,
- * and merging into a 4-bit base quantizes the sum again (a second
- * rounding).  Reading: each merged element is Wh + s * (sum over the rank
- * index, ascending, of B[n][i] * A[i][k]) evaluated in FP64 and rounded
- * once to FP32; the requantization is orc_quantize_nf4 of that FP32 matrix.
- * ---------------------------------------------------------------------- */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+/* keep[m, k] for a row-major [M, d] input: element (m, k) takes word m % 4
+ * of Philox4x32-10 at counter (k, floor(m / 4), offset_lo, offset_hi) under
+ * key (seed_lo, seed_hi), and is kept when that word u satisfies
+ * u >= floor(p * 2^32), so it is dropped with probability p (to 2^-32). */
+void orc_dropout_keep(int64_t M, int64_t d, float p, uint64_t seed, uint64_t offset,
+                      uint8_t *keep) {
+  const uint32_t thr = (uint32_t)floor((double)p * 4294967296.0);
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t k = 0; k < d; ++k) {
+      const uint32_t ctr[4] = {(uint32_t)k, (uint32_t)(m / 4), (uint32_t)offset,
+                               (uint32_t)(offset >> 32)};
+      uint32_t out[4];
+      orc_philox4x32_10(ctr, key, out);
+      keep[m * d + k] = out[m % 4] >= thr ? 1 : 0;
+    }
+  }
+}
+
 void orc_merge(const float *Wh, const float *A, const float *B, int64_t d_out,
                int64_t d_in, int64_t r, float s, float *Wm) {
 #pragma omp parallel for schedule(static)

@@ -546,3 +546,97 @@ def test_clip_coefficient_matches_torch_and_is_scale_invariant(orc):
     for g in gs:
         np.testing.assert_allclose((g * k).astype(np.float32) * c2, g * c, rtol=1e-6)
     assert orc.clip_coef(1e-6, 0.3) == 1.0
+
+
+# ------------------------------------------------------------ LoRA dropout
+
+def test_philox_known_answers(orc):
+    """Philox4x32-10 reproduces the generator's published known answers
+    (fixture philox4x32_10_kat.txt, with its citation)."""
+    for line in read_golden_values("philox4x32_10_kat.txt"):
+        w = [int(t, 16) for t in line.split()]
+        out = orc.philox4x32_10(w[0:4], w[4:6])
+        assert [int(x) for x in out] == w[6:10]
+
+
+@pytest.mark.parametrize("p", [0.0, 0.05, 0.1, 0.5])
+def test_dropout_keep_rate_and_uniformity(orc, p):
+    """Each element is dropped with probability p: the kept fraction lies
+    within 5 binomial standard deviations of 1 - p, per row group of four
+    and per column (a wrong word index or counter would skew one of them)."""
+    M, d = 512, 1024
+    keep = orc.dropout_keep(M, d, p, seed=0x1234_5678_9ABC, offset=3)
+    n = keep.size
+    q = 1 - np.float32(p)
+    if p == 0:
+        assert keep.all()
+        return
+    sd = math.sqrt(n * p * (1 - p))
+    assert abs(keep.sum() - n * q) <= 5 * sd
+    for j in range(4):  # rows m with m % 4 == j use output word j
+        sub = keep[j::4]
+        assert abs(sub.sum() - sub.size * q) <= 5 * math.sqrt(sub.size * p * (1 - p))
+    cols = keep.sum(axis=0)
+    assert abs(cols.mean() - M * q) <= 5 * math.sqrt(M * p * (1 - p) / d)
+
+
+def test_dropout_masks_differ_by_seed_and_offset_only(orc):
+    """Same (seed, offset): the same mask (the backward regenerates the
+    forward's); another offset or seed: an independent mask, agreeing on
+    about q^2 + p^2 of the elements."""
+    p, M, d = 0.1, 256, 512
+    a = orc.dropout_keep(M, d, p, 11, 0)
+    assert np.array_equal(a, orc.dropout_keep(M, d, p, 11, 0))
+    for b in (orc.dropout_keep(M, d, p, 11, 1), orc.dropout_keep(M, d, p, 12, 0),
+              orc.dropout_keep(M, d, p, 11, 1 << 32)):
+        agree = float((a == b).mean())
+        assert abs(agree - (0.81 + 0.01)) < 0.01
+
+
+def test_dropout_linear_special_cases(orc):
+    """Keeping everything at p = 0 is the plain layer; keeping everything at
+    p scales the LoRA branch by 1 / (1 - p) exactly; dropped inputs do not
+    reach the LoRA branch, kept ones do."""
+    Wh, X, A, B, dY = _small_layer(21, d_out=16, d_in=128, M=6, r=4)
+    s = 4.0
+    ones = np.ones(X.shape, np.uint8)
+    np.testing.assert_array_equal(orc.linear_fwd(Wh, X, A, B, s, keep=ones, p=0.0),
+                                  orc.linear_fwd(Wh, X, A, B, s))
+    for got, ref in zip(orc.linear_bwd(Wh, X, dY, A, B, s, keep=ones, p=0.0),
+                        orc.linear_bwd(Wh, X, dY, A, B, s)):
+        np.testing.assert_array_equal(got, ref)
+    Z = np.zeros_like(Wh)
+    p = 0.25  # 1 - p = 0.75: a power-of-two ratio keeps the scaling exact
+    np.testing.assert_allclose(orc.linear_fwd(Z, X, A, B, s, keep=ones, p=p),
+                               orc.linear_fwd(Z, X, A, B, s) / 0.75, rtol=1e-13)
+    keep = orc.dropout_keep(*X.shape, 0.3, 5, 9)
+    X2 = X.copy()
+    X2[keep == 0] = 123.0
+    np.testing.assert_array_equal(orc.linear_fwd(Z, X2, A, B, s, keep=keep, p=0.3),
+                                  orc.linear_fwd(Z, X, A, B, s, keep=keep, p=0.3))
+    X3 = X.copy()
+    X3[keep == 1] += 1.0
+    assert not np.array_equal(orc.linear_fwd(Z, X3, A, B, s, keep=keep, p=0.3),
+                              orc.linear_fwd(Z, X, A, B, s, keep=keep, p=0.3))
+
+
+@pytest.mark.parametrize("shape", [(24, 128, 5, 3), (33, 192, 9, 8)])
+def test_dropout_backward_adjoint_identities(orc, shape):
+    """With the mask fixed, Y is still linear in X, A and B separately, so
+    <dY, Y(V)> = <grad, V> pins the dropout backward (the mask on dX's LoRA
+    term, the dropped input in dA) to the dropout forward."""
+    d_out, d_in, M, r = shape
+    Wh, X, A, B, dY = _small_layer(30 + M, d_out, d_in, M, r)
+    s, p = 16.0 / r, 0.1
+    keep = orc.dropout_keep(M, d_in, p, 77, 1)
+    rng = np.random.default_rng(31)
+    dX, dA, dB = orc.linear_bwd(Wh, X, dY, A, B, s, keep=keep, p=p)
+    VX = rng.normal(size=X.shape).astype(np.float32)
+    lhs = _inner(dY, orc.linear_fwd(Wh, VX, A, B, s, keep=keep, p=p))
+    assert abs(lhs - _inner(dX, VX)) <= 1e-10 * (abs(lhs) + 1)
+    VA = rng.normal(size=A.shape).astype(np.float32)
+    lhs = _inner(dY, orc.linear_fwd(np.zeros_like(Wh), X, VA, B, s, keep=keep, p=p))
+    assert abs(lhs - _inner(dA, VA)) <= 1e-10 * (abs(lhs) + 1)
+    VB = rng.normal(size=B.shape).astype(np.float32)
+    lhs = _inner(dY, orc.linear_fwd(np.zeros_like(Wh), X, A, VB, s, keep=keep, p=p))
+    assert abs(lhs - _inner(dB, VB)) <= 1e-10 * (abs(lhs) + 1)
