@@ -9,6 +9,8 @@ T = s X A^T) then backward (dX, dA, dB), 14 library calls.  Useful FLOPs per
 projection = 4 M d_in d_out + 6 M r (d_in + d_out).
 
 The same line also carries, each measured in the same run:
+  dropout  the headline step in training mode with LoRA dropout p = 0.05
+           (the principles page's configuration), same FLOP count;
   decode   fused forward at M = 1, 4, 16 over the 7B layer in one grouped call
            per layer, scored as HBM GB/s over the packed weight bytes (NF4
            codes + FP8 scale codes + FP32 second-level scales + mean); four
@@ -152,8 +154,10 @@ class Activations:
     """Per projection shape: X, dY, outputs, saved T and workspaces, shared by
     every layer (layers run one after another on one stream)."""
 
-    def __init__(self, shapes, M, config, dev):
+    def __init__(self, shapes, M, config, dev, dropout=False):
         self.buf = {}
+        fop = q.QLORA_OP_FWD_DROPOUT if dropout else q.QLORA_OP_FWD
+        bop = q.QLORA_OP_BWD_DROPOUT if dropout else q.QLORA_OP_BWD
         for p, (name, d_out, d_in) in enumerate(shapes):
             key = (d_out, d_in)
             if key in self.buf:
@@ -166,23 +170,34 @@ class Activations:
                 dA=torch.empty((R, d_in), dtype=torch.float32, device=dev),
                 dB=torch.empty((d_out, R), dtype=torch.float32, device=dev),
                 T=torch.empty((M, R), dtype=torch.float32, device=dev),
-                wsf=torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_FWD, d_out, d_in, M, R),
+                wsf=torch.empty(q.qlora_workspace_bytes(fop, d_out, d_in, M, R),
                                 dtype=torch.uint8, device=dev),
-                wsb=torch.empty(q.qlora_workspace_bytes(q.QLORA_OP_BWD, d_out, d_in, M, R),
+                wsb=torch.empty(q.qlora_workspace_bytes(bop, d_out, d_in, M, R),
                                 dtype=torch.uint8, device=dev))
 
 
-def train_step(layer, acts, timer=None):
-    for it in layer.items:
+def train_step(layer, acts, timer=None, p_drop=None, step=0):
+    for n, it in enumerate(layer.items):
         a = acts.buf[(it["d_out"], it["d_in"])]
         if timer:
             timer.arm("fwd")
-        q.qlora_linear_fwd(it["w"], a["X"], it["A"], it["B"], ALPHA, Y=a["Y"], T_save=a["T"],
-                           workspace=a["wsf"])
+        if p_drop is None:
+            q.qlora_linear_fwd(it["w"], a["X"], it["A"], it["B"], ALPHA, Y=a["Y"],
+                               T_save=a["T"], workspace=a["wsf"])
+        else:
+            drop = q.Dropout(p_drop, seed=0x5EED, offset=len(layer.items) * step + n)
+            q.qlora_linear_fwd_dropout(it["w"], a["X"], it["A"], it["B"], ALPHA, drop,
+                                       Y=a["Y"], T_save=a["T"], workspace=a["wsf"])
         if timer:
             timer.arm("bwd")
-        q.qlora_linear_bwd(it["w"], a["X"], a["dY"], it["A"], it["B"], ALPHA, T_saved=a["T"],
-                           dX=a["dX"], dA=a["dA"], dB=a["dB"], workspace=a["wsb"])
+        if p_drop is None:
+            q.qlora_linear_bwd(it["w"], a["X"], a["dY"], it["A"], it["B"], ALPHA,
+                               T_saved=a["T"], dX=a["dX"], dA=a["dA"], dB=a["dB"],
+                               workspace=a["wsb"])
+        else:
+            q.qlora_linear_bwd_dropout(it["w"], a["X"], a["dY"], it["A"], it["B"], ALPHA, drop,
+                                       T_saved=a["T"], dX=a["dX"], dA=a["dA"], dB=a["dB"],
+                                       workspace=a["wsb"])
 
 
 def timed(fn, steps, warmup):
@@ -233,6 +248,37 @@ def bench_train7b(dev, steps, warmup):
                          avg_launch_ms=(sum(dur_f) + sum(dur_b)) / (len(dur_f) + len(dur_b))))
     log(f"7B fwd+bwd: {res['tflops']:.1f} TFLOP/s ({res['ms_per_step']:.3f} ms/step); "
         f"fused GEMM fwd {ach_f:.1f} bwd {ach_b:.1f} TFLOP/s")
+    del layer, acts
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_dropout7b(dev, steps, warmup, p_drop=0.05):
+    """The headline step with LoRA dropout p = 0.05 (training mode): mask
+    generation in the forward and again in the backward, masked LoRA input,
+    and the masked LoRA term of dX inside the backward GEMM."""
+    M = 4096
+    layer = Layer(inputs.LLAMA_7B, M, 3, 0, dev)
+    acts = Activations(inputs.LLAMA_7B, M, 3, dev, dropout=True)
+    torch.cuda.synchronize()
+    flops = sum(useful_flops(M, d_out, d_in, R) for _, d_out, d_in in inputs.LLAMA_7B)
+    for i in range(warmup):
+        train_step(layer, acts, p_drop=p_drop, step=i)
+    torch.cuda.synchronize()
+    timer = KernelTimer()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        train_step(layer, acts, timer, p_drop=p_drop, step=warmup + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    dur_b = timer.durations_ms("bwd")
+    fl_b = [2 * M * d_in * (d_out + R) for _, d_out, d_in in inputs.LLAMA_7B] * steps
+    res = dict(p=p_drop, tflops=flops * steps / el / 1e12, ms_per_step=el / steps * 1e3,
+               bwd_gemm_avg_us=sum(dur_b) / len(dur_b) * 1e3,
+               bwd_gemm_tflops=sum(fl_b) / (sum(dur_b) * 1e-3) / 1e12)
+    log(f"7B fwd+bwd with LoRA dropout p={p_drop}: {res['tflops']:.1f} TFLOP/s "
+        f"({res['ms_per_step']:.3f} ms/step); masked backward GEMM {res['bwd_gemm_tflops']:.1f} "
+        f"TFLOP/s")
     del layer, acts
     torch.cuda.empty_cache()
     return res
@@ -453,7 +499,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--skip", default="", help="comma list of: decode,quant,merge,adamw,stack65b,cpu")
+    ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,merge,adamw,stack65b,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MB (a plain copy "
@@ -480,6 +526,8 @@ def main():
 
     train = bench_train7b(dev, args.steps, args.warmup)
     extra = {}
+    if "dropout" not in skip:
+        extra["dropout_7b"] = bench_dropout7b(dev, args.steps, args.warmup)
     if "decode" not in skip:
         extra["decode_7b"] = bench_decode7b(dev, args.steps, args.warmup)
     if "quant" not in skip:

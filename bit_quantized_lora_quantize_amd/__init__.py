@@ -7,11 +7,14 @@ plus the seeded synthetic-input generators (inputs.py).
 from ._lib import (  # noqa: F401
     AdamwParam,
     AdamwParamSet,
+    Dropout,
     FwdItem,
     NF4Weight,
     QLORA_MAX_GROUP,
     QLORA_OP_BWD,
+    QLORA_OP_BWD_DROPOUT,
     QLORA_OP_FWD,
+    QLORA_OP_FWD_DROPOUT,
     QLORA_OP_QUANTIZE,
     QloraError,
     header_functions,
@@ -19,10 +22,13 @@ from ._lib import (  # noqa: F401
     qlora_abi_version,
     qlora_adamw_step,
     qlora_dequant_bf16,
+    qlora_dropout_mask,
     qlora_grad_sumsq,
     qlora_sumsq_workspace_bytes,
     qlora_linear_bwd,
+    qlora_linear_bwd_dropout,
     qlora_linear_fwd,
+    qlora_linear_fwd_dropout,
     qlora_linear_fwd_many,
     qlora_merge_nf4,
     qlora_nf4_sizes,

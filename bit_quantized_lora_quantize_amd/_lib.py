@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libqlora.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qlora.h")
 
 QLORA_OP_QUANTIZE, QLORA_OP_FWD, QLORA_OP_BWD = 0, 1, 2
+QLORA_OP_FWD_DROPOUT, QLORA_OP_BWD_DROPOUT = 3, 4
 QLORA_MAX_GROUP = 8
 BLOCK, GROUP = 64, 256
 
@@ -36,6 +37,10 @@ class _FwdItem(ctypes.Structure):
     _fields_ = [("w", _Nf4), ("X", _P), ("A", _P), ("B", _P), ("r", _I64),
                 ("lora_alpha", ctypes.c_float), ("Y", _P), ("T_save", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _Dropout(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_float), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
 
 
 class _AdamwParam(ctypes.Structure):
@@ -83,6 +88,13 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.qlora_time_next_weight_kernel.argtypes = [_P, _P]
+        L.qlora_dropout_mask.argtypes = [_P, _I64, _I64, ctypes.POINTER(_Dropout), _P, _P, _P]
+        L.qlora_linear_fwd_dropout.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
+                                               ctypes.c_float, ctypes.POINTER(_Dropout), _P, _P,
+                                               _P, ctypes.c_size_t, _P]
+        L.qlora_linear_bwd_dropout.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
+                                               ctypes.c_float, ctypes.POINTER(_Dropout), _P, _P,
+                                               _P, _P, _P, ctypes.c_size_t, _P]
         _lib = L
     return _lib
 
@@ -315,10 +327,20 @@ def qlora_adamw_step(params, lr: float, beta1: float = 0.9, beta2: float = 0.999
            "qlora_adamw_step")
 
 
-def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
-                     lora_alpha: float, Y: Optional[torch.Tensor] = None,
-                     T_save: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+@dataclass
+class Dropout:
+    """LoRA dropout of the training-mode forward and its backward: drop
+    probability p, generator key `seed` and counter words `offset` (a new
+    offset per layer and step; the backward passes the same values)."""
+    p: float
+    seed: int
+    offset: int = 0
+
+    def c_struct(self) -> _Dropout:
+        return _Dropout(float(self.p), int(self.seed) & (2**64 - 1), int(self.offset) & (2**64 - 1))
+
+
+def _fwd(q, X, A, B, lora_alpha, Y, T_save, workspace, dropout):
     M = X.shape[0]
     r = A.shape[0]
     _need(X, torch.bfloat16, (M, q.d_in), "X")
@@ -328,13 +350,52 @@ def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     _need(Y, torch.bfloat16, (M, q.d_out), "Y")
     if T_save is not None:
         _need(T_save, torch.float32, (M, r), "T_save")
-    need = qlora_workspace_bytes(QLORA_OP_FWD, q.d_out, q.d_in, M, r)
+    op = QLORA_OP_FWD if dropout is None else QLORA_OP_FWD_DROPOUT
+    need = qlora_workspace_bytes(op, q.d_out, q.d_in, M, r)
     ws = workspace if workspace is not None else _workspace(need, X.device)
     qs = q.c_struct()
-    _check(lib().qlora_linear_fwd(ctypes.byref(qs), _ptr(X), M, _ptr(A), _ptr(B), r,
-                                  float(lora_alpha), _ptr(Y), _ptr(T_save), _ptr(ws), ws.numel(),
-                                  _stream(X.device)), "qlora_linear_fwd")
+    if dropout is None:
+        _check(lib().qlora_linear_fwd(ctypes.byref(qs), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                      float(lora_alpha), _ptr(Y), _ptr(T_save), _ptr(ws),
+                                      ws.numel(), _stream(X.device)), "qlora_linear_fwd")
+    else:
+        ds = dropout.c_struct()
+        _check(lib().qlora_linear_fwd_dropout(ctypes.byref(qs), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                              float(lora_alpha), ctypes.byref(ds), _ptr(Y),
+                                              _ptr(T_save), _ptr(ws), ws.numel(),
+                                              _stream(X.device)), "qlora_linear_fwd_dropout")
     return Y
+
+
+def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                     lora_alpha: float, Y: Optional[torch.Tensor] = None,
+                     T_save: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    return _fwd(q, X, A, B, lora_alpha, Y, T_save, workspace, None)
+
+
+def qlora_linear_fwd_dropout(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             lora_alpha: float, dropout: Dropout,
+                             Y: Optional[torch.Tensor] = None,
+                             T_save: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Training-mode forward: the LoRA branch sees keep * X / (1 - p)."""
+    return _fwd(q, X, A, B, lora_alpha, Y, T_save, workspace, dropout)
+
+
+def qlora_dropout_mask(X: torch.Tensor, dropout: Dropout, X_kept: Optional[torch.Tensor] = None,
+                       keep_bits: Optional[torch.Tensor] = None, want_bits: bool = False):
+    """(X with dropped elements cleared, keep words [d, ceil(M/32)] or None)."""
+    M, d = X.shape
+    _need(X, torch.bfloat16, (M, d), "X")
+    X_kept = X_kept if X_kept is not None else torch.empty_like(X)
+    _need(X_kept, torch.bfloat16, (M, d), "X_kept")
+    if want_bits and keep_bits is None:
+        keep_bits = torch.empty((d, (M + 31) // 32), dtype=torch.int32, device=X.device)
+    ds = dropout.c_struct()
+    _check(lib().qlora_dropout_mask(_ptr(X), M, d, ctypes.byref(ds), _ptr(X_kept),
+                                    _ptr(keep_bits), _stream(X.device)), "qlora_dropout_mask")
+    return X_kept, keep_bits
 
 
 @dataclass
@@ -365,11 +426,7 @@ def qlora_linear_fwd_many(items: Sequence[FwdItem], M: int) -> None:
     _check(lib().qlora_linear_fwd_many(len(items), arr, M, _stream(dev)), "qlora_linear_fwd_many")
 
 
-def qlora_linear_bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
-                     B: torch.Tensor, lora_alpha: float, T_saved: Optional[torch.Tensor] = None,
-                     need_dx: bool = True, dX: Optional[torch.Tensor] = None,
-                     dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None):
+def _bwd(q, X, dY, A, B, lora_alpha, T_saved, need_dx, dX, dA, dB, workspace, dropout):
     M = X.shape[0]
     r = A.shape[0]
     dev = X.device
@@ -383,11 +440,38 @@ def qlora_linear_bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
         dX = torch.empty((M, q.d_in), dtype=torch.bfloat16, device=dev)
     dA = dA if dA is not None else torch.empty((r, q.d_in), dtype=torch.float32, device=dev)
     dB = dB if dB is not None else torch.empty((q.d_out, r), dtype=torch.float32, device=dev)
-    need = qlora_workspace_bytes(QLORA_OP_BWD, q.d_out, q.d_in, M, r)
+    op = QLORA_OP_BWD if dropout is None else QLORA_OP_BWD_DROPOUT
+    need = qlora_workspace_bytes(op, q.d_out, q.d_in, M, r)
     ws = workspace if workspace is not None else _workspace(need, dev)
     qs = q.c_struct()
-    _check(lib().qlora_linear_bwd(ctypes.byref(qs), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r,
-                                  float(lora_alpha), _ptr(T_saved), _ptr(dX if need_dx else None),
-                                  _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream(dev)),
-           "qlora_linear_bwd")
+    if dropout is None:
+        _check(lib().qlora_linear_bwd(ctypes.byref(qs), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B),
+                                      r, float(lora_alpha), _ptr(T_saved),
+                                      _ptr(dX if need_dx else None), _ptr(dA), _ptr(dB),
+                                      _ptr(ws), ws.numel(), _stream(dev)), "qlora_linear_bwd")
+    else:
+        ds = dropout.c_struct()
+        _check(lib().qlora_linear_bwd_dropout(ctypes.byref(qs), _ptr(X), _ptr(dY), M, _ptr(A),
+                                              _ptr(B), r, float(lora_alpha), ctypes.byref(ds),
+                                              _ptr(T_saved), _ptr(dX if need_dx else None),
+                                              _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                              _stream(dev)), "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB
+
+
+def qlora_linear_bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                     B: torch.Tensor, lora_alpha: float, T_saved: Optional[torch.Tensor] = None,
+                     need_dx: bool = True, dX: Optional[torch.Tensor] = None,
+                     dA: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    return _bwd(q, X, dY, A, B, lora_alpha, T_saved, need_dx, dX, dA, dB, workspace, None)
+
+
+def qlora_linear_bwd_dropout(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
+                             B: torch.Tensor, lora_alpha: float, dropout: Dropout,
+                             T_saved: Optional[torch.Tensor] = None, need_dx: bool = True,
+                             dX: Optional[torch.Tensor] = None, dA: Optional[torch.Tensor] = None,
+                             dB: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None):
+    """Backward of qlora_linear_fwd_dropout (same X and dropout)."""
+    return _bwd(q, X, dY, A, B, lora_alpha, T_saved, need_dx, dX, dA, dB, workspace, dropout)

@@ -213,6 +213,40 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   return p;
 }
 
+// LoRA dropout buffers, after the region of the plan they extend: the
+// masked LoRA input [M][d_in] and (backward) the keep words [d_in][ldw].
+struct DropPlan {
+  uint16_t* xm;
+  uint32_t* keep;
+  int64_t ldw;
+  size_t bytes;
+};
+
+DropPlan plan_drop(size_t base_bytes, int64_t M, int64_t d_in, bool with_bits, void* ws) {
+  DropPlan d{};
+  Carver c(ws);
+  c.off = base_bytes;
+  d.xm = c.take<uint16_t>(M * d_in);
+  d.ldw = cdiv(std::max<int64_t>(M, 1), 32);
+  if (with_bits) d.keep = c.take<uint32_t>(d_in * d.ldw);
+  d.bytes = c.off + 256;
+  return d;
+}
+
+// Generator parameters of a dropout request; QLORA_ERR_SHAPE unless
+// 0 <= p < 1.  thr = floor(p 2^32) (exact in FP64).
+int dropout_params(const qlora_dropout_t* drop, DropoutArgs* a) {
+  if (!drop) return QLORA_ERR_NULL;
+  if (!(drop->p >= 0.0f && drop->p < 1.0f)) return QLORA_ERR_SHAPE;
+  *a = DropoutArgs{};
+  a->thr = (uint32_t)std::floor((double)drop->p * 4294967296.0);
+  a->key_lo = (uint32_t)drop->seed;
+  a->key_hi = (uint32_t)(drop->seed >> 32);
+  a->off_lo = (uint32_t)drop->offset;
+  a->off_hi = (uint32_t)(drop->offset >> 32);
+  return QLORA_OK;
+}
+
 // ------------------------------------------------ nearest-level table
 // Decision thresholds between adjacent NF4 levels: t_i is the smallest FP32
 // value above the exact midpoint, so x >= t_i <=> x > midpoint, and a value
@@ -277,6 +311,8 @@ struct FwdItemArgs {
   float* T_save;
   void* ws;
   size_t ws_bytes;
+  const uint16_t* XA;  // LoRA branch input: X, or X after dropout
+  float sc;            // LoRA scale: alpha / r, or alpha / r / (1 - p)
 };
 
 // Descriptors of the small-M forward for a group: T into T_save (or the
@@ -301,6 +337,7 @@ int64_t small_gemv_args(const FwdItemArgs* items, int count, int64_t M, GemvArgs
     d.scale2 = q->scale2;
     d.mean = q->scale_mean;
     d.X = f.X;
+    d.XA = f.XA;
     d.A = f.A;
     d.B = f.B;
     d.t_buf = f.T_save ? f.T_save : p.t_buf;
@@ -309,7 +346,7 @@ int64_t small_gemv_args(const FwdItemArgs* items, int count, int64_t M, GemvArgs
     d.d_out = q->d_out;
     d.d_in = q->d_in;
     d.r = f.r;
-    d.t_scale = f.alpha / (float)f.r;
+    d.t_scale = f.sc;
     d.ksplit = gs.ksplit;
     d.ss_per_split = gs.ss_per;
     d.tiles = gs.tiles;
@@ -356,7 +393,7 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       const qlora_nf4_t* q = f.q;
       FwdPlan p = plan_fwd(q->d_out, q->d_in, M, f.r, f.ws);
       float* T = f.T_save ? f.T_save : p.t_buf;
-      RankRowsArgs ra{f.X,    f.A,     M,       f.r,     q->d_in, q->d_in, f.alpha / (float)f.r,
+      RankRowsArgs ra{f.XA,   f.A,     M,       f.r,     q->d_in, q->d_in, f.sc,
                       T,      p.t_hl,  p.rp,    nullptr, nullptr, 0};
       int s = rank_product(ra, p.r_part, st);
       if (s) return s;
@@ -374,6 +411,97 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
   int gwgs = 0, fwgs = 0;
   small_gemv_args(items, count, M, &ga, &gwgs, &fwgs);
   return hip_status(launch_gemv(ga, gwgs, fwgs, st));
+}
+
+// Argument checks shared by both backward entry points.
+int check_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY, int64_t M,
+              const uint16_t* A, const uint16_t* B, int64_t r, const float* T_saved,
+              const uint16_t* dX, const float* dA, const float* dB, const void* ws) {
+  int s = check_nf4(q);
+  if (s) return s;
+  if (M < 0 || M > kMaxTokens || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
+  if (q->d_out > kMaxLinearDim || q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
+  if (!dA || !dB || !ws) return QLORA_ERR_NULL;
+  if (M > 0 && (!X || !dY || !A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(T_saved) ||
+      !aligned16(dX) || !aligned16(dA) || !aligned16(dB) || !aligned16(ws))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+// The backward after the checks.  XA is the LoRA branch's input (X, or X
+// after dropout), sc the LoRA scale, keep the dropout keep words of the
+// input gradient's LoRA term (NULL: none).
+int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
+             int64_t keep_ld, const uint16_t* dY, int64_t M, const uint16_t* A,
+             const uint16_t* B, int64_t r, float sc, const float* T_saved, uint16_t* dX,
+             float* dA, float* dB, const BwdPlan& p, hipStream_t st) {
+  int s = QLORA_OK;
+  const int64_t d_out = q->d_out, d_in = q->d_in;
+  if (M == 0) {
+    s = hip_status(hipMemsetAsync(dA, 0, size_t(r * d_in) * sizeof(float), st));
+    if (!s) s = hip_status(hipMemsetAsync(dB, 0, size_t(d_out * r) * sizeof(float), st));
+    return s;
+  }
+  // T = s XA A^T (unless saved by the forward), and its transposed hi/lo copy
+  // (the same kernels and summation order as the forward, so a recomputed T
+  // equals a saved one bit for bit)
+  const float* T = T_saved;
+  if (!T && M > kSmallM) {
+    RankRowsArgs ra{XA, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
+    s = rank_product(ra, p.r_part, st);
+    if (s) return s;
+    T = p.t_buf;
+  } else {
+    if (!T) {
+      GemvArgs ga{};
+      ga.count = 1;
+      ga.M = (int)M;
+      ga.t_wgs = (int)cdiv(r, 16);
+      GemvDesc& d = ga.d[0];
+      d.X = XA;
+      d.XA = XA;
+      d.A = A;
+      d.t_buf = p.t_buf;
+      d.d_in = d_in;
+      d.d_out = d_out;
+      d.r = r;
+      d.t_scale = sc;
+      s = hip_status(launch_lora_down(ga, st));
+      if (s) return s;
+      T = p.t_buf;
+    }
+    s = hip_status(M > kSmallM
+                       ? launch_rank_finish_rows(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo,
+                                                 p.ldp, nullptr, 0, st)
+                       : launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
+                                            nullptr, 0, st));
+    if (s) return s;
+  }
+  // U = s dY B, through B^T so the contraction over d_out is contiguous
+  s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
+  if (s) return s;
+  {
+    RankRowsArgs ra{dY, p.bt, M, r, d_out, p.ldbt, sc, nullptr, p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
+    s = rank_product(ra, p.r_part, st);
+  }
+  if (s) return s;
+  // dX = dY Wh + U A (the U A term cleared at dropped positions)
+  if (dX) {
+    GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, dY, p.u_hl, A, dX,
+               M,        d_out,          d_in,      r,            keep, keep_ld};
+    s = hip_status(launch_gemm_bwd(g, st));
+    if (s) return s;
+  }
+  // dA = U^T XA ; dB = (T^T dY)^T
+  s = hip_status(launch_gram(p.ut_hi, p.ut_lo, p.ldp, XA, M, r, d_in, p.mper_a, p.ms_a,
+                             p.da_part, st));
+  if (!s) s = hip_status(launch_gram_finish(p.da_part, p.ms_a, r, d_in, false, dA, st));
+  if (!s)
+    s = hip_status(launch_gram(p.tt_hi, p.tt_lo, p.ldp, dY, M, r, d_out, p.mper_b, p.ms_b,
+                               p.db_part, st));
+  if (!s) s = hip_status(launch_gram_finish(p.db_part, p.ms_b, r, d_out, true, dB, st));
+  return s;
 }
 
 }  // namespace
@@ -421,6 +549,10 @@ size_t qlora_workspace_bytes(int op, int64_t d_out, int64_t d_in, int64_t M, int
   if (M < 0 || r < 1 || r > kMaxRank) return 0;
   if (op == QLORA_OP_FWD) return plan_fwd(d_out, d_in, M, r, nullptr).bytes;
   if (op == QLORA_OP_BWD) return plan_bwd(d_out, d_in, M, r, nullptr).bytes;
+  if (op == QLORA_OP_FWD_DROPOUT)
+    return plan_drop(plan_fwd(d_out, d_in, M, r, nullptr).bytes, M, d_in, false, nullptr).bytes;
+  if (op == QLORA_OP_BWD_DROPOUT)
+    return plan_drop(plan_bwd(d_out, d_in, M, r, nullptr).bytes, M, d_in, true, nullptr).bytes;
   return 0;
 }
 
@@ -549,7 +681,7 @@ int qlora_merge_nf4(const qlora_nf4_t* q, const uint16_t* A, const uint16_t* B, 
 int qlora_linear_fwd(const qlora_nf4_t* q, const uint16_t* X, int64_t M, const uint16_t* A,
                      const uint16_t* B, int64_t r, float lora_alpha, uint16_t* Y, float* T_save,
                      void* ws, size_t ws_bytes, void* stream) {
-  FwdItemArgs f{q, X, A, B, r, lora_alpha, Y, T_save, ws, ws_bytes};
+  FwdItemArgs f{q, X, A, B, r, lora_alpha, Y, T_save, ws, ws_bytes, X, lora_alpha / (float)r};
   return fwd_group(&f, 1, M, static_cast<hipStream_t>(stream));
 }
 
@@ -560,7 +692,8 @@ int qlora_linear_fwd_many(int count, const qlora_fwd_item* items, int64_t M, voi
   for (int i = 0; i < count; ++i) {
     const qlora_fwd_item& it = items[i];
     f[i] = FwdItemArgs{&it.w, it.X, it.A, it.B, it.r, it.lora_alpha, it.Y, it.T_save,
-                       it.workspace, it.workspace_bytes};
+                       it.workspace, it.workspace_bytes, it.X,
+                       it.r > 0 ? it.lora_alpha / (float)it.r : 0.0f};
   }
   return fwd_group(f, count, M, static_cast<hipStream_t>(stream));
 }
@@ -569,83 +702,87 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
                      const uint16_t* A, const uint16_t* B, int64_t r, float lora_alpha,
                      const float* T_saved, uint16_t* dX, float* dA, float* dB, void* ws,
                      size_t ws_bytes, void* stream) {
-  int s = check_nf4(q);
+  int s = check_bwd(q, X, dY, M, A, B, r, T_saved, dX, dA, dB, ws);
   if (s) return s;
-  if (M < 0 || M > kMaxTokens || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
-  if (q->d_out > kMaxLinearDim || q->d_in > kMaxLinearDim) return QLORA_ERR_SHAPE;
-  if (!dA || !dB || !ws) return QLORA_ERR_NULL;
-  if (M > 0 && (!X || !dY || !A || !B)) return QLORA_ERR_NULL;
-  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || !aligned16(T_saved) ||
-      !aligned16(dX) || !aligned16(dA) || !aligned16(dB) || !aligned16(ws))
-    return QLORA_ERR_ALIGN;
-  const int64_t d_out = q->d_out, d_in = q->d_in;
-  BwdPlan p = plan_bwd(d_out, d_in, M, r, ws);
+  const BwdPlan p = plan_bwd(q->d_out, q->d_in, M, r, ws);
   if (ws_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
+  return bwd_impl(q, X, nullptr, 0, dY, M, A, B, r, lora_alpha / (float)r, T_saved, dX, dA,
+                  dB, p, static_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_t* q, const uint16_t* X, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int64_t r, float lora_alpha,
+                             const qlora_dropout_t* drop, uint16_t* Y, float* T_save, void* ws,
+                             size_t ws_bytes, void* stream) {
+  DropoutArgs da;
+  int s = dropout_params(drop, &da);
+  if (s) return s;
+  FwdItemArgs f{q, X, A, B, r, lora_alpha, Y, T_save, ws, ws_bytes, X, 0.0f};
+  s = check_fwd_item(f, M);
+  if (s) return s;
+  if (M == 0) return QLORA_OK;
+  const int64_t d_in = q->d_in;
+  const DropPlan dp = plan_drop(plan_fwd(q->d_out, d_in, M, r, nullptr).bytes, M, d_in, false, ws);
+  if (ws_bytes < dp.bytes) return QLORA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (M == 0) {
-    s = hip_status(hipMemsetAsync(dA, 0, size_t(r * d_in) * sizeof(float), st));
-    if (!s) s = hip_status(hipMemsetAsync(dB, 0, size_t(d_out * r) * sizeof(float), st));
-    return s;
-  }
-  const float sc = lora_alpha / (float)r;
-  // T = s X A^T (unless saved by the forward), and its transposed hi/lo copy
-  // (the same kernels and summation order as the forward, so a recomputed T
-  // equals a saved one bit for bit)
-  const float* T = T_saved;
-  if (!T && M > kSmallM) {
-    RankRowsArgs ra{X, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
-    s = rank_product(ra, p.r_part, st);
-    if (s) return s;
-    T = p.t_buf;
-  } else {
-    if (!T) {
-      GemvArgs ga{};
-      ga.count = 1;
-      ga.M = (int)M;
-      ga.t_wgs = (int)cdiv(r, 16);
-      GemvDesc& d = ga.d[0];
-      d.X = X;
-      d.A = A;
-      d.t_buf = p.t_buf;
-      d.d_in = d_in;
-      d.d_out = d_out;
-      d.r = r;
-      d.t_scale = sc;
-      s = hip_status(launch_lora_down(ga, st));
-      if (s) return s;
-      T = p.t_buf;
-    }
-    s = hip_status(M > kSmallM
-                       ? launch_rank_finish_rows(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo,
-                                                 p.ldp, nullptr, 0, st)
-                       : launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
-                                            nullptr, 0, st));
-    if (s) return s;
-  }
-  // U = s dY B, through B^T so the contraction over d_out is contiguous
-  s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
+  da.X = X;
+  da.Xm = dp.xm;
+  da.M = M;
+  da.d = d_in;
+  da.ldw = dp.ldw;
+  s = hip_status(launch_dropout(da, st));
   if (s) return s;
-  {
-    RankRowsArgs ra{dY, p.bt, M, r, d_out, p.ldbt, sc, nullptr, p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
-    s = rank_product(ra, p.r_part, st);
-  }
+  f.XA = dp.xm;
+  f.sc = (lora_alpha / (float)r) / (1.0f - drop->p);
+  return fwd_group(&f, 1, M, st);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int64_t r,
+                             float lora_alpha, const qlora_dropout_t* drop, const float* T_saved,
+                             uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                             void* stream) {
+  DropoutArgs da;
+  int s = dropout_params(drop, &da);
   if (s) return s;
-  // dX = dY Wh + U A
-  if (dX) {
-    GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, dY, p.u_hl, A, dX,
-               M,        d_out,          d_in,      r};
-    s = hip_status(launch_gemm_bwd(g, st));
+  s = check_bwd(q, X, dY, M, A, B, r, T_saved, dX, dA, dB, ws);
+  if (s) return s;
+  const int64_t d_in = q->d_in;
+  const BwdPlan p = plan_bwd(q->d_out, d_in, M, r, ws);
+  const DropPlan dp = plan_drop(p.bytes, M, d_in, true, ws);
+  if (ws_bytes < dp.bytes) return QLORA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M > 0) {
+    da.X = X;
+    da.Xm = dp.xm;
+    da.keep = dp.keep;
+    da.M = M;
+    da.d = d_in;
+    da.ldw = dp.ldw;
+    s = hip_status(launch_dropout(da, st));
     if (s) return s;
   }
-  // dA = U^T X ; dB = (T^T dY)^T
-  s = hip_status(launch_gram(p.ut_hi, p.ut_lo, p.ldp, X, M, r, d_in, p.mper_a, p.ms_a,
-                             p.da_part, st));
-  if (!s) s = hip_status(launch_gram_finish(p.da_part, p.ms_a, r, d_in, false, dA, st));
-  if (!s)
-    s = hip_status(launch_gram(p.tt_hi, p.tt_lo, p.ldp, dY, M, r, d_out, p.mper_b, p.ms_b,
-                               p.db_part, st));
-  if (!s) s = hip_status(launch_gram_finish(p.db_part, p.ms_b, r, d_out, true, dB, st));
-  return s;
+  return bwd_impl(q, dp.xm, dp.keep, dp.ldw, dY, M, A, B, r,
+                  (lora_alpha / (float)r) / (1.0f - drop->p), T_saved, dX, dA, dB, p, st);
+}
+
+int qlora_dropout_mask(const uint16_t* X, int64_t M, int64_t d, const qlora_dropout_t* drop,
+                       uint16_t* X_kept, uint32_t* keep_bits, void* stream) {
+  DropoutArgs da;
+  int s = dropout_params(drop, &da);
+  if (s) return s;
+  if (M < 0 || M > kMaxTokens || d < 0 || d > kMaxLinearDim || d % 8) return QLORA_ERR_SHAPE;
+  if (M == 0 || d == 0) return QLORA_OK;
+  if (!X_kept && !keep_bits) return QLORA_ERR_NULL;
+  if (X_kept && !X) return QLORA_ERR_NULL;
+  if (!aligned16(X) || !aligned16(X_kept) || !aligned16(keep_bits)) return QLORA_ERR_ALIGN;
+  da.X = X;
+  da.Xm = X_kept;
+  da.keep = keep_bits;
+  da.M = M;
+  da.d = d;
+  da.ldw = cdiv(M, 32);
+  return hip_status(launch_dropout(da, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

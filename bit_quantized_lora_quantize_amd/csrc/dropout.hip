@@ -1,0 +1,111 @@
+// dropout.hip -- the LoRA branch's dropout mask (gfx950).
+//
+// [QP] "第 04 篇：QLoRA 原理" §6.3: in training mode the LoRA branch takes
+// D(x) instead of x, D an (inverted) dropout on the branch's input; the base
+// branch takes x; inference turns it off.  The 1 / (1 - p) of D is folded
+// into the LoRA scale by the caller, so here a dropped element becomes 0 and
+// a kept one passes unchanged (exact in BF16).
+//
+// The mask comes from a counter-based generator, so the backward regenerates
+// the forward's mask from (seed, offset) with no state in between:
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11).  Element (m, k) of a row-major [M, d] input takes
+// output word m % 4 of the generator at counter (k, m / 4, offset_lo,
+// offset_hi) under key (seed_lo, seed_hi) and is kept when that word is at
+// least thr = floor(p * 2^32).
+//
+// One thread owns two neighbouring columns and 32 rows: eight generator
+// calls per column give the 32 decisions, which become one keep word per
+// column (bit m % 32 of word [k][m / 32], the layout the input-gradient GEMM
+// reads), and the thread's 32 row pairs of X are copied with the dropped
+// elements cleared.  A wavefront spans 64 column pairs, so every X access is
+// a 256-byte row segment.
+#include "qlora_device.h"
+#include "qlora_kernels.h"
+
+namespace qlora {
+
+// One Philox round: (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)), M0 = 0xD2511F53, M1 = 0xCD9E8D57.  Each product is one 32 x 32
+// -> 64-bit multiply (v_mad_u64_u32), not separate high and low multiplies.
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                             uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+  const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+  c0 = n0;
+  c1 = (uint32_t)p1;
+  c2 = n2;
+  c3 = (uint32_t)p0;
+}
+
+// Ten rounds, the key growing by (0x9E3779B9, 0xBB67AE85) between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                              uint32_t& c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    philox_round(c0, c1, c2, c3, k0, k1);
+  }
+}
+
+// Keep bits of column k for rows 32 w .. 32 w + 31 (bit j = row 32 w + j).
+__device__ __forceinline__ uint32_t keep_word(uint32_t k, uint32_t w, const DropoutArgs& a) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t c0 = k, c1 = 8 * w + j, c2 = a.off_lo, c3 = a.off_hi;
+    philox4x32_10(c0, c1, c2, c3, a.key_lo, a.key_hi);
+    bits |= (c0 >= a.thr ? 1u : 0u) << (4 * j);
+    bits |= (c1 >= a.thr ? 1u : 0u) << (4 * j + 1);
+    bits |= (c2 >= a.thr ? 1u : 0u) << (4 * j + 2);
+    bits |= (c3 >= a.thr ? 1u : 0u) << (4 * j + 3);
+  }
+  return bits;
+}
+
+__global__ __launch_bounds__(256) void k_dropout(DropoutArgs a) {
+  const int64_t pairs = a.d / 2;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= pairs * a.ldw) return;
+  const uint32_t w = (uint32_t)(tid / pairs);
+  const uint32_t k = (uint32_t)(2 * (tid - (int64_t)w * pairs));
+  const int64_t m0 = 32 * (int64_t)w;
+  const int rows = a.M - m0 < 32 ? (int)(a.M - m0) : 32;
+  // row pairs of X first, so the loads are in flight during the generator
+  uint32_t x[32];
+  if (a.Xm) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      x[j] = j < rows ? *reinterpret_cast<const uint32_t*>(a.X + (m0 + j) * a.d + k) : 0u;
+  }
+  // rows past M get keep bit 0
+  const uint32_t live = rows == 32 ? 0xFFFFFFFFu : (1u << rows) - 1u;
+  const uint32_t b0 = keep_word(k, w, a) & live;
+  const uint32_t b1 = keep_word(k + 1, w, a) & live;
+  if (a.keep) {
+    a.keep[(int64_t)k * a.ldw + w] = b0;
+    a.keep[(int64_t)(k + 1) * a.ldw + w] = b1;
+  }
+  if (a.Xm) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j >= rows) break;
+      const uint32_t lo = ((b0 >> j) & 1u) ? 0x0000FFFFu : 0u;
+      const uint32_t hi = ((b1 >> j) & 1u) ? 0xFFFF0000u : 0u;
+      *reinterpret_cast<uint32_t*>(a.Xm + (m0 + j) * a.d + k) = x[j] & (lo | hi);
+    }
+  }
+}
+
+hipError_t launch_dropout(const DropoutArgs& a, hipStream_t st) {
+  const int64_t threads = (a.d / 2) * a.ldw;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dropout, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

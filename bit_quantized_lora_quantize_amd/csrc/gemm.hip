@@ -37,6 +37,9 @@
 //        the result is stored.
 // LoRA term: extra K steps over [hi(0..RP) | lo(0..RP)], RP = r rounded up
 // to 32, from the rank-r activations split into two BF16 terms beforehand.
+// They run before the weight steps, so with LoRA dropout ([QP §6.3]) the
+// backward clears the dropped positions of that term in the accumulators
+// before the base term is added.
 //
 // Workgroup order: consecutive workgroup ids are spread over the 8 XCDs, so
 // ids are remapped for each XCD to own a contiguous run of output tiles
@@ -366,7 +369,7 @@ __device__ __forceinline__ void ext_store(const Tile& t, const ExtStage& E, uint
     *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) = BWD ? perm8_bf16(E.b[j]) : E.b[j];
 }
 
-template <bool BWD, bool VEC>
+template <bool BWD, bool VEC, bool DROP>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -460,6 +463,32 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     }
     __syncthreads();
   }
+  if constexpr (DROP) {
+    // LoRA dropout (backward): the accumulators hold the LoRA term alone
+    // here; clear it at dropped (token, input) positions.  One keep word per
+    // 32 x 32 tile: rows 32 i .. +32 of the wavefront's 128 (bit = row in
+    // the tile, 8 (v / 4) + 4 h + v % 4 for element v) at the lane's column
+    // 32 j + (permuted lane column).
+    const int cj = (r32 & ~7) | (2 * (r32 & 3) + ((r32 >> 2) & 1));
+    uint32_t kw[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t m = t.m0 + 128 * wm + 32 * i;
+        const int64_t c = t.n0 + 128 * wn + 32 * j + cj;
+        kw[i][j] = (m < p.M && c < t.NOUT) ? p.keep[c * p.keep_ld + m / 32] : 0u;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t bit = (kw[i][j] >> (8 * (v >> 2) + 4 * h + (v & 3))) & 1u;
+          acc[i][j][v] = bit ? acc[i][j][v] : 0.0f;
+        }
+  }
   // weights: steps 0 and 1 restored, 2 and 3 in flight
   restore_act<BWD>(t, 0, g0, b0, lane);
   restore_w<BWD>(t, 0, g0, tab, true, b0);
@@ -535,26 +564,30 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
 }
 
-template <bool BWD, bool VEC>
+template <bool BWD, bool VEC, bool DROP>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<BWD, VEC>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      lds_bytes<BWD>());
+      reinterpret_cast<const void*>(&k_gemm<BWD, VEC, DROP>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BWD>());
   if (attr != hipSuccess) return attr;
   const int64_t NOUT = BWD ? a.d_in : a.d_out;
   const int64_t tiles = ((NOUT + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   weight_kernel_begin(st);
-  hipLaunchKernelGGL((k_gemm<BWD, VEC>), dim3((unsigned)tiles), dim3(256), lds_bytes<BWD>(), st, a);
+  hipLaunchKernelGGL((k_gemm<BWD, VEC, DROP>), dim3((unsigned)tiles), dim3(256), lds_bytes<BWD>(),
+                     st, a);
   weight_kernel_end(st);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) {
-  return launch_gemm<false, true>(a, st);
+  return launch_gemm<false, true, false>(a, st);
 }
 hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
   // dY rows are 16-byte aligned exactly when d_out % 8 == 0
-  return (a.d_out % 8) == 0 ? launch_gemm<true, true>(a, st) : launch_gemm<true, false>(a, st);
+  const bool vec = (a.d_out % 8) == 0;
+  if (a.keep)
+    return vec ? launch_gemm<true, true, true>(a, st) : launch_gemm<true, false, true>(a, st);
+  return vec ? launch_gemm<true, true, false>(a, st) : launch_gemm<true, false, false>(a, st);
 }
 
 }  // namespace qlora

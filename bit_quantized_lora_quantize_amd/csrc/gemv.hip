@@ -140,7 +140,7 @@ __device__ __forceinline__ void lora_down_block(const GemvDesc& d, int M, int b,
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const uint32_t din = (uint32_t)d.d_in;
-  const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(d.X, (int64_t)M * d.d_in * 2);   // rows past M: zero
+  const __amdgpu_buffer_rsrc_t rx = gemv_rsrc(d.XA, (int64_t)M * d.d_in * 2);  // rows past M: zero
   const __amdgpu_buffer_rsrc_t ra = gemv_rsrc(d.A, d.r * d.d_in * 2);          // rows past r: zero
   const uint32_t xrow = (uint32_t)r16 * din, arow = (uint32_t)(16 * b + r16) * din;
   const int nss = (int)((d.d_in / kBlock + 3) / 4);

@@ -181,6 +181,19 @@ struct AdamwScalars {
 hipError_t launch_adamw(const AdamwDesc* d, int count, const AdamwScalars& h,
                         const double* sumsq, hipStream_t st);
 
+// ------------------------------------------------- LoRA dropout mask
+// Xm = X with the dropped elements cleared (may be NULL) and the keep bits
+// keep[k * ldw + m / 32] (may be NULL); d even, X rows 4-byte aligned.
+struct DropoutArgs {
+  const uint16_t* X;
+  uint16_t* Xm;
+  uint32_t* keep;
+  int64_t M, d, ldw;      // ldw = ceil(M / 32)
+  uint32_t thr;           // keep when the generator word >= thr
+  uint32_t key_lo, key_hi, off_lo, off_hi;
+};
+hipError_t launch_dropout(const DropoutArgs& a, hipStream_t st);
+
 // ------------------------------------------------- LoRA merge
 // out[n][k] = RN_fp32(Wh[n][k] + scale * sum_i B[n][i] A[i][k]) (FP64
 // evaluation), Wh the restored BF16 weight of the quantized state.
@@ -217,6 +230,8 @@ struct GemvDesc {
   const float* scale2;
   const float* mean;
   const uint16_t* X;      // [M][d_in], 16-byte aligned
+  const uint16_t* XA;     // LoRA branch input [M][d_in] (X, or X with dropped
+                          // elements cleared), 16-byte aligned
   const uint16_t* A;      // [r][d_in], 16-byte aligned
   const uint16_t* B;      // [d_out][r]
   float* t_buf;           // T FP32 [M][r], 16-byte aligned
@@ -263,6 +278,10 @@ struct GemmArgs {
   const uint16_t* lw;     // B [d_out][r] (forward) or A [r][d_in] (backward)
   uint16_t* out;          // Y [M][d_out] or dX [M][d_in]
   int64_t M, d_out, d_in, r;
+  // backward with LoRA dropout: keep bit of (m, c) is bit m % 32 of
+  // keep[c * keep_ld + m / 32]; the LoRA term of dX is cleared where it is 0
+  const uint32_t* keep;
+  int64_t keep_ld;
 };
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st);

@@ -85,6 +85,8 @@ int qlora_nf4_sizes(int64_t d_out, int64_t d_in, size_t *codes_bytes,
 #define QLORA_OP_QUANTIZE 0
 #define QLORA_OP_FWD 1
 #define QLORA_OP_BWD 2
+#define QLORA_OP_FWD_DROPOUT 3
+#define QLORA_OP_BWD_DROPOUT 4
 
 /* Device workspace (bytes) that one call of `op` needs for these sizes
  * (M and r are ignored for QLORA_OP_QUANTIZE).  Host only.  Returns 0 for
@@ -223,6 +225,70 @@ typedef struct {
 
 int qlora_linear_fwd_many(int count, const qlora_fwd_item *items, int64_t M,
                           void *stream);
+
+/*
+ * LoRA dropout in training mode ([QP §6.3]: the LoRA branch takes D(x)
+ * instead of x, the base branch x; inference has no dropout):
+ *     D(X) = keep * X / (1 - p),
+ * keep drawn per element of X [M, d_in] from a counter-based generator, so
+ * the backward regenerates the forward's mask from the same parameters:
+ * element (m, k) takes output word m % 4 of Philox4x32-10 (Salmon, Moraes,
+ * Dror, Shaw, SC'11) at counter (k, floor(m / 4), offset_lo, offset_hi)
+ * under key (seed_lo, seed_hi), and is kept when that word is at least
+ * floor(p * 2^32).  Use a new offset (or seed) for every layer and step.
+ */
+typedef struct {
+  float p;          /* drop probability, 0 <= p < 1 (else QLORA_ERR_SHAPE) */
+  uint64_t seed;    /* generator key                                       */
+  uint64_t offset;  /* counter words 2 and 3                               */
+} qlora_dropout_t;
+
+/*
+ * The mask alone: X_kept = X with the dropped elements set to +0 (kept ones
+ * unchanged; the 1 / (1 - p) is not applied) and, if keep_bits is not NULL,
+ * keep_bits[k * ceil(M/32) + m/32] bit (m % 32) = keep of element (m, k)
+ * (bits of rows m >= M are 0).
+ *   X, X_kept  BF16 [M, d] (16B), d % 8 == 0, d <= 2^21, M <= 2^21;
+ *   X_kept or keep_bits may be NULL (not both; X may be NULL without X_kept).
+ */
+int qlora_dropout_mask(const uint16_t *X, int64_t M, int64_t d,
+                       const qlora_dropout_t *drop, uint16_t *X_kept,
+                       uint32_t *keep_bits, void *stream);
+
+/*
+ * qlora_linear_fwd with LoRA dropout:
+ *     Y = X Wh^T + s (D(X) A^T) B^T,   T = s D(X) A^T (saved in T_save).
+ * The kernels form keep * X (exact) and fold 1 / (1 - p) into the scale:
+ * s' = FP32(FP32(lora_alpha / r) / FP32(1 - p)).  With p = 0 the results
+ * equal qlora_linear_fwd's bit for bit.  Same arguments and limits as
+ * qlora_linear_fwd, plus `drop` (host pointer, not NULL); workspace (16B) >=
+ * qlora_workspace_bytes(QLORA_OP_FWD_DROPOUT, d_out, d_in, M, r).
+ */
+int qlora_linear_fwd_dropout(const qlora_nf4_t *q, const uint16_t *X,
+                             int64_t M, const uint16_t *A, const uint16_t *B,
+                             int64_t r, float lora_alpha,
+                             const qlora_dropout_t *drop, uint16_t *Y,
+                             float *T_save, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of qlora_linear_fwd_dropout for the same X and `drop` (the mask
+ * is regenerated, not stored):
+ *     U  = s dY B
+ *     dX = dY Wh + keep * (U A) / (1 - p)
+ *     dA = U^T D(X),   dB = dY^T T   with T = s D(X) A^T.
+ * Arguments and limits as qlora_linear_bwd, plus `drop`; T_saved (if given)
+ * must come from qlora_linear_fwd_dropout with the same `drop`; workspace
+ * (16B) >= qlora_workspace_bytes(QLORA_OP_BWD_DROPOUT, d_out, d_in, M, r).
+ * With p = 0 the results equal qlora_linear_bwd's bit for bit.
+ */
+int qlora_linear_bwd_dropout(const qlora_nf4_t *q, const uint16_t *X,
+                             const uint16_t *dY, int64_t M, const uint16_t *A,
+                             const uint16_t *B, int64_t r, float lora_alpha,
+                             const qlora_dropout_t *drop, const float *T_saved,
+                             uint16_t *dX, float *dA, float *dB,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * Optimizer step on the LoRA factors ([QP §7.3]: AdamW with one first and

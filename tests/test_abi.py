@@ -196,3 +196,40 @@ def test_optimizer_argument_errors(L):
     assert g(2, good, acc, ws, need - 1, None) == EWS
     assert g(1, nograd, acc, ws, need, None) == ENULL
     assert g(1, neg, acc, ws, need, None) == ESHAPE
+
+
+def test_dropout_argument_errors(L):
+    P = ctypes.c_void_p
+    D = _lib._Dropout
+    ok, bad_hi, bad_neg = D(0.1, 1, 2), D(1.0, 1, 2), D(-0.1, 1, 2)
+    X, Xk, bits = P(0x10000), P(0x20000), P(0x30000)
+    f = L.qlora_dropout_mask
+    assert f(X, 0, 64, ctypes.byref(ok), Xk, None, None) == OK     # nothing to do
+    assert f(X, 4, 64, None, Xk, None, None) == ENULL
+    assert f(X, 4, 64, ctypes.byref(bad_hi), Xk, None, None) == ESHAPE
+    assert f(X, 4, 64, ctypes.byref(bad_neg), Xk, None, None) == ESHAPE
+    assert f(X, 4, 60, ctypes.byref(ok), Xk, None, None) == ESHAPE  # d % 8
+    assert f(X, 4, 64, ctypes.byref(ok), None, None, None) == ENULL
+    assert f(None, 4, 64, ctypes.byref(ok), Xk, None, None) == ENULL
+    assert f(X, 4, 64, ctypes.byref(ok), P(0x20004), None, None) == EALIGN
+    assert f(X, (1 << 21) + 1, 64, ctypes.byref(ok), Xk, bits, None) == ESHAPE
+    w = _nf4(128, 64)
+    A, B, Y, ws = P(0x60000), P(0x70000), P(0x80000), P(0x90000)
+    fw = L.qlora_linear_fwd_dropout
+    assert fw(ctypes.byref(w), X, 4, A, B, 8, 16.0, None, Y, None, ws, 1 << 30, None) == ENULL
+    assert fw(ctypes.byref(w), X, 4, A, B, 8, 16.0, ctypes.byref(bad_hi), Y, None, ws, 1 << 30,
+              None) == ESHAPE
+    need = q.qlora_workspace_bytes(q.QLORA_OP_FWD_DROPOUT, 128, 64, 4, 8)
+    assert need > q.qlora_workspace_bytes(q.QLORA_OP_FWD, 128, 64, 4, 8)
+    assert fw(ctypes.byref(w), X, 4, A, B, 8, 16.0, ctypes.byref(ok), Y, None, ws, need - 1,
+              None) == EWS
+    bw = L.qlora_linear_bwd_dropout
+    dA, dB = P(0xA0000), P(0xB0000)
+    needb = q.qlora_workspace_bytes(q.QLORA_OP_BWD_DROPOUT, 128, 64, 40, 8)
+    assert needb > q.qlora_workspace_bytes(q.QLORA_OP_BWD, 128, 64, 40, 8) + 40 * 64 * 2
+    assert bw(ctypes.byref(w), X, X, 40, A, B, 8, 16.0, None, None, None, dA, dB, ws, needb,
+              None) == ENULL
+    assert bw(ctypes.byref(w), X, X, 40, A, B, 8, 16.0, ctypes.byref(ok), None, None, dA, dB, ws,
+              needb - 1, None) == EWS
+    assert bw(ctypes.byref(w), X, X, 40, A, B, 0, 16.0, ctypes.byref(ok), None, None, dA, dB, ws,
+              needb, None) == ESHAPE
