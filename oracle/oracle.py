@@ -57,6 +57,12 @@ def _load():
         lib.orc_scale_mean.argtypes = [P, I]
         lib.orc_scale_mean.restype = ctypes.c_float
         lib.orc_quantize_nf4.argtypes = [P, I, P, P, P, P, P]
+        lib.orc_quantize_nf4_blocked.argtypes = [P, I, I, I, P, P, P, P, P]
+        lib.orc_dequant_bf16_blocked.argtypes = [P, P, P, ctypes.c_float, I, I, I, P]
+        lib.orc_scale_mean_g.argtypes = [P, I, I]
+        lib.orc_scale_mean_g.restype = ctypes.c_float
+        lib.orc_restored_scale_g.argtypes = [P, P, ctypes.c_float, I, I]
+        lib.orc_restored_scale_g.restype = ctypes.c_float
         lib.orc_restored_scale.argtypes = [P, P, ctypes.c_float, I]
         lib.orc_restored_scale.restype = ctypes.c_float
         lib.orc_dequant_bf16.argtypes = [P, P, P, ctypes.c_float, I, P]
@@ -157,6 +163,50 @@ def quantize_nf4(W: np.ndarray, return_absmax: bool = False):
                              _ptr(mean), _ptr(absmax))
     out = (codes, scodes, s2, float(mean[0]))
     return out + (absmax,) if return_absmax else out
+
+
+def quantize_nf4_blocked(W: np.ndarray, block: int, group: int, return_absmax: bool = False):
+    """NF4 + double quantization of n = W.size values (flattened) with
+    first-level blocks of `block` and second-level groups of `group` scales;
+    a short last block or group is allowed.  [QP §5.5]
+
+    Returns (codes uint8[ceil(n/2)], scale_codes uint8[n1], s2 float32[G], mean)."""
+    W = _c(W, np.float32).ravel()
+    n = W.size
+    n1 = -(-n // block)
+    G = -(-n1 // group)
+    codes = np.empty((n + 1) // 2, np.uint8)
+    scodes = np.empty(n1, np.uint8)
+    s2 = np.empty(G, np.float32)
+    mean = np.zeros(1, np.float32)
+    absmax = np.empty(n1, np.float32)
+    _load().orc_quantize_nf4_blocked(_ptr(W), n, block, group, _ptr(codes), _ptr(scodes),
+                                     _ptr(s2), _ptr(mean), _ptr(absmax))
+    out = (codes, scodes, s2, float(mean[0]))
+    return out + (absmax,) if return_absmax else out
+
+
+def dequant_bf16_blocked(codes, scodes, s2, mean: float, n: int, block: int,
+                         group: int) -> np.ndarray:
+    """Restored weights (BF16 bit patterns, uint16[n]) of the blocked format."""
+    codes = _c(codes, np.uint8)
+    scodes = _c(scodes, np.uint8)
+    s2 = _c(s2, np.float32)
+    out = np.empty(n, np.uint16)
+    _load().orc_dequant_bf16_blocked(_ptr(codes), _ptr(scodes), _ptr(s2), float(mean), n,
+                                     block, group, _ptr(out))
+    return out
+
+
+def restored_scale_g(scodes, s2, mean: float, b: int, group: int) -> float:
+    sc = _c(scodes, np.uint8)
+    s2 = _c(s2, np.float32)
+    return float(_load().orc_restored_scale_g(_ptr(sc), _ptr(s2), float(mean), int(b), int(group)))
+
+
+def scale_mean_g(absmax: np.ndarray, group: int) -> float:
+    a = _c(absmax, np.float32)
+    return float(_load().orc_scale_mean_g(_ptr(a), a.size, group))
 
 
 def restored_scales(scodes: np.ndarray, s2: np.ndarray, mean: float) -> np.ndarray:

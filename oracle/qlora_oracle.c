@@ -163,58 +163,74 @@ static double tree_sum(double *v, int64_t len) {
   return v[0];
 }
 
-float orc_scale_mean(const float *absmax, int64_t n1) {
-  int64_t G = (n1 + ORC_GROUP - 1) / ORC_GROUP;
+/* Mean of the n1 first-level scales, summed in groups of B2 (a power of
+ * two) by the stride-halving tree, then by the same tree over the group
+ * sums padded with zeros to a power of two; quotient rounded to FP32. */
+float orc_scale_mean_g(const float *absmax, int64_t n1, int64_t B2) {
+  int64_t G = (n1 + B2 - 1) / B2;
   int64_t Gp = 1;
   while (Gp < G) Gp *= 2;
   double *part = (double *)calloc((size_t)Gp, sizeof(double));
-  double grp[ORC_GROUP];
+  double *grp = (double *)malloc((size_t)B2 * sizeof(double));
   for (int64_t g = 0; g < G; ++g) {
-    for (int j = 0; j < ORC_GROUP; ++j) {
-      int64_t b = g * ORC_GROUP + j;
+    for (int64_t j = 0; j < B2; ++j) {
+      int64_t b = g * B2 + j;
       grp[j] = (b < n1) ? (double)absmax[b] : 0.0;
     }
-    part[g] = tree_sum(grp, ORC_GROUP);
+    part[g] = tree_sum(grp, B2);
   }
   double S = tree_sum(part, Gp);
+  free(grp);
   free(part);
   return (float)(S / (double)n1);
 }
 
-void orc_quantize_nf4(const float *W, int64_t n, uint8_t *codes,
-                      uint8_t *scale_codes, float *s2, float *mean,
-                      float *absmax_out) {
-  int64_t n1 = n / ORC_BLOCK;
-  int64_t G = (n1 + ORC_GROUP - 1) / ORC_GROUP;
-  float *a = (float *)malloc((size_t)n1 * sizeof(float));
+float orc_scale_mean(const float *absmax, int64_t n1) {
+  return orc_scale_mean_g(absmax, n1, ORC_GROUP);
+}
 
-  /* First level: absmax per block of 64, normalize, nearest level, pack. */
+/* General block sizes [QP §5.5]: first-level blocks of B1 consecutive
+ * elements, second-level groups of B2 consecutive block scales (both powers
+ * of two), any n >= 1.  A last block shorter than B1 (n % B1 != 0) takes the
+ * absmax of the elements it has; a last group shorter than B2 likewise.
+ * codes has ceil(n/2) bytes; for odd n the high nibble of the last byte,
+ * which no element owns, is 0.  B1 = 64, B2 = 256 and n % 64 == 0 is the
+ * layer format above. */
+void orc_quantize_nf4_blocked(const float *W, int64_t n, int64_t B1, int64_t B2,
+                              uint8_t *codes, uint8_t *scale_codes, float *s2,
+                              float *mean, float *absmax_out) {
+  int64_t n1 = (n + B1 - 1) / B1;
+  int64_t G = (n1 + B2 - 1) / B2;
+  float *a = (float *)malloc((size_t)n1 * sizeof(float));
+  memset(codes, 0, (size_t)((n + 1) / 2));
+
+  /* First level: absmax per block, normalize, nearest level, pack. */
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < n1; ++b) {
-    const float *w = W + b * ORC_BLOCK;
+    const int64_t e0 = b * B1;
+    const int64_t len = (n - e0 < B1) ? n - e0 : B1;
     float m = 0.0f;
-    for (int j = 0; j < ORC_BLOCK; ++j) {
-      float v = fabsf(w[j]);
+    for (int64_t j = 0; j < len; ++j) {
+      float v = fabsf(W[e0 + j]);
       if (v > m) m = v;
     }
     a[b] = m;
-    uint8_t idx[ORC_BLOCK];
-    for (int j = 0; j < ORC_BLOCK; ++j) {
-      float x = (m == 0.0f) ? 0.0f : w[j] / m;
-      idx[j] = orc_nf4_index(x);
+    /* B1 is even, so a block owns whole bytes */
+    for (int64_t j = 0; j < len; ++j) {
+      float x = (m == 0.0f) ? 0.0f : W[e0 + j] / m;
+      uint8_t idx = orc_nf4_index(x);
+      int64_t e = e0 + j;
+      codes[e / 2] = (uint8_t)(codes[e / 2] | (e % 2 == 0 ? idx : (uint8_t)(idx << 4)));
     }
-    for (int j = 0; j < ORC_BLOCK / 2; ++j)
-      codes[b * (ORC_BLOCK / 2) + j] =
-          (uint8_t)(idx[2 * j] | (idx[2 * j + 1] << 4));
   }
   if (absmax_out) memcpy(absmax_out, a, (size_t)n1 * sizeof(float));
 
-  /* Second level: subtract the mean, then per group of 256 an FP32 scale
+  /* Second level: subtract the mean, then per group an FP32 scale
    * s2 = max|centred| / 448 and FP8 codes of centred / s2. */
-  float mu = orc_scale_mean(a, n1);
+  float mu = orc_scale_mean_g(a, n1, B2);
   *mean = mu;
   for (int64_t g = 0; g < G; ++g) {
-    int64_t b0 = g * ORC_GROUP, b1 = b0 + ORC_GROUP;
+    int64_t b0 = g * B2, b1 = b0 + B2;
     if (b1 > n1) b1 = n1;
     float mg = 0.0f;
     for (int64_t b = b0; b < b1; ++b) {
@@ -231,31 +247,49 @@ void orc_quantize_nf4(const float *W, int64_t n, uint8_t *codes,
   free(a);
 }
 
+void orc_quantize_nf4(const float *W, int64_t n, uint8_t *codes,
+                      uint8_t *scale_codes, float *s2, float *mean,
+                      float *absmax_out) {
+  orc_quantize_nf4_blocked(W, n, ORC_BLOCK, ORC_GROUP, codes, scale_codes, s2, mean,
+                           absmax_out);
+}
+
 /* Restored first-level scale of block b [QP §5.2 restore order; §6.1]. */
+float orc_restored_scale_g(const uint8_t *scale_codes, const float *s2,
+                           float mean, int64_t b, int64_t B2) {
+  volatile float p = orc_fp8_decode(scale_codes[b]) * s2[b / B2];
+  return p + mean;
+}
+
 float orc_restored_scale(const uint8_t *scale_codes, const float *s2,
                          float mean, int64_t b) {
-  volatile float p = orc_fp8_decode(scale_codes[b]) * s2[b / ORC_GROUP];
-  return p + mean;
+  return orc_restored_scale_g(scale_codes, s2, mean, b, ORC_GROUP);
 }
 
 /* Double dequantization to BF16 [QP §2.3, §6.1]: restored weight of element
  * e is RNE_bf16(codebook[idx_e] * restored_scale(block of e)). */
-void orc_dequant_bf16(const uint8_t *codes, const uint8_t *scale_codes,
-                      const float *s2, float mean, int64_t n, uint16_t *out) {
+void orc_dequant_bf16_blocked(const uint8_t *codes, const uint8_t *scale_codes,
+                              const float *s2, float mean, int64_t n, int64_t B1,
+                              int64_t B2, uint16_t *out) {
   float c[16];
   orc_codebook(c);
-  int64_t n1 = n / ORC_BLOCK;
+  int64_t n1 = (n + B1 - 1) / B1;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < n1; ++b) {
-    float ah = orc_restored_scale(scale_codes, s2, mean, b);
-    for (int j = 0; j < ORC_BLOCK; ++j) {
-      int64_t e = b * ORC_BLOCK + j;
+    float ah = orc_restored_scale_g(scale_codes, s2, mean, b, B2);
+    for (int64_t j = 0; j < B1 && b * B1 + j < n; ++j) {
+      int64_t e = b * B1 + j;
       uint8_t byte = codes[e / 2];
       int idx = (e % 2 == 0) ? (byte & 15) : (byte >> 4);
       volatile float prod = c[idx] * ah;
       out[e] = orc_bf16_rne(prod);
     }
   }
+}
+
+void orc_dequant_bf16(const uint8_t *codes, const uint8_t *scale_codes,
+                      const float *s2, float mean, int64_t n, uint16_t *out) {
+  orc_dequant_bf16_blocked(codes, scale_codes, s2, mean, n, ORC_BLOCK, ORC_GROUP, out);
 }
 
 /* ------------------------------------------------------------------------

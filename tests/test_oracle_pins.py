@@ -640,3 +640,133 @@ def test_dropout_backward_adjoint_identities(orc, shape):
     VB = rng.normal(size=B.shape).astype(np.float32)
     lhs = _inner(dY, orc.linear_fwd(np.zeros_like(Wh), X, A, VB, s, keep=keep, p=p))
     assert abs(lhs - _inner(dB, VB)) <= 1e-10 * (abs(lhs) + 1)
+
+
+# ------------------------------------------------ general block sizes [QP §5.5]
+
+def _planted_blocks(orc, n, B1, k, seed):
+    """n values in blocks of B1 (last block shorter when n % B1 != 0), each
+    block a shuffle of codebook indices that contains both ends (0 and 15),
+    scaled by 2^k; returns (W, planted indices)."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, 16, size=n).astype(np.uint8)
+    for b0 in range(0, n, B1):
+        blk = idx[b0:b0 + B1]
+        blk[0], blk[1] = 0, 15
+        rng.shuffle(blk)
+    W = (orc.codebook()[idx].astype(np.float64) * 2.0 ** k).astype(np.float32)
+    return W, idx
+
+
+@pytest.mark.parametrize("B1,B2,n", [(32, 256, 32 * 700 + 6), (128, 16, 128 * 50 + 127),
+                                     (1024, 256, 1024 * 9 + 2), (4096, 1024, 4096 * 3 + 7),
+                                     (64, 64, 64 * 1000)])
+def test_blocked_planted_codebook_blocks(orc, B1, B2, n):
+    """Known answer at any block size, with a short last block and (odd n)
+    a half-used last byte: absmax = 2^k everywhere, mean 2^k, s2 = 0 and
+    FP8 code 0, the planted indices (element 2j low nibble; no element's
+    nibble is 0), and restored weights RNE_bf16(c) 2^k exactly."""
+    k = -5
+    W, idx = _planted_blocks(orc, n, B1, k, seed=B1 + n)
+    codes, scodes, s2, mean = orc.quantize_nf4_blocked(W, B1, B2)
+    n1 = -(-n // B1)
+    assert codes.size == (n + 1) // 2 and scodes.size == n1 and s2.size == -(-n1 // B2)
+    pad = np.concatenate([idx, np.zeros(n % 2, np.uint8)])
+    np.testing.assert_array_equal(codes, (pad[0::2] | (pad[1::2] << 4)).astype(np.uint8))
+    assert mean == 2.0 ** k and np.all(s2 == 0) and np.all(scodes == 0)
+    wh = orc.bf16_bits_to_f32(orc.dequant_bf16_blocked(codes, scodes, s2, mean, n, B1, B2))
+    c_bf16 = orc.bf16_bits_to_f32(orc.bf16_rne(orc.codebook()))
+    np.testing.assert_array_equal(wh, (c_bf16[idx].astype(np.float64) * 2.0 ** k).astype(np.float32))
+
+
+def _block_absmax(w, B):
+    n1 = -(-w.size // B)
+    pad = np.zeros(n1 * B, np.float32)
+    pad[:w.size] = np.abs(w)
+    return pad.reshape(n1, B).max(axis=1)
+
+
+def test_blocked_tail_absmax_and_nesting(orc):
+    """The absmax of every block, the short last one included, is the max
+    over exactly its elements (brute force), and blocks of 2B are unions of
+    two blocks of B: absmax_2B[b] = max(absmax_B[2b], absmax_B[2b+1])."""
+    rng = np.random.default_rng(40)
+    n = 1_000_003
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    prev = None
+    for B1 in (32, 64, 128, 256, 512, 2048):
+        *_, a = orc.quantize_nf4_blocked(w, B1, 256, return_absmax=True)
+        np.testing.assert_array_equal(a, _block_absmax(w, B1))
+        if prev is not None and B1 == 2 * prev[0]:
+            p = np.concatenate([prev[1], np.zeros(prev[1].size % 2, np.float32)])
+            np.testing.assert_array_equal(a, np.maximum(p[0::2], p[1::2]))
+        prev = (B1, a)
+
+
+@pytest.mark.parametrize("B2", [16, 64, 1024])
+def test_blocked_scale_mean_any_group(orc, B2):
+    """The tree-summed mean with groups of B2 equals the exactly rounded
+    mean within one FP32 rounding."""
+    rng = np.random.default_rng(B2)
+    for n1 in (1, B2 - 1, B2 + 1, 5 * B2 + 3, 40001):
+        a = np.abs(rng.normal(0, 0.05, n1)).astype(np.float32)
+        exact = math.fsum(a.astype(np.float64).tolist()) / n1
+        assert abs(orc.scale_mean_g(a, B2) - exact) <= 0.5 * np.spacing(np.float32(exact)) * (1 + 1e-6)
+
+
+@pytest.mark.parametrize("B1,B2", [(32, 256), (256, 64), (128, 1024)])
+def test_blocked_roundtrip_error_bound(orc, B1, B2):
+    """The error decomposition bound of the layer format at other block
+    sizes, on a length that leaves a short last block and group."""
+    rng = np.random.default_rng(41)
+    n = 300_001
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    pos = rng.choice(n, size=n // 1000, replace=False)
+    w[pos] = np.where(rng.random(pos.size) < 0.5, -0.2, 0.2).astype(np.float32)
+    codes, scodes, s2, mean, absmax = orc.quantize_nf4_blocked(w, B1, B2, return_absmax=True)
+    c = orc.codebook().astype(np.float64)
+    idx = _unpack(codes)[:n]
+    a = np.repeat(absmax.astype(np.float64), B1)[:n]
+    gap = np.maximum(np.diff(c)[np.clip(idx - 1, 0, 14)], np.diff(c)[np.clip(idx, 0, 14)])
+    wd = w.astype(np.float64)
+    assert np.all(np.abs(wd - c[idx] * a) <= a * gap / 2 * (1 + 1e-6) + 1e-9)
+    s2b = np.repeat(np.repeat(s2.astype(np.float64), B2)[: absmax.size], B1)[:n]
+    ah = np.repeat([orc.restored_scale_g(scodes, s2, mean, b, B2) for b in range(absmax.size)],
+                   B1)[:n].astype(np.float64)
+    y = np.abs(a - mean) / np.where(s2b > 0, s2b, 1)
+    half = np.where(y < 2 ** -6, 2.0 ** -10, 2.0 ** (np.floor(np.log2(np.maximum(y, 2 ** -6))) - 4))
+    assert np.all(np.abs(a - ah) <= s2b * half * (1 + 1e-5) + 4 * np.spacing(np.float32(a.max())))
+    wh = orc.bf16_bits_to_f32(
+        orc.dequant_bf16_blocked(codes, scodes, s2, mean, n, B1, B2)).astype(np.float64)
+    bound = a * gap / 2 + np.abs(c[idx]) * np.abs(a - ah) + np.abs(wh) * 2.0 ** -8 + 1e-9
+    assert np.all(np.abs(wd - wh) <= bound * (1 + 1e-5))
+
+
+def test_blocked_group_max_maps_to_448(orc):
+    rng = np.random.default_rng(42)
+    w = rng.normal(0, 0.02, 64 * 64 * 9 + 100).astype(np.float32)
+    B1, B2 = 64, 64
+    codes, scodes, s2, mean, absmax = orc.quantize_nf4_blocked(w, B1, B2, return_absmax=True)
+    for g in range(s2.size):
+        d = absmax[g * B2:(g + 1) * B2] - np.float32(mean)
+        j = int(np.argmax(np.abs(d)))
+        assert scodes[g * B2 + j] & 0x7F == 0x7E
+
+
+def test_blocked_metadata_and_error_follow_block_size(orc):
+    """[QP §5.5]: scale metadata is about 8/B1 + 32/(B1 B2) bits per weight
+    (inversely proportional to B1), and smaller blocks give a lower
+    quantization error on normal weights with outliers."""
+    rng = np.random.default_rng(43)
+    n = 64 * 4096
+    w = rng.normal(0, 0.02, n).astype(np.float32)
+    pos = rng.choice(n, size=n // 1000, replace=False)
+    w[pos] = np.where(rng.random(pos.size) < 0.5, -0.2, 0.2).astype(np.float32)
+    errs = []
+    for B1 in (32, 64, 256, 1024):
+        codes, scodes, s2, mean = orc.quantize_nf4_blocked(w, B1, 256)
+        bits = (codes.nbytes + scodes.nbytes + s2.nbytes + 4) * 8 / n
+        assert abs(bits - (4 + 8 / B1 + 32 / (B1 * 256) + 32 / n)) < 32 / n + 1e-12
+        wh = orc.bf16_bits_to_f32(orc.dequant_bf16_blocked(codes, scodes, s2, mean, n, B1, 256))
+        errs.append(float(np.mean(np.abs(wh.astype(np.float64) - w))))
+    assert errs == sorted(errs), errs
