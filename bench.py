@@ -18,6 +18,8 @@ The same line also carries, each measured in the same run:
            last-level cache holds none of them;
   quant    quantize and dequantize of the 7B layer, GB/s over the algorithmic
            bytes (read FP32 W + write packed state; read packed + write BF16);
+  blocked  quantize / dequantize of the 7B layer as flat arrays at first-level
+           block sizes 32, 128 and 256 (groups of 256), GB/s as for quant;
   merge    LoRA merge into the restored base plus requantization of the 7B
            layer (r = 64), GB/s over packed-read + FP32 write/read + packed write;
   adamw    one clipped AdamW step (global-norm sum of squares, then the
@@ -356,18 +358,56 @@ def bench_quant7b(dev, steps, warmup):
 
     res = {}
     for name, fn, nbytes in (("quantize", qstep, bq), ("dequant", dstep, bd)):
-        for _ in range(warmup):
-            fn(None)
-        torch.cuda.synchronize()
+        # wall clock without timing events between the launches, then one
+        # more pass with the weight kernel of every call bracketed by events
+        el = timed(fn, steps, warmup) / steps
         tm = KernelTimer()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            fn(i, tm)
+        fn(None, tm)
         torch.cuda.synchronize()
-        el = (time.perf_counter() - t0) / steps
-        res[name] = dict(layer_us=el * 1e6, gbps=nbytes / el / 1e9, bytes=nbytes)
-        log(f"{name} 7B layer: {el * 1e6:.1f} us = {nbytes / el / 1e9:.0f} GB/s")
+        dur = tm.durations_ms(name[0])
+        res[name] = dict(layer_us=el * 1e6, gbps=nbytes / el / 1e9, bytes=nbytes,
+                         weight_kernel_us=sum(dur) * 1e3)
+        log(f"{name} 7B layer: {el * 1e6:.1f} us = {nbytes / el / 1e9:.0f} GB/s "
+            f"(weight kernel {sum(dur) * 1e3:.1f} us)")
     del Ws, qs, outs, wss
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_blocked7b(dev, steps, warmup):
+    """Quantize and dequantize the 7B layer's weights as flat arrays at other
+    first-level block sizes (second-level groups of 256); algorithmic bytes
+    as for the layer format, with that block size's metadata."""
+    Ws = [inputs.weight(d_out, d_in, 1, 0, outliers=True, device=dev, proj=p).view(-1)
+          for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B)]
+    n = sum(W.numel() for W in Ws)
+    res = {}
+    for block in (32, 128, 256):
+        qs = [q.qlora_quantize_nf4_blocked(W, block, 256) for W in Ws]
+        outs = [torch.empty(W.numel(), dtype=torch.bfloat16, device=dev) for W in Ws]
+        wss = [torch.empty(q.qlora_quantize_blocked_workspace_bytes(W.numel(), block, 256),
+                           dtype=torch.uint8, device=dev) for W in Ws]
+        packed = sum(t.numel() * t.element_size() for b in qs
+                     for t in (b.codes, b.scale_codes, b.scale2, b.scale_mean))
+
+        def qstep(i, Ws=Ws, qs=qs, wss=wss, block=block):
+            for W, b, ws in zip(Ws, qs, wss):
+                q.qlora_quantize_nf4_blocked(W, block, 256, out=b, workspace=ws)
+
+        def dstep(i, qs=qs, outs=outs):
+            for b, o in zip(qs, outs):
+                q.qlora_dequant_bf16_blocked(b, out=o)
+
+        eq = timed(qstep, steps, warmup) / steps
+        ed = timed(dstep, steps, warmup) / steps
+        res[f"B{block}"] = dict(quantize_us=eq * 1e6, quantize_gbps=(4 * n + packed) / eq / 1e9,
+                                dequant_us=ed * 1e6, dequant_gbps=(packed + 2 * n) / ed / 1e9,
+                                bits_per_weight=packed * 8 / n)
+        log(f"blocked B1={block}: quantize {eq * 1e6:.1f} us = {(4 * n + packed) / eq / 1e9:.0f} "
+            f"GB/s; dequant {ed * 1e6:.1f} us = {(packed + 2 * n) / ed / 1e9:.0f} GB/s; "
+            f"{packed * 8 / n:.4f} bits/weight")
+        del qs, outs, wss
+    del Ws
     torch.cuda.empty_cache()
     return res
 
@@ -499,7 +539,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,merge,adamw,stack65b,cpu")
+    ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,blocked,merge,adamw,stack65b,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MB (a plain copy "
@@ -532,6 +572,8 @@ def main():
         extra["decode_7b"] = bench_decode7b(dev, args.steps, args.warmup)
     if "quant" not in skip:
         extra["quant_7b"] = bench_quant7b(dev, max(3, args.steps // 2), 1)
+    if "blocked" not in skip:
+        extra["blocked_7b"] = bench_blocked7b(dev, max(3, args.steps // 2), 1)
     if "merge" not in skip:
         extra["merge_7b"] = bench_merge7b(dev, max(3, args.steps // 2), 1)
     if "adamw" not in skip:

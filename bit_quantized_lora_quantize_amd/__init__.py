@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     AdamwParamSet,
     Dropout,
     FwdItem,
+    NF4Blocked,
     NF4Weight,
     QLORA_MAX_GROUP,
     QLORA_OP_BWD,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     qlora_abi_version,
     qlora_adamw_step,
     qlora_dequant_bf16,
+    qlora_dequant_bf16_blocked,
     qlora_dropout_mask,
     qlora_grad_sumsq,
     qlora_sumsq_workspace_bytes,
@@ -31,8 +33,11 @@ from ._lib import (  # noqa: F401
     qlora_linear_fwd_dropout,
     qlora_linear_fwd_many,
     qlora_merge_nf4,
+    qlora_nf4_blocked_sizes,
     qlora_nf4_sizes,
+    qlora_quantize_blocked_workspace_bytes,
     qlora_quantize_nf4,
+    qlora_quantize_nf4_blocked,
     qlora_status_string,
     qlora_time_next_weight_kernel,
     qlora_workspace_bytes,

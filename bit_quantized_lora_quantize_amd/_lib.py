@@ -39,6 +39,12 @@ class _FwdItem(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class _Nf4Blocked(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("block", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scale_codes", ctypes.c_void_p),
+                ("scale2", ctypes.c_void_p), ("scale_mean", ctypes.c_void_p)]
+
+
 class _Dropout(ctypes.Structure):
     _fields_ = [("p", ctypes.c_float), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
 
@@ -88,6 +94,12 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.qlora_time_next_weight_kernel.argtypes = [_P, _P]
+        L.qlora_nf4_blocked_sizes.argtypes = [_I64, _I64, _I64] + [ctypes.POINTER(ctypes.c_size_t)] * 3
+        L.qlora_quantize_blocked_workspace_bytes.restype = ctypes.c_size_t
+        L.qlora_quantize_blocked_workspace_bytes.argtypes = [_I64, _I64, _I64]
+        L.qlora_quantize_nf4_blocked.argtypes = [_P, ctypes.POINTER(_Nf4Blocked), _P,
+                                                 ctypes.c_size_t, _P]
+        L.qlora_dequant_bf16_blocked.argtypes = [ctypes.POINTER(_Nf4Blocked), _P, _P]
         L.qlora_dropout_mask.argtypes = [_P, _I64, _I64, ctypes.POINTER(_Dropout), _P, _P, _P]
         L.qlora_linear_fwd_dropout.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
                                                ctypes.c_float, ctypes.POINTER(_Dropout), _P, _P,
@@ -211,6 +223,70 @@ def qlora_dequant_bf16(q: NF4Weight, out: Optional[torch.Tensor] = None) -> torc
     qs = q.c_struct()
     _check(lib().qlora_dequant_bf16(ctypes.byref(qs), _ptr(Wb), _stream(q.device)),
            "qlora_dequant_bf16")
+    return Wb
+
+
+@dataclass
+class NF4Blocked:
+    """NF4 + double quantization of a flat array at general block sizes."""
+    n: int
+    block: int
+    group: int
+    codes: torch.Tensor        # uint8 [ceil(n/2)]
+    scale_codes: torch.Tensor  # uint8 [ceil(n/block)]
+    scale2: torch.Tensor       # float32 [ceil(n1/group)]
+    scale_mean: torch.Tensor   # float32 [1]
+
+    @staticmethod
+    def empty(n: int, block: int = 64, group: int = 256, device="cuda") -> "NF4Blocked":
+        cb, sb, s2b = qlora_nf4_blocked_sizes(n, block, group)
+        return NF4Blocked(n, block, group,
+                          torch.empty(cb, dtype=torch.uint8, device=device),
+                          torch.empty(sb, dtype=torch.uint8, device=device),
+                          torch.empty(s2b // 4, dtype=torch.float32, device=device),
+                          torch.empty(1, dtype=torch.float32, device=device))
+
+    def c_struct(self) -> _Nf4Blocked:
+        return _Nf4Blocked(self.n, self.block, self.group, self.codes.data_ptr(),
+                           self.scale_codes.data_ptr(), self.scale2.data_ptr(),
+                           self.scale_mean.data_ptr())
+
+
+def qlora_nf4_blocked_sizes(n: int, block: int, group: int) -> tuple[int, int, int]:
+    out = [ctypes.c_size_t() for _ in range(3)]
+    _check(lib().qlora_nf4_blocked_sizes(n, block, group, *[ctypes.byref(o) for o in out]),
+           "qlora_nf4_blocked_sizes")
+    return tuple(o.value for o in out)
+
+
+def qlora_quantize_blocked_workspace_bytes(n: int, block: int, group: int) -> int:
+    return int(lib().qlora_quantize_blocked_workspace_bytes(n, block, group))
+
+
+def qlora_quantize_nf4_blocked(W: torch.Tensor, block: int = 64, group: int = 256,
+                               out: Optional[NF4Blocked] = None,
+                               workspace: Optional[torch.Tensor] = None) -> NF4Blocked:
+    """Quantize the values of W (FP32, any shape, contiguous) as one flat
+    array with first-level blocks of `block` and groups of `group` scales."""
+    if W.dtype != torch.float32 or not W.is_contiguous() or not W.is_cuda:
+        raise ValueError("W: expected a contiguous float32 tensor on the GPU")
+    n = W.numel()
+    q = out if out is not None else NF4Blocked.empty(n, block, group, W.device)
+    need = qlora_quantize_blocked_workspace_bytes(n, q.block, q.group)
+    ws = workspace if workspace is not None else _workspace(need, W.device)
+    qs = q.c_struct()
+    _check(lib().qlora_quantize_nf4_blocked(_ptr(W), ctypes.byref(qs), _ptr(ws), ws.numel(),
+                                            _stream(W.device)), "qlora_quantize_nf4_blocked")
+    return q
+
+
+def qlora_dequant_bf16_blocked(q: NF4Blocked, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    Wb = out if out is not None else torch.empty(q.n, dtype=torch.bfloat16, device=q.codes.device)
+    if Wb.dtype != torch.bfloat16 or Wb.numel() != q.n or not Wb.is_contiguous():
+        raise ValueError("out: expected a contiguous bfloat16 tensor of n elements")
+    qs = q.c_struct()
+    _check(lib().qlora_dequant_bf16_blocked(ctypes.byref(qs), _ptr(Wb), _stream(Wb.device)),
+           "qlora_dequant_bf16_blocked")
     return Wb
 
 

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libqlora")
 LIB = os.path.join(PKG, "libqlora.so")
 
-SOURCES = ["quant.hip", "lora.hip", "gemv.hip", "gemm.hip", "merge.hip", "optim.hip", "dropout.hip", "api.cpp"]
+SOURCES = ["quant.hip", "quant_blocked.hip", "lora.hip", "gemv.hip", "gemm.hip", "merge.hip", "optim.hip", "dropout.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -213,6 +213,41 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   return p;
 }
 
+// General block sizes: supported parameters and the workspace.
+bool blocked_ok(int64_t n, int64_t block, int64_t group) {
+  const auto pow2 = [](int64_t v) { return v > 0 && (v & (v - 1)) == 0; };
+  return n >= 1 && n <= (int64_t(1) << 40) && pow2(block) && block >= 32 && block <= 4096 &&
+         pow2(group) && group >= 16 && group <= 1024;
+}
+
+struct BlockedPlan {
+  float* absmax;
+  double* part;
+  size_t bytes;
+};
+
+BlockedPlan plan_blocked(int64_t n, int64_t block, int64_t group, void* ws) {
+  BlockedPlan p{};
+  const int64_t n1 = cdiv(n, block), G = cdiv(n1, group);
+  int64_t Gp = 1;
+  while (Gp < G) Gp *= 2;
+  Carver c(ws);
+  p.absmax = c.take<float>(n1);
+  p.part = c.take<double>(Gp);
+  p.bytes = c.off + 256;
+  return p;
+}
+
+int check_blocked(const qlora_nf4_blocked_t* q) {
+  if (!q) return QLORA_ERR_NULL;
+  if (!blocked_ok(q->n, q->block, q->group)) return QLORA_ERR_SHAPE;
+  if (!q->codes || !q->scale_codes || !q->scale2 || !q->scale_mean) return QLORA_ERR_NULL;
+  if (!aligned16(q->codes) || (reinterpret_cast<uintptr_t>(q->scale2) & 3u) ||
+      (reinterpret_cast<uintptr_t>(q->scale_mean) & 3u))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
 // LoRA dropout buffers, after the region of the plan they extend: the
 // masked LoRA input [M][d_in] and (backward) the keep words [d_in][ldw].
 struct DropPlan {
@@ -764,6 +799,45 @@ int qlora_linear_bwd_dropout(const qlora_nf4_t* q, const uint16_t* X, const uint
   }
   return bwd_impl(q, dp.xm, dp.keep, dp.ldw, dY, M, A, B, r,
                   (lora_alpha / (float)r) / (1.0f - drop->p), T_saved, dX, dA, dB, p, st);
+}
+
+int qlora_nf4_blocked_sizes(int64_t n, int64_t block, int64_t group, size_t* codes_bytes,
+                            size_t* scale_codes_bytes, size_t* scale2_bytes) {
+  if (!codes_bytes || !scale_codes_bytes || !scale2_bytes) return QLORA_ERR_NULL;
+  if (!blocked_ok(n, block, group)) return QLORA_ERR_SHAPE;
+  const int64_t n1 = cdiv(n, block);
+  *codes_bytes = size_t(cdiv(n, 2));
+  *scale_codes_bytes = size_t(n1);
+  *scale2_bytes = size_t(cdiv(n1, group)) * sizeof(float);
+  return QLORA_OK;
+}
+
+size_t qlora_quantize_blocked_workspace_bytes(int64_t n, int64_t block, int64_t group) {
+  if (!blocked_ok(n, block, group)) return 0;
+  return plan_blocked(n, block, group, nullptr).bytes;
+}
+
+int qlora_quantize_nf4_blocked(const float* W, const qlora_nf4_blocked_t* q, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int s = check_blocked(q);
+  if (s) return s;
+  if (!W || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(W) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  const BlockedPlan p = plan_blocked(q->n, q->block, q->group, ws);
+  if (ws_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
+  const BlockedQuant bq{W, q->n, q->block, q->group, q->codes, q->scale_codes, q->scale2,
+                        q->scale_mean, p.absmax, p.part};
+  return hip_status(launch_quantize_blocked(bq, lut(), static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dequant_bf16_blocked(const qlora_nf4_blocked_t* q, uint16_t* W_bf16, void* stream) {
+  int s = check_blocked(q);
+  if (s) return s;
+  if (!W_bf16) return QLORA_ERR_NULL;
+  if (!aligned16(W_bf16)) return QLORA_ERR_ALIGN;
+  return hip_status(launch_dequant_blocked(q->codes, q->scale_codes, q->scale2, q->scale_mean,
+                                           q->n, q->block, q->group, W_bf16,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int qlora_dropout_mask(const uint16_t* X, int64_t M, int64_t d, const qlora_dropout_t* drop,

@@ -32,6 +32,30 @@ struct QuantWorkspace {
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale_codes,
                            float* scale2, float* mean, const QuantWorkspace& ws,
                            const IndexLut& lut, hipStream_t st);
+// The top of the mean's tree: part[0..Gp) (Gp a power of two) summed by the
+// stride-halving tree, mean = FP32(sum / n1).
+void launch_mean_tree(double* part, int64_t Gp, int64_t n1, float* mean, hipStream_t st);
+// Workgroups for `work` items at `per_block` per workgroup, in [1, max_blocks].
+int grid_for(int64_t work, int per_block, int max_blocks);
+
+// General block sizes: first-level blocks of `block` elements (a power of
+// two, 32..4096), second-level groups of `group` scales (a power of two,
+// 16..1024), any n >= 1 (short last block and group).  Workspace: absmax
+// FP32 [n1], part FP64 [power of two >= ceil(n1 / group)].
+struct BlockedQuant {
+  const float* W;
+  int64_t n, block, group;
+  uint8_t* codes;
+  uint8_t* scale_codes;
+  float* scale2;
+  float* mean;
+  float* absmax;
+  double* part;
+};
+hipError_t launch_quantize_blocked(const BlockedQuant& q, const IndexLut& lut, hipStream_t st);
+hipError_t launch_dequant_blocked(const uint8_t* codes, const uint8_t* scale_codes,
+                                  const float* scale2, const float* mean, int64_t n,
+                                  int64_t block, int64_t group, uint16_t* out, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, const float* scale2,
                           const float* mean, int64_t n, uint16_t* out, hipStream_t st);
 

@@ -177,11 +177,22 @@ __global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict_
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-static int grid_for(int64_t work, int per_block, int max_blocks) {
+int grid_for(int64_t work, int per_block, int max_blocks) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
   if (g > max_blocks) g = max_blocks;
   return (int)g;
+}
+
+void launch_mean_tree(double* part, int64_t Gp, int64_t n1, float* mean, hipStream_t st) {
+  int64_t len = Gp;
+  while (len > kTreeLds) {
+    int64_t half = len / 2;
+    hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((half + 255) / 256)), dim3(256), 0, st,
+                       part, half);
+    len = half;
+  }
+  hipLaunchKernelGGL(k_tree_final, dim3(1), dim3(1024), 0, st, part, len, n1, mean);
 }
 
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale_codes,
@@ -197,14 +208,7 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   weight_kernel_end(st);
   hipLaunchKernelGGL(k_group_sums, dim3((unsigned)((Gp + 3) / 4)), dim3(256), 0, st, ws.absmax,
                      n1, G, Gp, ws.part);
-  int64_t len = Gp;
-  while (len > kTreeLds) {
-    int64_t half = len / 2;
-    hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((half + 255) / 256)), dim3(256), 0, st,
-                       ws.part, half);
-    len = half;
-  }
-  hipLaunchKernelGGL(k_tree_final, dim3(1), dim3(1024), 0, st, ws.part, len, n1, mean);
+  launch_mean_tree(ws.part, Gp, n1, mean, st);
   hipLaunchKernelGGL(k_scale_dq, dim3((unsigned)((G + 3) / 4)), dim3(256), 0, st, ws.absmax, n1,
                      G, mean, scale_codes, scale2);
   return hipGetLastError();

@@ -227,6 +227,53 @@ int qlora_linear_fwd_many(int count, const qlora_fwd_item *items, int64_t M,
                           void *stream);
 
 /*
+ * General block sizes ([QP §5.5]: the first-level block size B1 trades
+ * scale metadata, about 8 / B1 bits per weight after double quantization,
+ * against error; the second-level group size B2 makes the same trade for
+ * the scales).  The same quantization as qlora_quantize_nf4 over a flat
+ * array of n >= 1 values with
+ *   block  B1: a power of two, 32 <= B1 <= 4096 (the layer format uses 64),
+ *   group  B2: a power of two, 16 <= B2 <= 1024 (the layer format uses 256),
+ * and no divisibility requirement: a short last block takes the absmax of
+ * the elements it has, a short last group likewise.  With n1 = ceil(n/B1)
+ * and G = ceil(n1/B2):
+ *   codes        uint8[ceil(n/2)] (16B); for odd n the high nibble of the
+ *                last byte is 0.
+ *   scale_codes  uint8[n1];  scale2 float[G];  scale_mean float[1].
+ * With B1 = 64, B2 = 256 and n % 64 == 0 the bytes equal those of
+ * qlora_quantize_nf4 for the same values.  n <= 2^40.
+ */
+typedef struct {
+  int64_t n;
+  int64_t block;
+  int64_t group;
+  uint8_t *codes;
+  uint8_t *scale_codes;
+  float *scale2;
+  float *scale_mean;
+} qlora_nf4_blocked_t;
+
+/* Buffer sizes of the blocked format (host only); QLORA_ERR_SHAPE for an
+ * unsupported n, block or group. */
+int qlora_nf4_blocked_sizes(int64_t n, int64_t block, int64_t group,
+                            size_t *codes_bytes, size_t *scale_codes_bytes,
+                            size_t *scale2_bytes);
+
+/* Workspace of qlora_quantize_nf4_blocked (host only); 0 when unsupported. */
+size_t qlora_quantize_blocked_workspace_bytes(int64_t n, int64_t block,
+                                              int64_t group);
+
+/* Quantize W (FP32 [n], (16B)) into q.  workspace (16B) >=
+ * qlora_quantize_blocked_workspace_bytes(n, block, group). */
+int qlora_quantize_nf4_blocked(const float *W, const qlora_nf4_blocked_t *q,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Double dequantization of q to BF16 [n] (16B). */
+int qlora_dequant_bf16_blocked(const qlora_nf4_blocked_t *q, uint16_t *W_bf16,
+                               void *stream);
+
+/*
  * LoRA dropout in training mode ([QP §6.3]: the LoRA branch takes D(x)
  * instead of x, the base branch x; inference has no dropout):
  *     D(X) = keep * X / (1 - p),

@@ -233,3 +233,33 @@ def test_dropout_argument_errors(L):
               needb - 1, None) == EWS
     assert bw(ctypes.byref(w), X, X, 40, A, B, 0, 16.0, ctypes.byref(ok), None, None, dA, dB, ws,
               needb, None) == ESHAPE
+
+
+def test_blocked_sizes_and_argument_errors(L):
+    P = ctypes.c_void_p
+    assert q.qlora_nf4_blocked_sizes(1001, 32, 16) == (501, 32, 8)
+    assert q.qlora_nf4_blocked_sizes(64 * 256 * 3, 64, 256) == (64 * 384, 768, 12)
+    for bad in ((0, 64, 256), (100, 48, 256), (100, 16, 256), (100, 8192, 256), (100, 64, 8),
+                (100, 64, 2048), (100, 64, 100), ((1 << 40) + 1, 64, 256)):
+        with pytest.raises(q.QloraError):
+            q.qlora_nf4_blocked_sizes(*bad)
+        assert q.qlora_quantize_blocked_workspace_bytes(*bad) == 0
+    need = q.qlora_quantize_blocked_workspace_bytes(1000, 32, 16)
+    assert need >= 32 * 4 + 8
+    B = _lib._Nf4Blocked
+    good = B(1000, 32, 16, 0x10000, 0x20000, 0x30000, 0x40000)
+    W, ws = P(0x50000), P(0x60000)
+    f = L.qlora_quantize_nf4_blocked
+    assert f(W, None, ws, need, None) == ENULL
+    assert f(W, ctypes.byref(B(1000, 24, 16, 0x10000, 0x20000, 0x30000, 0x40000)), ws, need,
+             None) == ESHAPE
+    assert f(W, ctypes.byref(B(1000, 32, 16, 0, 0x20000, 0x30000, 0x40000)), ws, need,
+             None) == ENULL
+    assert f(W, ctypes.byref(B(1000, 32, 16, 0x10008, 0x20000, 0x30000, 0x40000)), ws, need,
+             None) == EALIGN
+    assert f(None, ctypes.byref(good), ws, need, None) == ENULL
+    assert f(P(0x50004), ctypes.byref(good), ws, need, None) == EALIGN
+    assert f(W, ctypes.byref(good), ws, need - 1, None) == EWS
+    g = L.qlora_dequant_bf16_blocked
+    assert g(ctypes.byref(good), None, None) == ENULL
+    assert g(ctypes.byref(good), P(0x70002), None) == EALIGN

@@ -1,0 +1,80 @@
+"""GPU parity of NF4 double quantization and dequantization at general block
+sizes ([QP §5.5]) with short last blocks and groups: every byte of the
+quantized state and every restored BF16 weight equal to the CPU oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_lora_quantize_amd as q
+from bit_quantized_lora_quantize_amd import inputs
+from parity_util import bits16, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _values(n, cfg, outliers=True):
+    # n weights with the layer recipe (N(0, 0.02), 0.1 % outliers at 10 std)
+    rows = -(-n // 64)
+    return inputs.weight(rows, 64, config=cfg, outliers=outliers).ravel()[:n].contiguous()
+
+
+def _check(orc, W, block, group):
+    n = W.numel()
+    say(f"blocked parity: n={n} block={block} group={group}")
+    qb = q.qlora_quantize_nf4_blocked(W.to(DEV), block, group)
+    wh = q.qlora_dequant_bf16_blocked(qb)
+    torch.cuda.synchronize()
+    codes, scodes, s2, mean = orc.quantize_nf4_blocked(W.numpy(), block, group)
+    assert np.array_equal(qb.codes.cpu().numpy(), codes), "NF4 codes differ"
+    assert np.array_equal(qb.scale_codes.cpu().numpy(), scodes), "FP8 scale codes differ"
+    assert np.array_equal(qb.scale2.cpu().numpy().view(np.uint32), s2.view(np.uint32)), \
+        "second-level scales differ"
+    assert np.float32(qb.scale_mean.item()).view(np.uint32) == np.float32(mean).view(np.uint32)
+    ref = orc.dequant_bf16_blocked(codes, scodes, s2, mean, n, block, group)
+    assert np.array_equal(bits16(wh), ref), "restored weights differ"
+
+
+CASES = [  # (n, block, group)
+    (1, 32, 16),
+    (7, 32, 16),
+    (1001, 32, 16),
+    (64 * 1000 + 7, 64, 256),
+    (300_001, 128, 64),
+    ((1 << 20) + 3, 256, 1024),
+    (512 * 33 + 500, 512, 32),
+    (1024 * 50 + 9, 1024, 512),
+    (2048 * 77 + 100, 2048, 128),
+    (4096 * 3 + 7, 4096, 256),
+    (4096 * 4096, 128, 256),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_blocked_bit_exact(orc, case):
+    n, block, group = case
+    _check(orc, _values(n, 140 + CASES.index(case)), block, group)
+
+
+def test_blocked_zero_and_planted_tail(orc):
+    """An all-zero array, and a tail block holding only zeros."""
+    _check(orc, torch.zeros(777, dtype=torch.float32), 32, 16)
+    W = _values(64 * 100 + 33, 150)
+    W[64 * 100:] = 0
+    _check(orc, W, 64, 16)
+
+
+def test_blocked_64_256_equals_layer_format(orc):
+    """B1 = 64, B2 = 256 on a whole number of rows: the same bytes as the
+    layer-format quantizer (one down-projection weight)."""
+    d_out, d_in = 4096, 11008
+    W = inputs.weight(d_out, d_in, config=151, outliers=True).to(DEV)
+    w = q.qlora_quantize_nf4(W)
+    qb = q.qlora_quantize_nf4_blocked(W, 64, 256)
+    a = q.qlora_dequant_bf16(w)
+    b = q.qlora_dequant_bf16_blocked(qb)
+    torch.cuda.synchronize()
+    assert torch.equal(w.codes, qb.codes) and torch.equal(w.scale_codes, qb.scale_codes)
+    assert torch.equal(w.scale2.view(torch.int32), qb.scale2.view(torch.int32))
+    assert torch.equal(w.scale_mean.view(torch.int32), qb.scale_mean.view(torch.int32))
+    assert torch.equal(a.view(torch.int16).ravel(), b.view(torch.int16))
