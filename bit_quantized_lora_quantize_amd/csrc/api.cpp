@@ -166,7 +166,7 @@ struct BwdPlan {
   int64_t rp;         // r rounded up to 32
   uint16_t* u_hl;     // [M][2 rp] BF16 hi | lo of U
   int64_t ldp;        // token stride of the transposed hi/lo copies
-  uint16_t *ut_hi, *ut_lo, *tt_hi, *tt_lo;  // [r][ldp]
+  uint16_t *ut_hi, *ut_lo, *tt_hi, *tt_lo;  // [round_up(r, 32)][ldp], fragment order
   int ms_a, ms_b;     // token splits of dA and dB
   int64_t mper_a, mper_b;
   float* da_part;     // [ms_a][r][d_in]
@@ -177,10 +177,14 @@ struct BwdPlan {
 // Token split of dA / dB: about 512 workgroups (64 columns x one split
 // each); a split is a multiple of 512 tokens (four wavefronts of whole
 // pairs of 64-token blocks).
+#ifndef QLORA_GRAM_TARGET_WGS
+#define QLORA_GRAM_TARGET_WGS 512
+#endif
 int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
   (void)r;
   const int64_t ctiles = cdiv(N, 64);
-  const int64_t ms = std::max<int64_t>(1, std::min<int64_t>(cdiv(512, ctiles), cdiv(M, 256)));
+  const int64_t ms = std::max<int64_t>(
+      1, std::min<int64_t>(cdiv(QLORA_GRAM_TARGET_WGS, ctiles), cdiv(M, 256)));
   *per = round_up(cdiv(std::max<int64_t>(M, 1), ms), 512);
   return (int)std::max<int64_t>(1, cdiv(M, *per));
 }
@@ -201,10 +205,12 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
     p.r_part = c.take<float>(ks * M * r);
   }
   p.ldp = round_up(std::max<int64_t>(M, 1), 16);
-  p.ut_hi = c.take<uint16_t>(r * p.ldp);
-  p.ut_lo = c.take<uint16_t>(r * p.ldp);
-  p.tt_hi = c.take<uint16_t>(r * p.ldp);
-  p.tt_lo = c.take<uint16_t>(r * p.ldp);
+  // fragment-ordered transposed copies: round_up(r, 32) rows
+  const int64_t rf = round_up(r, 32);
+  p.ut_hi = c.take<uint16_t>(rf * p.ldp);
+  p.ut_lo = c.take<uint16_t>(rf * p.ldp);
+  p.tt_hi = c.take<uint16_t>(rf * p.ldp);
+  p.tt_lo = c.take<uint16_t>(rf * p.ldp);
   p.ms_a = token_splits(M, d_in, r, &p.mper_a);
   p.ms_b = token_splits(M, d_out, r, &p.mper_b);
   p.da_part = c.take<float>((int64_t)p.ms_a * r * d_in);

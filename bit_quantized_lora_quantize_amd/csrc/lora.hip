@@ -204,9 +204,9 @@ __global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRo
         a.hl[m * 2 * a.rp + a.rp + n] = lb;
       }
     }
-    if (a.ht && n < a.N) {
-      a.ht[(int64_t)n * a.ldt + m] = hb;
-      a.lt[(int64_t)n * a.ldt + m] = lb;
+    if (a.ht && n < (a.N + 31) / 32 * 32) {   // NC >= round_up(N, 32); zero past N
+      a.ht[frag_index(n, m, a.ldt)] = hb;
+      a.lt[frag_index(n, m, a.ldt)] = lb;
     }
   }
 }
@@ -448,10 +448,12 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
   const FinishDesc& d = a.d[di];
   const int64_t idx = (int64_t)(wg - d.wg_begin) * 256 + threadIdx.x;
   const int64_t ldt = d.ldt > 0 ? d.ldt : d.M;
-  if (idx >= d.N * ldt) return;
+  // the transposed copies cover rows up to round_up(N, 32) (zeros past N)
+  const int64_t nt = d.ht ? (d.N + 31) / 32 * 32 : d.N;
+  if (idx >= nt * ldt) return;
   const int64_t n = idx / ldt, m = idx % ldt;
   float v = 0.0f;
-  if (m < d.M) {
+  if (m < d.M && n < d.N) {
     const int64_t e = m * d.N + n, count = d.M * d.N;
     float acc = d.part[e];
     for (int s = 1; s < d.splits; ++s) acc = __fadd_rn(acc, d.part[(int64_t)s * count + e]);
@@ -463,10 +465,10 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
   const uint16_t hb = (uint16_t)(__float_as_uint(hi) >> 16);
   const uint16_t lb = (uint16_t)(pack_bf16x2(lo, 0.0f) & 0xFFFFu);
   if (d.ht) {
-    d.ht[idx] = hb;
-    d.lt[idx] = lb;
+    d.ht[frag_index(n, m, ldt)] = hb;
+    d.lt[frag_index(n, m, ldt)] = lb;
   }
-  if (d.hl && m < d.M) {
+  if (d.hl && m < d.M && n < d.N) {
     uint16_t* row = d.hl + m * 2 * d.rp;
     row[n] = hb;
     row[d.rp + n] = lb;
@@ -536,12 +538,21 @@ __global__ __launch_bounds__(256) void k_rank_finish_rows(FinishDesc d) {
   }
   if (!d.ht) return;
   __syncthreads();
-  for (int idx = t; idx < 64 * 16; idx += 256) {
-    const int cn = idx >> 4, r = idx & 15;
-    const int64_t nn = nc + cn, m = m0 + r;
-    if (nn < d.N && m < ldt) {
-      d.ht[nn * ldt + m] = th[cn][r];
-      d.lt[nn * ldt + m] = tl[cn][r];
+  // fragment order: the tile's 16 tokens are one 16-token slice, so each
+  // (column, half) pair is one 16-byte piece
+  if (t < 128) {
+    const int cn = t >> 1, hh = t & 1;
+    const int64_t nn = nc + cn, m = m0 + 8 * hh;
+    if (nn < (d.N + 31) / 32 * 32 && m < ldt) {
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ph[j] = (uint32_t)th[cn][8 * hh + 2 * j] | ((uint32_t)th[cn][8 * hh + 2 * j + 1] << 16);
+        pl[j] = (uint32_t)tl[cn][8 * hh + 2 * j] | ((uint32_t)tl[cn][8 * hh + 2 * j + 1] << 16);
+      }
+      const int64_t f = frag_index(nn, m, ldt);
+      *reinterpret_cast<u32x4*>(d.ht + f) = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      *reinterpret_cast<u32x4*>(d.lt + f) = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
   }
 }
@@ -558,8 +569,9 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // part[s][i][c] = sum_{m in split s} P[m][i] Q[m][c], i < R <= 256.  The
 // contraction runs over tokens, the row index of both operands.  P arrives
-// transposed and split (hi / lo BF16 [R][ldp], zero past M), so its MFMA
-// operand (eight consecutive tokens of one row i) is a 16-byte load from L2.
+// transposed and split (hi / lo BF16, zero past M and R) in fragment order,
+// so the MFMA row operand of a 32-row block and 16 tokens is one contiguous
+// 1 KB load per wavefront from L2.
 // Q (X or dY) is streamed from HBM: each wavefront copies blocks of 64 token
 // rows x 64 columns into an LDS region of its own and reads the column
 // operands (eight consecutive tokens of one column) with transposing LDS
@@ -612,7 +624,6 @@ __device__ __forceinline__ void gram_block(const uint16_t* Q, int64_t M, __amdgp
                                            int64_t N, int64_t m, int lane, uint8_t* wl,
                                            uint32_t wr, uint32_t rd, u32x4 (&x)[8],
                                            f32x16 (&acc)[RB][2]) {
-  const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + wr + i * 8 * kGramLd * 2) = x[i];
   u32x4 ph[4][RB], pl[4][RB];
@@ -620,7 +631,8 @@ __device__ __forceinline__ void gram_block(const uint16_t* Q, int64_t M, __amdgp
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int ib = 0; ib < RB; ++ib) {
-      const uint32_t po = (uint32_t)(((32 * ib + r32) * ldp + m + 16 * t + 8 * h) * 2);
+      // fragment order: one contiguous 1 KB chunk per (row block, 16 tokens)
+      const uint32_t po = (uint32_t)(((ib * (ldp >> 4) + (m >> 4) + t) * 64 + lane) * 16);
       ph[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, po, 0, 0));
       pl[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, po, 0, 0));
     }
@@ -669,8 +681,9 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi
   if (m_end > m_lim) m_end = m_lim;
   uint8_t* wl = glds + w * kGramWaveBytes;
 
-  const __amdgpu_buffer_rsrc_t rh = rank_rsrc(Pt_hi, R * ldp * 2);  // rows past R read zero
-  const __amdgpu_buffer_rsrc_t rl = rank_rsrc(Pt_lo, R * ldp * 2);
+  // fragment-ordered copies of round_up(R, 32) rows; row blocks past them read zero
+  const __amdgpu_buffer_rsrc_t rh = rank_rsrc(Pt_hi, (R + 31) / 32 * 32 * ldp * 2);
+  const __amdgpu_buffer_rsrc_t rl = rank_rsrc(Pt_lo, (R + 31) / 32 * 32 * ldp * 2);
 
   f32x16 acc[RB][2];
 #pragma unroll
@@ -795,7 +808,8 @@ hipError_t launch_rank_finish(const FinishArgs& a0, hipStream_t st) {
   for (int i = 0; i < a.count; ++i) {
     a.d[i].wg_begin = wgs;
     const int64_t ldt = a.d[i].ldt > 0 ? a.d[i].ldt : a.d[i].M;
-    wgs += (int)((a.d[i].N * ldt + 255) / 256);
+    const int64_t nt = a.d[i].ht ? (a.d[i].N + 31) / 32 * 32 : a.d[i].N;
+    wgs += (int)((nt * ldt + 255) / 256);
   }
   if (wgs == 0) return hipSuccess;
   hipLaunchKernelGGL(k_rank_finish, dim3(wgs), dim3(256), 0, st, a);

@@ -94,8 +94,18 @@ hipError_t launch_rank_small(const RankSmallArgs& a, hipStream_t st);
 //   v[m][n] = scale * sum_k P[m][k] Q[n][k],  P [M][K], Q [N][ldq], N <= 256.
 // Outputs, each optional (NULL skips): out FP32 [M][N]; hl BF16 [M][2 rp],
 // hi | lo split of v with zeros for n in [N, rp) (rp a multiple of 32,
-// rp >= N); ht / lt BF16 [N][ldt] transposed hi / lo with zeros for m in
-// [M, ldt) (ldt a multiple of 16, >= M).
+// rp >= N); ht / lt the transposed hi / lo BF16 copies, element (n, m) at
+// frag_index(n, m, ldt), with zeros for m in [M, ldt) and n in [N, round_up(N,
+// 32)) (ldt a multiple of 16, >= M; round_up(N, 32) * ldt elements).
+// Fragment order of the transposed rank-r copies (the token contraction's
+// MFMA row operand): 32-row x 16-token chunks of 1 KB, chunk (i / 32, k / 16)
+// at chunk index (i / 32) * (ldt / 16) + k / 16, and inside a chunk the
+// 16-byte piece of lane (i % 32) + 32 ((k / 8) % 2) holding tokens k & ~7 ..
+// +8, so a wavefront reads one chunk with one contiguous 1 KB load.
+__host__ __device__ inline int64_t frag_index(int64_t i, int64_t k, int64_t ldt) {
+  return (((i >> 5) * (ldt >> 4) + (k >> 4)) * 64 + (i & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
+}
+
 struct RankRowsArgs {
   const uint16_t* P;
   const uint16_t* Q;
@@ -128,7 +138,7 @@ inline int rank_k_splits(int64_t M, int64_t K, int64_t* kper) {
 
 // Finish of split partials: v[m][n] = scale * sum_s part[s][m][n] (s
 // ascending).  out (optional) = v, FP32 [M][N]; ht/lt (optional) = the
-// transposed hi/lo BF16 pair of v, [N][ldt] with zeros for m in [M, ldt).
+// transposed hi/lo BF16 pair of v in fragment order (as for RankRowsArgs).
 // Up to kMaxGroup independent problems per launch.
 struct FinishDesc {
   const float* part;
