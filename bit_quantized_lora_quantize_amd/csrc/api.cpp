@@ -488,7 +488,14 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
   // (the same kernels and summation order as the forward, so a recomputed T
   // equals a saved one bit for bit)
   const float* T = T_saved;
-  if (!T && M > kSmallM) {
+  // large M with a saved T: its transposed copies are formed in the finish
+  // launch of U below
+  bool t_with_u = false;
+  FinishDesc t_copy{};
+  if (T && M > kSmallM) {
+    t_with_u = true;
+    t_copy = FinishDesc{T, nullptr, p.tt_hi, p.tt_lo, M, r, p.ldp, 1.0f, 1, 0, nullptr, 0};
+  } else if (!T && M > kSmallM) {
     RankRowsArgs ra{XA, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
     s = rank_product(ra, p.r_part, st);
     if (s) return s;
@@ -512,11 +519,8 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
       if (s) return s;
       T = p.t_buf;
     }
-    s = hip_status(M > kSmallM
-                       ? launch_rank_finish_rows(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo,
-                                                 p.ldp, nullptr, 0, st)
-                       : launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
-                                            nullptr, 0, st));
+    s = hip_status(launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
+                                      nullptr, 0, st));
     if (s) return s;
   }
   // U = s dY B, through B^T so the contraction over d_out is contiguous
@@ -524,7 +528,8 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
   if (s) return s;
   {
     RankRowsArgs ra{dY, p.bt, M, r, d_out, p.ldbt, sc, nullptr, p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
-    s = rank_product(ra, p.r_part, st);
+    s = t_with_u ? hip_status(launch_rank_split(ra, p.r_part, st, &t_copy))
+                 : rank_product(ra, p.r_part, st);
   }
   if (s) return s;
   // dX = dY Wh + U A (the U A term cleared at dropped positions)
@@ -534,15 +539,12 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
     s = hip_status(launch_gemm_bwd(g, st));
     if (s) return s;
   }
-  // dA = U^T XA ; dB = (T^T dY)^T
-  s = hip_status(launch_gram(p.ut_hi, p.ut_lo, p.ldp, XA, M, r, d_in, p.mper_a, p.ms_a,
-                             p.da_part, st));
-  if (!s) s = hip_status(launch_gram_finish(p.da_part, p.ms_a, r, d_in, false, dA, st));
-  if (!s)
-    s = hip_status(launch_gram(p.tt_hi, p.tt_lo, p.ldp, dY, M, r, d_out, p.mper_b, p.ms_b,
-                               p.db_part, st));
-  if (!s) s = hip_status(launch_gram_finish(p.db_part, p.ms_b, r, d_out, true, dB, st));
-  return s;
+  // dA = U^T XA ; dB = (T^T dY)^T, both contractions in one launch and
+  // both finishes in another
+  const GramProblem gp[2] = {
+      {p.ut_hi, p.ut_lo, XA, d_in, p.mper_a, p.ms_a, p.da_part, dA, false},
+      {p.tt_hi, p.tt_lo, dY, d_out, p.mper_b, p.ms_b, p.db_part, dB, true}};
+  return hip_status(launch_grams(gp, 2, p.ldp, M, r, st));
 }
 
 }  // namespace

@@ -488,10 +488,17 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
 // outputs are read and written along n, and the transposed copies go
 // through an LDS tile so that they are written along m.  Each thread keeps
 // four elements' partial loads in flight per split.
-__global__ __launch_bounds__(256) void k_rank_finish_rows(FinishDesc d) {
+__global__ __launch_bounds__(256) void k_rank_finish_rows(FinishArgs fa) {
   constexpr int EU = 4;
   __shared__ uint16_t th[64][18], tl[64][18];   // [n][m], padded
+  const FinishDesc& d = fa.d[blockIdx.z];
   const int64_t m0 = (int64_t)blockIdx.x * 16, nc = (int64_t)blockIdx.y * 64;
+  {
+    // this problem's tiles (the grid covers the largest problem of the list)
+    const int64_t rows = d.ht && d.ldt > d.M ? d.ldt : d.M;
+    const int64_t ncols = d.hl && d.rp > d.N ? d.rp : d.N;
+    if (m0 >= rows || nc >= (ncols + 63) / 64 * 64) return;
+  }
   const int t = threadIdx.x, col = t & 63, rq = t >> 6;
   const int64_t count = d.M * d.N;
   const int64_t ldt = d.ldt > 0 ? d.ldt : d.M;
@@ -659,18 +666,38 @@ __device__ __forceinline__ void gram_block(const uint16_t* Q, int64_t M, __amdgp
   }
 }
 
+struct GramDesc {
+  const uint16_t* Pt_hi;
+  const uint16_t* Pt_lo;
+  const uint16_t* Q;
+  int64_t N, m_per_split;
+  float* part;
+  int ctiles;     // 64-column tiles
+  int wg_begin;   // first workgroup of the problem
+};
+struct GramArgs {
+  GramDesc d[2];
+  int count;
+  int64_t ldp, M, R;
+};
+
 template <int RB, bool VEC>
-__global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi,
-                                              const uint16_t* __restrict__ Pt_lo, int64_t ldp,
-                                              const uint16_t* __restrict__ Q, int64_t M,
-                                              int64_t R, int64_t N, int64_t m_per_split,
-                                              float* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
   extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
+  // problem of this workgroup, then its column tile and token split
+  const int di = (ga.count > 1 && (int)blockIdx.x >= ga.d[1].wg_begin) ? 1 : 0;
+  const GramDesc& gd = ga.d[di];
+  const uint16_t* __restrict__ Pt_hi = gd.Pt_hi;
+  const uint16_t* __restrict__ Pt_lo = gd.Pt_lo;
+  const uint16_t* __restrict__ Q = gd.Q;
+  const int64_t ldp = ga.ldp, M = ga.M, R = ga.R, N = gd.N, m_per_split = gd.m_per_split;
+  float* __restrict__ part = gd.part;
+  const int local = (int)blockIdx.x - gd.wg_begin;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, h = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
-  const int s = blockIdx.y;
+  const int64_t c0 = (int64_t)(local % gd.ctiles) * 64;
+  const int s = local / gd.ctiles;
   // m_per_split is a multiple of 512: each quarter is whole pairs of
   // 64-token blocks.  Tokens at or past M read as zero in Q, so their
   // (finite) products add nothing and every block runs all four slices.
@@ -735,16 +762,28 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Pt_hi
   }
 }
 
-__global__ __launch_bounds__(256) void k_gram_finish(const float* __restrict__ part, int splits,
-                                                     int64_t R, int64_t N, int transposed,
-                                                     float* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t count = R * N;
+struct GramFinishArgs {
+  const float* part[2];
+  float* out[2];
+  int64_t N[2];
+  int splits[2];
+  int transposed[2];
+  int64_t begin1;   // first element index of problem 1
+  int count;
+  int64_t R;
+};
+
+__global__ __launch_bounds__(256) void k_gram_finish(GramFinishArgs a) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int di = (a.count > 1 && idx >= a.begin1) ? 1 : 0;
+  if (di) idx -= a.begin1;
+  const int64_t N = a.N[di], count = a.R * N;
   if (idx >= count) return;
+  const float* part = a.part[di];
   float acc = part[idx];
-  for (int s = 1; s < splits; ++s) acc = __fadd_rn(acc, part[(int64_t)s * count + idx]);
+  for (int s = 1; s < a.splits[di]; ++s) acc = __fadd_rn(acc, part[(int64_t)s * count + idx]);
   const int64_t i = idx / N, c = idx % N;
-  out[transposed ? c * R + i : idx] = acc;
+  a.out[di][a.transposed[di] ? c * a.R + i : idx] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -765,12 +804,16 @@ static hipError_t launch_rank_part_t(const RankRowsArgs& a, float* part, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st) {
+hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st,
+                             const FinishDesc* extra) {
   // 16-byte row pieces need K and ldq multiples of 8 and aligned bases;
   // other layouts take the one-pass kernel, which loads elements
   if (a.K % 8 != 0 || a.ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15) ||
-      (reinterpret_cast<uintptr_t>(a.Q) & 15))
-    return launch_rank_rows(a, st);
+      (reinterpret_cast<uintptr_t>(a.Q) & 15)) {
+    hipError_t e = launch_rank_rows(a, st);
+    if (e == hipSuccess && extra) e = launch_rank_finish_rows(extra, 1, st);
+    return e;
+  }
   int64_t kper = 0;
   const int ks = rank_k_splits(a.M, a.K, &kper);
   hipError_t e;
@@ -779,19 +822,36 @@ hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st)
   else if (a.N <= 128) e = launch_rank_part_t<8>(a, part, kper, ks, st);
   else e = launch_rank_part_t<16>(a, part, kper, ks, st);
   if (e != hipSuccess) return e;
-  return launch_rank_finish_rows(part, ks, a.M, a.N, a.scale, a.out, a.ht, a.lt, a.ldt, a.hl, a.rp,
-                                 st);
+  FinishDesc d[2];
+  d[0] = FinishDesc{part, a.out, a.ht, a.lt, a.M, a.N, a.ht ? a.ldt : a.M, a.scale, ks, 0, a.hl,
+                    a.rp};
+  if (extra) d[1] = *extra;
+  return launch_rank_finish_rows(d, extra ? 2 : 1, st);
+}
+
+hipError_t launch_rank_finish_rows(const FinishDesc* d, int count, hipStream_t st) {
+  FinishArgs a{};
+  a.count = count;
+  int64_t gx = 0, gy = 0;
+  for (int i = 0; i < count; ++i) {
+    a.d[i] = d[i];
+    if (a.d[i].ldt <= 0) a.d[i].ldt = a.d[i].M;
+    const int64_t rows = d[i].ht && a.d[i].ldt > d[i].M ? a.d[i].ldt : d[i].M;
+    const int64_t ncols = d[i].hl && d[i].rp > d[i].N ? d[i].rp : d[i].N;
+    gx = std::max(gx, (rows + 15) / 16);
+    gy = std::max(gy, (ncols + 63) / 64);
+  }
+  if (gx == 0 || gy == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rank_finish_rows, dim3((unsigned)gx, (unsigned)gy, (unsigned)count),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_rank_finish_rows(const float* part, int splits, int64_t M, int64_t N,
                                    float scale, float* out, uint16_t* ht, uint16_t* lt,
                                    int64_t ldt, uint16_t* hl, int64_t rp, hipStream_t st) {
   const FinishDesc d{part, out, ht, lt, M, N, ht ? ldt : M, scale, splits, 0, hl, rp};
-  const int64_t rows = ht && ldt > M ? ldt : M;
-  const int64_t ncols = hl && rp > N ? rp : N;
-  hipLaunchKernelGGL(k_rank_finish_rows, dim3((unsigned)((rows + 15) / 16), (unsigned)((ncols + 63) / 64)),
-                     dim3(256), 0, st, d);
-  return hipGetLastError();
+  return launch_rank_finish_rows(&d, 1, st);
 }
 
 hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st) {
@@ -834,28 +894,32 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
 }
 
 template <int RB, bool VEC>
-static hipError_t launch_gram_t(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
-                                const uint16_t* Q, int64_t M, int64_t R, int64_t N,
-                                int64_t m_per_split, int splits, float* part, hipStream_t st) {
+static hipError_t launch_gram_t(const GramArgs& a, int wgs, hipStream_t st) {
   constexpr int lds = 4 * kGramWaveBytes > 32 * RB * 64 * 4 ? 4 * kGramWaveBytes : 32 * RB * 64 * 4;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gram<RB, VEC>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  dim3 grid((unsigned)((N + 63) / 64), (unsigned)splits);
-  hipLaunchKernelGGL((k_gram<RB, VEC>), grid, dim3(256), lds, st, Pt_hi, Pt_lo, ldp, Q, M, R, N,
-                     m_per_split, part);
+  hipLaunchKernelGGL((k_gram<RB, VEC>), dim3((unsigned)wgs), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
-                       const uint16_t* Q, int64_t M, int64_t R, int64_t N, int64_t m_per_split,
-                       int splits, float* part, hipStream_t st) {
-  const bool vec = (N % 8) == 0;
-#define QLORA_GRAM(RB)                                                                       \
-  return vec ? launch_gram_t<RB, true>(Pt_hi, Pt_lo, ldp, Q, M, R, N, m_per_split, splits,   \
-                                       part, st)                                             \
-             : launch_gram_t<RB, false>(Pt_hi, Pt_lo, ldp, Q, M, R, N, m_per_split, splits,  \
-                                        part, st)
+// One contraction launch for problems sharing the 16-byte row loads or not.
+static hipError_t launch_gram_group(const GramProblem* p, int count, int64_t ldp, int64_t M,
+                                    int64_t R, bool vec, hipStream_t st) {
+  GramArgs a{};
+  a.count = count;
+  a.ldp = ldp;
+  a.M = M;
+  a.R = R;
+  int wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    a.d[i] = GramDesc{p[i].Pt_hi, p[i].Pt_lo, p[i].Q, p[i].N, p[i].m_per_split, p[i].part,
+                      (int)((p[i].N + 63) / 64), wgs};
+    wgs += a.d[i].ctiles * p[i].splits;
+  }
+  if (wgs == 0) return hipSuccess;
+#define QLORA_GRAM(RB) \
+  return vec ? launch_gram_t<RB, true>(a, wgs, st) : launch_gram_t<RB, false>(a, wgs, st)
   if (R <= 32) { QLORA_GRAM(1); }
   if (R <= 64) { QLORA_GRAM(2); }
   if (R <= 128) { QLORA_GRAM(4); }
@@ -863,11 +927,34 @@ hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp
 #undef QLORA_GRAM
 }
 
-hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,
-                              bool transposed, float* out, hipStream_t st) {
-  const int64_t count = R * N;
-  hipLaunchKernelGGL(k_gram_finish, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
-                     part, splits, R, N, transposed ? 1 : 0, out);
+hipError_t launch_grams(const GramProblem* p, int count, int64_t ldp, int64_t M, int64_t R,
+                        hipStream_t st) {
+  if (count < 1 || count > 2) return hipErrorInvalidValue;
+  const bool v0 = (p[0].N % 8) == 0;
+  hipError_t e;
+  if (count == 2 && ((p[1].N % 8) == 0) == v0) {
+    e = launch_gram_group(p, 2, ldp, M, R, v0, st);
+  } else {
+    e = launch_gram_group(p, 1, ldp, M, R, v0, st);
+    if (e == hipSuccess && count == 2)
+      e = launch_gram_group(p + 1, 1, ldp, M, R, (p[1].N % 8) == 0, st);
+  }
+  if (e != hipSuccess) return e;
+  GramFinishArgs f{};
+  f.count = count;
+  f.R = R;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    f.part[i] = p[i].part;
+    f.out[i] = p[i].out;
+    f.N[i] = p[i].N;
+    f.splits[i] = p[i].splits;
+    f.transposed[i] = p[i].transposed ? 1 : 0;
+    if (i == 1) f.begin1 = total;
+    total += R * p[i].N;
+  }
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gram_finish, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, f);
   return hipGetLastError();
 }
 

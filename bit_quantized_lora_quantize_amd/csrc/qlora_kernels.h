@@ -122,7 +122,11 @@ hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st);
 // The same product (same outputs) through K-split partials part
 // [rank_k_splits(M, K)][M][N] FP32 and k_rank_finish (splits added in order);
 // K or ldq not a multiple of 8, or unaligned P / Q, take launch_rank_rows.
-hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st);
+// extra (optional): one more finish problem with the same M, run in the same
+// finish launch.
+struct FinishDesc;
+hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st,
+                             const FinishDesc* extra = nullptr);
 // K splits of launch_rank_split: about 512 workgroups of 64 rows; each split
 // a multiple of 128 columns.  *kper receives the split length.
 inline int rank_k_splits(int64_t M, int64_t K, int64_t* kper) {
@@ -162,27 +166,40 @@ hipError_t launch_rank_finish(const float* part, int splits, int64_t M, int64_t 
                               float* out, uint16_t* ht, uint16_t* lt, int64_t ldt,
                               uint16_t* hl, int64_t rp, hipStream_t st);
 
-// The same finish for many rows (one workgroup per 64 rows, coalesced
-// partial reads and transposed writes through LDS); identical outputs.
+// The same finish for many rows (one workgroup per 16 rows x 64 columns,
+// coalesced partial reads and transposed writes through LDS); identical
+// outputs.  The list form runs up to kMaxGroup problems with the same M in
+// one launch.
 hipError_t launch_rank_finish_rows(const float* part, int splits, int64_t M, int64_t N,
                                    float scale, float* out, uint16_t* ht, uint16_t* lt,
                                    int64_t ldt, uint16_t* hl, int64_t rp, hipStream_t st);
+hipError_t launch_rank_finish_rows(const FinishDesc* d, int count, hipStream_t st);
 
 // Transpose of a BF16 matrix in[rows][cols] into out[cols][ldo]:
 // out[c][i] = in[i][c] for i < rows, and 0 for i in [rows, ldo).
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  int64_t ldo, hipStream_t st);
 
-// part[s][i][c] = sum over tokens m in split s of P[m][i] * Q[m][c], with P
-// given transposed as a hi + lo BF16 pair Pt_hi/Pt_lo [R][ldp] (ldp >= M,
-// a multiple of 16, zero-padded) and Q BF16 [M][N] (16-byte aligned), R <=
-// 256.  m_per_split is a multiple of 512.
-hipError_t launch_gram(const uint16_t* Pt_hi, const uint16_t* Pt_lo, int64_t ldp,
-                       const uint16_t* Q, int64_t M, int64_t R, int64_t N, int64_t m_per_split,
-                       int splits, float* part, hipStream_t st);
-// out = sum_s part[s] (s ascending); transposed: out[c][i] else out[i][c].
-hipError_t launch_gram_finish(const float* part, int splits, int64_t R, int64_t N,
-                              bool transposed, float* out, hipStream_t st);
+// Token contractions out = P^T Q over the M tokens: part[s][i][c] = sum
+// over tokens m in split s of P[m][i] * Q[m][c], then out = sum_s part[s]
+// (s ascending), out[c][i] if transposed else out[i][c].  P is given
+// transposed as a hi + lo BF16 pair in fragment order (frag_index, ldp >= M
+// a multiple of 16, round_up(R, 32) rows, zero-padded); Q BF16 [M][N]
+// (16-byte aligned); R <= 256; m_per_split a multiple of 512.  Up to two
+// problems with the same M, R and ldp run in one contraction launch and one
+// finish launch.
+struct GramProblem {
+  const uint16_t* Pt_hi;
+  const uint16_t* Pt_lo;
+  const uint16_t* Q;
+  int64_t N, m_per_split;
+  int splits;
+  float* part;   // [splits][R][N]
+  float* out;
+  bool transposed;
+};
+hipError_t launch_grams(const GramProblem* p, int count, int64_t ldp, int64_t M, int64_t R,
+                        hipStream_t st);
 
 // ------------------------------------------------- optimizer step
 // Tensors are handled in batches of up to kOptBatch per launch (descriptors
