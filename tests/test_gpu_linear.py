@@ -164,6 +164,23 @@ def test_llama7b_training_shape(orc, proj):
     _check_layer(orc, W, A, B, X, dY, rows=rows, label=f"7B {name} train")
 
 
+@pytest.mark.parametrize("proj", [0, 4, 6])
+def test_llama65b_layer_shapes(orc, proj):
+    """The 65B stack's configuration on its three projection shapes (q 8192 x
+    8192, gate 22016 x 8192, down 8192 x 22016) at M = 2048 tokens, r = 64:
+    quantized state bit for bit, Y and dX on sampled rows, dA and dB in full,
+    for layer 79's seeds (the stack's last layer)."""
+    name, d_out, d_in = inputs.LLAMA_65B[proj]
+    M = 2048
+    W = inputs.weight(d_out, d_in, 4, 79, device=DEV, proj=proj)
+    A, B = inputs.lora_factors(d_out, d_in, 64, 4, 79, device=DEV, proj=proj)
+    X = inputs.activations(M, d_in, 4, 0, inputs.T_X, device=DEV, proj=proj)
+    dY = inputs.activations(M, d_out, 4, 0, inputs.T_DY, device=DEV, proj=proj)
+    rng = np.random.default_rng(65 + proj)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 14, replace=False)]))
+    _check_layer(orc, W, A, B, X, dY, rows=rows, label=f"65B {name} layer 79")
+
+
 def test_linear_tokens_beyond_2gib(orc):
     """Activations larger than 2 GiB, so that byte offsets over a whole
     tensor would not fit 32 bits: M = 5 x 65536 tokens of width 4096 (2.7 GB
