@@ -314,11 +314,16 @@ def bench_decode7b(dev, steps, warmup, copies=4):
         for i in range(max(warmup, 2) * copies):
             step(i)
         torch.cuda.synchronize()
+        # whole calls back to back (no timing events between them), then the
+        # same calls again with the weight kernel of each bracketed by events
         t0 = time.perf_counter()
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
         for i in range(n):
             step(i, timer)
         torch.cuda.synchronize()
-        el = time.perf_counter() - t0
         durs = timer.durations_ms("gemv")
         k_avg = sum(durs) / len(durs) * 1e-3
         out[f"M{M}"] = dict(layer_us=el / n * 1e6, gbps=scored / (el / n) / 1e9,

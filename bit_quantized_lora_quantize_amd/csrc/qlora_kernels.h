@@ -129,10 +129,13 @@ hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st,
                              const FinishDesc* extra = nullptr);
 // K splits of launch_rank_split: about 512 workgroups of 64 rows; each split
 // a multiple of 128 columns.  *kper receives the split length.
+#ifndef QLORA_RANK_TARGET_WGS
+#define QLORA_RANK_TARGET_WGS 512
+#endif
 inline int rank_k_splits(int64_t M, int64_t K, int64_t* kper) {
   const int64_t rb = (M + 63) / 64;
   const int64_t maxs = (K + 127) / 128;
-  int64_t ks = (512 + rb - 1) / rb;
+  int64_t ks = (QLORA_RANK_TARGET_WGS + rb - 1) / rb;
   ks = ks < 1 ? 1 : (ks > maxs ? maxs : ks);
   int64_t per = ((K + ks - 1) / ks + 127) / 128 * 128;
   if (per < 128) per = 128;
