@@ -118,12 +118,22 @@ __global__ __launch_bounds__(1024) void k_sumsq_final(SumsqBatch b, const double
   if (threadIdx.x == 0) sums[t] = s[0];
 }
 
-// acc += t[0] + t[1] + ... (in that order)
-__global__ void k_sumsq_accumulate(const double* __restrict__ t, int count, double* acc) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double a = acc[0];
-  for (int i = 0; i < count; ++i) a = __dadd_rn(a, t[i]);
-  acc[0] = a;
+// acc += t[0] + t[1] + ... (in that order).  The tensor sums are staged in
+// LDS by the whole workgroup, 1024 at a time, and added by one thread.
+__global__ __launch_bounds__(256) void k_sumsq_accumulate(const double* __restrict__ t, int count,
+                                                          double* acc) {
+  __shared__ double s[1024];
+  double a = 0.0;
+  if (threadIdx.x == 0) a = acc[0];
+  for (int c0 = 0; c0 < count; c0 += 1024) {
+    const int len = count - c0 < 1024 ? count - c0 : 1024;
+    for (int i = threadIdx.x; i < len; i += blockDim.x) s[i] = t[c0 + i];
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int i = 0; i < len; ++i) a = __dadd_rn(a, s[i]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) acc[0] = a;
 }
 
 int64_t sumsq_part_len(int64_t n) {
@@ -160,7 +170,7 @@ hipError_t launch_sumsq(const float* const* grads, const int64_t* n, int count, 
     }
     hipLaunchKernelGGL(k_sumsq_final, dim3(b.count), dim3(1024), 0, st, b, part, sums + b0);
   }
-  hipLaunchKernelGGL(k_sumsq_accumulate, dim3(1), dim3(64), 0, st, sums, count, acc);
+  hipLaunchKernelGGL(k_sumsq_accumulate, dim3(1), dim3(256), 0, st, sums, count, acc);
   return hipGetLastError();
 }
 
