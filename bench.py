@@ -60,20 +60,29 @@ R, ALPHA = 64, 16.0
 # HBM bytes per fused-GEMM launch (mean over the 14 launches of one training
 # step), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a
 # 1024 MB device copy (factors 2.0 and 1.0).  Valid only for the kernel
-# sources with this SHA-1 (gemm.hip, qlora_device.h, qlora_kernels.h);
-# reported as null otherwise.
-GEMM_TRAFFIC_BYTES = 268.81e6
-GEMM_TRAFFIC_SHA1 = "8faa01196ddc704d5312d9c537886989720e7f49"
+# sources with this SHA-1 (gemm_source_sha1); reported as null otherwise.
+GEMM_TRAFFIC_BYTES = 268.80e6
+GEMM_TRAFFIC_SHA1 = "ee4279b2479bd403d90fd56bb4ffca3009f51cee"
+
+
+def gemm_source_sha1():
+    """SHA-1 of what decides the fused GEMM's memory traffic: gemm.hip,
+    qlora_device.h and the GemmArgs declaration in qlora_kernels.h."""
+    import hashlib
+    import re
+    csrc = os.path.join(_ROOT, "bit_quantized_lora_quantize_amd", "csrc")
+    h = hashlib.sha1()
+    for f in ("gemm.hip", "qlora_device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(csrc, "qlora_kernels.h")) as fh:
+        m = re.search(r"struct GemmArgs \{.*?\};", fh.read(), re.S)
+    h.update(m.group(0).encode() if m else b"")
+    return h.hexdigest()
 
 
 def gemm_traffic():
-    import hashlib
-    csrc = os.path.join(_ROOT, "bit_quantized_lora_quantize_amd", "csrc")
-    h = hashlib.sha1()
-    for f in ("gemm.hip", "qlora_device.h", "qlora_kernels.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    return GEMM_TRAFFIC_BYTES if h.hexdigest() == GEMM_TRAFFIC_SHA1 else None
+    return GEMM_TRAFFIC_BYTES if gemm_source_sha1() == GEMM_TRAFFIC_SHA1 else None
 
 
 def log(msg):
