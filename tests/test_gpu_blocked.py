@@ -78,3 +78,11 @@ def test_blocked_64_256_equals_layer_format(orc):
     assert torch.equal(w.scale2.view(torch.int32), qb.scale2.view(torch.int32))
     assert torch.equal(w.scale_mean.view(torch.int32), qb.scale_mean.view(torch.int32))
     assert torch.equal(a.view(torch.int16).ravel(), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", [(2, 32, 16), (3, 4096, 1024), (4095, 4096, 16), (1 << 16, 32, 1024)])
+def test_blocked_small_and_single_block(orc, case):
+    """The smallest arrays, a single short block at the largest block size,
+    and a single short group at the largest group size."""
+    n, block, group = case
+    _check(orc, _values(n, 160 + n % 97), block, group)

@@ -130,3 +130,30 @@ def test_dropout_llama7b_training_shape(orc, proj):
     rows = np.array([0, 1, 255, 256, 2047, 4000, 4095])
     say(f"dropout 7B {name}")
     _check_dropout(orc, (d_out, d_in, M, r), 130 + proj, rows=rows)
+
+
+def test_dropout_empty_batch_and_extreme_parameters(orc):
+    """M = 0 does nothing (and zeroes dA, dB); p = 0.99 keeps about one in a
+    hundred and still matches the oracle; seeds and offsets use all 64 bits."""
+    d_out, d_in, r = 64, 128, 8
+    W, A, B, X, dY = _layer(d_out, d_in, 1, r, 125)
+    w = q.qlora_quantize_nf4(W.to(DEV))
+    X0 = torch.empty((0, d_in), dtype=torch.bfloat16, device=DEV)
+    dY0 = torch.empty((0, d_out), dtype=torch.bfloat16, device=DEV)
+    drop = q.Dropout(0.5, seed=(1 << 64) - 1, offset=(1 << 63) + 5)
+    Y = q.qlora_linear_fwd_dropout(w, X0, A.to(DEV), B.to(DEV), ALPHA, drop)
+    dA = torch.full((r, d_in), 3.0, device=DEV)
+    dB = torch.full((d_out, r), 3.0, device=DEV)
+    _, dA, dB = q.qlora_linear_bwd_dropout(w, X0, dY0, A.to(DEV), B.to(DEV), ALPHA, drop,
+                                           dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, d_out)
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+    Xm = inputs.activations(70, 136, 126, tensor=inputs.T_X)
+    Xk, bits = q.qlora_dropout_mask(Xm.to(DEV), drop, want_bits=True)
+    keep = orc.dropout_keep(70, 136, drop.p, drop.seed, drop.offset)
+    torch.cuda.synchronize()
+    ref = np.where(keep.astype(bool), bits16(Xm).reshape(70, 136), np.uint16(0))
+    assert np.array_equal(bits16(Xk).reshape(70, 136), ref)
+    assert np.array_equal(bits.cpu().numpy().view(np.uint32), _pack_keep(keep))
+    _check_dropout(orc, (96, 192, 48, 8), 127, p=0.99)

@@ -134,3 +134,22 @@ def test_adamw_zero_grad_decay_only(orc):
     torch.cuda.synchronize()
     assert np.array_equal(_bits(t.param.cpu().numpy()), _bits(p))
     assert not t.m.any().item() and not t.v.any().item()
+
+
+def test_adamw_degenerate_hyperparameters(orc):
+    """lr = 0 leaves the parameters unchanged (moments still move); beta1 =
+    beta2 = 0 makes the step g / (|g| + eps) scaled by lr; both bit-exact."""
+    n = 3000
+    p0 = inputs.normal((n,), 0.05, inputs.seed(154, 0, inputs.T_A)).numpy()
+    g, m, v = (x.numpy() for x in inputs.optimizer_state(n, 154, step=1))
+    for lr, b1, b2 in ((0.0, 0.9, 0.999), (1e-3, 0.0, 0.0)):
+        t = q.AdamwParam(torch.from_numpy(p0.copy()).to(DEV), torch.from_numpy(g).to(DEV),
+                         torch.from_numpy(m.copy()).to(DEV), torch.from_numpy(v.copy()).to(DEV))
+        q.qlora_adamw_step([t], lr=lr, beta1=b1, beta2=b2, eps=1e-8, weight_decay=0.1, step=2)
+        pr, mr, vr, _ = orc.adamw(p0, g, m, v, lr, b1, b2, 1e-8, 0.1, 2)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(t.param.cpu().numpy()), _bits(pr)), (lr, b1, b2)
+        assert np.array_equal(_bits(t.m.cpu().numpy()), _bits(mr)), (lr, b1, b2)
+        assert np.array_equal(_bits(t.v.cpu().numpy()), _bits(vr)), (lr, b1, b2)
+        if lr == 0.0:
+            assert np.array_equal(_bits(t.param.cpu().numpy()), _bits(p0))
