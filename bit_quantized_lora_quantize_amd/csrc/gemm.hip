@@ -109,16 +109,22 @@ struct Tile {
   // LDS offsets (bytes, relative to a buffer)
   uint32_t wa, wb;                 // restore stores
   uint32_t ra, rb;                 // fragment reads
+  // activations loaded straight into LDS (unpadded 64-byte rows, 16-byte
+  // pieces swizzled): global offset of the lane's piece in pass 0, the
+  // LoRA-step store offset, and the fragment read offset of slice 0
+  uint32_t vd, wad, rad;
 };
 
 // ------------------------------------------------------------------ loads
 // VEC: activation rows 16-byte aligned (K % 8 == 0); always so in the
 // forward direction (K = d_in, a multiple of 64).
-template <bool BWD, bool VEC>
+template <bool BWD, bool VEC, bool DMA>
 __device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int step,
                                           bool with_scale, Stage& g) {
   const uint32_t k0 = (uint32_t)step * BK;
-  if (!BWD || VEC) {
+  if (DMA) {
+    // activations go straight to LDS (dma_act)
+  } else if (!BWD || VEC) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) g.x[q] = ld128(t.act, t.vx + q * t.sx, k0 * 2);
   } else {
@@ -160,6 +166,30 @@ __device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int 
   }
 }
 
+// Activations of a step straight into LDS: each of a wavefront's four
+// 16-byte-per-lane buffer loads fills 1 KB of the buffer's activation
+// region, rows 64 q + 16 w .. +16 of 64 bytes each, lane l landing at byte
+// 16 l.  Lane l loads row 64 q + 16 w + l / 4, piece (l % 4) ^ ((l / 8) % 4)
+// of the step's 32 columns, so that piece c of row m sits at byte
+// 64 m + 16 (c ^ ((m / 2) % 4)) and the fragment reads are free of bank
+// conflicts.  Rows past M read zero (bounds-checked loads).
+__device__ __forceinline__ void dma_act(const Tile& t, int step, uint8_t* buf, int wu) {
+  const uint32_t k0 = (uint32_t)step * BK;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        t.act, (__attribute__((address_space(3))) void*)(buf + (64 * q + 16 * wu) * 64), 16,
+        t.vd + q * t.sx, k0 * 2, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (the loads straight into LDS count as such).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // ---------------------------------------------------------------- restore
 // Activations: pass q of the thread covers row 64 q + 16 w + (lane & 15),
 // columns 8 (lane >> 4) .. +8 of the step.
@@ -191,27 +221,41 @@ __device__ __forceinline__ void restore_table(const Tile& t, int step, const Sta
   tab = nf4_table(scale);
 }
 
-// Eight weights (codes dword j of the segment) looked up and stored.
+// Eight weights (codes dword j of the segment) looked up and stored.  The
+// forward with activations loaded straight into LDS keeps both operands in
+// natural order; otherwise the weights take the lookup's own order (the
+// activations are permuted to match on their way into LDS, the backward
+// undoes the column order at the store).
+template <bool NATURAL>
 __device__ __forceinline__ void restore_dq(const Tile& t, int j, const Stage& g,
                                            const Nf4Table& tab, uint8_t* buf) {
   const uint32_t cw = j == 0 ? g.c.x : j == 1 ? g.c.y : j == 2 ? g.c.z : g.c.w;
-  *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) = nf4_dequant8_perm(cw, tab);
+  *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) =
+      NATURAL ? nf4_dequant8(cw, tab) : nf4_dequant8_perm(cw, tab);
 }
 
-template <bool BWD>
+template <bool BWD, bool DMA>
 __device__ __forceinline__ void restore_w(const Tile& t, int step, const Stage& g, Nf4Table& tab,
                                           bool new_table, uint8_t* buf) {
   if (new_table) restore_table<BWD>(t, step, g, tab);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) restore_dq(t, j, g, tab, buf);
+  for (int j = 0; j < 4; ++j) restore_dq<!BWD && DMA>(t, j, g, tab, buf);
 }
 
 // -------------------------------------------------------------- fragments
-template <bool BWD>
+template <bool BWD, bool DMA>
 __device__ __forceinline__ void read_frags(const Tile& t, const uint8_t* buf, int ks, Frags& f) {
+  if (DMA) {
+    // swizzled 64-byte rows: slice ks of row m is piece (2 ks + h) ^ ((m / 2) % 4)
+    const uint32_t ra = t.rad ^ (32u * (uint32_t)ks);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const u32x4*>(buf + t.ra + (32 * i * LDA + 16 * ks) * 2);
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = *reinterpret_cast<const u32x4*>(buf + ra + 32 * 64 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = *reinterpret_cast<const u32x4*>(buf + t.ra + (32 * i * LDA + 16 * ks) * 2);
+  }
   if (!BWD) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -256,51 +300,61 @@ __device__ __forceinline__ void half_schedule() {
 // in f0) and slice 0 of step s+1 is read from bn.  The three buffers and the
 // stages are distinct.  The step runs as two halves of 16 MFMAs, each with
 // about half the restore work.
-template <bool BWD, bool VEC, bool EVEN>
+template <bool BWD, bool VEC, bool DMA, bool EVEN>
 __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, int s,
                                             const uint8_t* __restrict__ bc,
                                             const uint8_t* __restrict__ bn,
                                             uint8_t* __restrict__ bw, const Stage& gr,
                                             Stage& gl, Nf4Table& tab, Frags& f0, Frags& f1,
-                                            f32x16 (&acc)[4][4], int lane) {
+                                            f32x16 (&acc)[4][4], int lane, int wu) {
   // even steps open a quantization block (forward); every backward step
   // holds new rows
   constexpr bool kTable = BWD || EVEN;
   constexpr int kFirst = kTable ? 1 : 2;   // lookups in the first half
-  load_step<BWD, VEC>(p, t, s + 4, kTable, gl);
-  read_frags<BWD>(t, bc, 1, f1);
+  if (DMA) {
+    // activations of step s + 2 straight into bw, ahead of this step's other loads
+    dma_act(t, s + 2, bw, wu);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_step<BWD, VEC, DMA>(p, t, s + 4, kTable, gl);
+  read_frags<BWD, DMA>(t, bc, 1, f1);
   mma_slice(f0, acc);
-  restore_act<BWD, false>(t, s + 2, gr, bw, lane);   // s + 2 < nk - 1: a full step
+  if (!DMA) restore_act<BWD, false>(t, s + 2, gr, bw, lane);   // s + 2 < nk - 1: a full step
   if (kTable) restore_table<BWD>(t, s + 2, gr, tab);
 #pragma unroll
-  for (int j = 0; j < kFirst; ++j) restore_dq(t, j, gr, tab, bw);
+  for (int j = 0; j < kFirst; ++j) restore_dq<!BWD && DMA>(t, j, gr, tab, bw);
   half_schedule<5, true>();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = kFirst; j < 4; ++j) restore_dq(t, j, gr, tab, bw);
-  read_frags<BWD>(t, bn, 0, f0);
+  for (int j = kFirst; j < 4; ++j) restore_dq<!BWD && DMA>(t, j, gr, tab, bw);
+  read_frags<BWD, DMA>(t, bn, 0, f0);
   mma_slice(f1, acc);
   half_schedule<5, false>();
+  // the activations of step s + 1 (loaded one step ago) must be in LDS
+  // before the barrier: only this step's loads may still be in flight
+  if (DMA) wait_vmem<4 + (kTable ? 3 : 1)>();
   __syncthreads();
 }
 
 // Generic K step (any s < nk): the same work with the load, restore and
 // next-step read skipped past the end.
-template <bool BWD, bool VEC, bool EVEN>
+template <bool BWD, bool VEC, bool DMA, bool EVEN>
 __device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s,
                                        const uint8_t* bc, const uint8_t* bn, uint8_t* bw,
                                        const Stage& gr, Stage& gl, Nf4Table& tab, Frags& f0,
-                                       Frags& f1, f32x16 (&acc)[4][4], int lane) {
+                                       Frags& f1, f32x16 (&acc)[4][4], int lane, int wu) {
   constexpr bool kTable = BWD || EVEN;
-  if (s + 4 < t.nk) load_step<BWD, VEC>(p, t, s + 4, kTable, gl);
-  read_frags<BWD>(t, bc, 1, f1);
+  if (DMA && s + 2 < t.nk) dma_act(t, s + 2, bw, wu);
+  if (s + 4 < t.nk) load_step<BWD, VEC, DMA>(p, t, s + 4, kTable, gl);
+  read_frags<BWD, DMA>(t, bc, 1, f1);
   mma_slice(f0, acc);
   if (s + 2 < t.nk) {
-    restore_act<BWD>(t, s + 2, gr, bw, lane);
-    restore_w<BWD>(t, s + 2, gr, tab, kTable, bw);
+    if (!DMA) restore_act<BWD>(t, s + 2, gr, bw, lane);
+    restore_w<BWD, DMA>(t, s + 2, gr, tab, kTable, bw);
   }
-  if (s + 1 < t.nk) read_frags<BWD>(t, bn, 0, f0);
+  if (s + 1 < t.nk) read_frags<BWD, DMA>(t, bn, 0, f0);
   mma_slice(f1, acc);
+  if (DMA) wait_vmem<0>();
   __syncthreads();
 }
 
@@ -357,10 +411,15 @@ __device__ __forceinline__ void ext_load(const GemmArgs& p, const Tile& t, int64
   }
 }
 
-template <bool BWD>
+template <bool BWD, bool DMA>
 __device__ __forceinline__ void ext_store(const Tile& t, const ExtStage& E, uint8_t* buf) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(buf + t.wa + q * 64 * LDA * 2) = E.a[q];
+  for (int q = 0; q < 4; ++q) {
+    if (DMA)
+      *reinterpret_cast<u32x4*>(buf + t.wad + q * 64 * 64) = E.a[q];   // swizzled 64-byte rows
+    else
+      *reinterpret_cast<u32x4*>(buf + t.wa + q * 64 * LDA * 2) = E.a[q];
+  }
   // forward: both operands in natural order (the permutation within eights
   // belongs to the NF4 steps only); backward: factor columns in the order
   // of the restored weights, undone at the store
@@ -369,7 +428,7 @@ __device__ __forceinline__ void ext_store(const Tile& t, const ExtStage& E, uint
     *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) = BWD ? perm8_bf16(E.b[j]) : E.b[j];
 }
 
-template <bool BWD, bool VEC, bool DROP>
+template <bool BWD, bool VEC, bool DROP, bool DMA>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -422,6 +481,17 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
   t.wa = (uint32_t)(((16 * w + (lane & 15)) * LDA + 8 * (lane >> 4)) * 2);
   t.ra = (uint32_t)(((128 * wm + r32) * LDA + 8 * h) * 2);
+  {
+    // activation pieces straight into LDS: lane l of pass q holds row
+    // 64 q + 16 w + l / 4, piece (l % 4) ^ ((l / 8) % 4); the LoRA-step store
+    // and the fragment reads use the same swizzle
+    const int lr = lane >> 2;
+    t.vd = (uint32_t)(((16 * w + lr) * t.K + 8 * ((lane & 3) ^ ((lr >> 1) & 3))) * 2);
+    const int er = lane & 15, ec = lane >> 4;
+    t.wad = (uint32_t)((16 * w + er) * 64 + 16 * (ec ^ ((er >> 1) & 3)));
+    t.rad = (uint32_t)((128 * wm + r32) * 64 + 16 * (h ^ ((r32 >> 1) & 3)));
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(w);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -444,8 +514,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // the rank-r activations, buffers 0 and 1 alternating, each step's global
   // data loaded one step ahead).  Loads are unconditional: steps past K read
   // zeros (buffer loads are bounds-checked) and are never consumed.
-  load_step<BWD, VEC>(p, t, 0, true, g0);
-  load_step<BWD, VEC>(p, t, 1, BWD, g1);
+  load_step<BWD, VEC, DMA>(p, t, 0, true, g0);
+  load_step<BWD, VEC, DMA>(p, t, 1, BWD, g1);
   {
     const int64_t RP = (p.r + 31) / 32 * 32;
     const int ne = (int)(2 * RP / BK);
@@ -453,11 +523,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     ext_load<BWD>(p, t, 0, RP, tid, lane, E);
     for (int e = 0; e < ne; ++e) {
       uint8_t* be = (e & 1) ? b1 : b0;
-      ext_store<BWD>(t, E, be);
+      ext_store<BWD, DMA>(t, E, be);
       if (e + 1 < ne) ext_load<BWD>(p, t, (int64_t)(e + 1) * BK, RP, tid, lane, E);
       __syncthreads();
-      read_frags<BWD>(t, be, 0, f0);
-      read_frags<BWD>(t, be, 1, f1);
+      read_frags<BWD, DMA>(t, be, 0, f0);
+      read_frags<BWD, DMA>(t, be, 1, f1);
       mma_slice(f0, acc);
       mma_slice(f1, acc);
     }
@@ -490,33 +560,44 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
         }
   }
   // weights: steps 0 and 1 restored, 2 and 3 in flight
-  restore_act<BWD>(t, 0, g0, b0, lane);
-  restore_w<BWD>(t, 0, g0, tab, true, b0);
-  restore_act<BWD>(t, 1, g1, b1, lane);
-  restore_w<BWD>(t, 1, g1, tab, BWD, b1);
-  load_step<BWD, VEC>(p, t, 2, true, g2);
-  load_step<BWD, VEC>(p, t, 3, BWD, g0);
+  if (DMA) {
+    // activations of steps 0 and 1 straight into their buffers, then the
+    // weight loads of steps 2 and 3; step 0's activations must have landed
+    // before the barrier (step 1's, step 2's and 3's loads may be in flight)
+    dma_act(t, 0, b0, wu);
+    dma_act(t, 1, b1, wu);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    restore_act<BWD>(t, 0, g0, b0, lane);
+    restore_act<BWD>(t, 1, g1, b1, lane);
+  }
+  restore_w<BWD, DMA>(t, 0, g0, tab, true, b0);
+  restore_w<BWD, DMA>(t, 1, g1, tab, BWD, b1);
+  load_step<BWD, VEC, DMA>(p, t, 2, true, g2);
+  load_step<BWD, VEC, DMA>(p, t, 3, BWD, g0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (DMA) wait_vmem<4 + 3 + (BWD ? 3 : 1)>();
   __syncthreads();
-  read_frags<BWD>(t, b0, 0, f0);
+  read_frags<BWD, DMA>(t, b0, 0, f0);
 
   // steady state: six steps per iteration (s = 0 mod 6), so that stage,
   // buffer and table parity are fixed for each of them
   int s = 0;
   for (; s + 9 < nk; s += 6) {
-    k_step_full<BWD, VEC, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
-    k_step_full<BWD, VEC, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
-    k_step_full<BWD, VEC, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
-    k_step_full<BWD, VEC, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
-    k_step_full<BWD, VEC, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
-    k_step_full<BWD, VEC, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
+    k_step_full<BWD, VEC, DMA, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
   }
   for (; s < nk; s += 6) {
-    k_step<BWD, VEC, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
-    if (s + 1 < nk) k_step<BWD, VEC, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
-    if (s + 2 < nk) k_step<BWD, VEC, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
-    if (s + 3 < nk) k_step<BWD, VEC, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane);
-    if (s + 4 < nk) k_step<BWD, VEC, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane);
-    if (s + 5 < nk) k_step<BWD, VEC, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane);
+    k_step<BWD, VEC, DMA, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    if (s + 1 < nk) k_step<BWD, VEC, DMA, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    if (s + 2 < nk) k_step<BWD, VEC, DMA, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
+    if (s + 3 < nk) k_step<BWD, VEC, DMA, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    if (s + 4 < nk) k_step<BWD, VEC, DMA, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    if (s + 5 < nk) k_step<BWD, VEC, DMA, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
   }
 
   // ---- epilogue: RNE to BF16, staged through LDS so that the global stores
@@ -564,30 +645,39 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
 }
 
-template <bool BWD, bool VEC, bool DROP>
+template <bool BWD, bool VEC, bool DROP, bool DMA>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<BWD, VEC, DROP>),
+      reinterpret_cast<const void*>(&k_gemm<BWD, VEC, DROP, DMA>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BWD>());
   if (attr != hipSuccess) return attr;
   const int64_t NOUT = BWD ? a.d_in : a.d_out;
   const int64_t tiles = ((NOUT + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   weight_kernel_begin(st);
-  hipLaunchKernelGGL((k_gemm<BWD, VEC, DROP>), dim3((unsigned)tiles), dim3(256), lds_bytes<BWD>(),
-                     st, a);
+  hipLaunchKernelGGL((k_gemm<BWD, VEC, DROP, DMA>), dim3((unsigned)tiles), dim3(256),
+                     lds_bytes<BWD>(), st, a);
   weight_kernel_end(st);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) {
-  return launch_gemm<false, true, false>(a, st);
+  // K = d_in is a multiple of 64: every step's activations are whole rows
+  return launch_gemm<false, true, false, true>(a, st);
 }
 hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
-  // dY rows are 16-byte aligned exactly when d_out % 8 == 0
+  // dY rows are 16-byte aligned exactly when d_out % 8 == 0; activations go
+  // straight to LDS when every K step is whole (d_out % 32 == 0), else
+  // through registers, which clear the columns past K of the last step
   const bool vec = (a.d_out % 8) == 0;
-  if (a.keep)
-    return vec ? launch_gemm<true, true, true>(a, st) : launch_gemm<true, false, true>(a, st);
-  return vec ? launch_gemm<true, true, false>(a, st) : launch_gemm<true, false, false>(a, st);
+  const bool dma = (a.d_out % BK) == 0;
+  if (a.keep) {
+    if (dma) return launch_gemm<true, true, true, true>(a, st);
+    return vec ? launch_gemm<true, true, true, false>(a, st)
+               : launch_gemm<true, false, true, false>(a, st);
+  }
+  if (dma) return launch_gemm<true, true, false, true>(a, st);
+  return vec ? launch_gemm<true, true, false, false>(a, st)
+             : launch_gemm<true, false, false, false>(a, st);
 }
 
 }  // namespace qlora
