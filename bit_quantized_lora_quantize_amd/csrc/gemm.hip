@@ -61,6 +61,13 @@ constexpr int buf_bytes() { return kABytes + (BWD ? kBBwdBytes : kBFwdBytes); }
 template <bool BWD>
 constexpr int lds_bytes() { return kNumBuf * buf_bytes<BWD>(); }
 constexpr int kXcds = 8;
+// VALU instructions placed after each MFMA of the two halves of a step
+#ifndef QLORA_GEMM_V1
+#define QLORA_GEMM_V1 3
+#endif
+#ifndef QLORA_GEMM_V2
+#define QLORA_GEMM_V2 5
+#endif
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -323,13 +330,13 @@ __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, in
   if (kTable) restore_table<BWD>(t, s + 2, gr, tab);
 #pragma unroll
   for (int j = 0; j < kFirst; ++j) restore_dq<!BWD && DMA>(t, j, gr, tab, bw);
-  half_schedule<5, true>();
+  half_schedule<QLORA_GEMM_V1, true>();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = kFirst; j < 4; ++j) restore_dq<!BWD && DMA>(t, j, gr, tab, bw);
   read_frags<BWD, DMA>(t, bn, 0, f0);
   mma_slice(f1, acc);
-  half_schedule<5, false>();
+  half_schedule<QLORA_GEMM_V2, false>();
   // the activations of step s + 1 (loaded one step ago) must be in LDS
   // before the barrier: only this step's loads may still be in flight
   if (DMA) wait_vmem<4 + (kTable ? 3 : 1)>();
