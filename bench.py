@@ -61,8 +61,8 @@ R, ALPHA = 64, 16.0
 # step), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a
 # 1024 MB device copy (factors 2.0 and 1.0).  Valid only for the kernel
 # sources with this SHA-1 (gemm_source_sha1); reported as null otherwise.
-GEMM_TRAFFIC_BYTES = 268.80e6
-GEMM_TRAFFIC_SHA1 = "ee4279b2479bd403d90fd56bb4ffca3009f51cee"
+GEMM_TRAFFIC_BYTES = 268.87e6
+GEMM_TRAFFIC_SHA1 = "7e723112e3df14056cc4f891177f20677a5f08f3"
 
 
 def gemm_source_sha1():
