@@ -14,12 +14,12 @@
 // offset_hi) under key (seed_lo, seed_hi) and is kept when that word is at
 // least thr = floor(p * 2^32).
 //
-// One thread owns two neighbouring columns and 32 rows: eight generator
-// calls per column give the 32 decisions, which become one keep word per
-// column (bit m % 32 of word [k][m / 32], the layout the input-gradient GEMM
-// reads), and the thread's 32 row pairs of X are copied with the dropped
-// elements cleared.  A wavefront spans 64 column pairs, so every X access is
-// a 256-byte row segment.
+// One thread owns two neighbouring columns and 16 rows: four generator calls
+// per column give the 16 decisions, half of a keep word per column (bit
+// m % 32 of word [k][m / 32], the layout the input-gradient GEMM reads), and
+// the thread's 16 row pairs of X are copied with the dropped elements
+// cleared.  A wavefront spans 64 column pairs, so every X access is a
+// 256-byte row segment.
 #include "qlora_device.h"
 #include "qlora_kernels.h"
 
@@ -52,12 +52,14 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
   }
 }
 
-// Keep bits of column k for rows 32 w .. 32 w + 31 (bit j = row 32 w + j).
-__device__ __forceinline__ uint32_t keep_word(uint32_t k, uint32_t w, const DropoutArgs& a) {
+// Keep bits of column k for rows 32 w + 16 hh .. +16 (bit j = row 32 w +
+// 16 hh + j): four generator calls.
+__device__ __forceinline__ uint32_t keep_half(uint32_t k, uint32_t w, uint32_t hh,
+                                              const DropoutArgs& a) {
   uint32_t bits = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t c0 = k, c1 = 8 * w + j, c2 = a.off_lo, c3 = a.off_hi;
+  for (int j = 0; j < 4; ++j) {
+    uint32_t c0 = k, c1 = 8 * w + 4 * hh + j, c2 = a.off_lo, c3 = a.off_hi;
     philox4x32_10(c0, c1, c2, c3, a.key_lo, a.key_hi);
     bits |= (c0 >= a.thr ? 1u : 0u) << (4 * j);
     bits |= (c1 >= a.thr ? 1u : 0u) << (4 * j + 1);
@@ -67,32 +69,36 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t k, uint32_t w, const Drop
   return bits;
 }
 
+// One thread per (column pair, 16 rows): two threads fill one keep word,
+// each its 16-bit half.
 __global__ __launch_bounds__(256) void k_dropout(DropoutArgs a) {
   const int64_t pairs = a.d / 2;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= pairs * a.ldw) return;
-  const uint32_t w = (uint32_t)(tid / pairs);
-  const uint32_t k = (uint32_t)(2 * (tid - (int64_t)w * pairs));
-  const int64_t m0 = 32 * (int64_t)w;
-  const int rows = a.M - m0 < 32 ? (int)(a.M - m0) : 32;
+  if (tid >= pairs * 2 * a.ldw) return;
+  const int64_t wh = tid / pairs;                       // 16-row unit: word w, half hh
+  const uint32_t w = (uint32_t)(wh >> 1), hh = (uint32_t)(wh & 1);
+  const uint32_t k = (uint32_t)(2 * (tid - wh * pairs));
+  const int64_t m0 = 32 * (int64_t)w + 16 * hh;
+  const int rows = a.M - m0 < 16 ? (a.M - m0 > 0 ? (int)(a.M - m0) : 0) : 16;
   // row pairs of X first, so the loads are in flight during the generator
-  uint32_t x[32];
+  uint32_t x[16];
   if (a.Xm) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
+    for (int j = 0; j < 16; ++j)
       x[j] = j < rows ? *reinterpret_cast<const uint32_t*>(a.X + (m0 + j) * a.d + k) : 0u;
   }
   // rows past M get keep bit 0
-  const uint32_t live = rows == 32 ? 0xFFFFFFFFu : (1u << rows) - 1u;
-  const uint32_t b0 = keep_word(k, w, a) & live;
-  const uint32_t b1 = keep_word(k + 1, w, a) & live;
+  const uint32_t live = (1u << rows) - 1u;
+  const uint32_t b0 = keep_half(k, w, hh, a) & live;
+  const uint32_t b1 = keep_half(k + 1, w, hh, a) & live;
   if (a.keep) {
-    a.keep[(int64_t)k * a.ldw + w] = b0;
-    a.keep[(int64_t)(k + 1) * a.ldw + w] = b1;
+    uint16_t* kh = reinterpret_cast<uint16_t*>(a.keep);
+    kh[2 * ((int64_t)k * a.ldw + w) + hh] = (uint16_t)b0;
+    kh[2 * ((int64_t)(k + 1) * a.ldw + w) + hh] = (uint16_t)b1;
   }
   if (a.Xm) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < 16; ++j) {
       if (j >= rows) break;
       const uint32_t lo = ((b0 >> j) & 1u) ? 0x0000FFFFu : 0u;
       const uint32_t hi = ((b1 >> j) & 1u) ? 0xFFFF0000u : 0u;
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(256) void k_dropout(DropoutArgs a) {
 }
 
 hipError_t launch_dropout(const DropoutArgs& a, hipStream_t st) {
-  const int64_t threads = (a.d / 2) * a.ldw;
+  const int64_t threads = (a.d / 2) * 2 * a.ldw;
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(k_dropout, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
