@@ -62,7 +62,7 @@ R, ALPHA = 64, 16.0
 # 1024 MB device copy (factors 2.0 and 1.0).  Valid only for the kernel
 # sources with this SHA-1 (gemm_source_sha1); reported as null otherwise.
 GEMM_TRAFFIC_BYTES = 268.87e6
-GEMM_TRAFFIC_SHA1 = "7e723112e3df14056cc4f891177f20677a5f08f3"
+GEMM_TRAFFIC_SHA1 = "1c3d4f97a1a95f8483626521c96ab352cf17d203"
 
 
 def gemm_source_sha1():

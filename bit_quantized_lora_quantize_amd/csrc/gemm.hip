@@ -337,8 +337,11 @@ __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, in
   read_frags<BWD, DMA>(t, bn, 0, f0);
   mma_slice(f1, acc);
   half_schedule<QLORA_GEMM_V2, false>();
-  // the activations of step s + 1 (loaded one step ago) must be in LDS
-  // before the barrier: only this step's loads may still be in flight
+  // the activations of step s + 2 (loads started at the top of this step)
+  // must be in LDS before the barrier, since the next step reads slice 0 of
+  // step s + 2: the barrier's release fence waits for every load straight
+  // into LDS, and wait_vmem only bounds what else may stay in flight (this
+  // step's weight loads)
   if (DMA) wait_vmem<4 + (kTable ? 3 : 1)>();
   __syncthreads();
 }
@@ -569,8 +572,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // weights: steps 0 and 1 restored, 2 and 3 in flight
   if (DMA) {
     // activations of steps 0 and 1 straight into their buffers, then the
-    // weight loads of steps 2 and 3; step 0's activations must have landed
-    // before the barrier (step 1's, step 2's and 3's loads may be in flight)
+    // weight loads of steps 2 and 3; both activation steps land before the
+    // barrier (its release fence waits for loads straight into LDS), the
+    // weight loads may still be in flight
     dma_act(t, 0, b0, wu);
     dma_act(t, 1, b1, wu);
     __builtin_amdgcn_sched_barrier(0);

@@ -87,6 +87,7 @@ SHAPES = [  # (d_out, d_in, M, r): small-M weight streaming and the fused GEMM
     (513, 1088, 33, 24),
     (264, 320, 300, 40),
     (96, 512, 129, 7),
+    (264, 320, 1100, 40),   # three 512-token GEMM tiles, ragged
 ]
 
 

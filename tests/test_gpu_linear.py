@@ -69,6 +69,7 @@ SMALL = [  # (d_out, d_in, M, r)
     (72, 192, 70, 100),     # large-M rank path, r in (64, 128]
     (136, 256, 48, 256),    # large-M rank path at the maximum rank
     (264, 320, 300, 40),    # two row tiles of the weight kernel, ragged in M and N
+    (264, 320, 1100, 40),   # three 512-token tiles of the GEMM, ragged in M, N and K
 ]
 
 
