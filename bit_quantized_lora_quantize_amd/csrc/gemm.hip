@@ -124,8 +124,11 @@ struct Tile {
 
 // ------------------------------------------------------------------ loads
 // VEC: activation rows 16-byte aligned (K % 8 == 0); always so in the
-// forward direction (K = d_in, a multiple of 64).
-template <bool BWD, bool VEC, bool DMA>
+// forward direction (K = d_in, a multiple of 64).  WIDE (backward): the
+// packed weights exceed what one buffer descriptor reaches with 32-bit
+// offsets, so each step builds descriptors based at its own rows; otherwise
+// one descriptor per tile serves every step through its scalar offset.
+template <bool BWD, bool VEC, bool DMA, bool WIDE>
 __device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int step,
                                           bool with_scale, Stage& g) {
   const uint32_t k0 = (uint32_t)step * BK;
@@ -156,8 +159,15 @@ __device__ __forceinline__ void load_step(const GemmArgs& p, const Tile& t, int 
       const int64_t blk = t.blk0 + k0 / 64;
       g.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t.s2, (uint32_t)(blk >> 8) * 4, 0, 0));
     }
-  } else {
+  } else if (!WIDE) {
     // row k0 + nl of W, columns c0 + 32 cg .. +32
+    const uint32_t nb = (uint32_t)(p.d_in / kBlock);
+    g.c = ld128(t.codes, (uint32_t)(t.nl * (p.d_in / 2) + 16 * t.cg), k0 * (uint32_t)(p.d_in / 2));
+    g.sc = __builtin_amdgcn_raw_buffer_load_b8(t.scodes, (uint32_t)t.nl * nb + (uint32_t)(t.cg >> 1),
+                                               k0 * nb, 0);
+    const int64_t blk = ((int64_t)k0 + t.nl) * nb + t.n0 / kBlock + (t.cg >> 1);
+    g.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(t.s2, (uint32_t)(blk >> 8) * 4, 0, 0));
+  } else {
     const int64_t row = (int64_t)k0;
     const int64_t nb = p.d_in / kBlock;
     const uint8_t* cbase = p.codes + row * (p.d_in / 2) + t.n0 / 2;
@@ -190,7 +200,11 @@ __device__ __forceinline__ void dma_act(const Tile& t, int step, uint8_t* buf, i
 }
 
 // Wait until at most N vector-memory operations of this wavefront are
-// outstanding (the loads straight into LDS count as such).
+// outstanding (the loads straight into LDS count as such).  Every barrier
+// after such loads carries its own wait: the compiler's fence at
+// __syncthreads does not track them through every control-flow shape.
+// Operations issued after the awaited ones (spill stores included) only make
+// a count stricter.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -307,7 +321,7 @@ __device__ __forceinline__ void half_schedule() {
 // in f0) and slice 0 of step s+1 is read from bn.  The three buffers and the
 // stages are distinct.  The step runs as two halves of 16 MFMAs, each with
 // about half the restore work.
-template <bool BWD, bool VEC, bool DMA, bool EVEN>
+template <bool BWD, bool VEC, bool DMA, bool WIDE, bool EVEN>
 __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, int s,
                                             const uint8_t* __restrict__ bc,
                                             const uint8_t* __restrict__ bn,
@@ -323,7 +337,7 @@ __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, in
     dma_act(t, s + 2, bw, wu);
     __builtin_amdgcn_sched_barrier(0);
   }
-  load_step<BWD, VEC, DMA>(p, t, s + 4, kTable, gl);
+  load_step<BWD, VEC, DMA, WIDE>(p, t, s + 4, kTable, gl);
   read_frags<BWD, DMA>(t, bc, 1, f1);
   mma_slice(f0, acc);
   if (!DMA) restore_act<BWD, false>(t, s + 2, gr, bw, lane);   // s + 2 < nk - 1: a full step
@@ -339,23 +353,22 @@ __device__ __forceinline__ void k_step_full(const GemmArgs& p, const Tile& t, in
   half_schedule<QLORA_GEMM_V2, false>();
   // the activations of step s + 2 (loads started at the top of this step)
   // must be in LDS before the barrier, since the next step reads slice 0 of
-  // step s + 2: the barrier's release fence waits for every load straight
-  // into LDS, and wait_vmem only bounds what else may stay in flight (this
-  // step's weight loads)
-  if (DMA) wait_vmem<4 + (kTable ? 3 : 1)>();
+  // step s + 2; only the weight loads issued after them (three with a new
+  // table, else one) may stay in flight
+  if (DMA) wait_vmem<kTable ? 3 : 1>();
   __syncthreads();
 }
 
 // Generic K step (any s < nk): the same work with the load, restore and
 // next-step read skipped past the end.
-template <bool BWD, bool VEC, bool DMA, bool EVEN>
+template <bool BWD, bool VEC, bool DMA, bool WIDE, bool EVEN>
 __device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s,
                                        const uint8_t* bc, const uint8_t* bn, uint8_t* bw,
                                        const Stage& gr, Stage& gl, Nf4Table& tab, Frags& f0,
                                        Frags& f1, f32x16 (&acc)[4][4], int lane, int wu) {
   constexpr bool kTable = BWD || EVEN;
   if (DMA && s + 2 < t.nk) dma_act(t, s + 2, bw, wu);
-  if (s + 4 < t.nk) load_step<BWD, VEC, DMA>(p, t, s + 4, kTable, gl);
+  if (s + 4 < t.nk) load_step<BWD, VEC, DMA, WIDE>(p, t, s + 4, kTable, gl);
   read_frags<BWD, DMA>(t, bc, 1, f1);
   mma_slice(f0, acc);
   if (s + 2 < t.nk) {
@@ -364,7 +377,7 @@ __device__ __forceinline__ void k_step(const GemmArgs& p, const Tile& t, int s,
   }
   if (s + 1 < t.nk) read_frags<BWD, DMA>(t, bn, 0, f0);
   mma_slice(f1, acc);
-  if (DMA) wait_vmem<0>();
+  if (DMA) wait_vmem<0>();   // this step's loads straight into LDS, whatever was issued
   __syncthreads();
 }
 
@@ -438,7 +451,7 @@ __device__ __forceinline__ void ext_store(const Tile& t, const ExtStage& E, uint
     *reinterpret_cast<u32x4*>(buf + kABytes + t.wb + 16 * j) = BWD ? perm8_bf16(E.b[j]) : E.b[j];
 }
 
-template <bool BWD, bool VEC, bool DROP, bool DMA>
+template <bool BWD, bool VEC, bool DROP, bool DMA, bool WIDE>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -483,6 +496,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   } else {
     t.nl = tid & 31;
     t.cg = tid >> 5;
+    if (!WIDE) {
+      // whole rows of W from column c0 on; each step adds its rows as the
+      // scalar offset
+      t.codes = make_rsrc(p.codes + t.n0 / 2, p.d_out * (p.d_in / 2) - t.n0 / 2);
+      t.scodes = make_rsrc(p.scodes + t.n0 / kBlock, p.d_out * nb - t.n0 / kBlock);
+    }
     t.wb = (uint32_t)((t.nl * LDT + 32 * t.cg) * 2);
     // transposing read: lane group g = lane / 16 covers columns
     // 16 (g & 1) .. +16 and contraction rows 8 (g >> 1) .. +4 (first read)
@@ -524,8 +543,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // the rank-r activations, buffers 0 and 1 alternating, each step's global
   // data loaded one step ahead).  Loads are unconditional: steps past K read
   // zeros (buffer loads are bounds-checked) and are never consumed.
-  load_step<BWD, VEC, DMA>(p, t, 0, true, g0);
-  load_step<BWD, VEC, DMA>(p, t, 1, BWD, g1);
+  load_step<BWD, VEC, DMA, WIDE>(p, t, 0, true, g0);
+  load_step<BWD, VEC, DMA, WIDE>(p, t, 1, BWD, g1);
   {
     const int64_t RP = (p.r + 31) / 32 * 32;
     const int ne = (int)(2 * RP / BK);
@@ -573,8 +592,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   if (DMA) {
     // activations of steps 0 and 1 straight into their buffers, then the
     // weight loads of steps 2 and 3; both activation steps land before the
-    // barrier (its release fence waits for loads straight into LDS), the
-    // weight loads may still be in flight
+    // barrier, the weight loads (3 + 3 backward, 3 + 1 forward) may still be
+    // in flight
     dma_act(t, 0, b0, wu);
     dma_act(t, 1, b1, wu);
     __builtin_amdgcn_sched_barrier(0);
@@ -584,10 +603,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
   restore_w<BWD, DMA>(t, 0, g0, tab, true, b0);
   restore_w<BWD, DMA>(t, 1, g1, tab, BWD, b1);
-  load_step<BWD, VEC, DMA>(p, t, 2, true, g2);
-  load_step<BWD, VEC, DMA>(p, t, 3, BWD, g0);
+  load_step<BWD, VEC, DMA, WIDE>(p, t, 2, true, g2);
+  load_step<BWD, VEC, DMA, WIDE>(p, t, 3, BWD, g0);
   __builtin_amdgcn_sched_barrier(0);
-  if (DMA) wait_vmem<4 + 3 + (BWD ? 3 : 1)>();
+  if (DMA) wait_vmem<3 + (BWD ? 3 : 1)>();
   __syncthreads();
   read_frags<BWD, DMA>(t, b0, 0, f0);
 
@@ -595,20 +614,20 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // buffer and table parity are fixed for each of them
   int s = 0;
   for (; s + 9 < nk; s += 6) {
-    k_step_full<BWD, VEC, DMA, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
-    k_step_full<BWD, VEC, DMA, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
-    k_step_full<BWD, VEC, DMA, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
-    k_step_full<BWD, VEC, DMA, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
-    k_step_full<BWD, VEC, DMA, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
-    k_step_full<BWD, VEC, DMA, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, WIDE, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, WIDE, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, WIDE, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, WIDE, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, WIDE, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    k_step_full<BWD, VEC, DMA, WIDE, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
   }
   for (; s < nk; s += 6) {
-    k_step<BWD, VEC, DMA, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
-    if (s + 1 < nk) k_step<BWD, VEC, DMA, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
-    if (s + 2 < nk) k_step<BWD, VEC, DMA, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
-    if (s + 3 < nk) k_step<BWD, VEC, DMA, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
-    if (s + 4 < nk) k_step<BWD, VEC, DMA, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
-    if (s + 5 < nk) k_step<BWD, VEC, DMA, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
+    k_step<BWD, VEC, DMA, WIDE, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    if (s + 1 < nk) k_step<BWD, VEC, DMA, WIDE, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    if (s + 2 < nk) k_step<BWD, VEC, DMA, WIDE, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
+    if (s + 3 < nk) k_step<BWD, VEC, DMA, WIDE, false>(p, t, s + 3, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
+    if (s + 4 < nk) k_step<BWD, VEC, DMA, WIDE, true>(p, t, s + 4, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
+    if (s + 5 < nk) k_step<BWD, VEC, DMA, WIDE, false>(p, t, s + 5, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
   }
 
   // ---- epilogue: RNE to BF16, staged through LDS so that the global stores
@@ -656,16 +675,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
 }
 
-template <bool BWD, bool VEC, bool DROP, bool DMA>
+template <bool BWD, bool VEC, bool DROP, bool DMA, bool WIDE = false>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm<BWD, VEC, DROP, DMA>),
+      reinterpret_cast<const void*>(&k_gemm<BWD, VEC, DROP, DMA, WIDE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<BWD>());
   if (attr != hipSuccess) return attr;
   const int64_t NOUT = BWD ? a.d_in : a.d_out;
   const int64_t tiles = ((NOUT + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   weight_kernel_begin(st);
-  hipLaunchKernelGGL((k_gemm<BWD, VEC, DROP, DMA>), dim3((unsigned)tiles), dim3(256),
+  hipLaunchKernelGGL((k_gemm<BWD, VEC, DROP, DMA, WIDE>), dim3((unsigned)tiles), dim3(256),
                      lds_bytes<BWD>(), st, a);
   weight_kernel_end(st);
   return hipGetLastError();
@@ -675,20 +694,29 @@ hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st) {
   // K = d_in is a multiple of 64: every step's activations are whole rows
   return launch_gemm<false, true, false, true>(a, st);
 }
-hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
+template <bool WIDE>
+static hipError_t launch_gemm_bwd_t(const GemmArgs& a, hipStream_t st) {
   // dY rows are 16-byte aligned exactly when d_out % 8 == 0; activations go
   // straight to LDS when every K step is whole (d_out % 32 == 0), else
   // through registers, which clear the columns past K of the last step
   const bool vec = (a.d_out % 8) == 0;
   const bool dma = (a.d_out % BK) == 0;
   if (a.keep) {
-    if (dma) return launch_gemm<true, true, true, true>(a, st);
-    return vec ? launch_gemm<true, true, true, false>(a, st)
-               : launch_gemm<true, false, true, false>(a, st);
+    if (dma) return launch_gemm<true, true, true, true, WIDE>(a, st);
+    return vec ? launch_gemm<true, true, true, false, WIDE>(a, st)
+               : launch_gemm<true, false, true, false, WIDE>(a, st);
   }
-  if (dma) return launch_gemm<true, true, false, true>(a, st);
-  return vec ? launch_gemm<true, true, false, false>(a, st)
-             : launch_gemm<true, false, false, false>(a, st);
+  if (dma) return launch_gemm<true, true, false, true, WIDE>(a, st);
+  return vec ? launch_gemm<true, true, false, false, WIDE>(a, st)
+             : launch_gemm<true, false, false, false, WIDE>(a, st);
+}
+
+hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
+  // one descriptor over the packed codes reaches them all with 32-bit
+  // offsets when they stay below 2^31 bytes (every weight of the 7B and 65B
+  // models: at most 90 MB)
+  const bool wide = a.d_out * (a.d_in / 2) > int64_t(0x7FFFFFFF);
+  return wide ? launch_gemm_bwd_t<true>(a, st) : launch_gemm_bwd_t<false>(a, st);
 }
 
 }  // namespace qlora
