@@ -132,14 +132,15 @@ __device__ __forceinline__ u32x4 nf4_dequant8_perm(uint32_t codes, const Nf4Tabl
 }
 
 // Same lookup, natural element order: (e0,e1), (e2,e3), (e4,e5), (e6,e7).
+// The indices are put in element order before the lookups (two byte
+// permutes of the even and odd nibbles), so each lookup yields the low and
+// high bytes of four consecutive weights and one permute per dword pairs them.
 __device__ __forceinline__ u32x4 nf4_dequant8(uint32_t codes, const Nf4Table& t) {
-  uint32_t le, he, lo, ho;
-  nf4_lookup4(codes & 0x0F0F0F0Fu, t, le, he);
-  nf4_lookup4((codes >> 4) & 0x0F0F0F0Fu, t, lo, ho);
-  uint32_t l03 = __builtin_amdgcn_perm(lo, le, 0x05010400u);  // L of e0 e1 e2 e3
-  uint32_t l47 = __builtin_amdgcn_perm(lo, le, 0x07030602u);
-  uint32_t h03 = __builtin_amdgcn_perm(ho, he, 0x05010400u);
-  uint32_t h47 = __builtin_amdgcn_perm(ho, he, 0x07030602u);
+  const uint32_t ev = codes & 0x0F0F0F0Fu;            // e0 e2 e4 e6
+  const uint32_t od = (codes >> 4) & 0x0F0F0F0Fu;     // e1 e3 e5 e7
+  uint32_t l03, h03, l47, h47;
+  nf4_lookup4(__builtin_amdgcn_perm(od, ev, 0x05010400u), t, l03, h03);   // e0 e1 e2 e3
+  nf4_lookup4(__builtin_amdgcn_perm(od, ev, 0x07030602u), t, l47, h47);   // e4 e5 e6 e7
   u32x4 r;
   r.x = __builtin_amdgcn_perm(h03, l03, 0x05010400u);
   r.y = __builtin_amdgcn_perm(h03, l03, 0x07030602u);
