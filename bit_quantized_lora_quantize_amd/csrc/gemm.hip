@@ -611,9 +611,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   read_frags<BWD, DMA>(t, b0, 0, f0);
 
   // steady state: six steps per iteration (s = 0 mod 6), so that stage,
-  // buffer and table parity are fixed for each of them
+  // buffer and table parity are fixed for each of them.  A full step only
+  // needs the next step to exist (it reads slice 0 of step s + 1): its
+  // loads and restores for steps s + 2 and s + 4 past K read zeros or
+  // in-bounds data that no step consumes, into buffers and registers already
+  // consumed.  Activations copied through registers take the generic step
+  // from two steps before the last one on, so that the last, partial step
+  // clears its columns past K.
+  constexpr int kMargin = DMA ? 7 : 10;   // iteration s runs while s + kMargin <= nk
   int s = 0;
-  for (; s + 9 < nk; s += 6) {
+  for (; s + kMargin <= nk; s += 6) {
     k_step_full<BWD, VEC, DMA, WIDE, true>(p, t, s + 0, b0, b1, b2, g2, g1, tab, f0, f1, acc, lane, wu);
     k_step_full<BWD, VEC, DMA, WIDE, false>(p, t, s + 1, b1, b2, b0, g0, g2, tab, f0, f1, acc, lane, wu);
     k_step_full<BWD, VEC, DMA, WIDE, true>(p, t, s + 2, b2, b0, b1, g1, g0, tab, f0, f1, acc, lane, wu);
