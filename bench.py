@@ -61,8 +61,8 @@ R, ALPHA = 64, 16.0
 # step), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a
 # 1024 MB device copy (factors 2.0 and 1.0).  Valid only for the kernel
 # sources with this SHA-1 (gemm_source_sha1); reported as null otherwise.
-GEMM_TRAFFIC_BYTES = 268.87e6
-GEMM_TRAFFIC_SHA1 = "1c3d4f97a1a95f8483626521c96ab352cf17d203"
+GEMM_TRAFFIC_BYTES = 273.41e6
+GEMM_TRAFFIC_SHA1 = "2a717c62cde607d0d72e591e19373b16d2881534"
 
 
 def gemm_source_sha1():
