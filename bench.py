@@ -560,7 +560,7 @@ def main():
                          "kernel of known size, for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     skip = set(s for s in args.skip.split(",") if s)

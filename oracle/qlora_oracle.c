@@ -19,7 +19,7 @@
  * bit tricks, so that a reader can check each against its definition.
  * Matrix products accumulate in FP64 over exactly-represented inputs.
  *
- * Readings where the pages are silent (each listed in the design doc):
+ * Readings where the pages are silent:
  *   - flatten order is row-major over W[d_out, d_in]; blocks of 64 follow it;
  *   - x = w / absmax is an IEEE FP32 division; a zero block maps to index 7;
  *   - nearest-level ties go to the lower index;
