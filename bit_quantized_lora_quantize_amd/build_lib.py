@@ -1,5 +1,10 @@
 """Build libqlora.so in-tree with hipcc for gfx950 (CDNA4).
 
+Also builds libqlora_wide.so, a test build identical except that the
+backward GEMM takes its per-step weight-descriptor path (otherwise used only
+for packed weights beyond 2^31 bytes) at every size, so that tests can check
+that path against the oracle at ordinary sizes.
+
 Usage: python -m bit_quantized_lora_quantize_amd.build_lib [--jobs N]
 """
 from __future__ import annotations
@@ -16,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libqlora")
 LIB = os.path.join(PKG, "libqlora.so")
+LIB_WIDE = os.path.join(PKG, "libqlora_wide.so")
 
 SOURCES = ["quant.hip", "quant_blocked.hip", "lora.hip", "gemv.hip", "gemm.hip", "merge.hip", "optim.hip", "dropout.hip", "api.cpp"]
 
@@ -41,9 +47,9 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, tag: str = "", defines: tuple = ()) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
+    cmd = [HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
@@ -55,16 +61,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 5) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 5) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        wide = ex.submit(_compile, "gemm.hip", "_wide", ("-DQLORA_WIDE_CODE_BYTES=0",))
+        objs = list(ex.map(_compile, SOURCES))
+        wide_obj = wide.result()
+    _link(objs, LIB)
+    _link([wide_obj if os.path.basename(o) == "gemm.hip.o" else o for o in objs], LIB_WIDE)
     return LIB
 
 

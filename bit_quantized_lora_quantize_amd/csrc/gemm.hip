@@ -718,11 +718,17 @@ static hipError_t launch_gemm_bwd_t(const GemmArgs& a, hipStream_t st) {
              : launch_gemm<true, false, false, false, WIDE>(a, st);
 }
 
+// Largest packed-code size (bytes) that one descriptor per tile serves.  A
+// test build sets it to 0 so that every backward takes the per-step path.
+#ifndef QLORA_WIDE_CODE_BYTES
+#define QLORA_WIDE_CODE_BYTES 0x7FFFFFFF
+#endif
+
 hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st) {
   // one descriptor over the packed codes reaches them all with 32-bit
   // offsets when they stay below 2^31 bytes (every weight of the 7B and 65B
   // models: at most 90 MB)
-  const bool wide = a.d_out * (a.d_in / 2) > int64_t(0x7FFFFFFF);
+  const bool wide = a.d_out * (a.d_in / 2) > int64_t(QLORA_WIDE_CODE_BYTES);
   return wide ? launch_gemm_bwd_t<true>(a, st) : launch_gemm_bwd_t<false>(a, st);
 }
 

@@ -4,9 +4,12 @@ The HIP path and the oracle receive the same seeded bytes; the oracle never
 sees a value the HIP path produced.  Tolerances (floating-point outputs vs the
 FP64-accumulating oracle): normwise-max relative 1e-2 and relative-Frobenius
 2e-3; quantized bytes and restored BF16 weights are compared bit for bit."""
+import contextlib
+import os
 import sys
 
 import numpy as np
+import pytest
 import torch
 
 FRO_TOL = 2e-3
@@ -58,3 +61,21 @@ def assert_quant_equal(w, ref):
         "second-level scales differ"
     assert np.float32(w.scale_mean.item()).view(np.uint32) == np.float32(mean).view(np.uint32), \
         "scale mean differs"
+
+
+@contextlib.contextmanager
+def wide_weight_library():
+    """Run the enclosed calls on libqlora_wide.so, the in-tree test build whose
+    backward GEMM builds its weight descriptors per K step at every size (the
+    production library does so only for packed weights beyond 2^31 bytes)."""
+    from bit_quantized_lora_quantize_amd import _lib
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libqlora_wide.so")
+    if not os.path.exists(path):
+        pytest.fail("libqlora_wide.so is not built (python -m bit_quantized_lora_quantize_amd.build_lib)")
+    saved = (_lib.LIB_PATH, _lib._lib)
+    _lib.LIB_PATH, _lib._lib = path, None
+    try:
+        yield
+    finally:
+        torch.cuda.synchronize()
+        _lib.LIB_PATH, _lib._lib = saved

@@ -36,6 +36,19 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, f)
 
 
+def test_wide_descriptor_test_build_exports_the_same(L):
+    """libqlora_wide.so (the test build whose backward GEMM takes the per-step
+    weight descriptors at every size) is built beside the library and exports
+    the same entry points."""
+    import os
+    wide = os.path.join(os.path.dirname(_lib.LIB_PATH), "libqlora_wide.so")
+    assert os.path.exists(wide), "libqlora_wide.so is not built"
+    out = subprocess.run(["nm", "-D", "--defined-only", wide], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(q.header_functions()) <= exported
+
+
 def test_status_strings_and_version(L):
     assert q.qlora_abi_version() >> 16 == 1
     for s in (OK, ENULL, ESHAPE, EALIGN, EWS, EHIP):

@@ -8,7 +8,7 @@ import torch
 
 import bit_quantized_lora_quantize_amd as q
 from bit_quantized_lora_quantize_amd import inputs
-from parity_util import assert_close, bits16, f32, oracle_quant, say
+from parity_util import assert_close, bits16, f32, oracle_quant, say, wide_weight_library
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -94,6 +94,14 @@ SHAPES = [  # (d_out, d_in, M, r): small-M weight streaming and the fused GEMM
 @pytest.mark.parametrize("shape", SHAPES)
 def test_dropout_linear(orc, shape):
     _check_dropout(orc, shape, 110 + SHAPES.index(shape))
+
+
+def test_dropout_wide_weight_descriptors(orc):
+    """The masked backward GEMM with per-step weight descriptors (the test
+    build that takes them at every size) against the oracle."""
+    with wide_weight_library():
+        _check_dropout(orc, (264, 320, 1100, 40), 145)
+        _check_dropout(orc, (256, 512, 300, 16), 146)
 
 
 def test_dropout_high_rate(orc):

@@ -7,7 +7,8 @@ import torch
 
 import bit_quantized_lora_quantize_amd as q
 from bit_quantized_lora_quantize_amd import inputs
-from parity_util import assert_close, assert_quant_equal, f32, oracle_quant, rel_errors, say
+from parity_util import (assert_close, assert_quant_equal, f32, oracle_quant, rel_errors, say,
+                         wide_weight_library)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -71,6 +72,21 @@ SMALL = [  # (d_out, d_in, M, r)
     (264, 320, 300, 40),    # two row tiles of the weight kernel, ragged in M and N
     (264, 320, 1100, 40),   # three 512-token tiles of the GEMM, ragged in M, N and K
 ]
+
+
+# backward activation paths: straight into LDS (d_out % 32 == 0), 16-byte
+# register loads (d_out % 8 == 0) and element loads (otherwise)
+WIDE = [(256, 512, 300, 16), (264, 320, 1100, 40), (130, 320, 17, 16)]
+
+
+@pytest.mark.parametrize("shape", WIDE)
+def test_linear_wide_weight_descriptors(orc, shape):
+    """The backward GEMM's per-step weight descriptors (taken in production for
+    packed weights beyond 2^31 bytes) against the oracle, through the test
+    build that takes them at every size."""
+    d_out, d_in, M, r = shape
+    with wide_weight_library():
+        _check_layer(orc, *_layer(d_out, d_in, M, r, 140 + WIDE.index(shape)), label=f"wide {shape}")
 
 
 @pytest.mark.parametrize("shape", SMALL)
