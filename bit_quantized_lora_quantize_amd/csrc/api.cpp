@@ -174,17 +174,19 @@ struct BwdPlan {
   size_t bytes;
 };
 
-// Token split of dA / dB: about 512 workgroups (64 columns x one split
-// each); a split is a multiple of 512 tokens (four wavefronts of whole
-// pairs of 64-token blocks).
+// Token split of dA / dB: about QLORA_GRAM_TARGET_WGS workgroups (256
+// columns x one split each, one 64-column tile per wavefront); a split is a
+// multiple of 512 tokens (whole pairs of 64-token blocks, and partials of
+// the same size as with one split per 64 columns and 128 tokens per
+// wavefront).
 #ifndef QLORA_GRAM_TARGET_WGS
 #define QLORA_GRAM_TARGET_WGS 512
 #endif
 int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
   (void)r;
-  const int64_t ctiles = cdiv(N, 64);
+  const int64_t cgroups = cdiv(N, 256);
   const int64_t ms = std::max<int64_t>(
-      1, std::min<int64_t>(cdiv(QLORA_GRAM_TARGET_WGS, ctiles), cdiv(M, 256)));
+      1, std::min<int64_t>(cdiv(QLORA_GRAM_TARGET_WGS, cgroups), cdiv(M, 512)));
   *per = round_up(cdiv(std::max<int64_t>(M, 1), ms), 512);
   return (int)std::max<int64_t>(1, cdiv(M, *per));
 }

@@ -672,7 +672,7 @@ struct GramDesc {
   const uint16_t* Q;
   int64_t N, m_per_split;
   float* part;
-  int ctiles;     // 64-column tiles
+  int cgroups;    // groups of four 64-column tiles
   int wg_begin;   // first workgroup of the problem
 };
 struct GramArgs {
@@ -681,10 +681,15 @@ struct GramArgs {
   int64_t ldp, M, R;
 };
 
+// Workgroup = one token split and a group of four 64-column tiles; wavefront
+// w takes column tile 4 g + w over the whole split.  The four wavefronts read
+// the same rank fragments at about the same time, so the compute unit's
+// vector cache serves most of them, and each wavefront's sums are complete
+// for its columns: no reduction between wavefronts.
 template <int RB, bool VEC>
 __global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
   extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
-  // problem of this workgroup, then its column tile and token split
+  // problem of this workgroup, then its column group and token split
   const int di = (ga.count > 1 && (int)blockIdx.x >= ga.d[1].wg_begin) ? 1 : 0;
   const GramDesc& gd = ga.d[di];
   const uint16_t* __restrict__ Pt_hi = gd.Pt_hi;
@@ -696,14 +701,14 @@ __global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, h = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
-  const int64_t c0 = (int64_t)(local % gd.ctiles) * 64;
-  const int s = local / gd.ctiles;
-  // m_per_split is a multiple of 512: each quarter is whole pairs of
-  // 64-token blocks.  Tokens at or past M read as zero in Q, so their
-  // (finite) products add nothing and every block runs all four slices.
-  const int64_t quarter = m_per_split / 4;
-  const int64_t m_begin = (int64_t)s * m_per_split + (int64_t)w * quarter;
-  int64_t m_end = m_begin + quarter;
+  const int64_t c0 = ((int64_t)(local % gd.cgroups) * 4 + w) * 64;
+  const int s = local / gd.cgroups;
+  // m_per_split is a multiple of 128: whole pairs of 64-token blocks.  Tokens
+  // at or past M read as zero in Q, so their (finite) products add nothing
+  // and every block runs all four slices.  Columns at or past N (a ragged
+  // last group) read in-bounds data or zeros and are never stored.
+  const int64_t m_begin = (int64_t)s * m_per_split;
+  int64_t m_end = m_begin + m_per_split;
   const int64_t m_lim = (M + 127) / 128 * 128;
   if (m_end > m_lim) m_end = m_lim;
   uint8_t* wl = glds + w * kGramWaveBytes;
@@ -736,30 +741,20 @@ __global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
     gram_block<RB, VEC>(Q, M, rh, rl, ldp, c0, N, m + kGramRows, lane, wl, wr, rd, xb, acc);
   }
 
-  // wavefront partials added in order 0, 1, 2, 3 in one FP32 tile
-  // [32 RB][64]; accumulator element v of lane l: row 8 (v/4) + 4 (l/32) + v%4,
-  // column l%32 of its 32 x 32 block
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(glds);
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  // accumulator element v of lane l: row 32 ib + 8 (v/4) + 4 (l/32) + v%4,
+  // column c0 + 32 cb + l%32; for each (ib, cb, v) the wavefront writes 32
+  // consecutive columns of one row of the split's partial
+  float* out = part + (int64_t)s * R * N;
 #pragma unroll
-      for (int ib = 0; ib < RB; ++ib)
+  for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = 32 * ib + 8 * (v >> 2) + 4 * h + (v & 3);
-            float* e = red + row * 64 + 32 * cb + r32;
-            *e = ww == 0 ? acc[ib][cb][v] : __fadd_rn(*e, acc[ib][cb][v]);
-          }
-    }
-    __syncthreads();
-  }
-  for (int idx = threadIdx.x; idx < 32 * RB * 64; idx += 256) {
-    const int64_t i = idx / 64, c = c0 + idx % 64;
-    if (i < R && c < N) part[((int64_t)s * R + i) * N + c] = red[idx];
-  }
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = 32 * ib + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int64_t c = c0 + 32 * cb + r32;
+        if (i < R && c < N) out[i * N + c] = acc[ib][cb][v];
+      }
 }
 
 struct GramFinishArgs {
@@ -895,7 +890,7 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
 
 template <int RB, bool VEC>
 static hipError_t launch_gram_t(const GramArgs& a, int wgs, hipStream_t st) {
-  constexpr int lds = 4 * kGramWaveBytes > 32 * RB * 64 * 4 ? 4 * kGramWaveBytes : 32 * RB * 64 * 4;
+  constexpr int lds = 4 * kGramWaveBytes;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gram<RB, VEC>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
@@ -914,8 +909,8 @@ static hipError_t launch_gram_group(const GramProblem* p, int count, int64_t ldp
   int wgs = 0;
   for (int i = 0; i < count; ++i) {
     a.d[i] = GramDesc{p[i].Pt_hi, p[i].Pt_lo, p[i].Q, p[i].N, p[i].m_per_split, p[i].part,
-                      (int)((p[i].N + 63) / 64), wgs};
-    wgs += a.d[i].ctiles * p[i].splits;
+                      (int)((p[i].N + 255) / 256), wgs};
+    wgs += a.d[i].cgroups * p[i].splits;
   }
   if (wgs == 0) return hipSuccess;
 #define QLORA_GRAM(RB) \
