@@ -61,8 +61,8 @@ R, ALPHA = 64, 16.0
 # step), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a
 # 1024 MB device copy (factors 2.0 and 1.0).  Valid only for the kernel
 # sources with this SHA-1 (gemm_source_sha1); reported as null otherwise.
-GEMM_TRAFFIC_BYTES = 273.41e6
-GEMM_TRAFFIC_SHA1 = "2a717c62cde607d0d72e591e19373b16d2881534"
+GEMM_TRAFFIC_BYTES = 273.42e6
+GEMM_TRAFFIC_SHA1 = "4e508d5cfbbb20d2f09d6d2c774931ea50b1fe00"
 
 
 def gemm_source_sha1():
