@@ -775,8 +775,18 @@ __global__ __launch_bounds__(256) void k_gram_finish(GramFinishArgs a) {
   const int64_t N = a.N[di], count = a.R * N;
   if (idx >= count) return;
   const float* part = a.part[di];
+  const int S = a.splits[di];
+  // splits added in order; four loads issued together
   float acc = part[idx];
-  for (int s = 1; s < a.splits[di]; ++s) acc = __fadd_rn(acc, part[(int64_t)s * count + idx]);
+  int s = 1;
+  for (; s + 4 <= S; s += 4) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = part[(int64_t)(s + u) * count + idx];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __fadd_rn(acc, v[u]);
+  }
+  for (; s < S; ++s) acc = __fadd_rn(acc, part[(int64_t)s * count + idx]);
   const int64_t i = idx / N, c = idx % N;
   a.out[di][a.transposed[di] ? c * a.R + i : idx] = acc;
 }
