@@ -582,10 +582,11 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 // Q (X or dY) is streamed from HBM: each wavefront copies blocks of 64 token
 // rows x 64 columns into an LDS region of its own and reads the column
 // operands (eight consecutive tokens of one column) with transposing LDS
-// reads (ds_read_b64_tr_b16); the next block's global loads are issued
-// before the current block's MFMAs.  A workgroup covers all R rows x 64
-// columns x one token split; its four wavefronts take consecutive quarters
-// of the split and their partial tiles are added in wavefront order in LDS.
+// reads (ds_read_b64_tr_b16); the global loads of the block two ahead are
+// issued before the current block's MFMAs.  A workgroup covers all R rows x
+// 256 columns x one token split, one 64-column tile per wavefront; the four
+// wavefronts walk the same tokens and read the same P chunks at about the
+// same time (mostly served by the compute unit's vector cache).
 // ---------------------------------------------------------------------------
 namespace {
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
