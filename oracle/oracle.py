@@ -57,6 +57,7 @@ def _load():
         lib.orc_scale_mean.argtypes = [P, I]
         lib.orc_scale_mean.restype = ctypes.c_float
         lib.orc_quantize_nf4.argtypes = [P, I, P, P, P, P, P]
+        lib.orc_quantize_nf4_sel.argtypes = [P, I, P, P, P, P, P]
         lib.orc_quantize_nf4_blocked.argtypes = [P, I, I, I, P, P, P, P, P]
         lib.orc_dequant_bf16_blocked.argtypes = [P, P, P, ctypes.c_float, I, I, I, P]
         lib.orc_scale_mean_g.argtypes = [P, I, I]
@@ -69,6 +70,7 @@ def _load():
         D = ctypes.c_double
         lib.orc_linear_fwd_rows.argtypes = [P, P, P, P, I, I, I, D, P, I, P, D, P]
         lib.orc_linear_bwd.argtypes = [P, P, P, P, P, I, I, I, I, D, P, I, P, D, P, P, P]
+        lib.orc_lora_down.argtypes = [P, P, I, I, I, D, P, D, P]
         lib.orc_philox4x32_10.argtypes = [P, P, P]
         lib.orc_dropout_keep.argtypes = [I, I, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, P]
         lib.orc_merge.argtypes = [P, P, P, I, I, I, ctypes.c_float, P]
@@ -163,6 +165,27 @@ def quantize_nf4(W: np.ndarray, return_absmax: bool = False):
                              _ptr(mean), _ptr(absmax))
     out = (codes, scodes, s2, float(mean[0]))
     return out + (absmax,) if return_absmax else out
+
+
+def quantize_nf4_sel(W: np.ndarray, group_sel: np.ndarray):
+    """The layer format with NF4 codes only for the 256-block groups g where
+    group_sel[g] is true (codes of other groups are 0); the FP8 scale codes,
+    second-level scales and mean are computed for every block, as by
+    quantize_nf4.  Returns (codes, scale_codes, s2, mean)."""
+    W = _c(W, np.float32)
+    n = W.size
+    assert n % BLOCK == 0
+    n1 = n // BLOCK
+    G = (n1 + GROUP - 1) // GROUP
+    sel = _c(np.asarray(group_sel, bool), np.uint8)
+    assert sel.size == G
+    codes = np.empty(n // 2, np.uint8)
+    scodes = np.empty(n1, np.uint8)
+    s2 = np.empty(G, np.float32)
+    mean = np.zeros(1, np.float32)
+    _load().orc_quantize_nf4_sel(_ptr(W), n, _ptr(sel), _ptr(codes), _ptr(scodes), _ptr(s2),
+                                 _ptr(mean))
+    return codes, scodes, s2, float(mean[0])
 
 
 def quantize_nf4_blocked(W: np.ndarray, block: int, group: int, return_absmax: bool = False):
@@ -287,6 +310,18 @@ def linear_fwd(Wh, X, A, B, s: float, rows=None, keep=None, p: float = 0.0) -> n
     _load().orc_linear_fwd_rows(_ptr(Wh), _ptr(X), _ptr(A), _ptr(B), d_out, d_in, r,
                                 float(s), _ptr(rows), rows.size, kp, q, _ptr(Y))
     return Y
+
+
+def lora_down(X, A, s: float, keep=None, p: float = 0.0) -> np.ndarray:
+    """T = s D(X) A^T in FP64, [M, r]: the LoRA branch's rank-r intermediate
+    (see linear_fwd for keep / p).  [QP §2.2]"""
+    X, A = (_c(t, np.float32) for t in (X, A))
+    M, d_in = X.shape
+    r = A.shape[0]
+    T = np.zeros((M, r), np.float64)
+    kp, q, _hold = _keep_args(keep, M, d_in, p)
+    _load().orc_lora_down(_ptr(X), _ptr(A), M, d_in, r, float(s), kp, q, _ptr(T))
+    return T
 
 
 def linear_bwd(Wh, X, dY, A, B, s: float, rows=None, want_dx=True, want_da=True,

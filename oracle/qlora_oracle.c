@@ -93,6 +93,14 @@ float orc_fp8_decode(uint8_t code) {
   return (float)(s ? -mag : mag);
 }
 
+/* The 127 non-negative finite E4M3FN magnitudes, code 0x00..0x7E, as
+ * decoded above (filled once when the library loads). */
+static double ORC_FP8_MAG[0x7F];
+
+__attribute__((constructor)) static void orc_fp8_table(void) {
+  for (int code = 0; code <= 0x7E; ++code) ORC_FP8_MAG[code] = (double)orc_fp8_decode((uint8_t)code);
+}
+
 /* Encode y as the nearest of the 127 non-negative finite E4M3FN magnitudes
  * (codes 0x00..0x7E, increasing), ties to the even code, |y| beyond 448
  * clamped to 448, sign bit = sign bit of y.  Never produces NaN. */
@@ -101,7 +109,7 @@ uint8_t orc_fp8_encode(float y) {
   int best = 0x7E;                 /* |y| >= 448: the largest finite, 448 */
   double bestd = INFINITY;
   for (int code = 0; code <= 0x7E && a < 448.0; ++code) {
-    double v = (double)orc_fp8_decode((uint8_t)code);
+    double v = ORC_FP8_MAG[code];
     double d = fabs(a - v);
     if (d < bestd || (d == bestd && (code & 1) == 0 && (best & 1) == 1)) {
       bestd = d;
@@ -195,10 +203,14 @@ float orc_scale_mean(const float *absmax, int64_t n1) {
  * absmax of the elements it has; a last group shorter than B2 likewise.
  * codes has ceil(n/2) bytes; for odd n the high nibble of the last byte,
  * which no element owns, is 0.  B1 = 64, B2 = 256 and n % 64 == 0 is the
- * layer format above. */
-void orc_quantize_nf4_blocked(const float *W, int64_t n, int64_t B1, int64_t B2,
-                              uint8_t *codes, uint8_t *scale_codes, float *s2,
-                              float *mean, float *absmax_out) {
+ * layer format above.
+ * group_sel (NULL: every group) limits the NF4 codes to the blocks of the
+ * groups g with group_sel[g] != 0; the codes of other blocks are left 0.
+ * Absmax, mean, second-level scales and FP8 codes are always computed for
+ * every block, since the mean depends on all of them. */
+static void quantize_impl(const float *W, int64_t n, int64_t B1, int64_t B2,
+                          const uint8_t *group_sel, uint8_t *codes, uint8_t *scale_codes,
+                          float *s2, float *mean, float *absmax_out) {
   int64_t n1 = (n + B1 - 1) / B1;
   int64_t G = (n1 + B2 - 1) / B2;
   float *a = (float *)malloc((size_t)n1 * sizeof(float));
@@ -215,6 +227,7 @@ void orc_quantize_nf4_blocked(const float *W, int64_t n, int64_t B1, int64_t B2,
       if (v > m) m = v;
     }
     a[b] = m;
+    if (group_sel && !group_sel[b / B2]) continue;
     /* B1 is even, so a block owns whole bytes */
     for (int64_t j = 0; j < len; ++j) {
       float x = (m == 0.0f) ? 0.0f : W[e0 + j] / m;
@@ -226,9 +239,11 @@ void orc_quantize_nf4_blocked(const float *W, int64_t n, int64_t B1, int64_t B2,
   if (absmax_out) memcpy(absmax_out, a, (size_t)n1 * sizeof(float));
 
   /* Second level: subtract the mean, then per group an FP32 scale
-   * s2 = max|centred| / 448 and FP8 codes of centred / s2. */
+   * s2 = max|centred| / 448 and FP8 codes of centred / s2.  Groups are
+   * independent of one another. */
   float mu = orc_scale_mean_g(a, n1, B2);
   *mean = mu;
+#pragma omp parallel for schedule(static)
   for (int64_t g = 0; g < G; ++g) {
     int64_t b0 = g * B2, b1 = b0 + B2;
     if (b1 > n1) b1 = n1;
@@ -247,11 +262,23 @@ void orc_quantize_nf4_blocked(const float *W, int64_t n, int64_t B1, int64_t B2,
   free(a);
 }
 
+void orc_quantize_nf4_blocked(const float *W, int64_t n, int64_t B1, int64_t B2,
+                              uint8_t *codes, uint8_t *scale_codes, float *s2,
+                              float *mean, float *absmax_out) {
+  quantize_impl(W, n, B1, B2, NULL, codes, scale_codes, s2, mean, absmax_out);
+}
+
 void orc_quantize_nf4(const float *W, int64_t n, uint8_t *codes,
                       uint8_t *scale_codes, float *s2, float *mean,
                       float *absmax_out) {
-  orc_quantize_nf4_blocked(W, n, ORC_BLOCK, ORC_GROUP, codes, scale_codes, s2, mean,
-                           absmax_out);
+  quantize_impl(W, n, ORC_BLOCK, ORC_GROUP, NULL, codes, scale_codes, s2, mean, absmax_out);
+}
+
+/* The layer format with NF4 codes only for the selected groups (see
+ * quantize_impl); everything else as orc_quantize_nf4. */
+void orc_quantize_nf4_sel(const float *W, int64_t n, const uint8_t *group_sel,
+                          uint8_t *codes, uint8_t *scale_codes, float *s2, float *mean) {
+  quantize_impl(W, n, ORC_BLOCK, ORC_GROUP, group_sel, codes, scale_codes, s2, mean, NULL);
 }
 
 /* Restored first-level scale of block b [QP §5.2 restore order; §6.1]. */
@@ -338,6 +365,22 @@ void orc_linear_fwd_rows(const float *Wh, const float *X, const float *A,
   }
 }
 
+/* The LoRA branch's rank-r intermediate alone [QP §2.2]:
+ *   T[m, i] = s * sum over c ascending of A[i, c] D(X)[m, c]     [M, r]
+ * (the quantity the forward hands to the backward).  FP64. */
+void orc_lora_down(const float *X, const float *A, int64_t M, int64_t d_in, int64_t r,
+                   double s, const uint8_t *keep, double keep_prob, double *T) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t i = 0; i < r; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < d_in; ++c)
+        acc += (double)A[i * d_in + c] * lora_input(X, keep, keep_prob, m * d_in + c);
+      T[m * r + i] = s * acc;
+    }
+  }
+}
+
 /* Backward of the same layer for upstream gradient dY [M, d_out]:
  *   U  = s dY B          [M, r]   (gradient reaching the LoRA bottleneck)
  *   T  = D(X) A^T        [M, r]
@@ -345,7 +388,10 @@ void orc_linear_fwd_rows(const float *Wh, const float *X, const float *A,
  *                         derivative of the dropout map, 1 without dropout)
  *   dA = U^T D(X)        [r, d_in]
  *   dB = s dY^T T        [d_out, r]
- * The frozen base contributes to dX but receives no gradient [QP §2.4]. */
+ * The frozen base contributes to dX but receives no gradient [QP §2.4].
+ * Every sum runs over its index in ascending order; the loops are nested so
+ * that the innermost one walks memory contiguously, which changes no sum's
+ * order. */
 void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
                     const float *A, const float *B, int64_t M, int64_t d_out,
                     int64_t d_in, int64_t r, double s, const int64_t *rows,
@@ -355,12 +401,14 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
   double *T = (double *)calloc((size_t)(M * r + 1), sizeof(double));
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; ++m) {
+    double *u = U + m * r;                     /* u[i] = sum over o of dY[m, o] B[o, i] */
+    for (int64_t o = 0; o < d_out; ++o)
+      for (int64_t i = 0; i < r; ++i) u[i] += (double)dY[m * d_out + o] * B[o * r + i];
     for (int64_t i = 0; i < r; ++i) {
-      double u = 0.0, t = 0.0;
-      for (int64_t o = 0; o < d_out; ++o) u += (double)dY[m * d_out + o] * B[o * r + i];
+      double t = 0.0;
       for (int64_t c = 0; c < d_in; ++c)
         t += lora_input(X, keep, keep_prob, m * d_in + c) * A[i * d_in + c];
-      U[m * r + i] = s * u;
+      u[i] = s * u[i];
       T[m * r + i] = t;
     }
   }
@@ -368,13 +416,16 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t k = 0; k < nrows; ++k) {
       int64_t m = rows[k];
+      double *base = (double *)calloc((size_t)(d_in > 0 ? d_in : 1), sizeof(double));
+      for (int64_t o = 0; o < d_out; ++o)      /* base[c] = sum over o of dY[m, o] Wh[o, c] */
+        for (int64_t c = 0; c < d_in; ++c) base[c] += (double)dY[m * d_out + o] * Wh[o * d_in + c];
       for (int64_t c = 0; c < d_in; ++c) {
-        double base = 0.0, lora = 0.0;
-        for (int64_t o = 0; o < d_out; ++o) base += (double)dY[m * d_out + o] * Wh[o * d_in + c];
+        double lora = 0.0;
         for (int64_t i = 0; i < r; ++i) lora += U[m * r + i] * A[i * d_in + c];
         if (keep) lora = keep[m * d_in + c] ? lora / keep_prob : 0.0;
-        dX[k * d_in + c] = base + lora;
+        dX[k * d_in + c] = base[c] + lora;
       }
+      free(base);
     }
   }
   if (dA) {      /* dA[i, c] = sum over m ascending of U[m, i] D(X)[m, c] */
@@ -389,12 +440,15 @@ void orc_linear_bwd(const float *Wh, const float *X, const float *dY,
   }
   if (dB) {      /* dB[o, i] = s * sum over m ascending of dY[m, o] T[m, i] */
 #pragma omp parallel for schedule(static)
-    for (int64_t o = 0; o < d_out; ++o) {
-      double *row = dB + o * r;
-      for (int64_t i = 0; i < r; ++i) row[i] = 0.0;
+    for (int64_t o0 = 0; o0 < d_out; o0 += 64) {
+      const int64_t o1 = o0 + 64 < d_out ? o0 + 64 : d_out;
+      for (int64_t o = o0; o < o1; ++o)
+        for (int64_t i = 0; i < r; ++i) dB[o * r + i] = 0.0;
       for (int64_t m = 0; m < M; ++m)
-        for (int64_t i = 0; i < r; ++i) row[i] += (double)dY[m * d_out + o] * T[m * r + i];
-      for (int64_t i = 0; i < r; ++i) row[i] = s * row[i];
+        for (int64_t o = o0; o < o1; ++o)
+          for (int64_t i = 0; i < r; ++i) dB[o * r + i] += (double)dY[m * d_out + o] * T[m * r + i];
+      for (int64_t o = o0; o < o1; ++o)
+        for (int64_t i = 0; i < r; ++i) dB[o * r + i] = s * dB[o * r + i];
     }
   }
   free(U);

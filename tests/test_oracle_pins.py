@@ -415,6 +415,63 @@ def test_rows_subset_matches_full(orc):
                                   orc.linear_bwd(Wh, X, dY, A, B, 0.5)[0][rows])
 
 
+def test_lora_down_one_hot_tokens_read_columns(orc):
+    """[QP §2.2] T = s D(X) A^T: a one-hot token e_k gives s times column k
+    of A (a transposed operand would give a row); with dropout, a kept one-hot
+    token gives s A[:, k] / (1 - p) and a dropped one gives 0."""
+    _, _, A, _, _ = _small_layer(40, d_out=4, d_in=64, M=2, r=5)
+    ks = [3, 40, 63]
+    E = np.zeros((3, 64), np.float32)
+    E[np.arange(3), ks] = 1
+    T = orc.lora_down(E, A, 0.25)
+    np.testing.assert_array_equal(T, 0.25 * A[:, ks].T.astype(np.float64))
+    keep = np.ones(E.shape, np.uint8)
+    keep[1, 40] = 0
+    T = orc.lora_down(E, A, 0.25, keep=keep, p=0.5)   # 1 - p = 0.5: exact scaling
+    np.testing.assert_array_equal(T[[0, 2]], 0.5 * A[:, [3, 63]].T.astype(np.float64))
+    assert np.all(T[1] == 0)
+
+
+def test_lora_down_is_the_forward_and_backward_intermediate(orc):
+    """T is the quantity that both the forward and dB use: with W = 0 and a
+    one-hot B row (B[o] = e_i), Y[:, o] = T[:, i]; with a one-hot dY row
+    (dY[m] = e_o, other rows 0), dB[o, :] = T[m, :].  Both hold bit for bit."""
+    Wh, X, A, B, dY = _small_layer(41, d_out=6, d_in=128, M=4, r=3)
+    s = 16.0 / 3
+    T = orc.lora_down(X, A, s)
+    B1 = np.zeros_like(B)
+    B1[2, 1] = 1
+    Y = orc.linear_fwd(np.zeros_like(Wh), X, A, B1, s)
+    np.testing.assert_array_equal(Y[:, 2], T[:, 1])
+    dY1 = np.zeros_like(dY)
+    dY1[3, 5] = 1
+    _, _, dB = orc.linear_bwd(Wh, X, dY1, A, B, s, want_dx=False, want_da=False)
+    np.testing.assert_array_equal(dB[5], T[3])
+    keep = orc.dropout_keep(*X.shape, 0.2, 3, 4)
+    Tk = orc.lora_down(X, A, s, keep=keep, p=0.2)
+    Y = orc.linear_fwd(np.zeros_like(Wh), X, A, B1, s, keep=keep, p=0.2)
+    np.testing.assert_array_equal(Y[:, 2], Tk[:, 1])
+
+
+def test_quantize_selected_groups_match_full(orc):
+    """The sampled-group quantization gives the full quantization's codes on
+    the selected groups, zero codes elsewhere, and the full scale state."""
+    rng = np.random.default_rng(42)
+    W = rng.normal(0, 0.02, (40, 1024)).astype(np.float32)   # 640 blocks, 3 groups
+    W.ravel()[rng.choice(W.size, 40, replace=False)] = 0.2
+    full = orc.quantize_nf4(W)
+    sel = np.array([True, False, True])
+    part = orc.quantize_nf4_sel(W, sel)
+    np.testing.assert_array_equal(part[1], full[1])
+    np.testing.assert_array_equal(part[2].view(np.uint32), full[2].view(np.uint32))
+    assert np.float32(part[3]) == np.float32(full[3])
+    per_group = 256 * 64 // 2
+    for g, on in enumerate(sel):
+        got = part[0][g * per_group:(g + 1) * per_group]
+        ref = full[0][g * per_group:(g + 1) * per_group]
+        np.testing.assert_array_equal(got, ref if on else np.zeros_like(ref))
+
+
 # ------------------------------------------------------------------ LoRA merge
 
 def test_merge_planted_powers_of_two(orc):
