@@ -21,6 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qlora.h")
 
 QLORA_OP_QUANTIZE, QLORA_OP_FWD, QLORA_OP_BWD = 0, 1, 2
 QLORA_OP_FWD_DROPOUT, QLORA_OP_BWD_DROPOUT = 3, 4
+QLORA_ERR_SCRATCH = -6
+QLORA_STATIC_SCRATCH_BYTES = 32 << 20
 QLORA_MAX_GROUP = 8
 BLOCK, GROUP = 64, 256
 
@@ -91,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
         L.qlora_linear_fwd_many.argtypes = [ctypes.c_int, ctypes.POINTER(_FwdItem), _I64, _P]
+        L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
+                                               ctypes.c_float, _P, _P, _P]
         L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.qlora_time_next_weight_kernel.argtypes = [_P, _P]
@@ -448,6 +452,26 @@ def qlora_linear_fwd(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
                      T_save: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     return _fwd(q, X, A, B, lora_alpha, Y, T_save, workspace, None)
+
+
+def qlora_linear_fwd_noalloc(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                             lora_alpha: float, Y: torch.Tensor,
+                             T_save: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qlora_linear_fwd with the library's fixed device scratch as its
+    workspace: the library allocates nothing (the caller passes Y)."""
+    M = X.shape[0]
+    r = A.shape[0]
+    _need(X, torch.bfloat16, (M, q.d_in), "X")
+    _need(A, torch.bfloat16, (r, q.d_in), "A")
+    _need(B, torch.bfloat16, (q.d_out, r), "B")
+    _need(Y, torch.bfloat16, (M, q.d_out), "Y")
+    if T_save is not None:
+        _need(T_save, torch.float32, (M, r), "T_save")
+    qs = q.c_struct()
+    _check(lib().qlora_linear_fwd_noalloc(ctypes.byref(qs), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                          float(lora_alpha), _ptr(Y), _ptr(T_save),
+                                          _stream(X.device)), "qlora_linear_fwd_noalloc")
+    return Y
 
 
 def qlora_linear_fwd_dropout(q: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

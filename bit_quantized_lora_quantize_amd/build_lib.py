@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build", "libqlora")
 LIB = os.path.join(PKG, "libqlora.so")
 LIB_WIDE = os.path.join(PKG, "libqlora_wide.so")
 
-SOURCES = ["quant.hip", "quant_blocked.hip", "lora.hip", "gemv.hip", "gemm.hip", "merge.hip", "optim.hip", "dropout.hip", "api.cpp"]
+SOURCES = ["quant.hip", "quant_blocked.hip", "lora.hip", "gemv.hip", "gemm.hip", "merge.hip", "optim.hip", "dropout.hip", "noalloc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -551,6 +551,18 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
 
 }  // namespace
 
+namespace qlora {
+// qlora_linear_fwd's argument checks for a workspace of ws_bytes bytes (not
+// dereferenced): QLORA_ERR_WORKSPACE when the call needs more.  Host only.
+int linear_fwd_check(const qlora_nf4_t* q, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int64_t r, uint16_t* Y, float* T_save, size_t ws_bytes) {
+  // a stand-in address that passes the workspace's null and alignment checks
+  void* const ws = reinterpret_cast<void*>(uintptr_t(256));
+  FwdItemArgs f{q, X, A, B, r, 0.0f, Y, T_save, ws, ws_bytes, X, 0.0f};
+  return check_fwd_item(f, M);
+}
+}  // namespace qlora
+
 // ===================================================================== ABI
 extern "C" {
 
@@ -562,6 +574,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_HIP: return "HIP runtime error";
+    case QLORA_ERR_SCRATCH: return "the call needs more than the library's fixed device scratch";
     default: return "unknown status";
   }
 }

@@ -7,6 +7,8 @@
 
 #include <algorithm>
 
+#include "qlora.h"
+
 namespace qlora {
 
 // Optional event pair around the next weight-kernel launch (timing aid).
@@ -339,5 +341,11 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_fwd(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_bwd(const GemmArgs& a, hipStream_t st);
+
+// ------------------------------------------------- host-side checks
+// qlora_linear_fwd's argument checks for a workspace of ws_bytes bytes (not
+// dereferenced): QLORA_ERR_WORKSPACE when the call needs more.
+int linear_fwd_check(const qlora_nf4_t* q, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int64_t r, uint16_t* Y, float* T_save, size_t ws_bytes);
 
 }  // namespace qlora

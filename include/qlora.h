@@ -10,7 +10,9 @@
  * Conventions for every entry point
  *   - Every array argument is a DEVICE pointer to caller-owned memory.  The
  *     library allocates nothing, frees nothing and keeps no state between
- *     calls; it never synchronizes.  Work is enqueued on `stream` (a
+ *     calls (the one exception is the fixed device array that
+ *     qlora_linear_fwd_noalloc works in); it never synchronizes.  Work is
+ *     enqueued on `stream` (a
  *     hipStream_t; NULL means the null stream) and the call returns at once.
  *   - All matrices are dense row-major.  BF16 values are passed as their
  *     uint16_t bit patterns.
@@ -39,7 +41,9 @@ typedef enum {
   QLORA_ERR_SHAPE = -2,      /* a size is out of its documented range        */
   QLORA_ERR_ALIGN = -3,      /* a (16B) pointer is not 16-byte aligned       */
   QLORA_ERR_WORKSPACE = -4,  /* workspace smaller than qlora_workspace_bytes */
-  QLORA_ERR_HIP = -5         /* the HIP runtime reported an error            */
+  QLORA_ERR_HIP = -5,        /* the HIP runtime reported an error            */
+  QLORA_ERR_SCRATCH = -6     /* the call needs more than the library's fixed
+                                device scratch (qlora_linear_fwd_noalloc)    */
 } qlora_status;
 
 /* Block sizes fixed by the method: 64 weights share one first-level scale
@@ -194,6 +198,27 @@ int qlora_linear_bwd(const qlora_nf4_t *q, const uint16_t *X,
                      const uint16_t *B, int64_t r, float lora_alpha,
                      const float *T_saved, uint16_t *dX, float *dA, float *dB,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace comes from a fixed device
+ * array inside the library, QLORA_STATIC_SCRATCH_BYTES bytes on each GPU the
+ * library runs on, held until the process ends; the call itself allocates
+ * nothing.  Same arguments, checks, kernels and results (bit for bit) as
+ * qlora_linear_fwd.  A call whose workspace (qlora_workspace_bytes(
+ * QLORA_OP_FWD, ...)) exceeds the array returns QLORA_ERR_SCRATCH and
+ * enqueues nothing; every projection shape of the LLaMA-7B and -65B layers
+ * fits at r <= 64 for any M up to 40000 tokens.  Every call on one GPU
+ * shares that GPU's array:
+ * calls that may overlap on one GPU (other streams, unordered host threads)
+ * race and must not be issued.  Nothing in the array needs to start at zero.
+ */
+#define QLORA_STATIC_SCRATCH_BYTES (32u << 20)
+int qlora_linear_fwd_noalloc(const qlora_nf4_t *q, const uint16_t *X, int64_t M,
+                             const uint16_t *A, const uint16_t *B, int64_t r,
+                             float lora_alpha, uint16_t *Y, float *T_save,
+                             void *stream);
 
 /*
  * Forward of up to QLORA_MAX_GROUP layers that share the token count M, in

@@ -276,3 +276,30 @@ def test_blocked_sizes_and_argument_errors(L):
     g = L.qlora_dequant_bf16_blocked
     assert g(ctypes.byref(good), None, None) == ENULL
     assert g(ctypes.byref(good), P(0x70002), None) == EALIGN
+
+
+def test_noalloc_forward_host_checks(L):
+    """qlora_linear_fwd_noalloc checks its arguments like qlora_linear_fwd and
+    rejects a call whose workspace exceeds the library's fixed device scratch
+    with its own status -- all before any GPU call.  Every LLaMA-7B and -65B
+    projection shape fits at r = 64 up to 40000 tokens, as its declaration
+    states."""
+    from bit_quantized_lora_quantize_amd import inputs
+    P = ctypes.c_void_p
+    ESCRATCH = q.QLORA_ERR_SCRATCH
+    assert q.qlora_status_string(ESCRATCH) != "unknown status"
+    f = L.qlora_linear_fwd_noalloc
+    X, A, B, Y = P(0x50000), P(0x60000), P(0x70000), P(0x80000)
+    w = _nf4(128, 64)
+    assert f(ctypes.byref(w), X, 4, A, B, 0, 16.0, Y, None, None) == ESHAPE
+    assert f(ctypes.byref(w), None, 4, A, B, 8, 16.0, Y, None, None) == ENULL
+    assert f(ctypes.byref(w), P(0x50002), 4, A, B, 8, 16.0, Y, None, None) == EALIGN
+    assert f(ctypes.byref(w), None, 0, None, None, 8, 16.0, None, None, None) == OK
+    lim = q.QLORA_STATIC_SCRATCH_BYTES
+    wbig = _nf4(4096, 4096)
+    M = 1 << 20
+    assert q.qlora_workspace_bytes(q.QLORA_OP_FWD, 4096, 4096, M, 256) > lim
+    assert f(ctypes.byref(wbig), X, M, A, B, 256, 16.0, Y, None, None) == ESCRATCH
+    for M in (1, 4, 16, 17, 2048, 4096, 40000):
+        for _, d_out, d_in in inputs.LLAMA_7B + inputs.LLAMA_65B:
+            assert q.qlora_workspace_bytes(q.QLORA_OP_FWD, d_out, d_in, M, 64) <= lim
