@@ -31,8 +31,17 @@ The same line also carries, each measured in the same run:
            LLaMA-65B-shaped stack (hidden 8192, FFN 22016) at M = 2048, one
            layer at a time, packed weights resident in HBM;
   roofline the dominant kernel (fused dequant-GEMM), timed per launch with HIP
-           events placed around it by the library on the launch stream;
-  cpu_baseline  the CPU oracle on a bounded sample of the headline workload.
+           events placed around it on the launch stream by the timing build
+           of the library (libqlora_timed.so: the same kernels plus that
+           event hook), in a pass of its own after the headline steps, which
+           run on libqlora.so without events;
+  peaks    the peaks this GPU reaches: a streaming read of a 4 GiB buffer and a
+           loop of back-to-back BF16 MFMAs (libqlora_peaks.so), beside the
+           published 8 TB/s and 2.5 PFLOP/s;
+  cpu_baseline  the CPU oracle on the host cores: the headline workload on a
+           token sample (extrapolated to the full step), and per configuration
+           (256 x 256 layer, 7B quantize + dequantize, 7B decode at M = 1, 4,
+           16, 7B training step, 65B stack) in cpu_baseline_configs.
 All inputs are seeded synthetic tensors (bit_quantized_lora_quantize_amd.inputs).
 """
 from __future__ import annotations
@@ -50,7 +59,7 @@ if _ROOT not in sys.path:
     sys.path.insert(0, _ROOT)
 
 import bit_quantized_lora_quantize_amd as q  # noqa: E402
-from bit_quantized_lora_quantize_amd import inputs  # noqa: E402
+from bit_quantized_lora_quantize_amd import _lib, inputs  # noqa: E402
 
 METRIC = "NF4-LoRA linear: eff. HBM GB/s (M<=16) & TFLOPS fwd+bwd (M=4096)"
 PEAK_HBM_GBS = 8000.0
@@ -122,8 +131,9 @@ class KernelTimer:
         return ev
 
     def arm(self, tag):
+        """Only inside _lib.library(_lib.TIMED_LIB_PATH)."""
         s, e = self._event(), self._event()
-        q.lib().qlora_time_next_weight_kernel(s, e)
+        q.qlora_time_next_weight_kernel(s, e)
         self.pairs.append((tag, s, e))
 
     def durations_ms(self, tag):
@@ -234,13 +244,20 @@ def bench_train7b(dev, steps, warmup):
     for _ in range(warmup):
         train_step(layer, acts)
     torch.cuda.synchronize()
-    timer = KernelTimer()
     t0 = time.perf_counter()
     for _ in range(steps):
-        train_step(layer, acts, timer)
+        train_step(layer, acts)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    # dominant kernel: the fused dequant-GEMM, forward and backward launches
+    # dominant kernel: the fused dequant-GEMM, forward and backward launches,
+    # timed per launch in a pass of its own on the timing build
+    timer = KernelTimer()
+    with _lib.library(_lib.TIMED_LIB_PATH):
+        train_step(layer, acts)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            train_step(layer, acts, timer)
+        torch.cuda.synchronize()
     gemm_flops_fwd = [2 * M * d_out * (d_in + R) for _, d_out, d_in in inputs.LLAMA_7B]
     gemm_flops_bwd = [2 * M * d_in * (d_out + R) for _, d_out, d_in in inputs.LLAMA_7B]
     dur_f = timer.durations_ms("fwd")
@@ -276,12 +293,18 @@ def bench_dropout7b(dev, steps, warmup, p_drop=0.05):
     for i in range(warmup):
         train_step(layer, acts, p_drop=p_drop, step=i)
     torch.cuda.synchronize()
-    timer = KernelTimer()
     t0 = time.perf_counter()
     for i in range(steps):
-        train_step(layer, acts, timer, p_drop=p_drop, step=warmup + i)
+        train_step(layer, acts, p_drop=p_drop, step=warmup + i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    timer = KernelTimer()
+    with _lib.library(_lib.TIMED_LIB_PATH):
+        train_step(layer, acts, p_drop=p_drop, step=warmup + steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            train_step(layer, acts, timer, p_drop=p_drop, step=warmup + steps + 1 + i)
+        torch.cuda.synchronize()
     dur_b = timer.durations_ms("bwd")
     fl_b = [2 * M * d_in * (d_out + R) for _, d_out, d_in in inputs.LLAMA_7B] * steps
     res = dict(p=p_drop, tflops=flops * steps / el / 1e12, ms_per_step=el / steps * 1e3,
@@ -330,9 +353,13 @@ def bench_decode7b(dev, steps, warmup, copies=4):
             step(i)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        for i in range(n):
-            step(i, timer)
-        torch.cuda.synchronize()
+        with _lib.library(_lib.TIMED_LIB_PATH):
+            for i in range(copies):
+                step(i)
+            torch.cuda.synchronize()
+            for i in range(n):
+                step(i, timer)
+            torch.cuda.synchronize()
         durs = timer.durations_ms("gemv")
         k_avg = sum(durs) / len(durs) * 1e-3
         out[f"M{M}"] = dict(layer_us=el / n * 1e6, gbps=scored / (el / n) / 1e9,
@@ -376,8 +403,11 @@ def bench_quant7b(dev, steps, warmup):
         # more pass with the weight kernel of every call bracketed by events
         el = timed(fn, steps, warmup) / steps
         tm = KernelTimer()
-        fn(None, tm)
-        torch.cuda.synchronize()
+        with _lib.library(_lib.TIMED_LIB_PATH):
+            fn(None)
+            torch.cuda.synchronize()
+            fn(None, tm)
+            torch.cuda.synchronize()
         dur = tm.durations_ms(name[0])
         res[name] = dict(layer_us=el * 1e6, gbps=nbytes / el / 1e9, bytes=nbytes,
                          weight_kernel_us=sum(dur) * 1e3)
@@ -522,30 +552,188 @@ def bench_stack65b(dev, steps, warmup):
     return res
 
 
-def cpu_baseline(tokens=128):
-    """The oracle's fwd + bwd of the 7B layer on `tokens` token rows."""
+class Peaks:
+    """The measurement kernels of libqlora_peaks.so."""
+
+    def __init__(self):
+        import ctypes
+        path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libqlora_peaks.so")
+        if not os.path.exists(path):
+            raise ImportError(f"libqlora_peaks.so is not built ({path})")
+        L = ctypes.CDLL(path)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.qlora_peak_stream_read.argtypes = [P, ctypes.c_int64, P, I, P]
+        L.qlora_peak_mfma.argtypes = [P, I, I, P]
+        self.L = L
+
+    @staticmethod
+    def _events_ms(fn, reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    def measure(self, dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        nbytes = 4 << 30
+        buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+        best_read = 0.0
+        for wgs in (1024, 2048, 4096, 8192):
+            def run(wgs=wgs):
+                assert self.L.qlora_peak_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), wgs,
+                                                     stream) == 0
+            ms = self._events_ms(run, 5)
+            best_read = max(best_read, nbytes / (ms * 1e-3) / 1e9)
+        del buf
+        fsink = torch.zeros(4096 * 256, dtype=torch.float32, device=dev)
+        iters, best_mfma = 1024, 0.0
+        for wgs in (512, 1024, 2048):
+            def run(wgs=wgs):
+                assert self.L.qlora_peak_mfma(fsink.data_ptr(), wgs, iters, stream) == 0
+            ms = self._events_ms(run, 3)
+            flops = wgs * 4 * iters * 4 * 2 * 32 * 32 * 16
+            best_mfma = max(best_mfma, flops / (ms * 1e-3) / 1e12)
+        torch.cuda.empty_cache()
+        log(f"measured peaks: streaming read {best_read:.0f} GB/s, BF16 MFMA loop "
+            f"{best_mfma:.1f} TFLOP/s")
+        return dict(hbm_read_gbs=round(best_read, 1), mfma_bf16_tflops=round(best_mfma, 1),
+                    read_kernel="16-byte loads over a 4 GiB buffer, best of 1024..8192 workgroups",
+                    mfma_kernel="v_mfma_f32_32x32x16_bf16, 4 independent accumulators per "
+                                "wavefront, best of 512..2048 workgroups")
+
+
+def _median_time(fn, runs):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def cpu_baselines(tokens=128, stack_tokens=32):
+    """The oracle (plain C, FP64 products, OpenMP over rows) on the host
+    cores, per configuration; quantization of the inputs untimed except in
+    the quantize + dequantize configuration.  Returns (the headline
+    workload's entry, all entries)."""
     import numpy as np
     import oracle
-    log(f"cpu baseline: oracle fwd+bwd of the 7B layer on {tokens} tokens")
+    cores = oracle.num_threads()
+    out = {}
+    f32 = lambda t: t.float().numpy()
+
+    def prep(d_out, d_in, config, layer=0, proj=0, outliers=False):
+        W = inputs.weight(d_out, d_in, config, layer, outliers=outliers, proj=proj).numpy()
+        st = oracle.quantize_nf4(W)
+        Wh = oracle.bf16_bits_to_f32(oracle.dequant_bf16(*st, W.size)).reshape(d_out, d_in)
+        return W, Wh
+
+    # 256 x 256, M = 16, r = 8: quantize, dequantize, forward and backward
+    log("cpu baseline: 256 x 256 layer")
+    W, _ = prep(256, 256, 0)
+    A, B = (f32(t) for t in inputs.lora_factors(256, 256, 8, 0))
+    X = f32(inputs.activations(16, 256, 0, 0, inputs.T_X))
+    dY = f32(inputs.activations(16, 256, 0, 0, inputs.T_DY))
+
+    def small():
+        st = oracle.quantize_nf4(W)
+        Wh = oracle.bf16_bits_to_f32(oracle.dequant_bf16(*st, W.size)).reshape(256, 256)
+        oracle.linear_fwd(Wh, X, A, B, 2.0)
+        oracle.linear_bwd(Wh, X, dY, A, B, 2.0)
+
+    t_all = _median_time(small, 3)
+    oracle.set_num_threads(1)
+    t_one = _median_time(small, 3)
+    oracle.set_num_threads(cores)
+    out["layer256_M16_r8"] = dict(ms=round(t_all * 1e3, 3), ms_1core=round(t_one * 1e3, 3),
+                                  cores=cores, runs="median of 3",
+                                  work="quantize + dequantize + fwd + bwd")
+
+    # 7B layer: quantize + dequantize (weights with outliers)
+    log("cpu baseline: 7B layer quantize + dequantize")
+    Ws = [inputs.weight(d_out, d_in, 1, 0, outliers=True, proj=p).numpy()
+          for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B)]
+    n = sum(w.size for w in Ws)
+    packed = sum(packed_bytes(d_out, d_in) for _, d_out, d_in in inputs.LLAMA_7B)
+    states = [oracle.quantize_nf4(w) for w in Ws]
+    tq = _median_time(lambda: [oracle.quantize_nf4(w) for w in Ws], 3)
+    td = _median_time(lambda: [oracle.dequant_bf16(*st, w.size) for st, w in zip(states, Ws)], 3)
+    out["llama7b_quant_dequant"] = dict(
+        quantize_ms=round(tq * 1e3, 1), quantize_gbs=round((4 * n + packed) / tq / 1e9, 3),
+        dequant_ms=round(td * 1e3, 1), dequant_gbs=round((packed + 2 * n) / td / 1e9, 3),
+        cores=cores, runs="median of 3")
+    del Ws, states
+
+    # 7B layer decode forward, M = 1, 4, 16 (all seven projections)
+    log("cpu baseline: 7B layer decode forward, M = 1, 4, 16")
+    r = R
+    layer7 = []
+    for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B):
+        _, Wh = prep(d_out, d_in, 2, 0, p)
+        A, B = (f32(t) for t in inputs.lora_factors(d_out, d_in, r, 2, 0, proj=p))
+        layer7.append((Wh, A, B, d_in))
+    dec = {}
+    for M in (1, 4, 16):
+        xs = [f32(inputs.activations(M, d_in, 2, 0, inputs.T_X, proj=p))
+              for p, (_, _, _, d_in) in enumerate(layer7)]
+        t = _median_time(lambda: [oracle.linear_fwd(Wh, X, A, B, ALPHA / r)
+                                  for (Wh, A, B, _), X in zip(layer7, xs)], 3)
+        dec[f"M{M}"] = dict(layer_ms=round(t * 1e3, 2), gbs=round(packed / t / 1e9, 4))
+    out["llama7b_decode"] = dict(dec, cores=cores, runs="median of 3",
+                                 gbs_over="packed weight bytes, as the GPU figure")
+    del layer7
+
+    # 7B layer training step on a token sample (the headline workload)
+    log(f"cpu baseline: 7B layer fwd + bwd on {tokens} tokens")
     total_t, flops = 0.0, 0
-    for p, (name, d_out, d_in) in enumerate(inputs.LLAMA_7B):
-        W = inputs.weight(d_out, d_in, 3, 0, proj=p).numpy()
-        codes, scodes, s2, mean = oracle.quantize_nf4(W)
-        Wh = oracle.bf16_bits_to_f32(oracle.dequant_bf16(codes, scodes, s2, mean, W.size)
-                                     ).reshape(d_out, d_in)
-        A, B = (t.float().numpy() for t in inputs.lora_factors(d_out, d_in, R, 3, 0, proj=p))
-        X = inputs.activations(tokens, d_in, 3, 0, inputs.T_X, proj=p).float().numpy()
-        dY = inputs.activations(tokens, d_out, 3, 0, inputs.T_DY, proj=p).float().numpy()
+    for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_7B):
+        _, Wh = prep(d_out, d_in, 3, 0, p)
+        A, B = (f32(t) for t in inputs.lora_factors(d_out, d_in, r, 3, 0, proj=p))
+        X = f32(inputs.activations(tokens, d_in, 3, 0, inputs.T_X, proj=p))
+        dY = f32(inputs.activations(tokens, d_out, 3, 0, inputs.T_DY, proj=p))
         t0 = time.perf_counter()
-        oracle.linear_fwd(Wh, X, A, B, ALPHA / R)
-        oracle.linear_bwd(Wh, X, dY, A, B, ALPHA / R)
+        oracle.linear_fwd(Wh, X, A, B, ALPHA / r)
+        oracle.linear_bwd(Wh, X, dY, A, B, ALPHA / r)
         total_t += time.perf_counter() - t0
-        flops += useful_flops(tokens, d_out, d_in, R)
-    return dict(value=flops / total_t / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
-                kind="oracle",
+        flops += useful_flops(tokens, d_out, d_in, r)
+    head = dict(value=flops / total_t / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
                 sample=f"fwd+bwd (Y, dX, dA, dB) of the 7 LLaMA-7B projections on {tokens} of "
-                       f"the 4096 tokens, r={R}, FP64 accumulation; quantization untimed; "
-                       f"{total_t:.1f} s of CPU time")
+                       f"the 4096 tokens, r={r}, FP64 accumulation, quantization untimed; "
+                       f"{total_t:.1f} s of CPU time; the full 4096-token step extrapolates "
+                       f"to {total_t * 4096 / tokens:.0f} s")
+    out["llama7b_train_M4096"] = dict(tflops=round(head["value"], 5),
+                                      sample_tokens=tokens, sample_s=round(total_t, 2),
+                                      step_s_extrapolated=round(total_t * 4096 / tokens, 1),
+                                      cores=cores, label="extrapolated (token sample x 4096 / "
+                                                         "sample)")
+
+    # 65B stack: layer 0 on a token sample, extrapolated to 2048 tokens x 80 layers
+    log(f"cpu baseline: 65B layer 0 fwd + bwd on {stack_tokens} tokens")
+    total_t, flops = 0.0, 0
+    for p, (_, d_out, d_in) in enumerate(inputs.LLAMA_65B):
+        _, Wh = prep(d_out, d_in, 4, 0, p)
+        A, B = (f32(t) for t in inputs.lora_factors(d_out, d_in, r, 4, 0, proj=p))
+        X = f32(inputs.activations(stack_tokens, d_in, 4, 0, inputs.T_X, proj=p))
+        dY = f32(inputs.activations(stack_tokens, d_out, 4, 0, inputs.T_DY, proj=p))
+        t0 = time.perf_counter()
+        oracle.linear_fwd(Wh, X, A, B, ALPHA / r)
+        oracle.linear_bwd(Wh, X, dY, A, B, ALPHA / r)
+        total_t += time.perf_counter() - t0
+        flops += useful_flops(stack_tokens, d_out, d_in, r)
+        del Wh
+    step_s = total_t * (2048 / stack_tokens) * inputs.LLAMA_65B_LAYERS
+    out["llama65b_stack_M2048"] = dict(tflops=round(flops / total_t / 1e12, 5),
+                                       sample="layer 0, 7 projections", sample_tokens=stack_tokens,
+                                       sample_s=round(total_t, 2),
+                                       step_s_extrapolated=round(step_s, 0), cores=cores,
+                                       label="extrapolated (layer 0 token sample x 2048 / "
+                                             "sample x 80 layers)")
+    return head, out
 
 
 def main():
@@ -553,8 +741,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,blocked,merge,adamw,stack65b,cpu")
-    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,blocked,merge,adamw,stack65b,peaks,cpu")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-stack-tokens", type=int, default=128)
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MB (a plain copy "
                          "kernel of known size, for scaling hardware byte counters)")
@@ -594,7 +783,8 @@ def main():
         extra["adamw_7b"] = bench_adamw7b(dev, args.steps, args.warmup)
     if "stack65b" not in skip:
         extra["stack_65b"] = bench_stack65b(dev, max(1, min(args.steps, 2)), 1)
-    cpu = None if "cpu" in skip else cpu_baseline(args.cpu_tokens)
+    peaks = None if "peaks" in skip else Peaks().measure(dev)
+    cpu, cpu_cfg = (None, None) if "cpu" in skip else cpu_baselines(args.cpu_tokens, args.cpu_stack_tokens)
 
     g = train["gemm"]
     line = {
@@ -623,7 +813,12 @@ def main():
                      "fwd_avg_us": round(g["fwd_avg_us"], 2), "bwd_avg_us": round(g["bwd_avg_us"], 2),
                      "fwd_tflops": round(g["fwd_tflops"], 2), "bwd_tflops": round(g["bwd_tflops"], 2)},
         "cpu_baseline": cpu,
+        "cpu_baseline_configs": cpu_cfg,
+        "peaks": peaks,
     }
+    if peaks:
+        line["roofline"]["measured_peak"] = peaks["mfma_bf16_tflops"]
+        line["roofline"]["frac_of_measured_peak"] = round(g["tflops"] / peaks["mfma_bf16_tflops"], 4)
     line.update(extra)
     print(json.dumps(line), flush=True)
 

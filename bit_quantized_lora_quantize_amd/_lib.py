@@ -7,6 +7,7 @@ no fallback of any kind, and calls raise when it is missing.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -17,6 +18,9 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqlora.so")
+# benchmark build: the same library plus qlora_time_next_weight_kernel
+# (include/qlora_timing.h)
+TIMED_LIB_PATH = os.path.join(_PKG, "libqlora_timed.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "qlora.h")
 
 QLORA_OP_QUANTIZE, QLORA_OP_FWD, QLORA_OP_BWD = 0, 1, 2
@@ -97,7 +101,8 @@ def lib() -> ctypes.CDLL:
                                                ctypes.c_float, _P, _P, _P]
         L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-        L.qlora_time_next_weight_kernel.argtypes = [_P, _P]
+        if hasattr(L, "qlora_time_next_weight_kernel"):     # libqlora_timed.so only
+            L.qlora_time_next_weight_kernel.argtypes = [_P, _P]
         L.qlora_nf4_blocked_sizes.argtypes = [_I64, _I64, _I64] + [ctypes.POINTER(ctypes.c_size_t)] * 3
         L.qlora_quantize_blocked_workspace_bytes.restype = ctypes.c_size_t
         L.qlora_quantize_blocked_workspace_bytes.argtypes = [_I64, _I64, _I64]
@@ -113,6 +118,25 @@ def lib() -> ctypes.CDLL:
                                                _P, _P, _P, ctypes.c_size_t, _P]
         _lib = L
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route the calls made inside the block through another in-tree build of
+    the library (libqlora_timed.so for per-kernel timing, or a test build);
+    the default library is restored afterwards."""
+    global LIB_PATH, _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{os.path.basename(path)} is not built ({path}); run "
+                          "python -m bit_quantized_lora_quantize_amd.build_lib")
+    saved = (LIB_PATH, _lib)
+    LIB_PATH, _lib = path, None
+    try:
+        yield lib()
+    finally:
+        if torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+        LIB_PATH, _lib = saved
 
 
 def header_functions() -> list[str]:
@@ -143,12 +167,15 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def qlora_time_next_weight_kernel(start: Optional["torch.cuda.Event"],
-                                  stop: Optional["torch.cuda.Event"]) -> None:
-    """Bracket the next weight-kernel launch with two recorded events."""
-    sp = ctypes.c_void_p(start.cuda_event) if start is not None else None
-    ep = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
-    _check(lib().qlora_time_next_weight_kernel(sp, ep), "qlora_time_next_weight_kernel")
+def qlora_time_next_weight_kernel(start, stop) -> None:
+    """Bracket the next weight-kernel launch with two recorded events
+    (hipEvent_t handles as integers or c_void_p); only inside
+    library(TIMED_LIB_PATH)."""
+    L = lib()
+    if not hasattr(L, "qlora_time_next_weight_kernel"):
+        raise RuntimeError("qlora_time_next_weight_kernel is only in libqlora_timed.so; "
+                           "use _lib.library(_lib.TIMED_LIB_PATH)")
+    _check(L.qlora_time_next_weight_kernel(start, stop), "qlora_time_next_weight_kernel")
 
 
 def qlora_nf4_sizes(d_out: int, d_in: int) -> tuple[int, int, int, int]:

@@ -1,9 +1,17 @@
 """Build libqlora.so in-tree with hipcc for gfx950 (CDNA4).
 
-Also builds libqlora_wide.so, a test build identical except that the
-backward GEMM takes its per-step weight-descriptor path (otherwise used only
-for packed weights beyond 2^31 bytes) at every size, so that tests can check
-that path against the oracle at ordinary sizes.
+Also builds two variants from the same sources:
+  libqlora_wide.so   a test build identical except that the backward GEMM
+                     takes its per-step weight-descriptor path (otherwise used
+                     only for packed weights beyond 2^31 bytes) at every size,
+                     so that tests can check that path against the oracle at
+                     ordinary sizes;
+  libqlora_peaks.so  not the library: the benchmark's streaming-read and
+                     MFMA-loop microbenchmarks (measured peaks);
+  libqlora_timed.so  a benchmark build that also exports
+                     qlora_time_next_weight_kernel (include/qlora_timing.h),
+                     an event pair around the next weight-kernel launch; the
+                     library proper keeps no such state.
 
 Usage: python -m bit_quantized_lora_quantize_amd.build_lib [--jobs N]
 """
@@ -22,6 +30,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libqlora")
 LIB = os.path.join(PKG, "libqlora.so")
 LIB_WIDE = os.path.join(PKG, "libqlora_wide.so")
+LIB_TIMED = os.path.join(PKG, "libqlora_timed.so")
+LIB_PEAKS = os.path.join(PKG, "libqlora_peaks.so")
+# sources that hold the timing hook or launch a weight kernel
+TIMED_SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "api.cpp"]
 
 SOURCES = ["quant.hip", "quant_blocked.hip", "lora.hip", "gemv.hip", "gemm.hip", "merge.hip", "optim.hip", "dropout.hip", "noalloc.hip", "api.cpp"]
 
@@ -70,18 +82,25 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
-def build(jobs: int = 5) -> str:
+def build(jobs: int = 6) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        # the slowest compile (the GEMM) of each variant first
         wide = ex.submit(_compile, "gemm.hip", "_wide", ("-DQLORA_WIDE_CODE_BYTES=0",))
+        timed = {src: ex.submit(_compile, src, "_timed", ("-DQLORA_TIMING_HOOK=1",))
+                 for src in TIMED_SOURCES}
+        peaks = ex.submit(_compile, "peaks.hip")
         objs = list(ex.map(_compile, SOURCES))
         wide_obj = wide.result()
+        timed_objs = {src: f.result() for src, f in timed.items()}
     _link(objs, LIB)
     _link([wide_obj if os.path.basename(o) == "gemm.hip.o" else o for o in objs], LIB_WIDE)
+    _link([timed_objs.get(os.path.basename(o)[:-2], o) for o in objs], LIB_TIMED)
+    _link([peaks.result()], LIB_PEAKS)
     return LIB
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
-    ap.add_argument("--jobs", type=int, default=5)
+    ap.add_argument("--jobs", type=int, default=6)
     print(build(ap.parse_args().jobs))

@@ -16,6 +16,10 @@
 using namespace qlora;
 
 // ------------------------------------------------------------ timing aid
+// Only in the timing build (libqlora_timed.so): an event pair the caller
+// arms for the next weight-kernel launch.  Process-wide, not thread-safe.
+#ifdef QLORA_TIMING_HOOK
+#include "qlora_timing.h"
 namespace {
 hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 bool g_ev_armed = false;
@@ -32,6 +36,14 @@ void weight_kernel_end(hipStream_t st) {
   g_ev_start = g_ev_stop = nullptr;
 }
 }  // namespace qlora
+
+extern "C" int qlora_time_next_weight_kernel(void* start_event, void* stop_event) {
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
+  g_ev_armed = g_ev_start != nullptr || g_ev_stop != nullptr;
+  return QLORA_OK;
+}
+#endif
 
 namespace {
 
@@ -580,13 +592,6 @@ const char* qlora_status_string(int status) {
 }
 
 int qlora_abi_version(void) { return (1 << 16) | 0; }
-
-int qlora_time_next_weight_kernel(void* start_event, void* stop_event) {
-  g_ev_start = static_cast<hipEvent_t>(start_event);
-  g_ev_stop = static_cast<hipEvent_t>(stop_event);
-  g_ev_armed = g_ev_start != nullptr || g_ev_stop != nullptr;
-  return QLORA_OK;
-}
 
 int qlora_nf4_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* scale_codes_bytes,
                     size_t* scale2_bytes, size_t* scale_mean_bytes) {

@@ -11,9 +11,16 @@
 
 namespace qlora {
 
-// Optional event pair around the next weight-kernel launch (timing aid).
+// Event pair around the next weight-kernel launch: only in the timing build
+// (QLORA_TIMING_HOOK, libqlora_timed.so) that benchmarks use to time single
+// kernels; the library itself keeps no state and these are empty.
+#ifdef QLORA_TIMING_HOOK
 void weight_kernel_begin(hipStream_t st);
 void weight_kernel_end(hipStream_t st);
+#else
+inline void weight_kernel_begin(hipStream_t) {}
+inline void weight_kernel_end(hipStream_t) {}
+#endif
 
 // ----------------------------------------------------------- quantization
 constexpr int kLutSize = 129;     // buckets floor(64 x) + 64 for x in [-1, 1]

@@ -418,19 +418,6 @@ int qlora_adamw_step(int count, const qlora_adamw_param *params, float lr,
                      int64_t step, const double *grad_sumsq,
                      float max_grad_norm, void *stream);
 
-/*
- * Timing aid for profilers and benchmarks.  The next launch of this
- * library's weight kernel -- the one kernel of a call that reads the packed
- * weights: the first quantization pass, the dequantization, the
- * weight-streaming forward (M <= 16) or the fused dequant-GEMM (forward or
- * input gradient) -- is bracketed by hipEventRecord(start_event) right before
- * it and hipEventRecord(stop_event) right after it, on the stream of that
- * call; the request is then cleared.  Events are hipEvent_t handles owned by
- * the caller; NULL, NULL clears a pending request.  Process-wide and not
- * thread-safe: the only state the library keeps between calls.
- */
-int qlora_time_next_weight_kernel(void *start_event, void *stop_event);
-
 /* Static English text for a qlora_status value. */
 const char *qlora_status_string(int status);
 

@@ -84,6 +84,7 @@ def _load():
         lib.orc_map_fp8_encode.argtypes = [P, I, P]
         lib.orc_map_bf16_rne.argtypes = [P, I, P]
         lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -99,6 +100,11 @@ def _c(a, dtype):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later parallel loops."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- scalars

@@ -604,6 +604,8 @@ void orc_map_bf16_rne(const float *x, int64_t n, uint16_t *out) {
 #ifdef _OPENMP
 #include <omp.h>
 int orc_num_threads(void) { return omp_get_max_threads(); }
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int orc_num_threads(void) { return 1; }
+void orc_set_num_threads(int n) { (void)n; }
 #endif

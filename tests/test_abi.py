@@ -49,6 +49,31 @@ def test_wide_descriptor_test_build_exports_the_same(L):
     assert set(q.header_functions()) <= exported
 
 
+def _exports(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+def test_timing_hook_only_in_the_timing_build(L):
+    """libqlora.so keeps no state between calls: the event hook that times
+    single kernels is exported only by the benchmark build libqlora_timed.so
+    (include/qlora_timing.h), which also exports every qlora.h entry point."""
+    import os
+    import re
+    assert "qlora_time_next_weight_kernel" not in _exports(_lib.LIB_PATH)
+    assert "qlora_time_next_weight_kernel" not in q.header_functions()
+    assert os.path.exists(_lib.TIMED_LIB_PATH), "libqlora_timed.so is not built"
+    timed = _exports(_lib.TIMED_LIB_PATH)
+    text = open(os.path.join(os.path.dirname(_lib.HEADER_PATH), "qlora_timing.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    timing_fns = set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text))
+    assert timing_fns == {"qlora_time_next_weight_kernel"}
+    assert set(q.header_functions()) | timing_fns <= timed
+    peaks = os.path.join(os.path.dirname(_lib.LIB_PATH), "libqlora_peaks.so")
+    assert {"qlora_peak_stream_read", "qlora_peak_mfma"} <= _exports(peaks)
+
+
 def test_status_strings_and_version(L):
     assert q.qlora_abi_version() >> 16 == 1
     for s in (OK, ENULL, ESHAPE, EALIGN, EWS, EHIP):
