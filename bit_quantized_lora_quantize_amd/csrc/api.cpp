@@ -110,42 +110,22 @@ QuantPlan plan_quant(int64_t d_out, int64_t d_in, void* ws) {
   return p;
 }
 
-struct GemvSplit {
-  int ksplit, ss_per, tiles;
-};
-// K split of the weight-streaming launch.  The work of a group is counted in
-// units of one kGemvRows-row tile times one 256-wide super-step; every item
-// gets about the same number of super-steps per workgroup (so that no long
-// K range finishes alone), chosen to give about kGemvTargetWgs workgroups in
-// all, with at most kGemvMaxSplit splits per item (bounding the partials)
-// and few enough super-steps that the staged X fits the kernel's LDS.
-#ifndef QLORA_GEMV_TARGET_WGS
-#define QLORA_GEMV_TARGET_WGS 1024
-#endif
-constexpr int64_t kGemvTargetWgs = QLORA_GEMV_TARGET_WGS;
-constexpr int64_t kGemvMaxSplit = 16;
-int64_t gemv_units(int64_t d_out, int64_t d_in) {
-  return cdiv(d_out, kGemvRows) * cdiv(d_in / kBlock, 4);
+// Small-M forward: T chunks of at least 4 super-steps (1024 columns: one
+// round of loads per T task), at most kGemvMaxChunks of them.
+int64_t gemv_nss(int64_t d_in) { return cdiv(d_in / kBlock, 4); }
+int64_t gemv_tchunk_ss(int64_t d_in) {
+  return std::max<int64_t>(4, cdiv(gemv_nss(d_in), kGemvMaxChunks));
 }
-GemvSplit gemv_split(int64_t d_out, int64_t d_in, int64_t M, int64_t total_units) {
-  const int64_t tiles = cdiv(d_out, kGemvRows);
-  const int64_t nss = cdiv(d_in / kBlock, 4);
-  const int64_t ss_max = (kGemvMaxLds / (M + 1) - 16) / 512;
-  int64_t per = std::max<int64_t>(1, cdiv(total_units, kGemvTargetWgs));
-  per = std::max(per, cdiv(nss, kGemvMaxSplit));
-  per = std::min({per, nss, ss_max});
-  const int64_t ks = cdiv(nss, per);
-  return {(int)ks, (int)cdiv(nss, ks), (int)tiles};
-}
+int64_t gemv_tchunks(int64_t d_in) { return cdiv(gemv_nss(d_in), gemv_tchunk_ss(d_in)); }
 
 struct FwdPlan {
   bool small;
-  float* t_buf;       // [M][r] when T_save is NULL
+  float* t_buf;       // [M][r] when T_save is NULL (large M)
   uint16_t* t_hl;     // [M][2 rp] BF16 hi | lo of T (large M)
   int64_t rp;         // r rounded up to 32
-  float* gemv_part;   // [ksplit][16][d_out] (small M)
+  float* gemv_part;   // [kGemvMaxSlots][M][d_out] (small M)
+  float* gemv_tpart;  // [gemv_tchunks(d_in)][M][r] (small M)
   float* r_part;      // [rank_k_splits(M, d_in)][M][r] (large M)
-  GemvSplit gs;
   size_t bytes;
 };
 
@@ -153,17 +133,15 @@ FwdPlan plan_fwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   FwdPlan p{};
   p.small = M <= kSmallM;
   Carver c(ws);
-  p.t_buf = c.take<float>(M * r);
   p.rp = round_up(r, 32);
   if (!p.small) {
     int64_t kper;
+    p.t_buf = c.take<float>(M * r);
     p.t_hl = c.take<uint16_t>(M * 2 * p.rp);
     p.r_part = c.take<float>((int64_t)rank_k_splits(M, d_in, &kper) * M * r);
-  }
-  if (p.small) {
-    // a problem alone gets the most splits it can get in any group
-    p.gs = gemv_split(d_out, d_in, M, gemv_units(d_out, d_in));
-    p.gemv_part = c.take<float>((int64_t)p.gs.ksplit * 16 * d_out);
+  } else {
+    p.gemv_part = c.take<float>((int64_t)kGemvMaxSlots * M * d_out);
+    p.gemv_tpart = c.take<float>(gemv_tchunks(d_in) * M * r);
   }
   p.bytes = c.off + 256;
   return p;
@@ -173,6 +151,7 @@ struct BwdPlan {
   float* t_buf;       // [M][r]
   float* r_part;      // rank-r partials: [kRankSmallSplits][M][r] (small M), else
                       // [max K splits of T and U][M][r]
+  float* t_part;      // small M: T chunk partials [gemv_tchunks(d_in)][M][r]
   int64_t ldbt;       // row stride of B^T
   uint16_t* bt;       // [r][ldbt]
   int64_t rp;         // r rounded up to 32
@@ -213,6 +192,7 @@ BwdPlan plan_bwd(int64_t d_out, int64_t d_in, int64_t M, int64_t r, void* ws) {
   p.u_hl = c.take<uint16_t>(M * 2 * p.rp);
   if (M <= kSmallM) {
     p.r_part = c.take<float>(kRankSmallSplits * M * r);
+    p.t_part = c.take<float>(gemv_tchunks(d_in) * M * r);
   } else {
     int64_t kper;
     const int64_t ks = std::max(rank_k_splits(M, d_in, &kper), rank_k_splits(M, d_out, &kper));
@@ -370,22 +350,29 @@ struct FwdItemArgs {
   float sc;            // LoRA scale: alpha / r, or alpha / r / (1 - p)
 };
 
-// Descriptors of the small-M forward for a group: T into T_save (or the
-// workspace), K splits balanced over the group.  Returns the group's units.
-int64_t small_gemv_args(const FwdItemArgs* items, int count, int64_t M, GemvArgs* ga, int* gwgs,
-                        int* fwgs) {
-  int64_t total_units = 0;
-  for (int i = 0; i < count; ++i)
-    total_units += gemv_units(items[i].q->d_out, items[i].q->d_in);
+// Descriptors and work partition of the small-M forward for a group (see
+// qlora_kernels.h): the kGemvWgs workgroups of the weight-streaming launch
+// are shared among the layers in proportion to their work (largest
+// remainders first), at least one each, and so that every range holds at
+// least ceil(nss / (kGemvMaxSlots - 1)) units: a tile then spans at most
+// kGemvMaxSlots workgroups.  A T task counts for half its chunk's
+// super-steps in units: its loads go straight into MFMAs (its time is
+// about one round trip to memory per four super-steps), while a weight
+// unit's time is mostly the restore of its 16384 weights.
+int gemv_task_cost(int64_t d_in) { return (int)std::max<int64_t>(1, gemv_tchunk_ss(d_in) / 2); }
+
+void small_gemv_args(const FwdItemArgs* items, int count, int64_t M, GemvArgs* ga) {
+  *ga = GemvArgs{};
   ga->count = count;
   ga->M = (int)M;
-  int twgs = 0;
-  *gwgs = *fwgs = 0;
+  ga->vec_b = true;
+  int64_t U = 0;
+  int tasks = 0, fin = 0;
+  int64_t cost[kMaxGroup];
   for (int i = 0; i < count; ++i) {
     const FwdItemArgs& f = items[i];
     const qlora_nf4_t* q = f.q;
     const FwdPlan p = plan_fwd(q->d_out, q->d_in, M, f.r, f.ws);
-    const GemvSplit gs = gemv_split(q->d_out, q->d_in, M, total_units);
     GemvDesc& d = ga->d[i];
     d.codes = q->codes;
     d.scodes = q->scale_codes;
@@ -395,25 +382,59 @@ int64_t small_gemv_args(const FwdItemArgs* items, int count, int64_t M, GemvArgs
     d.XA = f.XA;
     d.A = f.A;
     d.B = f.B;
-    d.t_buf = f.T_save ? f.T_save : p.t_buf;
+    d.T_save = f.T_save;
     d.Y = f.Y;
     d.part = p.gemv_part;
+    d.tpart = p.gemv_tpart;
     d.d_out = q->d_out;
     d.d_in = q->d_in;
     d.r = f.r;
     d.t_scale = f.sc;
-    d.ksplit = gs.ksplit;
-    d.ss_per_split = gs.ss_per;
-    d.tiles = gs.tiles;
-    d.tb_begin = twgs;
-    d.wg_begin = *gwgs;
-    d.fin_begin = *fwgs;
-    twgs += (int)cdiv(f.r, 16);
-    *gwgs += gs.tiles * gs.ksplit;
-    *fwgs += (int)cdiv(q->d_out, 64);
+    // d_out, d_in <= 2^21: fewer than 2^28 units and 2^12 tasks
+    d.tiles = (int)cdiv(q->d_out, kGemvRows);
+    d.nss = (int)gemv_nss(q->d_in);
+    d.units = d.tiles * d.nss;
+    d.tchunks = (int)gemv_tchunks(q->d_in);
+    d.tchunk_ss = (int)gemv_tchunk_ss(q->d_in);
+    d.n_tasks = (int)cdiv(f.r, 16) * d.tchunks;
+    d.tcost = gemv_task_cost(q->d_in);
+    d.toff = d.n_tasks * d.tcost;
+    d.task_begin = tasks;
+    d.fin_begin = fin;
+    cost[i] = (int64_t)d.toff + d.units;
+    U += cost[i];
+    tasks += d.n_tasks;
+    fin += (int)cdiv(q->d_out, 64);
+    if (f.r % 8 != 0 || !aligned16(f.B)) ga->vec_b = false;
   }
-  ga->t_wgs = twgs;
-  return total_units;
+  int64_t given = 0;
+  int64_t rem[kMaxGroup];
+  for (int i = 0; i < count; ++i) {
+    const int64_t share = (int64_t)kGemvWgs * cost[i];
+    ga->d[i].wgs = (int)(share / U);
+    rem[i] = share % U;
+    given += ga->d[i].wgs;
+  }
+  for (int64_t left = kGemvWgs - given; left > 0; --left) {
+    int best = 0;
+    for (int i = 1; i < count; ++i)
+      if (rem[i] > rem[best]) best = i;
+    ++ga->d[best].wgs;
+    rem[best] = -1;
+  }
+  int wg = 0;
+  for (int i = 0; i < count; ++i) {
+    GemvDesc& d = ga->d[i];
+    const int64_t cap = cost[i] / cdiv(d.nss, kGemvMaxSlots - 1);
+    d.wgs = (int)std::max<int64_t>(1, std::min<int64_t>(d.wgs, cap));
+    d.uq = (int)(cost[i] / d.wgs);
+    d.urem = (int)(cost[i] % d.wgs);
+    d.wg_begin = wg;
+    wg += d.wgs;
+  }
+  ga->wgs = wg;
+  ga->tasks = tasks;
+  ga->fin_wgs = fin;
 }
 
 int check_fwd_item(const FwdItemArgs& f, int64_t M) {
@@ -461,11 +482,10 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
   }
 
   // Small M: one weight-streaming launch for the whole group (whose first
-  // workgroups form T = s X A^T) and one finish launch.
-  GemvArgs ga{};
-  int gwgs = 0, fwgs = 0;
-  small_gemv_args(items, count, M, &ga, &gwgs, &fwgs);
-  return hip_status(launch_gemv(ga, gwgs, fwgs, st));
+  // workgroups also form the partials of T = s X A^T) and one finish launch.
+  GemvArgs ga;
+  small_gemv_args(items, count, M, &ga);
+  return hip_status(launch_gemv(ga, st));
 }
 
 // Argument checks shared by both backward entry points.
@@ -514,25 +534,31 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
     s = rank_product(ra, p.r_part, st);
     if (s) return s;
     T = p.t_buf;
+  } else if (!T) {
+    // the forward's T tasks alone, then the chunk partials added in the same
+    // order and scaled as in the forward's finish (same bits), with the
+    // transposed copies
+    GemvArgs ga{};
+    ga.count = 1;
+    ga.M = (int)M;
+    GemvDesc& d = ga.d[0];
+    d.XA = XA;
+    d.A = A;
+    d.tpart = p.t_part;
+    d.d_in = d_in;
+    d.d_out = d_out;
+    d.r = r;
+    d.tchunks = (int)gemv_tchunks(d_in);
+    d.tchunk_ss = (int)gemv_tchunk_ss(d_in);
+    d.n_tasks = (int)cdiv(r, 16) * d.tchunks;
+    ga.tasks = d.n_tasks;
+    s = hip_status(launch_gemv_tasks(ga, st));
+    if (s) return s;
+    s = hip_status(launch_rank_finish(p.t_part, d.tchunks, M, r, sc, p.t_buf, p.tt_hi, p.tt_lo,
+                                      p.ldp, nullptr, 0, st));
+    if (s) return s;
+    T = p.t_buf;
   } else {
-    if (!T) {
-      GemvArgs ga{};
-      ga.count = 1;
-      ga.M = (int)M;
-      ga.t_wgs = (int)cdiv(r, 16);
-      GemvDesc& d = ga.d[0];
-      d.X = XA;
-      d.XA = XA;
-      d.A = A;
-      d.t_buf = p.t_buf;
-      d.d_in = d_in;
-      d.d_out = d_out;
-      d.r = r;
-      d.t_scale = sc;
-      s = hip_status(launch_lora_down(ga, st));
-      if (s) return s;
-      T = p.t_buf;
-    }
     s = hip_status(launch_rank_finish(T, 1, M, r, 1.0f, nullptr, p.tt_hi, p.tt_lo, p.ldp,
                                       nullptr, 0, st));
     if (s) return s;

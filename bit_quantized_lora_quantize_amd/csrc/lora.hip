@@ -344,8 +344,7 @@ __global__ __launch_bounds__(256) void k_rank_small(RankSmallArgs a) {
   constexpr int S = kRankSmallSplits;
   __shared__ float red[16][16];
   const int wg = blockIdx.x;
-  int di = 0;
-  while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
+  const int di = group_index(a.count, wg, [&](int i) { return a.d[i].wg_begin; });
   const RankSmallDesc& d = a.d[di];
   const int local = wg - d.wg_begin;
   const int nblk = (int)((d.N + 15) / 16);
@@ -443,8 +442,7 @@ hipError_t launch_rank_small(const RankSmallArgs& a0, hipStream_t st) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
   const int wg = blockIdx.x;
-  int di = 0;
-  while (di + 1 < a.count && wg >= a.d[di + 1].wg_begin) ++di;
+  const int di = group_index(a.count, wg, [&](int i) { return a.d[i].wg_begin; });
   const FinishDesc& d = a.d[di];
   const int64_t idx = (int64_t)(wg - d.wg_begin) * 256 + threadIdx.x;
   const int64_t ldt = d.ldt > 0 ? d.ldt : d.M;

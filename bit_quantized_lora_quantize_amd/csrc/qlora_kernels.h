@@ -70,6 +70,20 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, cons
 
 // ------------------------------------------------------------- rank-r work
 constexpr int kMaxGroup = 8;
+// Index of the problem of a grouped launch that workgroup (or task) x
+// belongs to: the number of problems i >= 1 with begin(i) <= x, begin
+// nondecreasing.  All the begins are read at once (independent loads of
+// the kernel arguments), not one after another.
+template <typename Begin>
+__device__ __forceinline__ int group_index(int count, int x, Begin begin) {
+  int di = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) {
+    const int b = begin(i);
+    di += (i < count && x >= b) ? 1 : 0;
+  }
+  return di;
+}
 
 // Small-M rank-r product (M <= 16), up to kMaxGroup problems per launch, as
 // kRankSmallSplits partial sums over consecutive quarters of K:
@@ -275,57 +289,103 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 
 // ------------------------------------------------- small-M forward (GEMV)
 // Y[m][n] = RNE_bf16( sum_k X[m][k] Wh[n][k] + sum_i T[m][i] B[n][i] ),
-// T = t_scale * X A^T, for m < M <= 16.  The weight-streaming launch: its
-// first t_wgs workgroups each form one 16-rank block of T over the whole of
-// K into t_buf; the others each own kGemvRows rows and a K split of
-// ss_per_split 256-wide super-steps, stage their K slice of X in LDS and
-// write FP32 partials part[split][m][n].  The finish launch (one workgroup
-// per 64 columns) adds the splits in ascending order, applies the LoRA term
-// and writes Y.  launch_lora_down runs the T blocks alone (same code, same
-// bits).
-#ifndef QLORA_GEMV_ROWS
-#define QLORA_GEMV_ROWS 64
+// T = t_scale * XA A^T, for m < M <= 16, up to kMaxGroup layers per launch.
+//
+// Work.  A weight unit is one 64-row tile of one layer's weight times one
+// 256-wide K super-step; a layer's units are listed tile by tile,
+// super-step by super-step.  A T task forms one partial of T over a chunk
+// of tchunk_ss super-steps for 16 ranks: tpart[c][m][i] = sum over the
+// chunk's columns k of XA[m][k] A[i][k]; a layer has ceil(r / 16) x tchunks
+// of them.  Each layer's work is one list: its T tasks first, each counted
+// as tcost units, then its weight units (toff = n_tasks x tcost onwards).
+//
+// The weight-streaming launch gives layer i a block of wgs_i workgroups
+// (wg_begin ..), the blocks sized in proportion to the layers' work so that
+// the launch has kGemvWgs workgroups, four on every compute unit, each with
+// about the same work.  Workgroup j of a layer takes the contiguous range
+// gemv_unit_begin(j) .. gemv_unit_begin(j + 1) of the layer's list (uq or
+// uq + 1 units, the first urem workgroups one more): the T tasks that start
+// in it, then its weight units, writing one FP32 partial per tile it
+// touches into slot j - gemv_wg_of(toff + first unit of the tile) of that
+// tile (part[slot][m][n], at most kGemvMaxSlots slots per tile).
+//
+// The finish launch (one workgroup per 64 output columns) adds a tile's
+// slots in order, forms T = t_scale * (((tpart[0] + tpart[1]) + ...) in
+// chunk order, adds the LoRA term, rounds Y and, from the workgroup of the
+// first columns, writes T_save.  The backward's recompute of T runs the same
+// T tasks (launch_gemv_tasks) and k_rank_finish adds the same partials in
+// the same order: both get the same bits.
+#ifndef QLORA_GEMV_WGS
+#define QLORA_GEMV_WGS 1024
 #endif
-constexpr int kGemvRows = QLORA_GEMV_ROWS;   // a multiple of 64
+constexpr int kGemvRows = 64;                       // rows per tile (16 per wavefront)
+constexpr int kGemvWgs = QLORA_GEMV_WGS;            // workgroups of one launch
+constexpr int kGemvMaxSlots = 16;                   // partials per tile, at most
+constexpr int kGemvMaxChunks = 16;                  // T chunks per layer, at most
 struct GemvDesc {
   const uint8_t* codes;
   const uint8_t* scodes;
   const float* scale2;
   const float* mean;
-  const uint16_t* X;      // [M][d_in], 16-byte aligned
+  const uint16_t* X;      // [M][d_in], 16-byte aligned: the base product's input
   const uint16_t* XA;     // LoRA branch input [M][d_in] (X, or X with dropped
                           // elements cleared), 16-byte aligned
   const uint16_t* A;      // [r][d_in], 16-byte aligned
   const uint16_t* B;      // [d_out][r]
-  float* t_buf;           // T FP32 [M][r], 16-byte aligned
+  float* T_save;          // T FP32 [M][r] or NULL
   uint16_t* Y;            // [M][d_out]
-  float* part;            // [ksplit][16][d_out]
+  float* part;            // [kGemvMaxSlots][M][d_out]
+  float* tpart;           // [tchunks][M][r]
   int64_t d_out, d_in, r;
   float t_scale;
-  int ksplit;
-  int ss_per_split;       // 256-wide K super-steps per split
-  int tiles;              // kGemvRows-row tiles
-  int tb_begin;           // first T-block workgroup (blocks cdiv(r, 16))
-  int wg_begin;           // first streaming workgroup, counted after the T blocks
-  int fin_begin;          // first workgroup of the finish launch
+  int tiles;              // 64-row tiles
+  int nss;                // 256-wide super-steps of K
+  int units;              // weight units: tiles * nss
+  int tchunks;            // T chunks
+  int tchunk_ss;          // super-steps per T chunk
+  int n_tasks;            // T tasks: ceil(r / 16) * tchunks
+  int tcost;              // units a T task counts for
+  int toff;               // n_tasks * tcost
+  int task_begin;         // first T task of this layer (T tasks alone)
+  int wgs;                // workgroups of this layer in the streaming launch
+  int wg_begin;           // its first workgroup there
+  int uq, urem;           // (toff + units) / wgs and (toff + units) % wgs
+  int fin_begin;          // first finish workgroup of this layer
 };
 struct GemvArgs {
   GemvDesc d[kMaxGroup];
   int count;
   int M;
-  int t_wgs;              // T-block workgroups of all problems
+  int wgs;                // workgroups of the weight-streaming launch
+  int tasks;              // workgroups of a T-tasks-alone launch
+  int fin_wgs;            // workgroups of the finish launch
+  bool vec_b;             // every B 16-byte aligned with r % 8 == 0
 };
-// LDS of one workgroup (the staged X) and its limit: a quarter of the CU's
-// 160 KB for four resident workgroups
-#ifndef QLORA_GEMV_MAX_LDS
-#define QLORA_GEMV_MAX_LDS 40960
-#endif
-constexpr int64_t kGemvMaxLds = QLORA_GEMV_MAX_LDS;
-inline int64_t gemv_lds_bytes(int64_t M, int64_t ss_per_split) {
-  return std::max<int64_t>((M + 1) * (ss_per_split * 512 + 16), 4 * 16 * 16 * 4);  // X rows | T sums
+// First unit of workgroup j of a list split over workgroups with
+// q = units / wgs, rem = units % wgs (the first rem get one unit more), and
+// the workgroup of unit u.  Lists hold fewer than 2^31 units.
+__host__ __device__ inline int gemv_unit_begin(int j, int q, int rem) {
+  return j * q + (j < rem ? j : rem);
 }
-hipError_t launch_gemv(const GemvArgs& a, int total_wgs, int fin_wgs, hipStream_t st);
-hipError_t launch_lora_down(const GemvArgs& a, hipStream_t st);
+__host__ __device__ inline int gemv_wg_of(int u, int q, int rem) {
+  const int big = rem * (q + 1);
+  return u < big ? (int)((unsigned)u / (unsigned)(q + 1))
+                 : rem + (int)((unsigned)(u - big) / (unsigned)q);
+}
+// LDS of the weight-streaming launch: a ring of kGemvRing staged X
+// super-steps of 16 rows x 512 bytes (rows past M zero), which also holds a
+// T task's reduction buffer.
+#ifndef QLORA_GEMV_RING
+#define QLORA_GEMV_RING 4
+#endif
+constexpr int kGemvRing = QLORA_GEMV_RING;
+inline int64_t gemv_lds_bytes(int64_t M) {
+  (void)M;
+  return (int64_t)kGemvRing * 16 * 512;
+}
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t st);
+// The T tasks of `a` alone (one workgroup per task; no weight streaming).
+hipError_t launch_gemv_tasks(const GemvArgs& a, hipStream_t st);
 
 // ------------------------------------------------- large-M fused GEMM
 // Forward: Y = RNE_bf16(X Wh^T + [T_hi T_lo] [B B]^T), dequant tiles in LDS.
