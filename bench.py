@@ -6,7 +6,11 @@ of one LLaMA-7B-shaped decoder layer's seven projections (q, k, v, o 4096 x
 sequence 1024), LoRA rank 64, alpha 16, NF4 + FP8 double-quantized frozen
 base, BF16 activations.  One step = for every projection: forward (saving
 T = s X A^T) then backward (dX, dA, dB), 14 library calls.  Useful FLOPs per
-projection = 4 M d_in d_out + 6 M r (d_in + d_out).
+projection = 4 M d_in d_out + 6 M r (d_in + d_out).  Before the W warm-up
+steps the step runs back to back for --settle-ms (default 300 ms, reported
+as settle_ms): after an idle gap the GPU's clocks need some 30-40 ms of
+continuous load to settle, and the first fused-GEMM launches run 10-15 %
+slower until they do.
 
 The same line also carries, each measured in the same run:
   dropout  the headline step in training mode with LoRA dropout p = 0.05
@@ -234,13 +238,29 @@ def timed(fn, steps, warmup):
 
 # -------------------------------------------------------------- workloads
 
-def bench_train7b(dev, steps, warmup):
+def settle(step, settle_ms):
+    """Untimed steps back to back for at least settle_ms before the warm-up:
+    after an idle gap the GPU's clocks take some 30-40 ms of continuous load
+    to reach their steady state (the first fused-GEMM launches after idle run
+    10-15 % slower), and the warm-up steps alone cover less than that."""
+    n = 0
+    t_end = time.perf_counter() + settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    return n
+
+
+def bench_train7b(dev, steps, warmup, settle_ms=0.0):
     M = 4096
     log(f"7B layer fwd+bwd: M={M} r={R}; quantizing 7 projections")
     layer = Layer(inputs.LLAMA_7B, M, 3, 0, dev)
     acts = Activations(inputs.LLAMA_7B, M, 3, dev)
     torch.cuda.synchronize()
     flops = sum(useful_flops(M, d_out, d_in, R) for _, d_out, d_in in inputs.LLAMA_7B)
+    n_settle = settle(lambda: train_step(layer, acts), settle_ms)
+    log(f"settle: {n_settle} untimed steps in {settle_ms:.0f} ms, then {warmup} warm-up steps")
     for _ in range(warmup):
         train_step(layer, acts)
     torch.cuda.synchronize()
@@ -741,6 +761,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps back to back for this long before the warm-up steps "
+                         "(clock ramp after idle)")
     ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,blocked,merge,adamw,stack65b,peaks,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-stack-tokens", type=int, default=128)
@@ -767,7 +790,7 @@ def main():
         log(f"copy calibration: {args.copy_mb} MB read + {args.copy_mb} MB written")
         del src, dst
 
-    train = bench_train7b(dev, args.steps, args.warmup)
+    train = bench_train7b(dev, args.steps, args.warmup, args.settle_ms)
     extra = {}
     if "dropout" not in skip:
         extra["dropout_7b"] = bench_dropout7b(dev, args.steps, args.warmup)
@@ -794,6 +817,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(train["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
