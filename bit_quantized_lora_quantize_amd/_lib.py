@@ -17,7 +17,10 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqlora.so")
+# QLORA_LIB names another build of the same library (for instance the
+# host-sanitized libqlora_san.so)
+LIB_PATH = os.environ.get("QLORA_LIB") or os.path.join(_PKG, "libqlora.so")
+SAN_LIB_PATH = os.path.join(_PKG, "libqlora_san.so")
 # benchmark build: the same library plus qlora_time_next_weight_kernel
 # (include/qlora_timing.h)
 TIMED_LIB_PATH = os.path.join(_PKG, "libqlora_timed.so")

@@ -11,7 +11,12 @@ Also builds two variants from the same sources:
   libqlora_timed.so  a benchmark build that also exports
                      qlora_time_next_weight_kernel (include/qlora_timing.h),
                      an event pair around the next weight-kernel launch; the
-                     library proper keeps no such state.
+                     library proper keeps no such state;
+  libqlora_san.so    a test build whose host code in api.cpp and noalloc.hip
+                     (argument checks, plans, workspace carving) is built with
+                     AddressSanitizer and UndefinedBehaviorSanitizer; the GPU
+                     code is the same.  Loaded with the clang ASan runtime
+                     preloaded (tests/test_sanitized.py).
 
 Usage: python -m bit_quantized_lora_quantize_amd.build_lib [--jobs N]
 """
@@ -32,6 +37,12 @@ LIB = os.path.join(PKG, "libqlora.so")
 LIB_WIDE = os.path.join(PKG, "libqlora_wide.so")
 LIB_TIMED = os.path.join(PKG, "libqlora_timed.so")
 LIB_PEAKS = os.path.join(PKG, "libqlora_peaks.so")
+LIB_SAN = os.path.join(PKG, "libqlora_san.so")
+# host code built with sanitizers in libqlora_san.so (each -fsanitize= applies
+# to the host pass only)
+SAN_SOURCES = ["api.cpp", "noalloc.hip"]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 # sources that hold the timing hook or launch a weight kernel
 TIMED_SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "api.cpp"]
 
@@ -90,12 +101,15 @@ def build(jobs: int = 6) -> str:
         timed = {src: ex.submit(_compile, src, "_timed", ("-DQLORA_TIMING_HOOK=1",))
                  for src in TIMED_SOURCES}
         peaks = ex.submit(_compile, "peaks.hip")
+        san = {src: ex.submit(_compile, src, "_san", tuple(SAN_FLAGS)) for src in SAN_SOURCES}
         objs = list(ex.map(_compile, SOURCES))
         wide_obj = wide.result()
         timed_objs = {src: f.result() for src, f in timed.items()}
+        san_objs = {src: f.result() for src, f in san.items()}
     _link(objs, LIB)
     _link([wide_obj if os.path.basename(o) == "gemm.hip.o" else o for o in objs], LIB_WIDE)
     _link([timed_objs.get(os.path.basename(o)[:-2], o) for o in objs], LIB_TIMED)
+    _link([san_objs.get(os.path.basename(o)[:-2], o) for o in objs], LIB_SAN)
     _link([peaks.result()], LIB_PEAKS)
     return LIB
 

@@ -9,31 +9,79 @@
 
 namespace qlora {
 
-// ---------------------------------------------------------------------------
-// Kernel 1: per 64-weight block, absmax, x = w / absmax, nearest NF4 level,
-// two indices per byte.  Eight lanes own one block (8 FP32 values each, two
-// 16-byte loads); the block maximum is an exact max over the 8 lanes.
-// The nearest level uses a 129-bucket table over x in [-1, 1]: bucket
-// floor(64 x) + 64 is exact (a power-of-two scale), holds at most one
-// decision threshold, and gives idx = base + (x >= threshold).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_absmax_encode(const float* __restrict__ W,
-                                                       int64_t n1,
-                                                       uint8_t* __restrict__ codes,
-                                                       float* __restrict__ absmax,
-                                                       IndexLut lut) {
-  __shared__ uint2 s_lut[kLutSize];
-  for (int i = threadIdx.x; i < kLutSize; i += blockDim.x)
-    s_lut[i] = make_uint2(__float_as_uint(lut.thr[i]), (uint32_t)lut.base[i]);
-  __syncthreads();
+// x = w / m for |w| <= m with m in [2^-64, 2^64]: Newton-Raphson division by
+// fused multiply-add (Markstein, "IA-64 and Elementary Functions", 2000):
+// a refined reciprocal r1 of m, then two correction steps of the quotient.
+// These are the steps of the IEEE single-precision division on this GPU
+// when neither operand needs scaling; in this range only quotients of
+// magnitude below 2^-126 could need it, and those fall in the bucket next
+// to 0 whose code does not depend on their exact value (the decision
+// thresholds nearest 0 are -0.0455 and 0.0398).
+__device__ __forceinline__ float div_for_code(float w, float m) {
+  const float r = __builtin_amdgcn_rcpf(m);
+  const float r1 = __builtin_fmaf(__builtin_fmaf(-m, r, 1.0f), r, r);
+  const float q0 = __fmul_rn(w, r1);
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-m, q0, w), r1, q0);
+  return __builtin_fmaf(__builtin_fmaf(-m, q1, w), r1, q1);
+}
 
+// ---------------------------------------------------------------------------
+// First level and group sums: per 64-weight block, absmax, x = w / absmax,
+// nearest NF4 level, two indices per byte; per group of kGroup = 256 blocks,
+// the FP64 sum of the block absmax values.  One workgroup of 512 threads per
+// group (2048 items of 8 weights), every load of the group issued before
+// its first encode through a descriptor over the group's bytes (items past
+// n1 read zero and are not stored).  Eight lanes own one block (8 FP32
+// values each, two 16-byte loads); the block maximum is an exact max over
+// the 8 lanes.  The nearest level uses a 129-bucket table over x in
+// [-1, 1]: bucket floor(64 x) + 64 is exact (a power-of-two scale), holds at
+// most one decision threshold, and gives idx = base + (x >= threshold).
+// The group's absmax values also go to LDS, and wavefront 0 forms the
+// group's sum by the stride-halving tree (j += j + 128, then j += j + 64,
+// ..., j += j + 1; blocks past n1 count 0).  Workgroups of the padding
+// groups G .. Gp - 1 write 0.
+// ---------------------------------------------------------------------------
+constexpr int kEncodeThreads = 512;
+constexpr int kEncodeItems = kGroup * 8 / kEncodeThreads;   // items per thread
+
+__global__ __launch_bounds__(kEncodeThreads) void k_absmax_encode(const float* __restrict__ W,
+                                                                  int64_t n1, int64_t G,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  float* __restrict__ absmax,
+                                                                  double* __restrict__ part,
+                                                                  IndexLut lut) {
+  __shared__ uint2 s_lut[kLutSize];
+  __shared__ float s_am[kGroup];
+  const int64_t g = blockIdx.x;
+  const int t = threadIdx.x;
+  if (g >= G) {
+    if (t == 0) part[g] = 0.0;
+    return;
+  }
+  // the decision table first: its loads are waited for before any weight
+  // load is in flight
+  if (t < kLutSize) s_lut[t] = make_uint2(__float_as_uint(lut.thr[t]), (uint32_t)lut.base[t]);
   const int64_t items = n1 * 8;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(W + it * 8);
-    f32x4 v0 = __builtin_nontemporal_load(p);
-    f32x4 v1 = __builtin_nontemporal_load(p + 1);
-    float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const int64_t c0 = g * (kGroup * 8);
+  const int64_t cbytes = (items - c0 < kGroup * 8 ? items - c0 : kGroup * 8) * 32;
+  const uint64_t wb = reinterpret_cast<uint64_t>(W + c0 * 8);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(wb >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wb)),
+      0, __builtin_amdgcn_readfirstlane((int)cbytes), 0x00020000);
+  f32x4 v[kEncodeItems][2];
+#pragma unroll
+  for (int k = 0; k < kEncodeItems; ++k) {
+    const uint32_t off = (uint32_t)(t + kEncodeThreads * k) * 32u;
+    v[k][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+    v[k][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16, 0, 0));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kEncodeItems; ++k) {
+    const int64_t it = c0 + t + kEncodeThreads * k;
+    const float w[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w,
+                        v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
     float m = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(w[e]));
@@ -41,12 +89,14 @@ __global__ __launch_bounds__(256) void k_absmax_encode(const float* __restrict__
     m = fmaxf(m, __shfl_xor(m, 2, 8));
     m = fmaxf(m, __shfl_xor(m, 4, 8));
     uint32_t packed = 0;
+    // the block's lanes take the same branch (m is the block maximum)
+    const bool fast = m >= 0x1p-64f && m <= 0x1p64f;
     if (m == 0.0f) {
       packed = 0x77777777u;  // zero block: every element is the exact-zero level
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = __fdiv_rn(w[e], m);
+        float x = fast ? div_for_code(w[e], m) : __fdiv_rn(w[e], m);
         int b = (int)__builtin_floorf(x * 64.0f) + 64;
         b = b < 0 ? 0 : (b > kLutSize - 1 ? kLutSize - 1 : b);  // finite x is in [-1, 1]
         uint2 ent = s_lut[b];
@@ -54,41 +104,30 @@ __global__ __launch_bounds__(256) void k_absmax_encode(const float* __restrict__
         packed |= idx << (4 * e);
       }
     }
-    reinterpret_cast<uint32_t*>(codes)[it] = packed;
-    if ((it & 7) == 0) absmax[it >> 3] = m;
+    if (it < items) {
+      reinterpret_cast<uint32_t*>(codes)[it] = packed;
+      if ((t & 7) == 0) absmax[it >> 3] = m;
+    }
+    if ((t & 7) == 0) s_am[(t >> 3) + (kEncodeThreads / 8) * k] = m;   // 0 past n1
   }
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 2: FP64 sum of each group of 256 absmax values by the stride-halving
-// tree (j += j+128, then j += j+64, ... , j += j+1), one wavefront per group.
-// Groups past the last real one are written as 0 up to the padded count.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_group_sums(const float* __restrict__ absmax, int64_t n1,
-                                                    int64_t G, int64_t Gp,
-                                                    double* __restrict__ part) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= Gp) return;
-  if (g >= G) {
-    if (lane == 0) part[g] = 0.0;
-    return;
-  }
-  double v[4];
+  __syncthreads();
+  if (t < 64) {
+    double d[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int64_t b = g * kGroup + lane + 64 * q;
-    v[q] = (b < n1) ? (double)absmax[b] : 0.0;
-  }
-  v[0] = v[0] + v[2];  // half = 128
-  v[1] = v[1] + v[3];
-  v[0] = v[0] + v[1];  // half = 64
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = g * kGroup + t + 64 * q;
+      d[q] = (b < n1) ? (double)s_am[t + 64 * q] : 0.0;
+    }
+    d[0] = d[0] + d[2];  // half = 128
+    d[1] = d[1] + d[3];
+    d[0] = d[0] + d[1];  // half = 64
 #pragma unroll
-  for (int half = 32; half >= 1; half >>= 1) {
-    double o = __shfl_down(v[0], half, 64);
-    v[0] = v[0] + o;
+    for (int half = 32; half >= 1; half >>= 1) {
+      double o = __shfl_down(d[0], half, 64);
+      d[0] = d[0] + o;
+    }
+    if (t == 0) part[g] = d[0];
   }
-  if (lane == 0) part[g] = v[0];
 }
 
 // One level of the stride-halving tree over a power-of-two array in global
@@ -112,38 +151,83 @@ __global__ __launch_bounds__(1024) void k_tree_final(const double* __restrict__ 
   if (threadIdx.x == 0) mean[0] = (float)(s[0] / (double)n1);
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 3: second level.  One wavefront per group of 256 scales: centred
-// d = a - mean, s2 = max|d| / 448, code = FP8 E4M3FN(d / s2) (RNE, saturating);
-// s2 == 0 stores code 0.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_scale_dq(const float* __restrict__ absmax, int64_t n1,
-                                                  int64_t G, const float* __restrict__ mean_p,
-                                                  uint8_t* __restrict__ scale_codes,
-                                                  float* __restrict__ scale2) {
+// Mean and second level.  Wavefront 0 of every workgroup adds the len group
+// sums (len a power of two, <= kTreeLds) by the stride-halving tree, the
+// same additions in the same order as k_tree_final: element j sits in lane
+// j % 64, register j / 64, so the levels with half >= 64 add registers
+// within a lane and the last six add across lanes.  Every workgroup thus
+// holds the same mean (workgroup 0 stores it).  Then each wavefront encodes
+// kScaleGroups groups, g = kScaleGroups (4 blockIdx + w) + i: centred
+// d = a - mean, s2 = max|d| / 448, code = FP8 E4M3FN(d / s2) (RNE,
+// saturating); s2 == 0 stores code 0.  The groups' absmax values are loaded
+// before the tree.
+constexpr int kScaleGroups = 4;
+constexpr int kTreeRegs = kTreeLds / 64;
+
+__global__ __launch_bounds__(256) void k_mean_scale_dq(const double* __restrict__ part, int64_t len,
+                                                       const float* __restrict__ absmax, int64_t n1,
+                                                       int64_t G, float* __restrict__ mean_out,
+                                                       uint8_t* __restrict__ scale_codes,
+                                                       float* __restrict__ scale2) {
+  __shared__ float s_mean;
   const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= G) return;
-  const float mean = mean_p[0];
-  float d[4];
-  bool ok[4];
-  float mg = 0.0f;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + w) * kScaleGroups;
+  float a[kScaleGroups][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int64_t b = g * kGroup + lane + 64 * q;
-    ok[q] = b < n1;
-    d[q] = ok[q] ? __fsub_rn(absmax[b], mean) : 0.0f;
-    mg = fmaxf(mg, fabsf(d[q]));
+  for (int i = 0; i < kScaleGroups; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = (g0 + i) * kGroup + lane + 64 * q;
+      a[i][q] = (g0 + i < G && b < n1) ? absmax[b] : 0.0f;
+    }
+  if (w == 0) {
+    double v[kTreeRegs];
+#pragma unroll
+    for (int i = 0; i < kTreeRegs; ++i) v[i] = (lane + 64 * i < len) ? part[lane + 64 * i] : 0.0;
+#pragma unroll
+    for (int h = kTreeRegs / 2; h >= 1; h /= 2) {
+      if (len >= 128 * h) {
+#pragma unroll
+        for (int i = 0; i < h; ++i) v[i] = v[i] + v[i + h];
+      }
+    }
+#pragma unroll
+    for (int half = 32; half >= 1; half >>= 1) {
+      const double o = __shfl_down(v[0], half, 64);
+      if (len >= 2 * half) v[0] = v[0] + o;
+    }
+    if (lane == 0) {
+      const float mean = (float)(v[0] / (double)n1);
+      s_mean = mean;
+      if (blockIdx.x == 0) mean_out[0] = mean;
+    }
   }
+  __syncthreads();
+  const float mean = s_mean;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, __shfl_xor(mg, off, 64));
-  const float s2 = __fdiv_rn(mg, 448.0f);
-  if (lane == 0) scale2[g] = s2;
+  for (int i = 0; i < kScaleGroups; ++i) {
+    const int64_t g = g0 + i;
+    if (g >= G) break;
+    float d[4];
+    float mg = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (!ok[q]) continue;
-    uint32_t code = (s2 == 0.0f) ? 0u : f32_to_fp8e4m3_rne_sat(__fdiv_rn(d[q], s2));
-    scale_codes[g * kGroup + lane + 64 * q] = (uint8_t)code;
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = (g * kGroup + lane + 64 * q) < n1;
+      d[q] = ok ? __fsub_rn(a[i][q], mean) : 0.0f;
+      mg = fmaxf(mg, fabsf(d[q]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, __shfl_xor(mg, off, 64));
+    const float s2 = __fdiv_rn(mg, 448.0f);
+    if (lane == 0) scale2[g] = s2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = g * kGroup + lane + 64 * q;
+      if (b >= n1) continue;
+      const uint32_t code = (s2 == 0.0f) ? 0u : f32_to_fp8e4m3_rne_sat(__fdiv_rn(d[q], s2));
+      scale_codes[b] = (uint8_t)code;
+    }
   }
 }
 
@@ -202,15 +286,23 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   const int64_t G = (n1 + kGroup - 1) / kGroup;
   int64_t Gp = 1;
   while (Gp < G) Gp *= 2;
+  // encode with the group sums (Gp workgroups), the tree levels above
+  // kTreeLds one launch each, then the last levels fused with the
+  // second-level encode
   weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_absmax_encode, dim3(grid_for(n1 * 8, 256, 8192)), dim3(256), 0, st, W,
-                     n1, codes, ws.absmax, lut);
+  hipLaunchKernelGGL(k_absmax_encode, dim3((unsigned)Gp), dim3(kEncodeThreads), 0, st, W, n1, G,
+                     codes, ws.absmax, ws.part, lut);
   weight_kernel_end(st);
-  hipLaunchKernelGGL(k_group_sums, dim3((unsigned)((Gp + 3) / 4)), dim3(256), 0, st, ws.absmax,
-                     n1, G, Gp, ws.part);
-  launch_mean_tree(ws.part, Gp, n1, mean, st);
-  hipLaunchKernelGGL(k_scale_dq, dim3((unsigned)((G + 3) / 4)), dim3(256), 0, st, ws.absmax, n1,
-                     G, mean, scale_codes, scale2);
+  int64_t len = Gp;
+  while (len > kTreeLds) {
+    const int64_t half = len / 2;
+    hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((half + 255) / 256)), dim3(256), 0, st,
+                       ws.part, half);
+    len = half;
+  }
+  hipLaunchKernelGGL(k_mean_scale_dq, dim3((unsigned)((G + 4 * kScaleGroups - 1) / (4 * kScaleGroups))),
+                     dim3(256), 0, st, ws.part,
+                     len, ws.absmax, n1, G, mean, scale_codes, scale2);
   return hipGetLastError();
 }
 

@@ -157,7 +157,10 @@ int qlora_merge_nf4(const qlora_nf4_t *q, const uint16_t *A, const uint16_t *B,
  * where Wh is the restored BF16 weight.  Products take BF16 inputs and
  * accumulate in FP32; Y is rounded once to BF16.  The rank-r intermediate
  * T = s X A^T is formed in FP32 and enters the second product as the sum of
- * two BF16 terms (hi + lo), so it carries about 16 significant bits.
+ * two BF16 terms (hi + lo), so it carries about 16 significant bits.  T is
+ * deliberately not a BF16 tensor: one BF16 rounding of T (and of U in the
+ * backward) would spend most of the 2e-3 relative error allowed for dA and
+ * dB, so it is saved and handed to the backward as FP32.
  *   X       BF16 [M, d_in]  (16B)        M >= 0 tokens (M = 0: no work)
  *   A       BF16 [r, d_in]  (16B)        1 <= r <= 256
  *   B       BF16 [d_out, r]              any alignment

@@ -19,7 +19,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qlora_oracle.c")
-_LIB = os.path.join(_HERE, "libqlora_oracle.so")
+# QLORA_ORACLE_SANITIZE=1: the same source built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (gcc), for runs with libasan and libubsan
+# preloaded
+_SANITIZE = os.environ.get("QLORA_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libqlora_oracle_san.so" if _SANITIZE else "libqlora_oracle.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
 
 BLOCK = 64    # first-level block [QP §3.4]
 GROUP = 256   # second-level block [QP §5.2]
@@ -27,15 +33,18 @@ GROUP = 256   # second-level block [QP §5.2]
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
+def build(force: bool = False, sanitize: bool = _SANITIZE) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction); with
+    sanitize, the sanitized build libqlora_oracle_san.so."""
+    lib = os.path.join(_HERE, "libqlora_oracle_san.so" if sanitize else "libqlora_oracle.so")
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp"
         subprocess.check_call([
             "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            *(SAN_FLAGS if sanitize else []),
             "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():

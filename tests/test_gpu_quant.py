@@ -93,3 +93,33 @@ def test_large_group_tree(orc):
     the scale-mean tree runs its global-memory levels before the LDS ones."""
     W = inputs.weight(8192, 22016, config=4, layer=0, device=DEV, proj=6)
     _roundtrip(orc, W.cpu(), "65B down_proj")
+
+
+@pytest.mark.parametrize("shape", [(257, 1024), (4096, 4096)])
+def test_quantized_state_file_roundtrip(orc, tmp_path, shape):
+    """The quantized state is the four buffers the principles page lists for
+    a stored 4-bit weight (§5.3): packed codes, 8-bit block-scale codes, the
+    FP32 second-level scales and the mean.  Copied to the host, written to a
+    file, read back into fresh device buffers and dequantized, it restores
+    the same BF16 bytes as the original buffers (and as the oracle)."""
+    d_out, d_in = shape
+    W = inputs.weight(d_out, d_in, config=7, layer=0, outliers=True)
+    w = _roundtrip(orc, W, "state file round trip")
+    ref = q.qlora_dequant_bf16(w)
+    path = tmp_path / "nf4_state.npz"
+    np.savez(path, codes=w.codes.cpu().numpy(), scale_codes=w.scale_codes.cpu().numpy(),
+             scale2=w.scale2.cpu().numpy(), scale_mean=w.scale_mean.cpu().numpy(),
+             shape=np.array([d_out, d_in], dtype=np.int64))
+    del w
+    torch.cuda.synchronize()
+    with np.load(path) as f:                      # no pickles: plain arrays only
+        d_out2, d_in2 = (int(v) for v in f["shape"])
+        w2 = q.NF4Weight(d_out2, d_in2,
+                         torch.from_numpy(f["codes"]).to(DEV),
+                         torch.from_numpy(f["scale_codes"]).to(DEV),
+                         torch.from_numpy(f["scale2"]).to(DEV),
+                         torch.from_numpy(f["scale_mean"]).to(DEV))
+    out = q.qlora_dequant_bf16(w2)
+    torch.cuda.synchronize()
+    assert (d_out2, d_in2) == (d_out, d_in)
+    assert np.array_equal(bits16(out), bits16(ref)), "reloaded state restores different bytes"
