@@ -20,8 +20,10 @@ The same line also carries, each measured in the same run:
            codes + FP8 scale codes + FP32 second-level scales + mean); four
            distinct quantized copies of the layer rotate so the 256 MB
            last-level cache holds none of them;
-  quant    quantize and dequantize of the 7B layer, GB/s over the algorithmic
-           bytes (read FP32 W + write packed state; read packed + write BF16);
+  quant    quantize and dequantize of the 7B layer's seven projections, each
+           as one grouped call (quantize, dequant) and as seven single calls
+           (quantize_each, dequant_each), GB/s over the algorithmic bytes (read
+           FP32 W + write packed state; read packed + write BF16);
   blocked  quantize / dequantize of the 7B layer as flat arrays at first-level
            block sizes 32, 128 and 256 (groups of 256), GB/s as for quant;
   merge    LoRA merge into the restored base plus requantization of the 7B
@@ -405,20 +407,33 @@ def bench_quant7b(dev, steps, warmup):
     bq = 4 * n + packed
     bd = packed + 2 * n
 
+    # the layer's seven projections in one grouped call (the way a layer is
+    # loaded), and as seven single calls
     def qstep(i, tm=None):
+        if tm:
+            tm.arm("q")
+        q.qlora_quantize_nf4_many(Ws, outs=qs, workspaces=wss)
+
+    def dstep(i, tm=None):
+        if tm:
+            tm.arm("d")
+        q.qlora_dequant_bf16_many(qs, outs=outs)
+
+    def qstep_each(i, tm=None):
         for W, w, ws in zip(Ws, qs, wss):
             if tm:
                 tm.arm("q")
             q.qlora_quantize_nf4(W, out=w, workspace=ws)
 
-    def dstep(i, tm=None):
+    def dstep_each(i, tm=None):
         for w, o in zip(qs, outs):
             if tm:
                 tm.arm("d")
             q.qlora_dequant_bf16(w, out=o)
 
     res = {}
-    for name, fn, nbytes in (("quantize", qstep, bq), ("dequant", dstep, bd)):
+    for name, fn, nbytes in (("quantize", qstep, bq), ("dequant", dstep, bd),
+                             ("quantize_each", qstep_each, bq), ("dequant_each", dstep_each, bd)):
         # wall clock without timing events between the launches, then one
         # more pass with the weight kernel of every call bracketed by events
         el = timed(fn, steps, warmup) / steps

@@ -48,6 +48,14 @@ class _FwdItem(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class _QuantItem(ctypes.Structure):
+    _fields_ = [("W", _P), ("q", _Nf4), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _DequantItem(ctypes.Structure):
+    _fields_ = [("q", _Nf4), ("W_bf16", _P)]
+
+
 class _Nf4Blocked(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("block", ctypes.c_int64), ("group", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("scale_codes", ctypes.c_void_p),
@@ -100,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_fwd.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
                                        ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
         L.qlora_linear_fwd_many.argtypes = [ctypes.c_int, ctypes.POINTER(_FwdItem), _I64, _P]
+        L.qlora_quantize_nf4_many.argtypes = [ctypes.c_int, ctypes.POINTER(_QuantItem), _P]
+        L.qlora_dequant_bf16_many.argtypes = [ctypes.c_int, ctypes.POINTER(_DequantItem), _P]
         L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_Nf4), _P, _I64, _P, _P, _I64,
                                                ctypes.c_float, _P, _P, _P]
         L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_Nf4), _P, _P, _I64, _P, _P, _I64,
@@ -258,6 +268,49 @@ def qlora_dequant_bf16(q: NF4Weight, out: Optional[torch.Tensor] = None) -> torc
     _check(lib().qlora_dequant_bf16(ctypes.byref(qs), _ptr(Wb), _stream(q.device)),
            "qlora_dequant_bf16")
     return Wb
+
+
+def qlora_quantize_nf4_many(Ws: Sequence[torch.Tensor],
+                            outs: Optional[Sequence[NF4Weight]] = None,
+                            workspaces: Optional[Sequence[torch.Tensor]] = None) -> list:
+    """qlora_quantize_nf4 for up to QLORA_MAX_GROUP tensors in one call (the
+    same results bit for bit)."""
+    if not 1 <= len(Ws) <= QLORA_MAX_GROUP:
+        raise ValueError(f"1 .. {QLORA_MAX_GROUP} tensors per call")
+    arr = (_QuantItem * len(Ws))()
+    qs, keep = [], []
+    for i, W in enumerate(Ws):
+        d_out, d_in = W.shape
+        _need(W, torch.float32, (d_out, d_in), "W")
+        q = outs[i] if outs is not None else NF4Weight.empty(d_out, d_in, W.device)
+        if workspaces is not None:
+            ws = workspaces[i]
+        else:
+            ws = _workspace(qlora_workspace_bytes(QLORA_OP_QUANTIZE, d_out, d_in), W.device)
+        keep.append(ws)
+        arr[i] = _QuantItem(W.data_ptr(), q.c_struct(), ws.data_ptr(), ws.numel())
+        qs.append(q)
+    _check(lib().qlora_quantize_nf4_many(len(Ws), arr, _stream(Ws[0].device)),
+           "qlora_quantize_nf4_many")
+    return qs
+
+
+def qlora_dequant_bf16_many(qs: Sequence[NF4Weight],
+                            outs: Optional[Sequence[torch.Tensor]] = None) -> list:
+    """qlora_dequant_bf16 for up to QLORA_MAX_GROUP weights in one call."""
+    if not 1 <= len(qs) <= QLORA_MAX_GROUP:
+        raise ValueError(f"1 .. {QLORA_MAX_GROUP} weights per call")
+    arr = (_DequantItem * len(qs))()
+    res = []
+    for i, q in enumerate(qs):
+        Wb = outs[i] if outs is not None else torch.empty((q.d_out, q.d_in), dtype=torch.bfloat16,
+                                                          device=q.device)
+        _need(Wb, torch.bfloat16, (q.d_out, q.d_in), "W_bf16")
+        arr[i] = _DequantItem(q.c_struct(), Wb.data_ptr())
+        res.append(Wb)
+    _check(lib().qlora_dequant_bf16_many(len(qs), arr, _stream(qs[0].device)),
+           "qlora_dequant_bf16_many")
+    return res
 
 
 @dataclass

@@ -667,6 +667,42 @@ int qlora_dequant_bf16(const qlora_nf4_t* q, uint16_t* W_bf16, void* stream) {
                                    q->d_out * q->d_in, W_bf16, static_cast<hipStream_t>(stream)));
 }
 
+int qlora_quantize_nf4_many(int count, const qlora_quant_item* items, void* stream) {
+  if (count < 1 || count > kMaxGroup) return QLORA_ERR_SHAPE;
+  if (!items) return QLORA_ERR_NULL;
+  QuantList a{};
+  a.count = count;
+  for (int i = 0; i < count; ++i) {
+    const qlora_quant_item& it = items[i];
+    int s = check_nf4(&it.q);
+    if (s) return s;
+    if (!it.W || !it.workspace) return QLORA_ERR_NULL;
+    if (!aligned16(it.W) || !aligned16(it.workspace)) return QLORA_ERR_ALIGN;
+    const QuantPlan p = plan_quant(it.q.d_out, it.q.d_in, it.workspace);
+    if (it.workspace_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
+    a.d[i] = quant_item(it.W, p.n, it.q.codes, it.q.scale_codes, it.q.scale2, it.q.scale_mean,
+                        QuantWorkspace{p.absmax, p.part});
+  }
+  return hip_status(launch_quantize_list(a, lut(), static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dequant_bf16_many(int count, const qlora_dequant_item* items, void* stream) {
+  if (count < 1 || count > kMaxGroup) return QLORA_ERR_SHAPE;
+  if (!items) return QLORA_ERR_NULL;
+  DequantList a{};
+  a.count = count;
+  for (int i = 0; i < count; ++i) {
+    const qlora_dequant_item& it = items[i];
+    int s = check_nf4(&it.q);
+    if (s) return s;
+    if (!it.W_bf16) return QLORA_ERR_NULL;
+    if (!aligned16(it.W_bf16)) return QLORA_ERR_ALIGN;
+    a.d[i] = DequantItem{it.q.codes, it.q.scale_codes, it.q.scale2, it.q.scale_mean,
+                         it.q.d_out * it.q.d_in / kBlock, it.W_bf16, 0, 0};
+  }
+  return hip_status(launch_dequant_list(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_sumsq_workspace_bytes(int count, const qlora_adamw_param* params) {
   if (count < 0 || (count > 0 && !params)) return 0;
   int64_t len = 0;

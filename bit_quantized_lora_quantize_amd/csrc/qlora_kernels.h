@@ -85,6 +85,49 @@ __device__ __forceinline__ int group_index(int count, int x, Begin begin) {
   return di;
 }
 
+// Quantize / dequantize of up to kMaxGroup tensors per launch (one list),
+// each with the arithmetic of a single call.  Encode workgroups: Gp per
+// tensor from enc_begin; second-level workgroups from scale_begin;
+// dequantize workgroups: wgs per tensor from begin.
+struct QuantItem {
+  const float* W;
+  int64_t n1, G, Gp;
+  int64_t len;            // tree length left for the last launch (<= kTreeLds)
+  uint8_t* codes;
+  uint8_t* scale_codes;
+  float* scale2;
+  float* mean;
+  float* absmax;          // workspace [n1]
+  double* part;           // workspace [Gp]
+  int enc_begin, scale_begin;
+};
+struct QuantList {
+  QuantItem d[kMaxGroup];
+  int count;
+  int enc_wgs, scale_wgs;
+};
+// One QuantItem of a tensor of n weights (its len and begins are set by
+// launch_quantize_list).
+QuantItem quant_item(const float* W, int64_t n, uint8_t* codes, uint8_t* scale_codes,
+                     float* scale2, float* mean, const QuantWorkspace& ws);
+hipError_t launch_quantize_list(QuantList& a, const IndexLut& lut, hipStream_t st);
+
+struct DequantItem {
+  const uint8_t* codes;
+  const uint8_t* scale_codes;
+  const float* scale2;
+  const float* mean;
+  int64_t n1;
+  uint16_t* out;
+  int wgs, begin;
+};
+struct DequantList {
+  DequantItem d[kMaxGroup];
+  int count;
+  int wgs;
+};
+hipError_t launch_dequant_list(DequantList& a, hipStream_t st);
+
 // Small-M rank-r product (M <= 16), up to kMaxGroup problems per launch, as
 // kRankSmallSplits partial sums over consecutive quarters of K:
 //   part[s][m][n] = sum_{k in quarter s} P[m][k] Q[n][k],

@@ -44,15 +44,17 @@ __device__ __forceinline__ float div_for_code(float w, float m) {
 constexpr int kEncodeThreads = 512;
 constexpr int kEncodeItems = kGroup * 8 / kEncodeThreads;   // items per thread
 
-__global__ __launch_bounds__(kEncodeThreads) void k_absmax_encode(const float* __restrict__ W,
-                                                                  int64_t n1, int64_t G,
-                                                                  uint8_t* __restrict__ codes,
-                                                                  float* __restrict__ absmax,
-                                                                  double* __restrict__ part,
-                                                                  IndexLut lut) {
+__global__ __launch_bounds__(kEncodeThreads) void k_absmax_encode(QuantList a, IndexLut lut) {
   __shared__ uint2 s_lut[kLutSize];
   __shared__ float s_am[kGroup];
-  const int64_t g = blockIdx.x;
+  const int di = group_index(a.count, (int)blockIdx.x, [&](int i) { return a.d[i].enc_begin; });
+  const QuantItem& d = a.d[di];
+  const float* __restrict__ W = d.W;
+  const int64_t n1 = d.n1, G = d.G;
+  uint8_t* __restrict__ codes = d.codes;
+  float* __restrict__ absmax = d.absmax;
+  double* __restrict__ part = d.part;
+  const int64_t g = (int64_t)blockIdx.x - d.enc_begin;
   const int t = threadIdx.x;
   if (g >= G) {
     if (t == 0) part[g] = 0.0;
@@ -164,22 +166,27 @@ __global__ __launch_bounds__(1024) void k_tree_final(const double* __restrict__ 
 constexpr int kScaleGroups = 4;
 constexpr int kTreeRegs = kTreeLds / 64;
 
-__global__ __launch_bounds__(256) void k_mean_scale_dq(const double* __restrict__ part, int64_t len,
-                                                       const float* __restrict__ absmax, int64_t n1,
-                                                       int64_t G, float* __restrict__ mean_out,
-                                                       uint8_t* __restrict__ scale_codes,
-                                                       float* __restrict__ scale2) {
+__global__ __launch_bounds__(256) void k_mean_scale_dq(QuantList a) {
   __shared__ float s_mean;
+  const int di = group_index(a.count, (int)blockIdx.x, [&](int i) { return a.d[i].scale_begin; });
+  const QuantItem& d = a.d[di];
+  const double* __restrict__ part = d.part;
+  const float* __restrict__ absmax = d.absmax;
+  const int64_t len = d.len, n1 = d.n1, G = d.G;
+  float* __restrict__ mean_out = d.mean;
+  uint8_t* __restrict__ scale_codes = d.scale_codes;
+  float* __restrict__ scale2 = d.scale2;
+  const int64_t wg = (int64_t)blockIdx.x - d.scale_begin;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t g0 = ((int64_t)blockIdx.x * 4 + w) * kScaleGroups;
-  float a[kScaleGroups][4];
+  const int64_t g0 = (wg * 4 + w) * kScaleGroups;
+  float am[kScaleGroups][4];
 #pragma unroll
   for (int i = 0; i < kScaleGroups; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t b = (g0 + i) * kGroup + lane + 64 * q;
-      a[i][q] = (g0 + i < G && b < n1) ? absmax[b] : 0.0f;
+      am[i][q] = (g0 + i < G && b < n1) ? absmax[b] : 0.0f;
     }
   if (w == 0) {
     double v[kTreeRegs];
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(256) void k_mean_scale_dq(const double* __restrict_
     if (lane == 0) {
       const float mean = (float)(v[0] / (double)n1);
       s_mean = mean;
-      if (blockIdx.x == 0) mean_out[0] = mean;
+      if (wg == 0) mean_out[0] = mean;
     }
   }
   __syncthreads();
@@ -209,13 +216,13 @@ __global__ __launch_bounds__(256) void k_mean_scale_dq(const double* __restrict_
   for (int i = 0; i < kScaleGroups; ++i) {
     const int64_t g = g0 + i;
     if (g >= G) break;
-    float d[4];
+    float dv[4];
     float mg = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool ok = (g * kGroup + lane + 64 * q) < n1;
-      d[q] = ok ? __fsub_rn(a[i][q], mean) : 0.0f;
-      mg = fmaxf(mg, fabsf(d[q]));
+      dv[q] = ok ? __fsub_rn(am[i][q], mean) : 0.0f;
+      mg = fmaxf(mg, fabsf(dv[q]));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, __shfl_xor(mg, off, 64));
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(256) void k_mean_scale_dq(const double* __restrict_
     for (int q = 0; q < 4; ++q) {
       const int64_t b = g * kGroup + lane + 64 * q;
       if (b >= n1) continue;
-      const uint32_t code = (s2 == 0.0f) ? 0u : f32_to_fp8e4m3_rne_sat(__fdiv_rn(d[q], s2));
+      const uint32_t code = (s2 == 0.0f) ? 0u : f32_to_fp8e4m3_rne_sat(__fdiv_rn(dv[q], s2));
       scale_codes[b] = (uint8_t)code;
     }
   }
@@ -236,21 +243,23 @@ __global__ __launch_bounds__(256) void k_mean_scale_dq(const double* __restrict_
 // 16-entry BF16 table RNE(level_i * scale), byte-permute lookups of eight
 // weights per lane.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_dequant_bf16(const uint8_t* __restrict__ codes,
-                                                      const uint8_t* __restrict__ scale_codes,
-                                                      const float* __restrict__ scale2,
-                                                      const float* __restrict__ mean_p,
-                                                      int64_t n1, uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_dequant_bf16(DequantList a) {
   // One code dword (eight weights, 16 output bytes) per thread: eight
   // consecutive threads share a block (each builds its table), and a
   // wavefront reads 256 contiguous code bytes and writes 1 KB of contiguous
-  // output, so every store fills whole cache lines.
-  const float mean = mean_p[0];
-  const int64_t nunits = n1 * 8;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
-  u32x4* ov = reinterpret_cast<u32x4*>(out);
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += stride) {
+  // output, so every store fills whole cache lines.  A tensor's workgroups
+  // stride over its units.
+  const int di = group_index(a.count, (int)blockIdx.x, [&](int i) { return a.d[i].begin; });
+  const DequantItem& d = a.d[di];
+  const uint8_t* __restrict__ scale_codes = d.scale_codes;
+  const float* __restrict__ scale2 = d.scale2;
+  const float mean = d.mean[0];
+  const int64_t nunits = d.n1 * 8;
+  const int64_t stride = (int64_t)d.wgs * blockDim.x;
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(d.codes);
+  u32x4* ov = reinterpret_cast<u32x4*>(d.out);
+  for (int64_t u = (int64_t)(blockIdx.x - d.begin) * blockDim.x + threadIdx.x; u < nunits;
+       u += stride) {
     const int64_t b = u >> 3;
     const uint32_t c = __builtin_nontemporal_load(cw + u);
     const Nf4Table t = nf4_table(restored_scale(scale_codes[b], scale2[b >> 8], mean));
@@ -279,41 +288,84 @@ void launch_mean_tree(double* part, int64_t Gp, int64_t n1, float* mean, hipStre
   hipLaunchKernelGGL(k_tree_final, dim3(1), dim3(1024), 0, st, part, len, n1, mean);
 }
 
+QuantItem quant_item(const float* W, int64_t n, uint8_t* codes, uint8_t* scale_codes,
+                     float* scale2, float* mean, const QuantWorkspace& ws) {
+  QuantItem d{};
+  d.W = W;
+  d.n1 = n / kBlock;
+  d.G = (d.n1 + kGroup - 1) / kGroup;
+  d.Gp = 1;
+  while (d.Gp < d.G) d.Gp *= 2;
+  d.codes = codes;
+  d.scale_codes = scale_codes;
+  d.scale2 = scale2;
+  d.mean = mean;
+  d.absmax = ws.absmax;
+  d.part = ws.part;
+  return d;
+}
+
+hipError_t launch_quantize_list(QuantList& a, const IndexLut& lut, hipStream_t st) {
+  // encode with the group sums (Gp workgroups per tensor), the tree levels
+  // above kTreeLds one launch each, then the last levels fused with the
+  // second-level encode
+  int enc = 0, sc = 0;
+  for (int i = 0; i < a.count; ++i) {
+    QuantItem& d = a.d[i];
+    d.enc_begin = enc;
+    d.scale_begin = sc;
+    enc += (int)d.Gp;
+    sc += (int)((d.G + 4 * kScaleGroups - 1) / (4 * kScaleGroups));
+    d.len = d.Gp;
+  }
+  a.enc_wgs = enc;
+  a.scale_wgs = sc;
+  weight_kernel_begin(st);
+  hipLaunchKernelGGL(k_absmax_encode, dim3((unsigned)enc), dim3(kEncodeThreads), 0, st, a, lut);
+  weight_kernel_end(st);
+  for (int i = 0; i < a.count; ++i) {
+    QuantItem& d = a.d[i];
+    while (d.len > kTreeLds) {
+      const int64_t half = d.len / 2;
+      hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((half + 255) / 256)), dim3(256), 0, st,
+                         d.part, half);
+      d.len = half;
+    }
+  }
+  hipLaunchKernelGGL(k_mean_scale_dq, dim3((unsigned)sc), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale_codes,
                            float* scale2, float* mean, const QuantWorkspace& ws,
                            const IndexLut& lut, hipStream_t st) {
-  const int64_t n1 = n / kBlock;
-  const int64_t G = (n1 + kGroup - 1) / kGroup;
-  int64_t Gp = 1;
-  while (Gp < G) Gp *= 2;
-  // encode with the group sums (Gp workgroups), the tree levels above
-  // kTreeLds one launch each, then the last levels fused with the
-  // second-level encode
-  weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_absmax_encode, dim3((unsigned)Gp), dim3(kEncodeThreads), 0, st, W, n1, G,
-                     codes, ws.absmax, ws.part, lut);
-  weight_kernel_end(st);
-  int64_t len = Gp;
-  while (len > kTreeLds) {
-    const int64_t half = len / 2;
-    hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((half + 255) / 256)), dim3(256), 0, st,
-                       ws.part, half);
-    len = half;
+  QuantList a{};
+  a.count = 1;
+  a.d[0] = quant_item(W, n, codes, scale_codes, scale2, mean, ws);
+  return launch_quantize_list(a, lut, st);
+}
+
+hipError_t launch_dequant_list(DequantList& a, hipStream_t st) {
+  int wgs = 0;
+  for (int i = 0; i < a.count; ++i) {
+    DequantItem& d = a.d[i];
+    d.wgs = grid_for(d.n1 * 8, 256, 8192);
+    d.begin = wgs;
+    wgs += d.wgs;
   }
-  hipLaunchKernelGGL(k_mean_scale_dq, dim3((unsigned)((G + 4 * kScaleGroups - 1) / (4 * kScaleGroups))),
-                     dim3(256), 0, st, ws.part,
-                     len, ws.absmax, n1, G, mean, scale_codes, scale2);
+  a.wgs = wgs;
+  weight_kernel_begin(st);
+  hipLaunchKernelGGL(k_dequant_bf16, dim3((unsigned)wgs), dim3(256), 0, st, a);
+  weight_kernel_end(st);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale_codes, const float* scale2,
                           const float* mean, int64_t n, uint16_t* out, hipStream_t st) {
-  const int64_t n1 = n / kBlock;
-  weight_kernel_begin(st);
-  hipLaunchKernelGGL(k_dequant_bf16, dim3(grid_for(n1 * 8, 256, 8192)), dim3(256), 0, st, codes,
-                     scale_codes, scale2, mean, n1, out);
-  weight_kernel_end(st);
-  return hipGetLastError();
+  DequantList a{};
+  a.count = 1;
+  a.d[0] = DequantItem{codes, scale_codes, scale2, mean, n / kBlock, out, 0, 0};
+  return launch_dequant_list(a, st);
 }
 
 }  // namespace qlora

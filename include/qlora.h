@@ -255,6 +255,34 @@ int qlora_linear_fwd_many(int count, const qlora_fwd_item *items, int64_t M,
                           void *stream);
 
 /*
+ * Quantize (dequantize) up to QLORA_MAX_GROUP tensors in one call: the same
+ * operation as qlora_quantize_nf4 (qlora_dequant_bf16) for every item, with
+ * the same results bit for bit, in two launches (one) for the whole list
+ * when no tensor has more than 2^20 first-level blocks, so the projections
+ * of a layer pay the launch and call overhead once.  Each item has its own
+ * input, output and (quantize) workspace sized by
+ * qlora_workspace_bytes(QLORA_OP_QUANTIZE, ...); items must not share any
+ * of them.  Returns the first failing item's status (nothing enqueued on
+ * argument errors) or QLORA_ERR_SHAPE when count is not in
+ * 1 .. QLORA_MAX_GROUP.
+ */
+typedef struct {
+  const float *W;           /* FP32 [q.d_out, q.d_in] (16B) */
+  qlora_nf4_t q;            /* output state */
+  void *workspace;          /* (16B) */
+  size_t workspace_bytes;
+} qlora_quant_item;
+
+int qlora_quantize_nf4_many(int count, const qlora_quant_item *items, void *stream);
+
+typedef struct {
+  qlora_nf4_t q;            /* input state */
+  uint16_t *W_bf16;         /* BF16 [q.d_out, q.d_in] (16B) output */
+} qlora_dequant_item;
+
+int qlora_dequant_bf16_many(int count, const qlora_dequant_item *items, void *stream);
+
+/*
  * General block sizes ([QP §5.5]: the first-level block size B1 trades
  * scale metadata, about 8 / B1 bits per weight after double quantization,
  * against error; the second-level group size B2 makes the same trade for

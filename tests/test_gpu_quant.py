@@ -123,3 +123,36 @@ def test_quantized_state_file_roundtrip(orc, tmp_path, shape):
     torch.cuda.synchronize()
     assert (d_out2, d_in2) == (d_out, d_in)
     assert np.array_equal(bits16(out), bits16(ref)), "reloaded state restores different bytes"
+
+
+def test_quantize_many_matches_single_calls(orc):
+    """The grouped call on the 7B layer's seven projections plus two small
+    and ragged tensors (9 > 8 would be refused, so 8 items): every state and
+    every restored BF16 weight equals a single call's, bit for bit, and the
+    small ones equal the oracle's."""
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008), (4096, 4096), (11008, 4096),
+              (4096, 4096), (37, 320), (1, 64)]
+    Ws = [inputs.weight(d_out, d_in, config=5, layer=0, outliers=True, device=DEV, proj=i)
+          for i, (d_out, d_in) in enumerate(shapes)]
+    say("quantize_many: 8 tensors")
+    many = q.qlora_quantize_nf4_many(Ws)
+    outs = q.qlora_dequant_bf16_many(many)
+    for i, W in enumerate(Ws):
+        one = q.qlora_quantize_nf4(W)
+        torch.cuda.synchronize()
+        for name in ("codes", "scale_codes", "scale2", "scale_mean"):
+            a, b = getattr(many[i], name), getattr(one, name)
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"item {i} {name}"
+        assert np.array_equal(bits16(outs[i]), bits16(q.qlora_dequant_bf16(one))), f"item {i} bf16"
+    for i in (6, 7):
+        ref, wh_bits, _ = oracle_quant(orc, Ws[i].cpu())
+        assert_quant_equal(many[i], ref)
+        assert np.array_equal(bits16(outs[i]), wh_bits)
+
+
+def test_quantize_many_refuses_bad_counts():
+    W = torch.zeros((64, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        q.qlora_quantize_nf4_many([W] * 9)
+    with pytest.raises(ValueError):
+        q.qlora_quantize_nf4_many([])
