@@ -212,7 +212,14 @@ def train_step(layer, acts, timer=None, p_drop=None, step=0):
             q.qlora_linear_fwd(it["w"], a["X"], it["A"], it["B"], ALPHA, Y=a["Y"],
                                T_save=a["T"], workspace=a["wsf"])
         else:
-            drop = q.Dropout(p_drop, seed=0x5EED, offset=len(layer.items) * step + n)
+            # the forward saves its keep bits for the backward (as T), so the
+            # mask is generated once per step
+            if "keep_rows" not in a:
+                M, d_in = a["X"].shape
+                m = q.Dropout(p_drop, 0).saved_mask(M, d_in, a["X"].device)
+                a["keep_rows"], a["keep_cols"] = m.keep_rows, m.keep_cols
+            drop = q.Dropout(p_drop, seed=0x5EED, offset=len(layer.items) * step + n,
+                             keep_rows=a["keep_rows"], keep_cols=a["keep_cols"])
             q.qlora_linear_fwd_dropout(it["w"], a["X"], it["A"], it["B"], ALPHA, drop,
                                        Y=a["Y"], T_save=a["T"], workspace=a["wsf"])
         if timer:

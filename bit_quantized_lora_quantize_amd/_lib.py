@@ -63,7 +63,8 @@ class _Nf4Blocked(ctypes.Structure):
 
 
 class _Dropout(ctypes.Structure):
-    _fields_ = [("p", ctypes.c_float), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+    _fields_ = [("p", ctypes.c_float), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64),
+                ("keep_rows", _P), ("keep_cols", _P)]
 
 
 class _AdamwParam(ctypes.Structure):
@@ -498,9 +499,22 @@ class Dropout:
     p: float
     seed: int
     offset: int = 0
+    # optional saved mask (M > 16): int32 [M, d_in / 32] and [d_in, ceil(M / 32)]
+    # device tensors the forward fills and the backward reads (saved_mask())
+    keep_rows: Optional[torch.Tensor] = None
+    keep_cols: Optional[torch.Tensor] = None
 
     def c_struct(self) -> _Dropout:
-        return _Dropout(float(self.p), int(self.seed) & (2**64 - 1), int(self.offset) & (2**64 - 1))
+        rows = self.keep_rows.data_ptr() if self.keep_rows is not None else None
+        cols = self.keep_cols.data_ptr() if self.keep_cols is not None else None
+        return _Dropout(float(self.p), int(self.seed) & (2**64 - 1), int(self.offset) & (2**64 - 1),
+                        rows, cols)
+
+    def saved_mask(self, M: int, d_in: int, device="cuda") -> "Dropout":
+        """The same dropout with buffers for the forward to save its mask in."""
+        rows = torch.empty((M, d_in // 32), dtype=torch.int32, device=device)
+        cols = torch.empty((d_in, (M + 31) // 32), dtype=torch.int32, device=device)
+        return Dropout(self.p, self.seed, self.offset, rows, cols)
 
 
 def _fwd(q, X, A, B, lora_alpha, Y, T_save, workspace, dropout):

@@ -248,10 +248,14 @@ int check_blocked(const qlora_nf4_blocked_t* q) {
   return QLORA_OK;
 }
 
-// LoRA dropout buffers, after the region of the plan they extend: the
-// masked LoRA input [M][d_in] and (backward) the keep words [d_in][ldw].
+// LoRA dropout buffers, after the region of the plan they extend.  Small M
+// (weight-streaming path): the masked LoRA input xm [M][d_in].  Larger M:
+// the row-major keep words rbits [M][d_in / 32], applied by the rank-r
+// kernels as they load X (no masked copy).  Backward: also the keep words
+// of the input-gradient GEMM, keep [d_in][ldw].
 struct DropPlan {
   uint16_t* xm;
+  uint32_t* rbits;
   uint32_t* keep;
   int64_t ldw;
   size_t bytes;
@@ -261,7 +265,8 @@ DropPlan plan_drop(size_t base_bytes, int64_t M, int64_t d_in, bool with_bits, v
   DropPlan d{};
   Carver c(ws);
   c.off = base_bytes;
-  d.xm = c.take<uint16_t>(M * d_in);
+  if (M <= kSmallM) d.xm = c.take<uint16_t>(M * d_in);
+  else d.rbits = c.take<uint32_t>(M * (d_in / 32));
   d.ldw = cdiv(std::max<int64_t>(M, 1), 32);
   if (with_bits) d.keep = c.take<uint32_t>(d_in * d.ldw);
   d.bytes = c.off + 256;
@@ -273,6 +278,7 @@ DropPlan plan_drop(size_t base_bytes, int64_t M, int64_t d_in, bool with_bits, v
 int dropout_params(const qlora_dropout_t* drop, DropoutArgs* a) {
   if (!drop) return QLORA_ERR_NULL;
   if (!(drop->p >= 0.0f && drop->p < 1.0f)) return QLORA_ERR_SHAPE;
+  if (!aligned16(drop->keep_rows) || !aligned16(drop->keep_cols)) return QLORA_ERR_ALIGN;
   *a = DropoutArgs{};
   a->thr = (uint32_t)std::floor((double)drop->p * 4294967296.0);
   a->key_lo = (uint32_t)drop->seed;
@@ -348,6 +354,7 @@ struct FwdItemArgs {
   size_t ws_bytes;
   const uint16_t* XA;  // LoRA branch input: X, or X after dropout
   float sc;            // LoRA scale: alpha / r, or alpha / r / (1 - p)
+  const uint32_t* xmask = nullptr;   // large M with dropout: keep words of XA = X
 };
 
 // Descriptors and work partition of the small-M forward for a group (see
@@ -470,7 +477,7 @@ int fwd_group(const FwdItemArgs* items, int count, int64_t M, hipStream_t st) {
       FwdPlan p = plan_fwd(q->d_out, q->d_in, M, f.r, f.ws);
       float* T = f.T_save ? f.T_save : p.t_buf;
       RankRowsArgs ra{f.XA,   f.A,     M,       f.r,     q->d_in, q->d_in, f.sc,
-                      T,      p.t_hl,  p.rp,    nullptr, nullptr, 0};
+                      T,      p.t_hl,  p.rp,    nullptr, nullptr, 0,        f.xmask};
       int s = rank_product(ra, p.r_part, st);
       if (s) return s;
       GemmArgs g{q->codes, q->scale_codes, q->scale2, q->scale_mean, f.X, p.t_hl, f.B, f.Y,
@@ -507,10 +514,10 @@ int check_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY, int64
 // The backward after the checks.  XA is the LoRA branch's input (X, or X
 // after dropout), sc the LoRA scale, keep the dropout keep words of the
 // input gradient's LoRA term (NULL: none).
-int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
-             int64_t keep_ld, const uint16_t* dY, int64_t M, const uint16_t* A,
-             const uint16_t* B, int64_t r, float sc, const float* T_saved, uint16_t* dX,
-             float* dA, float* dB, const BwdPlan& p, hipStream_t st) {
+int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* xmask,
+             const uint32_t* keep, int64_t keep_ld, const uint16_t* dY, int64_t M,
+             const uint16_t* A, const uint16_t* B, int64_t r, float sc, const float* T_saved,
+             uint16_t* dX, float* dA, float* dB, const BwdPlan& p, hipStream_t st) {
   int s = QLORA_OK;
   const int64_t d_out = q->d_out, d_in = q->d_in;
   if (M == 0) {
@@ -530,7 +537,8 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
     t_with_u = true;
     t_copy = FinishDesc{T, nullptr, p.tt_hi, p.tt_lo, M, r, p.ldp, 1.0f, 1, 0, nullptr, 0};
   } else if (!T && M > kSmallM) {
-    RankRowsArgs ra{XA, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp};
+    RankRowsArgs ra{XA, A, M, r, d_in, d_in, sc, p.t_buf, nullptr, 0, p.tt_hi, p.tt_lo, p.ldp,
+                    xmask};
     s = rank_product(ra, p.r_part, st);
     if (s) return s;
     T = p.t_buf;
@@ -582,8 +590,8 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* keep,
   // dA = U^T XA ; dB = (T^T dY)^T, both contractions in one launch and
   // both finishes in another
   const GramProblem gp[2] = {
-      {p.ut_hi, p.ut_lo, XA, d_in, p.mper_a, p.ms_a, p.da_part, dA, false},
-      {p.tt_hi, p.tt_lo, dY, d_out, p.mper_b, p.ms_b, p.db_part, dB, true}};
+      {p.ut_hi, p.ut_lo, XA, d_in, p.mper_a, p.ms_a, p.da_part, dA, false, xmask},
+      {p.tt_hi, p.tt_lo, dY, d_out, p.mper_b, p.ms_b, p.db_part, dB, true, nullptr}};
   return hip_status(launch_grams(gp, 2, p.ldp, M, r, st));
 }
 
@@ -617,7 +625,7 @@ const char* qlora_status_string(int status) {
   }
 }
 
-int qlora_abi_version(void) { return (1 << 16) | 0; }
+int qlora_abi_version(void) { return (1 << 16) | 1; }
 
 int qlora_nf4_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* scale_codes_bytes,
                     size_t* scale2_bytes, size_t* scale_mean_bytes) {
@@ -831,8 +839,8 @@ int qlora_linear_bwd(const qlora_nf4_t* q, const uint16_t* X, const uint16_t* dY
   if (s) return s;
   const BwdPlan p = plan_bwd(q->d_out, q->d_in, M, r, ws);
   if (ws_bytes < p.bytes) return QLORA_ERR_WORKSPACE;
-  return bwd_impl(q, X, nullptr, 0, dY, M, A, B, r, lora_alpha / (float)r, T_saved, dX, dA,
-                  dB, p, static_cast<hipStream_t>(stream));
+  return bwd_impl(q, X, nullptr, nullptr, 0, dY, M, A, B, r, lora_alpha / (float)r, T_saved, dX,
+                  dA, dB, p, static_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_fwd_dropout(const qlora_nf4_t* q, const uint16_t* X, int64_t M,
@@ -855,9 +863,21 @@ int qlora_linear_fwd_dropout(const qlora_nf4_t* q, const uint16_t* X, int64_t M,
   da.M = M;
   da.d = d_in;
   da.ldw = dp.ldw;
-  s = hip_status(launch_dropout(da, st));
+  if (M <= kSmallM) {
+    // the masked copy (M rows) for the weight-streaming launch's T
+    s = hip_status(launch_dropout(da, st));
+    f.XA = dp.xm;
+  } else {
+    // keep words only (also into the caller's saved-mask buffers when
+    // given); T's kernel clears the dropped elements as it loads X
+    const bool save = drop->keep_rows && drop->keep_cols;
+    uint32_t* rows = save ? drop->keep_rows : dp.rbits;
+    da.keep = save ? drop->keep_cols : nullptr;
+    s = hip_status(launch_dropout_bits(da, rows, st));
+    f.XA = X;
+    f.xmask = rows;
+  }
   if (s) return s;
-  f.XA = dp.xm;
   f.sc = (lora_alpha / (float)r) / (1.0f - drop->p);
   return fwd_group(&f, 1, M, st);
 }
@@ -877,18 +897,27 @@ int qlora_linear_bwd_dropout(const qlora_nf4_t* q, const uint16_t* X, const uint
   const DropPlan dp = plan_drop(p.bytes, M, d_in, true, ws);
   if (ws_bytes < dp.bytes) return QLORA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (M > 0) {
+  // the forward's saved mask (M > 16), else the mask regenerated
+  const bool saved = M > kSmallM && drop->keep_rows && drop->keep_cols;
+  if (M > 0 && !saved) {
     da.X = X;
     da.Xm = dp.xm;
     da.keep = dp.keep;
     da.M = M;
     da.d = d_in;
     da.ldw = dp.ldw;
-    s = hip_status(launch_dropout(da, st));
+    s = hip_status(M <= kSmallM ? launch_dropout(da, st) : launch_dropout_bits(da, dp.rbits, st));
     if (s) return s;
   }
-  return bwd_impl(q, dp.xm, dp.keep, dp.ldw, dY, M, A, B, r,
-                  (lora_alpha / (float)r) / (1.0f - drop->p), T_saved, dX, dA, dB, p, st);
+  const float sc = (lora_alpha / (float)r) / (1.0f - drop->p);
+  if (M <= kSmallM)
+    return bwd_impl(q, dp.xm, nullptr, dp.keep, dp.ldw, dY, M, A, B, r, sc, T_saved, dX, dA, dB,
+                    p, st);
+  if (saved)
+    return bwd_impl(q, X, drop->keep_rows, drop->keep_cols, dp.ldw, dY, M, A, B, r, sc, T_saved,
+                    dX, dA, dB, p, st);
+  return bwd_impl(q, X, dp.rbits, dp.keep, dp.ldw, dY, M, A, B, r, sc, T_saved, dX, dA, dB, p,
+                  st);
 }
 
 int qlora_nf4_blocked_sizes(int64_t n, int64_t block, int64_t group, size_t* codes_bytes,

@@ -107,6 +107,55 @@ __global__ __launch_bounds__(256) void k_dropout(DropoutArgs a) {
   }
 }
 
+// Keep bits only, for tiles of 32 rows x 32 columns: thread (quad q = t / 32,
+// column c = t % 32) makes the one generator call of rows 4 q .. 4 q + 3 at
+// column c.  A wavefront holds two quads x 32 columns, so a ballot of one row
+// of a quad is that row's 32-column word; the column words (32 rows) are put
+// together from the eight quads' nibbles in LDS.
+__global__ __launch_bounds__(256) void k_dropout_bits(DropoutArgs a, uint32_t* __restrict__ rbits) {
+  __shared__ uint8_t nib[8][32];
+  const int64_t col_tiles = a.d / 32;
+  const int64_t tile = blockIdx.x;
+  const int64_t r0 = (tile / col_tiles) * 32, k0 = (tile % col_tiles) * 32;
+  const int t = threadIdx.x, q = t >> 5, c = t & 31;
+  uint32_t c0 = (uint32_t)(k0 + c), c1 = (uint32_t)(r0 / 4 + q), c2 = a.off_lo, c3 = a.off_hi;
+  philox4x32_10(c0, c1, c2, c3, a.key_lo, a.key_hi);
+  const int64_t m = r0 + 4 * q;
+  const uint32_t live = a.M - m >= 4 ? 15u : (a.M > m ? (1u << (a.M - m)) - 1u : 0u);
+  const uint32_t bits = ((c0 >= a.thr ? 1u : 0u) | (c1 >= a.thr ? 2u : 0u) |
+                         (c2 >= a.thr ? 4u : 0u) | (c3 >= a.thr ? 8u : 0u)) & live;
+  if (rbits) {
+    const int64_t ldr = a.d / 32;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint64_t b = __ballot((bits >> r) & 1u);
+      // lanes 0..31: quad 2 (t / 64); lanes 32..63: quad 2 (t / 64) + 1
+      if ((t & 31) == 0) {
+        const int64_t row = m + r;
+        const uint32_t word = (t & 32) ? (uint32_t)(b >> 32) : (uint32_t)b;
+        if (row < a.M) rbits[row * ldr + k0 / 32] = word;
+      }
+    }
+  }
+  if (a.keep) {
+    nib[q][c] = (uint8_t)bits;
+    __syncthreads();
+    if (t < 32) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) word |= (uint32_t)nib[qq][t] << (4 * qq);
+      a.keep[(k0 + t) * a.ldw + r0 / 32] = word;
+    }
+  }
+}
+
+hipError_t launch_dropout_bits(const DropoutArgs& a, uint32_t* rbits, hipStream_t st) {
+  const int64_t tiles = ((a.M + 31) / 32) * (a.d / 32);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dropout_bits, dim3((unsigned)tiles), dim3(256), 0, st, a, rbits);
+  return hipGetLastError();
+}
+
 hipError_t launch_dropout(const DropoutArgs& a, hipStream_t st) {
   const int64_t threads = (a.d / 2) * 2 * a.ldw;
   if (threads == 0) return hipSuccess;

@@ -33,6 +33,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rank_rsrc(const void* base, in
                                            __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
+// Eight BF16 values (natural order, two per dword) with the ones whose bit
+// in b8 is 0 cleared (bit e for element e).
+__device__ __forceinline__ u32x4 keep8_bf16(u32x4 v, uint32_t b8) {
+  u32x4 m;
+  m.x = ((b8 & 0x01u) ? 0x0000FFFFu : 0u) | ((b8 & 0x02u) ? 0xFFFF0000u : 0u);
+  m.y = ((b8 & 0x04u) ? 0x0000FFFFu : 0u) | ((b8 & 0x08u) ? 0xFFFF0000u : 0u);
+  m.z = ((b8 & 0x10u) ? 0x0000FFFFu : 0u) | ((b8 & 0x20u) ? 0xFFFF0000u : 0u);
+  m.w = ((b8 & 0x40u) ? 0x0000FFFFu : 0u) | ((b8 & 0x80u) ? 0xFFFF0000u : 0u);
+  return v & m;
+}
+
 // Row groups of 16 tokens per workgroup (RG) and wavefronts (W): every
 // wavefront of a workgroup reads all of Q over its K range, so Q's L2
 // traffic is (M / 16 RG) times its size; RG trades that against the number
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRo
 template <int NB>
 constexpr int rank_kc() { return NB <= 4 ? 128 : (NB <= 8 ? 64 : 32); }
 
-template <int NB>
+template <int NB, bool MASK>
 __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __restrict__ part,
                                                    int64_t kper, int ks) {
   constexpr int KC = rank_kc<NB>();
@@ -245,6 +256,10 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
   const __amdgpu_buffer_rsrc_t rp = rank_rsrc(a.P + m0 * K, (a.M - m0) * K * 2);   // rows past M: zero
   const __amdgpu_buffer_rsrc_t rq = rank_rsrc(a.Q, a.N * a.ldq * 2);               // rows past N: zero
   const uint32_t prow = (uint32_t)((16 * w + r16) * K);                             // element offset
+  // MASK: keep words of P's rows (K / 32 per row), rows past M read as zero
+  const __amdgpu_buffer_rsrc_t rm =
+      rank_rsrc(MASK ? a.pmask + m0 * (K / 32) : nullptr, MASK ? (a.M - m0) * (K / 32) * 4 : 0);
+  const uint32_t mrow = (uint32_t)((16 * w + r16) * (K / 32));
   // Q pieces of this thread: row pr[u], 8 columns from pc[u] within the chunk
   uint32_t qrow[PIECES], qcol[PIECES];
 #pragma unroll
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
   }
   const uint32_t kend = (uint32_t)k_end;
 
-  auto load_chunk = [&](int c, u32x4 (&qv)[PIECES], u32x4 (&xv)[NS]) {
+  auto load_chunk = [&](int c, u32x4 (&qv)[PIECES], u32x4 (&xv)[NS], uint32_t (&mk)[NS]) {
     const uint32_t kc0 = (uint32_t)(k_begin + (int64_t)c * KC);
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
@@ -268,6 +283,9 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
       const uint32_t col = kc0 + 32 * j + 8 * g;
       const uint32_t off = col < kend ? (prow + col) * 2 : 0x80000000u;
       xv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+      if (MASK)
+        mk[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rm, col < kend ? (mrow + ((kc0 >> 5) + j)) * 4 : 0x80000000u, 0, 0);
     }
   };
   auto store_q = [&](int buf, const u32x4 (&qv)[PIECES]) {
@@ -278,29 +296,32 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf, const u32x4 (&xv)[NS]) {
+  auto compute = [&](int buf, const u32x4 (&xv)[NS], const uint32_t (&mk)[NS]) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
+    for (int j = 0; j < NS; ++j) {
+      const u32x4 x = MASK ? keep8_bf16(xv[j], mk[j] >> (8 * g)) : xv[j];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = mfma16(xv[j], *reinterpret_cast<const u32x4*>(&qs[buf][(16 * nb + r16) * LQ + 32 * j + 8 * g]),
+        acc[nb] = mfma16(x, *reinterpret_cast<const u32x4*>(&qs[buf][(16 * nb + r16) * LQ + 32 * j + 8 * g]),
                          acc[nb]);
+    }
   };
 
   u32x4 q0[PIECES], x0[NS], q1[PIECES], x1[NS];
+  uint32_t m0k[NS], m1k[NS];
   if (nchunks > 0) {
-    load_chunk(0, q0, x0);
+    load_chunk(0, q0, x0, m0k);
     store_q(0, q0);
   }
   __syncthreads();
   for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) load_chunk(c + 1, q1, x1);
-    compute(0, x0);
+    if (c + 1 < nchunks) load_chunk(c + 1, q1, x1, m1k);
+    compute(0, x0, m0k);
     if (c + 1 >= nchunks) break;
     store_q(1, q1);
     __syncthreads();
-    if (c + 2 < nchunks) load_chunk(c + 2, q0, x0);
-    compute(1, x1);
+    if (c + 2 < nchunks) load_chunk(c + 2, q0, x0, m0k);
+    compute(1, x1, m1k);
     if (c + 2 < nchunks) store_q(0, q0);
     __syncthreads();
   }
@@ -598,10 +619,25 @@ constexpr int kGramWaveBytes = kGramRows * kGramLd * 2;
 // loads row 8 i + l/8, columns 8 (l%8) .. +8, i = 0..7.
 // The descriptor is based at the block's first token, so offsets stay below
 // 64 rows of Q whatever M is; tokens past M read as zero.
-template <bool VEC>
-__device__ __forceinline__ void gram_load(const uint16_t* Q, int64_t M, int64_t m, int64_t c0,
-                                          int64_t N, int lane, u32x4 (&x)[8]) {
+// MASK: the keep words of Q's rows (qmask [M][N / 32], row-major bits; NULL:
+// every element kept) are loaded beside the block into mk, word
+// (row, col / 32), whose bits 8 (lane % 4) .. +8 are the lane's columns.
+template <bool VEC, bool MASK>
+__device__ __forceinline__ void gram_load(const uint16_t* Q, const uint32_t* qmask, int64_t M,
+                                          int64_t m, int64_t c0, int64_t N, int lane, u32x4 (&x)[8],
+                                          uint32_t (&mk)[8]) {
   const __amdgpu_buffer_rsrc_t rq = rank_rsrc(Q + (m < M ? m : M) * N, (M - m) * N * 2);
+  if (MASK) {
+    const int64_t nw = N / 32;
+    const __amdgpu_buffer_rsrc_t rm =
+        rank_rsrc(qmask ? qmask + (m < M ? m : M) * nw : nullptr, qmask ? (M - m) * nw * 4 : 0);
+    const uint32_t all = qmask ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = 8 * i + (lane >> 3), col = c0 + 8 * (lane & 7);
+      mk[i] = all | __builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)((row * nw + col / 32) * 4), 0, 0);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = 8 * i + (lane >> 3), col = c0 + 8 * (lane & 7);
@@ -624,14 +660,16 @@ __device__ __forceinline__ void gram_load(const uint16_t* Q, int64_t M, int64_t 
 // One 64-token block of a wavefront: stage Q block x (tokens m ..) in LDS,
 // load the block's rank operands and the Q block two ahead into x, then 4
 // token slices x RB x 2 x (hi, lo) MFMAs.
-template <int RB, bool VEC>
-__device__ __forceinline__ void gram_block(const uint16_t* Q, int64_t M, __amdgpu_buffer_rsrc_t rh,
-                                           __amdgpu_buffer_rsrc_t rl, int64_t ldp, int64_t c0,
-                                           int64_t N, int64_t m, int lane, uint8_t* wl,
-                                           uint32_t wr, uint32_t rd, u32x4 (&x)[8],
-                                           f32x16 (&acc)[RB][2]) {
+template <int RB, bool VEC, bool MASK>
+__device__ __forceinline__ void gram_block(const uint16_t* Q, const uint32_t* qmask, int64_t M,
+                                           __amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rl,
+                                           int64_t ldp, int64_t c0, int64_t N, int64_t m, int lane,
+                                           uint8_t* wl, uint32_t wr, uint32_t rd, u32x4 (&x)[8],
+                                           uint32_t (&mk)[8], f32x16 (&acc)[RB][2]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + wr + i * 8 * kGramLd * 2) = x[i];
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<u32x4*>(wl + wr + i * 8 * kGramLd * 2) =
+        MASK ? keep8_bf16(x[i], mk[i] >> (8 * (lane & 3))) : x[i];
   u32x4 ph[4][RB], pl[4][RB];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -642,7 +680,7 @@ __device__ __forceinline__ void gram_block(const uint16_t* Q, int64_t M, __amdgp
       ph[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, po, 0, 0));
       pl[t][ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, po, 0, 0));
     }
-  gram_load<VEC>(Q, M, m + 2 * kGramRows, c0, N, lane, x);
+  gram_load<VEC, MASK>(Q, qmask, M, m + 2 * kGramRows, c0, N, lane, x, mk);
   __builtin_amdgcn_sched_barrier(0);   // every load of the block ahead of its MFMAs
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -669,6 +707,7 @@ struct GramDesc {
   const uint16_t* Pt_hi;
   const uint16_t* Pt_lo;
   const uint16_t* Q;
+  const uint32_t* qmask;
   int64_t N, m_per_split;
   float* part;
   int cgroups;    // groups of four 64-column tiles
@@ -685,7 +724,7 @@ struct GramArgs {
 // the same rank fragments at about the same time, so the compute unit's
 // vector cache serves most of them, and each wavefront's sums are complete
 // for its columns: no reduction between wavefronts.
-template <int RB, bool VEC>
+template <int RB, bool VEC, bool MASK>
 __global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
   extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
   // problem of this workgroup, then its column group and token split
@@ -694,6 +733,7 @@ __global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
   const uint16_t* __restrict__ Pt_hi = gd.Pt_hi;
   const uint16_t* __restrict__ Pt_lo = gd.Pt_lo;
   const uint16_t* __restrict__ Q = gd.Q;
+  const uint32_t* qmask = gd.qmask;
   const int64_t ldp = ga.ldp, M = ga.M, R = ga.R, N = gd.N, m_per_split = gd.m_per_split;
   float* __restrict__ part = gd.part;
   const int local = (int)blockIdx.x - gd.wg_begin;
@@ -731,13 +771,15 @@ __global__ __launch_bounds__(256) void k_gram(GramArgs ga) {
   // range are in bounds or read zero and are never used; issuing them
   // unconditionally keeps the compiler's wait counts exact.
   u32x4 xa[8], xb[8];
-  gram_load<VEC>(Q, M, m_begin, c0, N, lane, xa);
+  uint32_t ma[8], mb[8];
+  gram_load<VEC, MASK>(Q, qmask, M, m_begin, c0, N, lane, xa, ma);
   __builtin_amdgcn_sched_barrier(0);   // issue order = use order
-  gram_load<VEC>(Q, M, m_begin + kGramRows, c0, N, lane, xb);
+  gram_load<VEC, MASK>(Q, qmask, M, m_begin + kGramRows, c0, N, lane, xb, mb);
   __builtin_amdgcn_sched_barrier(0);
   for (int64_t m = m_begin; m < m_end; m += 2 * kGramRows) {
-    gram_block<RB, VEC>(Q, M, rh, rl, ldp, c0, N, m, lane, wl, wr, rd, xa, acc);
-    gram_block<RB, VEC>(Q, M, rh, rl, ldp, c0, N, m + kGramRows, lane, wl, wr, rd, xb, acc);
+    gram_block<RB, VEC, MASK>(Q, qmask, M, rh, rl, ldp, c0, N, m, lane, wl, wr, rd, xa, ma, acc);
+    gram_block<RB, VEC, MASK>(Q, qmask, M, rh, rl, ldp, c0, N, m + kGramRows, lane, wl, wr, rd,
+                              xb, mb, acc);
   }
 
   // accumulator element v of lane l: row 32 ib + 8 (v/4) + 4 (l/32) + v%4,
@@ -804,7 +846,10 @@ template <int NB>
 static hipError_t launch_rank_part_t(const RankRowsArgs& a, float* part, int64_t kper, int ks,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(((a.M + 63) / 64) * ks);
-  hipLaunchKernelGGL(k_rank_part<NB>, dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+  if (a.pmask)
+    hipLaunchKernelGGL((k_rank_part<NB, true>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+  else
+    hipLaunchKernelGGL((k_rank_part<NB, false>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
   return hipGetLastError();
 }
 
@@ -812,6 +857,8 @@ hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st,
                              const FinishDesc* extra) {
   // 16-byte row pieces need K and ldq multiples of 8 and aligned bases;
   // other layouts take the one-pass kernel, which loads elements
+  if (a.pmask && (a.K % 32 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15)))
+    return hipErrorInvalidValue;   // keep bits: whole words per row, 16-byte rows
   if (a.K % 8 != 0 || a.ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15) ||
       (reinterpret_cast<uintptr_t>(a.Q) & 15)) {
     hipError_t e = launch_rank_rows(a, st);
@@ -897,13 +944,13 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
-template <int RB, bool VEC>
+template <int RB, bool VEC, bool MASK>
 static hipError_t launch_gram_t(const GramArgs& a, int wgs, hipStream_t st) {
   constexpr int lds = 4 * kGramWaveBytes;
-  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gram<RB, VEC>),
+  static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gram<RB, VEC, MASK>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_gram<RB, VEC>), dim3((unsigned)wgs), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_gram<RB, VEC, MASK>), dim3((unsigned)wgs), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -916,14 +963,22 @@ static hipError_t launch_gram_group(const GramProblem* p, int count, int64_t ldp
   a.M = M;
   a.R = R;
   int wgs = 0;
+  bool mask = false;
   for (int i = 0; i < count; ++i) {
-    a.d[i] = GramDesc{p[i].Pt_hi, p[i].Pt_lo, p[i].Q, p[i].N, p[i].m_per_split, p[i].part,
-                      (int)((p[i].N + 255) / 256), wgs};
+    a.d[i] = GramDesc{p[i].Pt_hi, p[i].Pt_lo, p[i].Q, p[i].qmask, p[i].N, p[i].m_per_split,
+                      p[i].part, (int)((p[i].N + 255) / 256), wgs};
     wgs += a.d[i].cgroups * p[i].splits;
+    if (p[i].qmask) {
+      if (p[i].N % 32 != 0) return hipErrorInvalidValue;
+      mask = true;
+    }
   }
   if (wgs == 0) return hipSuccess;
+  // keep bits: whole words per row and 16-byte row loads
+  if (mask && !vec) return hipErrorInvalidValue;
 #define QLORA_GRAM(RB) \
-  return vec ? launch_gram_t<RB, true>(a, wgs, st) : launch_gram_t<RB, false>(a, wgs, st)
+  return mask ? launch_gram_t<RB, true, true>(a, wgs, st) \
+              : (vec ? launch_gram_t<RB, true, false>(a, wgs, st) : launch_gram_t<RB, false, false>(a, wgs, st))
   if (R <= 32) { QLORA_GRAM(1); }
   if (R <= 64) { QLORA_GRAM(2); }
   if (R <= 128) { QLORA_GRAM(4); }

@@ -183,6 +183,10 @@ struct RankRowsArgs {
   uint16_t* ht;
   uint16_t* lt;
   int64_t ldt;
+  // optional keep bits of P (row-major words, bit k % 32 of word
+  // [m * K / 32 + k / 32]; K a multiple of 32): P elements with bit 0 count as
+  // zero.  Only launch_rank_split (k_rank_part) takes them.
+  const uint32_t* pmask = nullptr;
 };
 hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st);
 // The same product (same outputs) through K-split partials part
@@ -266,6 +270,9 @@ struct GramProblem {
   float* part;   // [splits][R][N]
   float* out;
   bool transposed;
+  // optional keep bits of Q (row-major words [M][N / 32], N a multiple of
+  // 32): Q elements with bit 0 count as zero
+  const uint32_t* qmask = nullptr;
 };
 hipError_t launch_grams(const GramProblem* p, int count, int64_t ldp, int64_t M, int64_t R,
                         hipStream_t st);
@@ -313,6 +320,11 @@ struct DropoutArgs {
   uint32_t key_lo, key_hi, off_lo, off_hi;
 };
 hipError_t launch_dropout(const DropoutArgs& a, hipStream_t st);
+// The same mask as keep bits only, in two layouts (either may be NULL):
+// keep [d][ldw] (bit m % 32 of word [k][m / 32], as launch_dropout) and
+// rbits [M][d / 32] (bit k % 32 of word [m][k / 32]), d a multiple of 32.
+// X and Xm are not used.
+hipError_t launch_dropout_bits(const DropoutArgs& a, uint32_t* rbits, hipStream_t st);
 
 // ------------------------------------------------- LoRA merge
 // out[n][k] = RN_fp32(Wh[n][k] + scale * sum_i B[n][i] A[i][k]) (FP64

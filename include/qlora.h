@@ -344,6 +344,17 @@ typedef struct {
   float p;          /* drop probability, 0 <= p < 1 (else QLORA_ERR_SHAPE) */
   uint64_t seed;    /* generator key                                       */
   uint64_t offset;  /* counter words 2 and 3                               */
+  /* Optional saved mask of a layer call with M > 16 tokens (ignored for
+   * M <= 16 and by qlora_dropout_mask), device memory (16B):
+   *   keep_rows  [M, d_in / 32] words: bit (k % 32) of word [m][k / 32]
+   *   keep_cols  [d_in, ceil(M / 32)] words: bit (m % 32) of word [k][m / 32]
+   * (bits of rows m >= M are 0).  When both are non-NULL,
+   * qlora_linear_fwd_dropout writes them, and qlora_linear_bwd_dropout reads
+   * them instead of regenerating the mask, so the generator runs once per
+   * training step; they must then hold the mask of the same M, d_in, p,
+   * seed and offset.  NULL: nothing written, the backward regenerates. */
+  uint32_t *keep_rows;
+  uint32_t *keep_cols;
 } qlora_dropout_t;
 
 /*
@@ -376,7 +387,8 @@ int qlora_linear_fwd_dropout(const qlora_nf4_t *q, const uint16_t *X,
 
 /*
  * Backward of qlora_linear_fwd_dropout for the same X and `drop` (the mask
- * is regenerated, not stored):
+ * is regenerated, or read from drop->keep_rows / keep_cols when both are
+ * given and M > 16):
  *     U  = s dY B
  *     dX = dY Wh + keep * (U A) / (1 - p)
  *     dA = U^T D(X),   dB = dY^T T   with T = s D(X) A^T.

@@ -264,7 +264,14 @@ def test_dropout_argument_errors(L):
     bw = L.qlora_linear_bwd_dropout
     dA, dB = P(0xA0000), P(0xB0000)
     needb = q.qlora_workspace_bytes(q.QLORA_OP_BWD_DROPOUT, 128, 64, 40, 8)
-    assert needb > q.qlora_workspace_bytes(q.QLORA_OP_BWD, 128, 64, 40, 8) + 40 * 64 * 2
+    # M > 16: keep words in both layouts (no masked copy of X); M <= 16: the
+    # masked copy of X and the keep words of the GEMM
+    assert needb >= q.qlora_workspace_bytes(q.QLORA_OP_BWD, 128, 64, 40, 8) + 40 * 2 * 4 + 64 * 2 * 4
+    assert (q.qlora_workspace_bytes(q.QLORA_OP_BWD_DROPOUT, 128, 64, 4, 8) >=
+            q.qlora_workspace_bytes(q.QLORA_OP_BWD, 128, 64, 4, 8) + 4 * 64 * 2 + 64 * 4)
+    misaligned = D(0.1, 1, 2, 0x40004, 0x50000)
+    assert bw(ctypes.byref(w), X, X, 40, A, B, 8, 16.0, ctypes.byref(misaligned), None, None, dA,
+              dB, ws, needb, None) == EALIGN
     assert bw(ctypes.byref(w), X, X, 40, A, B, 8, 16.0, None, None, None, dA, dB, ws, needb,
               None) == ENULL
     assert bw(ctypes.byref(w), X, X, 40, A, B, 8, 16.0, ctypes.byref(ok), None, None, dA, dB, ws,

@@ -166,3 +166,40 @@ def test_dropout_empty_batch_and_extreme_parameters(orc):
     assert np.array_equal(bits16(Xk).reshape(70, 136), ref)
     assert np.array_equal(bits.cpu().numpy().view(np.uint32), _pack_keep(keep))
     _check_dropout(orc, (96, 192, 48, 8), 127, p=0.99)
+
+
+def _pack_rows(keep):
+    """keep [M, d] (0/1) -> words [M, d/32], bit k % 32 of word k / 32."""
+    M, d = keep.shape
+    w = np.zeros((M, d // 32), np.uint64)
+    for j in range(32):
+        w |= keep[:, j::32].astype(np.uint64) << np.uint64(j)
+    return w.astype(np.uint32)
+
+
+@pytest.mark.parametrize("shape", [(256, 1024, 300, 64), (4096, 4096, 4096, 64)])
+def test_dropout_saved_mask(orc, shape):
+    """The forward writes its mask into the caller's keep_rows / keep_cols
+    (equal to the oracle's mask in both layouts), and the backward that reads
+    them gives the same dX, dA and dB bit for bit as the backward that
+    regenerates the mask."""
+    d_out, d_in, M, r = shape
+    say(f"dropout saved mask: {shape}")
+    W, A, B, X, dY = _layer(d_out, d_in, M, r, 11)
+    w = q.qlora_quantize_nf4(W.to(DEV))
+    X, dY, A, B = X.to(DEV), dY.to(DEV), A.to(DEV), B.to(DEV)
+    drop = q.Dropout(P, seed=77, offset=5)
+    saved = drop.saved_mask(M, d_in, DEV)
+    T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    Y = q.qlora_linear_fwd_dropout(w, X, A, B, ALPHA, saved, T_save=T)
+    Y2 = q.qlora_linear_fwd_dropout(w, X, A, B, ALPHA, drop)
+    g_saved = q.qlora_linear_bwd_dropout(w, X, dY, A, B, ALPHA, saved, T_saved=T)
+    g_regen = q.qlora_linear_bwd_dropout(w, X, dY, A, B, ALPHA, drop, T_saved=T)
+    torch.cuda.synchronize()
+    keep = orc.dropout_keep(M, d_in, P, drop.seed, drop.offset)
+    assert np.array_equal(saved.keep_cols.cpu().numpy().view(np.uint32), _pack_keep(keep))
+    assert np.array_equal(saved.keep_rows.cpu().numpy().view(np.uint32), _pack_rows(keep))
+    assert np.array_equal(bits16(Y), bits16(Y2)), "saving the mask changed Y"
+    for a, b, name in zip(g_saved, g_regen, ("dX", "dA", "dB")):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), name
