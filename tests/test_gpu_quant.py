@@ -156,3 +156,24 @@ def test_quantize_many_refuses_bad_counts():
         q.qlora_quantize_nf4_many([W] * 9)
     with pytest.raises(ValueError):
         q.qlora_quantize_nf4_many([])
+
+
+def test_quantize_many_with_large_group_tree(orc):
+    """A list whose middle tensor has 11008 second-level groups (8192 x 22016,
+    the 65B down projection): its tree runs the global-memory levels between
+    the list's two launches.  Equal to single calls bit for bit, and the
+    small ragged neighbours equal the oracle."""
+    shapes = [(5, 192), (8192, 22016), (257, 1024)]
+    Ws = [inputs.weight(d_out, d_in, config=6, layer=1, device=DEV, proj=i)
+          for i, (d_out, d_in) in enumerate(shapes)]
+    say("quantize_many: list with an 11008-group tensor")
+    many = q.qlora_quantize_nf4_many(Ws)
+    for i, W in enumerate(Ws):
+        one = q.qlora_quantize_nf4(W)
+        torch.cuda.synchronize()
+        for name in ("codes", "scale_codes", "scale2", "scale_mean"):
+            assert torch.equal(getattr(many[i], name).view(torch.uint8),
+                               getattr(one, name).view(torch.uint8)), f"item {i} {name}"
+    for i in (0, 2):
+        ref, _, _ = oracle_quant(orc, Ws[i].cpu())
+        assert_quant_equal(many[i], ref)
