@@ -167,18 +167,21 @@ struct BwdPlan {
 
 // Token split of dA / dB: about QLORA_GRAM_TARGET_WGS workgroups (256
 // columns x one split each, one 64-column tile per wavefront); a split is a
-// multiple of 512 tokens (whole pairs of 64-token blocks, and partials of
-// the same size as with one split per 64 columns and 128 tokens per
-// wavefront).
+// multiple of QLORA_GRAM_SPLIT_TOKENS tokens (whole pairs of 64-token blocks).
+// Longer splits mean fewer FP32 partials for the finish to add: at 4096
+// tokens, four splits of 1024 measured faster overall than eight of 512.
 #ifndef QLORA_GRAM_TARGET_WGS
 #define QLORA_GRAM_TARGET_WGS 512
+#endif
+#ifndef QLORA_GRAM_SPLIT_TOKENS
+#define QLORA_GRAM_SPLIT_TOKENS 1024
 #endif
 int token_splits(int64_t M, int64_t N, int64_t r, int64_t* per) {
   (void)r;
   const int64_t cgroups = cdiv(N, 256);
   const int64_t ms = std::max<int64_t>(
-      1, std::min<int64_t>(cdiv(QLORA_GRAM_TARGET_WGS, cgroups), cdiv(M, 512)));
-  *per = round_up(cdiv(std::max<int64_t>(M, 1), ms), 512);
+      1, std::min<int64_t>(cdiv(QLORA_GRAM_TARGET_WGS, cgroups), cdiv(M, QLORA_GRAM_SPLIT_TOKENS)));
+  *per = round_up(cdiv(std::max<int64_t>(M, 1), ms), QLORA_GRAM_SPLIT_TOKENS);
   return (int)std::max<int64_t>(1, cdiv(M, *per));
 }
 
@@ -571,11 +574,18 @@ int bwd_impl(const qlora_nf4_t* q, const uint16_t* XA, const uint32_t* xmask,
                                       nullptr, 0, st));
     if (s) return s;
   }
-  // U = s dY B, through B^T so the contraction over d_out is contiguous
-  s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
-  if (s) return s;
+  // U = s dY B.  For large M with whole 16-byte pieces of dY's and B's rows,
+  // the K-split kernel stages B as stored; otherwise through B^T, so that
+  // the contraction over d_out is contiguous.  Same products, same bits.
+  const bool b_as_stored = M > kSmallM && d_out % 8 == 0 && r % 8 == 0 && aligned16(B);
+  if (!b_as_stored) {
+    s = hip_status(launch_transpose_bf16(B, d_out, r, p.bt, p.ldbt, st));
+    if (s) return s;
+  }
   {
-    RankRowsArgs ra{dY, p.bt, M, r, d_out, p.ldbt, sc, nullptr, p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
+    RankRowsArgs ra{dY, b_as_stored ? B : p.bt, M, r, d_out, b_as_stored ? r : p.ldbt, sc, nullptr,
+                    p.u_hl, p.rp, p.ut_hi, p.ut_lo, p.ldp};
+    ra.q_kn = b_as_stored;
     s = t_with_u ? hip_status(launch_rank_split(ra, p.r_part, st, &t_copy))
                  : rank_product(ra, p.r_part, st);
   }

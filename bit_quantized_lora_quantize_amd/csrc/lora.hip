@@ -222,6 +222,9 @@ __global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRo
   }
 }
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
 // ---------------------------------------------------------------------------
 // Large M, split over K: part[s][m][n] = sum over k in split s of P[m][k]
 // Q[n][k] (FP32), P [M][K], Q [N][ldq], N <= 16 NB.  Workgroup = 64 rows
@@ -232,18 +235,27 @@ __global__ __launch_bounds__(64 * rank_rows_waves<NB>()) void k_rank_rows(RankRo
 // from memory, one chunk ahead.  Rows past M or N and columns past the
 // split read as zero.  k_rank_finish adds the splits in order.  K and ldq
 // are multiples of 8 and P, Q 16-byte aligned (checked by the launcher).
+// QT: Q is given as stored [K][ldq] (element (n, k) at Q[k * ldq + n], as
+// the rank-r factor B [d_out][r] serves U = dY B); its chunk is staged in LDS
+// row k by row k and the MFMA operand (eight consecutive k of one column per
+// lane) comes from two transposing LDS reads.
+#ifndef QLORA_RANK_KC4
+#define QLORA_RANK_KC4 128
+#endif
 template <int NB>
-constexpr int rank_kc() { return NB <= 4 ? 128 : (NB <= 8 ? 64 : 32); }
+constexpr int rank_kc() { return NB <= 4 ? QLORA_RANK_KC4 : (NB <= 8 ? 64 : 32); }
 
-template <int NB, bool MASK>
+template <int NB, bool MASK, bool QT>
 __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __restrict__ part,
                                                    int64_t kper, int ks) {
   constexpr int KC = rank_kc<NB>();
   constexpr int NR = 16 * NB;                 // Q rows staged (zero past N)
-  constexpr int LQ = KC + 8;                  // LDS row, BF16 elements (16 B pad: conflict-free reads)
+  // LDS row, BF16 elements: [n][k] rows of KC (16 B pad: conflict-free
+  // reads), or with QT [k][n] rows of NR
+  constexpr int LQ = QT ? NR + 8 : KC + 8;
   constexpr int PIECES = NR * KC / 8 / 256;   // 16-byte Q pieces per thread per chunk
   constexpr int NS = KC / 32;                 // MFMA K slices per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2][NR * LQ];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][QT ? KC * LQ : NR * LQ];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int rb = blockIdx.x / ks, sp = blockIdx.x % ks;
@@ -254,19 +266,21 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
   const int nchunks = (int)((k_end - k_begin + KC - 1) / KC);
 
   const __amdgpu_buffer_rsrc_t rp = rank_rsrc(a.P + m0 * K, (a.M - m0) * K * 2);   // rows past M: zero
-  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(a.Q, a.N * a.ldq * 2);               // rows past N: zero
+  const __amdgpu_buffer_rsrc_t rq = rank_rsrc(a.Q, (QT ? K : a.N) * a.ldq * 2);   // rows past N: zero
   const uint32_t prow = (uint32_t)((16 * w + r16) * K);                             // element offset
   // MASK: keep words of P's rows (K / 32 per row), rows past M read as zero
   const __amdgpu_buffer_rsrc_t rm =
       rank_rsrc(MASK ? a.pmask + m0 * (K / 32) : nullptr, MASK ? (a.M - m0) * (K / 32) * 4 : 0);
   const uint32_t mrow = (uint32_t)((16 * w + r16) * (K / 32));
-  // Q pieces of this thread: row pr[u], 8 columns from pc[u] within the chunk
+  // Q pieces of this thread: LDS row qrow[u], 8 elements from qcol[u]
+  // (row n and chunk columns k, or with QT chunk row k and columns n)
   uint32_t qrow[PIECES], qcol[PIECES];
 #pragma unroll
   for (int u = 0; u < PIECES; ++u) {
     const int piece = threadIdx.x + 256 * u;
-    qrow[u] = (uint32_t)(piece / (KC / 8));
-    qcol[u] = (uint32_t)(8 * (piece % (KC / 8)));
+    constexpr int per_row = (QT ? NR : KC) / 8;
+    qrow[u] = (uint32_t)(piece / per_row);
+    qcol[u] = (uint32_t)(8 * (piece % per_row));
   }
   const uint32_t kend = (uint32_t)k_end;
 
@@ -274,8 +288,16 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
     const uint32_t kc0 = (uint32_t)(k_begin + (int64_t)c * KC);
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
-      const uint32_t col = kc0 + qcol[u];
-      const uint32_t off = col < kend ? (qrow[u] * (uint32_t)a.ldq + col) * 2 : 0x80000000u;
+      uint32_t off;
+      if (QT) {
+        // row k of Q as stored; columns past N read zero
+        const uint32_t k = kc0 + qrow[u];
+        off = (k < kend && qcol[u] < (uint32_t)a.N) ? (k * (uint32_t)a.ldq + qcol[u]) * 2
+                                                     : 0x80000000u;
+      } else {
+        const uint32_t col = kc0 + qcol[u];
+        off = col < kend ? (qrow[u] * (uint32_t)a.ldq + col) * 2 : 0x80000000u;
+      }
       qv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
 #pragma unroll
@@ -301,9 +323,22 @@ __global__ __launch_bounds__(256) void k_rank_part(RankRowsArgs a, float* __rest
     for (int j = 0; j < NS; ++j) {
       const u32x4 x = MASK ? keep8_bf16(xv[j], mk[j] >> (8 * g)) : xv[j];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[nb] = mfma16(x, *reinterpret_cast<const u32x4*>(&qs[buf][(16 * nb + r16) * LQ + 32 * j + 8 * g]),
-                         acc[nb]);
+      for (int nb = 0; nb < NB; ++nb) {
+        u32x4 qf;
+        if (QT) {
+          // lane group g reads rows k = 32 j + 8 g + (r16 / 4) (then + 4),
+          // columns 16 nb + 4 (r16 % 4) .. +4; lane r16 receives column
+          // 16 nb + r16 of the four rows
+          const uint16_t* pb = &qs[buf][(32 * j + 8 * g + (r16 >> 2)) * LQ + 16 * nb + 4 * (r16 & 3)];
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(pb));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(pb + 4 * LQ));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          qf = u32x4{l2.x, l2.y, h2.x, h2.y};
+        } else {
+          qf = *reinterpret_cast<const u32x4*>(&qs[buf][(16 * nb + r16) * LQ + 32 * j + 8 * g]);
+        }
+        acc[nb] = mfma16(x, qf, acc[nb]);
+      }
     }
   };
 
@@ -608,8 +643,6 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 // same time (mostly served by the compute unit's vector cache).
 // ---------------------------------------------------------------------------
 namespace {
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 constexpr int kGramRows = 64;                      // token rows per wavefront block
 constexpr int kGramLd = 80;                        // LDS row: 64 columns + pad (40 dwords, = 8 mod 32)
 constexpr int kGramWaveBytes = kGramRows * kGramLd * 2;
@@ -804,32 +837,70 @@ struct GramFinishArgs {
   int64_t N[2];
   int splits[2];
   int transposed[2];
-  int64_t begin1;   // first element index of problem 1
+  int begin1;   // first workgroup of problem 1
   int count;
   int64_t R;
 };
 
+// Finish of the token-split partials: out = sum_s part[s] (s ascending).
+// Workgroup = a tile of 32 rows (i < R) x 64 columns (c < N) of the [R][N]
+// partials; the wavefronts read whole 256-byte row pieces of every split.
+// out[i][c] is written the same way; the transposed out[c][i] (dB) goes
+// through LDS so that each wavefront writes runs of 32 consecutive i.
+constexpr int kGfTi = 32, kGfTc = 64;
+
 __global__ __launch_bounds__(256) void k_gram_finish(GramFinishArgs a) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int di = (a.count > 1 && idx >= a.begin1) ? 1 : 0;
-  if (di) idx -= a.begin1;
-  const int64_t N = a.N[di], count = a.R * N;
-  if (idx >= count) return;
-  const float* part = a.part[di];
+  __shared__ float tile[kGfTi][kGfTc + 1];
+  int wg = (int)blockIdx.x;
+  const int di = (a.count > 1 && wg >= a.begin1) ? 1 : 0;
+  if (di) wg -= a.begin1;
+  const int64_t N = a.N[di], R = a.R, count = R * N;
+  const int64_t ctiles = (N + kGfTc - 1) / kGfTc;
+  const int64_t i0 = (wg / ctiles) * kGfTi, c0 = (wg % ctiles) * kGfTc;
+  const float* __restrict__ part = a.part[di];
+  float* __restrict__ out = a.out[di];
   const int S = a.splits[di];
-  // splits added in order; four loads issued together
-  float acc = part[idx];
-  int s = 1;
-  for (; s + 4 <= S; s += 4) {
-    float v[4];
+  const int t = threadIdx.x;
+  const int64_t c = c0 + (t & 63);
+  constexpr int EU = kGfTi / 4;
+  constexpr int SG = 8;   // splits whose loads are issued together
+  float acc[EU];
+  int64_t e[EU];
+  bool ok[EU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = part[(int64_t)(s + u) * count + idx];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc = __fadd_rn(acc, v[u]);
+  for (int k = 0; k < EU; ++k) {
+    const int64_t i = i0 + (t >> 6) + 4 * k;
+    ok[k] = i < R && c < N;
+    e[k] = ok[k] ? i * N + c : 0;
   }
-  for (; s < S; ++s) acc = __fadd_rn(acc, part[(int64_t)s * count + idx]);
-  const int64_t i = idx / N, c = idx % N;
-  a.out[di][a.transposed[di] ? c * a.R + i : idx] = acc;
+  for (int s0 = 0; s0 < S; s0 += SG) {
+    float v[SG][EU];
+#pragma unroll
+    for (int j = 0; j < SG; ++j)
+#pragma unroll
+      for (int k = 0; k < EU; ++k)
+        v[j][k] = (ok[k] && s0 + j < S) ? part[(int64_t)(s0 + j) * count + e[k]] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < SG; ++j)
+#pragma unroll
+      for (int k = 0; k < EU; ++k)
+        if (s0 + j < S) acc[k] = (s0 + j == 0) ? v[j][k] : __fadd_rn(acc[k], v[j][k]);
+  }
+  if (!a.transposed[di]) {
+#pragma unroll
+    for (int k = 0; k < EU; ++k)
+      if (ok[k]) out[e[k]] = acc[k];
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < EU; ++k) tile[(t >> 6) + 4 * k][t & 63] = acc[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kGfTc / 8; ++k) {
+    const int ii = t & 31, cc = (t >> 5) + 8 * k;
+    const int64_t i = i0 + ii, cn = c0 + cc;
+    if (i < R && cn < N) out[cn * R + i] = tile[ii][cc];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -846,10 +917,14 @@ template <int NB>
 static hipError_t launch_rank_part_t(const RankRowsArgs& a, float* part, int64_t kper, int ks,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(((a.M + 63) / 64) * ks);
-  if (a.pmask)
-    hipLaunchKernelGGL((k_rank_part<NB, true>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+  if (a.pmask && a.q_kn)
+    hipLaunchKernelGGL((k_rank_part<NB, true, true>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+  else if (a.pmask)
+    hipLaunchKernelGGL((k_rank_part<NB, true, false>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+  else if (a.q_kn)
+    hipLaunchKernelGGL((k_rank_part<NB, false, true>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
   else
-    hipLaunchKernelGGL((k_rank_part<NB, false>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
+    hipLaunchKernelGGL((k_rank_part<NB, false, false>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
   return hipGetLastError();
 }
 
@@ -859,6 +934,11 @@ hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st,
   // other layouts take the one-pass kernel, which loads elements
   if (a.pmask && (a.K % 32 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15)))
     return hipErrorInvalidValue;   // keep bits: whole words per row, 16-byte rows
+  // Q as stored [K][ldq]: whole 16-byte pieces of its rows, and only this
+  // kernel takes that layout
+  if (a.q_kn && (a.N % 8 != 0 || a.ldq % 8 != 0 || a.K % 8 != 0 ||
+                 (reinterpret_cast<uintptr_t>(a.P) & 15) || (reinterpret_cast<uintptr_t>(a.Q) & 15)))
+    return hipErrorInvalidValue;
   if (a.K % 8 != 0 || a.ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15) ||
       (reinterpret_cast<uintptr_t>(a.Q) & 15)) {
     hipError_t e = launch_rank_rows(a, st);
@@ -1009,11 +1089,11 @@ hipError_t launch_grams(const GramProblem* p, int count, int64_t ldp, int64_t M,
     f.N[i] = p[i].N;
     f.splits[i] = p[i].splits;
     f.transposed[i] = p[i].transposed ? 1 : 0;
-    if (i == 1) f.begin1 = total;
-    total += R * p[i].N;
+    if (i == 1) f.begin1 = (int)total;
+    total += ((R + kGfTi - 1) / kGfTi) * ((p[i].N + kGfTc - 1) / kGfTc);
   }
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gram_finish, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, f);
+  hipLaunchKernelGGL(k_gram_finish, dim3((unsigned)total), dim3(256), 0, st, f);
   return hipGetLastError();
 }
 

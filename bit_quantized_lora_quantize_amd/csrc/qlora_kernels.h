@@ -187,6 +187,10 @@ struct RankRowsArgs {
   // [m * K / 32 + k / 32]; K a multiple of 32): P elements with bit 0 count as
   // zero.  Only launch_rank_split (k_rank_part) takes them.
   const uint32_t* pmask = nullptr;
+  // Q given as stored [K][ldq] (element (n, k) at Q[k * ldq + n]) instead of
+  // [N][ldq]: only launch_rank_split takes it, with N, ldq and K multiples
+  // of 8 and P, Q 16-byte aligned.
+  bool q_kn = false;
 };
 hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st);
 // The same product (same outputs) through K-split partials part
@@ -258,7 +262,7 @@ hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols,
 // (s ascending), out[c][i] if transposed else out[i][c].  P is given
 // transposed as a hi + lo BF16 pair in fragment order (frag_index, ldp >= M
 // a multiple of 16, round_up(R, 32) rows, zero-padded); Q BF16 [M][N]
-// (16-byte aligned); R <= 256; m_per_split a multiple of 512.  Up to two
+// (16-byte aligned); R <= 256; m_per_split a multiple of 128.  Up to two
 // problems with the same M, R and ldp run in one contraction launch and one
 // finish launch.
 struct GramProblem {

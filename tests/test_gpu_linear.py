@@ -68,6 +68,7 @@ SMALL = [  # (d_out, d_in, M, r)
     (96, 512, 129, 7),
     (72, 192, 70, 100),     # large-M rank path, r in (64, 128]
     (136, 256, 48, 256),    # large-M rank path at the maximum rank
+    (200, 256, 40, 128),    # large-M rank path, r in (64, 128], B read as stored
     (264, 320, 300, 40),    # two row tiles of the weight kernel, ragged in M and N
     (264, 320, 1100, 40),   # three 512-token tiles of the GEMM, ragged in M, N and K
 ]
@@ -121,6 +122,26 @@ def test_special_cases(orc):
     _, _, dB = q.qlora_linear_bwd(w, Xd, dYd, torch.zeros_like(A).to(DEV), B.to(DEV), ALPHA)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+
+
+@pytest.mark.parametrize("shape", [(264, 320, 300, 40), (200, 256, 40, 128),
+                                   (136, 256, 48, 256), (256, 512, 300, 16)])
+def test_u_from_b_as_stored_matches_transposed(orc, shape):
+    """For large M the backward's U = s dY B reads B as stored (whole 16-byte
+    pieces of its rows, transposing LDS reads) when B is 16-byte aligned, and
+    goes through a transposed copy of B otherwise: the same products, so the
+    same bits in dX, dA and dB."""
+    d_out, d_in, M, r = shape
+    W, A, B, X, dY = (t.to(DEV) for t in _layer(d_out, d_in, M, r, 73))
+    w = q.qlora_quantize_nf4(W)
+    buf = torch.zeros(B.numel() + 8, dtype=B.dtype, device=DEV)
+    Bu = buf[1:1 + B.numel()].view(d_out, r)   # 2 bytes past a 16-byte boundary
+    Bu.copy_(B)
+    assert B.data_ptr() % 16 == 0 and Bu.data_ptr() % 16 == 2
+    res = [q.qlora_linear_bwd(w, X, dY, A, Bx, ALPHA) for Bx in (B, Bu)]
+    torch.cuda.synchronize()
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
 
 
 def test_deterministic(orc):
