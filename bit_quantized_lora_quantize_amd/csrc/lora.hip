@@ -917,9 +917,7 @@ template <int NB>
 static hipError_t launch_rank_part_t(const RankRowsArgs& a, float* part, int64_t kper, int ks,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(((a.M + 63) / 64) * ks);
-  if (a.pmask && a.q_kn)
-    hipLaunchKernelGGL((k_rank_part<NB, true, true>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
-  else if (a.pmask)
+  if (a.pmask)
     hipLaunchKernelGGL((k_rank_part<NB, true, false>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
   else if (a.q_kn)
     hipLaunchKernelGGL((k_rank_part<NB, false, true>), dim3(grid), dim3(256), 0, st, a, part, kper, ks);
@@ -934,9 +932,9 @@ hipError_t launch_rank_split(const RankRowsArgs& a, float* part, hipStream_t st,
   // other layouts take the one-pass kernel, which loads elements
   if (a.pmask && (a.K % 32 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15)))
     return hipErrorInvalidValue;   // keep bits: whole words per row, 16-byte rows
-  // Q as stored [K][ldq]: whole 16-byte pieces of its rows, and only this
-  // kernel takes that layout
-  if (a.q_kn && (a.N % 8 != 0 || a.ldq % 8 != 0 || a.K % 8 != 0 ||
+  // Q as stored [K][ldq]: whole 16-byte pieces of its rows, only this kernel
+  // takes that layout, and not with keep bits (U = dY B has none)
+  if (a.q_kn && (a.pmask || a.N % 8 != 0 || a.ldq % 8 != 0 || a.K % 8 != 0 ||
                  (reinterpret_cast<uintptr_t>(a.P) & 15) || (reinterpret_cast<uintptr_t>(a.Q) & 15)))
     return hipErrorInvalidValue;
   if (a.K % 8 != 0 || a.ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(a.P) & 15) ||

@@ -189,7 +189,7 @@ struct RankRowsArgs {
   const uint32_t* pmask = nullptr;
   // Q given as stored [K][ldq] (element (n, k) at Q[k * ldq + n]) instead of
   // [N][ldq]: only launch_rank_split takes it, with N, ldq and K multiples
-  // of 8 and P, Q 16-byte aligned.
+  // of 8, P, Q 16-byte aligned and no keep bits.
   bool q_kn = false;
 };
 hipError_t launch_rank_rows(const RankRowsArgs& a, hipStream_t st);
