@@ -153,9 +153,13 @@ class KernelTimer:
         return out
 
     def __del__(self):
+        # through type(self): at interpreter exit the module's globals may be gone
+        hip = type(self)._hip
+        if hip is None:
+            return
         for _, s, e in getattr(self, "pairs", []):
-            KernelTimer._hip.hipEventDestroy(s)
-            KernelTimer._hip.hipEventDestroy(e)
+            hip.hipEventDestroy(s)
+            hip.hipEventDestroy(e)
 
 
 # ------------------------------------------------------------------ layers
