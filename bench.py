@@ -97,7 +97,8 @@ def gemm_source_sha1():
 
 
 def gemm_traffic():
-    return GEMM_TRAFFIC_BYTES if gemm_source_sha1() == GEMM_TRAFFIC_SHA1 else None
+    # counted at r = 64 on the GEMM sources of that SHA-1
+    return GEMM_TRAFFIC_BYTES if gemm_source_sha1() == GEMM_TRAFFIC_SHA1 and R == 64 else None
 
 
 def log(msg):
@@ -793,10 +794,14 @@ def main():
     ap.add_argument("--skip", default="", help="comma list of: dropout,decode,quant,blocked,merge,adamw,stack65b,peaks,cpu")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-stack-tokens", type=int, default=128)
+    ap.add_argument("--rank", type=int, default=64,
+                    help="LoRA rank r of every leg (the headline figure is quoted at 64)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MB (a plain copy "
                          "kernel of known size, for scaling hardware byte counters)")
     args = ap.parse_args()
+    global R
+    R = args.rank
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -850,7 +855,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama7b_layer_7proj_fwd_bwd_M4096_r64",
+        "config": {"workload": f"llama7b_layer_7proj_fwd_bwd_M4096_r{R}",
                    "tokens": 4096, "rank": R, "lora_alpha": ALPHA,
                    "projections": [f"{n} {o}x{i}" for n, o, i in inputs.LLAMA_7B],
                    "quant": "NF4 block 64 + FP8 E4M3FN double quant block 256",
