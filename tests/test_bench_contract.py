@@ -1,7 +1,7 @@
 """bench.py's command-line contract on the CPU: one GPU only (a request for
 more exits with status 2 and a message, before any device is touched), and
-the stored GEMM traffic figure is tied to the GEMM sources it was measured
-on."""
+the stored GEMM traffic figure is tied to the GEMM sources and the rank it
+was measured on."""
 import os
 import subprocess
 import sys
@@ -26,3 +26,13 @@ def test_traffic_figure_follows_the_gemm_sources(monkeypatch):
     assert bench.gemm_traffic() == bench.GEMM_TRAFFIC_BYTES
     monkeypatch.setattr(bench, "GEMM_TRAFFIC_SHA1", "0" * 40)
     assert bench.gemm_traffic() is None
+
+
+def test_traffic_figure_is_for_rank_64(monkeypatch):
+    """The stored counter figure was taken at r = 64: other ranks report none."""
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(bench, "R", 8)
+    assert bench.gemm_traffic() is None
+    monkeypatch.setattr(bench, "R", 64)
+    assert bench.gemm_traffic() == bench.GEMM_TRAFFIC_BYTES
