@@ -144,15 +144,21 @@ def test_u_from_b_as_stored_matches_transposed(orc, shape):
         assert torch.equal(x, y)
 
 
-def test_deterministic(orc):
-    d_out, d_in, M, r = 320, 1024, 16, 64
+@pytest.mark.parametrize("shape", [(320, 1024, 16, 64),      # weight-streaming forward
+                                   (264, 320, 1100, 40),     # K splits, token splits, ragged
+                                   (1024, 2048, 2200, 64)])  # several splits of every kind
+def test_deterministic(orc, shape):
+    """Split reductions add their partials in a fixed order: the same call
+    twice gives the same bits, on the small-M path and on the large-M one."""
+    d_out, d_in, M, r = shape
     W, A, B, X, dY = (t.to(DEV) for t in _layer(d_out, d_in, M, r, 72))
     w = q.qlora_quantize_nf4(W)
     outs = []
     for _ in range(2):
-        Y = q.qlora_linear_fwd(w, X, A, B, ALPHA)
+        T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+        Y = q.qlora_linear_fwd(w, X, A, B, ALPHA, T_save=T)
         dX, dA, dB = q.qlora_linear_bwd(w, X, dY, A, B, ALPHA)
-        outs.append((Y.clone(), dX.clone(), dA.clone(), dB.clone()))
+        outs.append((Y.clone(), T.clone(), dX.clone(), dA.clone(), dB.clone()))
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
